@@ -1,0 +1,283 @@
+"""Oracle for the MTP draft step, greedy verification and MTP-cache rollback.
+
+TEST INFRASTRUCTURE ONLY. This is a plain, slow CPU implementation written from
+the pages. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import it; the product library never does, and it
+shares no code with the HIP path (inputs come from ``mtp_synth`` only).
+
+Arithmetic is NumPy in float32 by default (``dt=np.float64`` re-runs the same
+steps in double precision). Matrices are row-major ``[out, in]``, ``y = W @ x``.
+
+Sources (page title, then section):
+  [SPEC]  speculators user guide, "MTP (Multi-Token Prediction)",
+          How It Works > Architecture; Step Weight Formula.
+  [OVMTP] devnotes, "How OpenVINO MTP Speculative Decoding Works Internally",
+          sections "The MTP inputs", "KV cache", "Stateful execution",
+          "Shared embeddings reduce duplication", "Correctness before performance".
+  [OVSD]  OpenVINO GenAI docs, "Speculative Decoding", Overview and
+          "Measuring Effectiveness".
+  [FI]    forceinjection, "MTP 深度解析", sections 4.2 (self-speculation) and
+          4.4 (chaining on the predicted token).
+
+Readings where the pages are silent (each is the plainest one the rest supports):
+  concat order: [RMSNorm(h); RMSNorm(e)], hidden first, as [SPEC] lists them.
+  recursion: the hidden state fed to step k+1 is the decoder-layer output before
+    the final norm; the final norm only feeds the lm_head.
+  token input: step 1 takes last_tokens, step k>1 the token drafted at step k-1.
+  positions: step k uses RoPE position pos+k-1 and writes cache slot len+k-1.
+  decoder layer: pre-norm residual blocks, no biases, no QK-norm, scale 1/sqrt(d),
+    causal over all cached slots including the new one, SwiGLU with silu(x)=x*sigmoid(x).
+  RMSNorm: x * (mean(x^2) + eps)^(-1/2) * g, eps from the config.
+  RoPE: rotate-half pairs (i, i+d/2), inv_freq_i = theta^(-2i/d); cos/sin are
+    evaluated in float64 from the integer position and rounded to float32.
+  argmax ties: the lowest vocabulary index wins.
+  new K/V entries are rounded to the cache dtype when they are written, and
+    attention reads them back from the cache.
+  verify: row j of the target logits scores the token after input j of
+    [last_token, d_1 .. d_K]; accepted_len counts accepted drafts (0..K);
+    next_token is the target's argmax at the first mismatch (row K if all match).
+  rollback: slot k (from the pair (h^(k-1), tok_{k-1})) is kept iff tok_{k-1}
+    was committed, so len advances by min(a+1, K) and pos by a+1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- dtypes
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even) and return it widened to float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = ((u + 0x7FFF + lsb) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def as_float(a: np.ndarray, storage: str, dt=np.float32) -> np.ndarray:
+    """Storage array (float32, or bf16 bits when storage == 'bf16') -> dt."""
+    if storage == "bf16":
+        return widen_bf16(a).astype(dt, copy=False)
+    return np.asarray(a, dtype=np.float32).astype(dt, copy=False)
+
+
+# ----------------------------------------------------------------------------- building blocks
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x * (mean(x^2) + eps)^(-1/2) * g.  [SPEC] Architecture:
+    the hidden state and the token embedding are each normalized separately."""
+    dt = x.dtype
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return (x / np.sqrt(ms + dt.type(eps))) * g
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x)."""
+    one = x.dtype.type(1)
+    return x / (one + np.exp(-x))
+
+
+def rope_tables(position: int, head_dim: int, theta: float, dt=np.float32):
+    """cos/sin of position * theta^(-2i/d), i < d/2, in float64, rounded to dt."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    ang = float(position) * inv_freq
+    return np.cos(ang).astype(dt), np.sin(ang).astype(dt)
+
+
+def rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate-half RoPE on the last axis: (x1, x2) -> (x1*c - x2*s, x2*c + x1*s)."""
+    h = x.shape[-1] // 2
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def gqa_attention(q: np.ndarray, kc: np.ndarray, vc: np.ndarray) -> np.ndarray:
+    """One query per head over T cached slots.
+
+    q [n_q, d]; kc, vc [n_kv, T, d]; query head h reads kv head h // (n_q / n_kv).
+    softmax(q.K^T / sqrt(d)) V per head.  -> [n_q, d]
+    """
+    n_q, d = q.shape
+    n_kv = kc.shape[0]
+    grp = n_q // n_kv
+    dt = q.dtype
+    out = np.empty_like(q)
+    scale = dt.type(1.0 / np.sqrt(d))
+    for h in range(n_q):
+        kk = kc[h // grp]
+        vv = vc[h // grp]
+        s = (kk @ q[h]) * scale
+        s = s - s.max()
+        p = np.exp(s)
+        p = p / p.sum()
+        out[h] = p @ vv
+    return out
+
+
+def argmax_lowest(x: np.ndarray) -> np.ndarray:
+    """argmax over the last axis; the lowest index wins ties (numpy's rule)."""
+    return np.argmax(x, axis=-1)
+
+
+# ----------------------------------------------------------------------------- weights
+
+class OracleWeights:
+    """The MTP head's weights widened to the oracle's arithmetic dtype once.
+
+    The embedding table stays in storage dtype; only gathered rows are widened.
+    """
+
+    def __init__(self, cfg, weights: dict, dt=np.float32):
+        self.cfg, self.dt = cfg, dt
+        self.storage = cfg.dtype
+        self.embed_store = weights["embed"]
+        self.w = {k: as_float(v, cfg.dtype, dt) for k, v in weights.items() if k != "embed"}
+
+    def embed_rows(self, tokens: np.ndarray) -> np.ndarray:
+        return as_float(self.embed_store[np.asarray(tokens, np.int64)], self.storage, self.dt)
+
+
+# ----------------------------------------------------------------------------- the draft step
+
+def draft(cfg, W: OracleWeights, hidden: np.ndarray, last_tokens: np.ndarray,
+          k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray, pos: np.ndarray,
+          K: int, force_tokens: np.ndarray | None = None) -> dict:
+    """K recursive MTP draft steps for every sequence.  [SPEC] Architecture; [FI] 4.4.
+
+    hidden [B, H] (storage dtype); last_tokens [B]; k_cache/v_cache [B, n_kv, S, d]
+    (storage dtype, updated in place with slots len..len+K-1); lens/pos [B] (returned
+    advanced by K). force_tokens [B, K]: step k+1 consumes force_tokens[:, k] instead
+    of the oracle's own draft (teacher forcing).
+
+    Returns draft_tokens [B, K], hidden_steps [K, B, H] (h^(k)), logits [K, B, V],
+    top1 / margin [K, B] (largest logit, and its gap to the second largest),
+    lens, pos.
+    """
+    dt = W.dt
+    w = W.w
+    B, H, V = hidden.shape[0], cfg.hidden, cfg.vocab
+    nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
+    eps = cfg.rms_eps
+    bf16_cache = cfg.dtype == "bf16"
+    lens = np.asarray(lens, np.int64).copy()
+    pos = np.asarray(pos, np.int64).copy()
+    h = as_float(hidden, cfg.dtype, dt)
+    tok = np.asarray(last_tokens, np.int64).copy()
+    drafts = np.zeros((B, K), np.int64)
+    hsteps = np.zeros((K, B, H), dt)
+    logits_all = np.zeros((K, B, V), dt)
+    top1 = np.zeros((K, B), dt)
+    margin = np.zeros((K, B), dt)
+    for k in range(K):
+        # Shared-embedding gather, separate RMSNorms, concat, 2H -> H projection.
+        e = W.embed_rows(tok)
+        hn = rmsnorm(h, w["g_h"], eps)
+        en = rmsnorm(e, w["g_e"], eps)
+        x = np.concatenate([hn, en], axis=1) @ w["w_eh"].T
+        # Standard pre-norm decoder layer: attention block.
+        a = rmsnorm(x, w["g_attn"], eps)
+        q = (a @ w["w_q"].T).reshape(B, nq, d)
+        kn = (a @ w["w_k"].T).reshape(B, nkv, d)
+        vn = (a @ w["w_v"].T).reshape(B, nkv, d)
+        o = np.zeros((B, nq, d), dt)
+        for b in range(B):
+            p = int(pos[b]) + k
+            slot = int(lens[b]) + k
+            cos, sin = rope_tables(p, d, cfg.rope_theta, dt)
+            qb = rope(q[b], cos, sin)
+            kb = rope(kn[b], cos, sin)
+            vb = vn[b]
+            if bf16_cache:
+                k_cache[b, :, slot, :] = _store_bf16(kb)
+                v_cache[b, :, slot, :] = _store_bf16(vb)
+            else:
+                k_cache[b, :, slot, :] = kb.astype(np.float32)
+                v_cache[b, :, slot, :] = vb.astype(np.float32)
+            kc = as_float(k_cache[b, :, :slot + 1, :], cfg.dtype, dt)
+            vc = as_float(v_cache[b, :, :slot + 1, :], cfg.dtype, dt)
+            o[b] = gqa_attention(qb, kc, vc)
+        x1 = x + o.reshape(B, nq * d) @ w["w_o"].T
+        # MLP block (SwiGLU).
+        m = rmsnorm(x1, w["g_mlp"], eps)
+        act = silu(m @ w["w_gate"].T) * (m @ w["w_up"].T)
+        x2 = x1 + act @ w["w_down"].T
+        # Final norm + shared lm_head + argmax.
+        lg = rmsnorm(x2, w["g_final"], eps) @ w["lm_head"].T
+        dk = argmax_lowest(lg)
+        srt = np.partition(lg, V - 2, axis=1)[:, V - 2:]
+        top1[k] = srt[:, 1]
+        margin[k] = srt[:, 1] - srt[:, 0]
+        drafts[:, k] = dk
+        hsteps[k] = x2
+        logits_all[k] = lg
+        # Recursion: the next step consumes this step's hidden state and token.
+        h = x2
+        tok = dk if force_tokens is None else np.asarray(force_tokens, np.int64)[:, k]
+    return {"draft_tokens": drafts, "hidden_steps": hsteps, "logits": logits_all,
+            "top1": top1, "margin": margin, "lens": lens + K, "pos": pos + K}
+
+
+def _store_bf16(x: np.ndarray) -> np.ndarray:
+    """float -> bfloat16 bit patterns (round to nearest even)."""
+    r = round_to_bf16(np.asarray(x, np.float32))
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------- verify / rollback
+
+def verify(target_logits: np.ndarray, draft_tokens: np.ndarray):
+    """Greedy verification.  [OVSD] Overview; [FI] 4.2.
+
+    target_logits [B, K+1, V]: row j scores the token after input j of
+    [last_token, d_1 .. d_K].  The target's token at row j is its argmax (lowest
+    index on ties).  Drafts are accepted while they equal the target's token;
+    the first divergent position (or row K when all K match) supplies the bonus
+    token.  Returns accepted_len [B] in 0..K and next_token [B].
+    """
+    t = np.asarray(target_logits)
+    d = np.asarray(draft_tokens, np.int64).reshape(t.shape[0], -1)
+    B, K = d.shape
+    g = argmax_lowest(t)
+    acc = np.zeros(B, np.int64)
+    nxt = np.zeros(B, np.int64)
+    for b in range(B):
+        a = 0
+        while a < K and d[b, a] == g[b, a]:
+            a += 1
+        acc[b] = a
+        nxt[b] = g[b, a]
+    return acc, nxt
+
+
+def kv_rollback(lens: np.ndarray, pos: np.ndarray, accepted_len: np.ndarray, K: int):
+    """Cut the MTP cache back to the committed prefix.  [OVMTP] Stateful execution;
+    [OVSD] Overview (drafting resumes after the first divergent token).
+
+    On entry lens/pos are the values after a K-step draft (advanced by K).
+    Slot k = 1..K came from the pair (h^(k-1), tok_{k-1}); it stays iff tok_{k-1}
+    was committed, i.e. k <= a + 1.  pos moves to the position of the last
+    verified input, a + 1 past the draft's starting position.
+    """
+    a = np.asarray(accepted_len, np.int64)
+    lens = np.asarray(lens, np.int64) - K + np.minimum(a + 1, K)
+    pos = np.asarray(pos, np.int64) - K + a + 1
+    return lens, pos
+
+
+def step_weights(beta: float, K: int) -> np.ndarray:
+    """Normalised exponential-decay step weights alpha_k = beta^(k-1) / sum_j beta^(j-1).
+    [SPEC] Step Weight Formula."""
+    num = np.array([beta ** (k - 1) for k in range(1, K + 1)], np.float64)
+    return num / num.sum()
+
+
+def tokens_per_iteration(accepted_len: np.ndarray) -> np.ndarray:
+    """Tokens emitted per target iteration: the accepted drafts plus the bonus token.
+    [OVSD] Measuring Effectiveness."""
+    return np.asarray(accepted_len, np.int64) + 1

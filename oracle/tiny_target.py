@@ -1,0 +1,103 @@
+"""A small synthetic verifier for end-to-end checks of speculative decoding.
+
+TEST INFRASTRUCTURE ONLY (same rules as ``mtp_oracle``).
+
+The target is a random causal decoder stack of the MTP head's shape that shares
+the head's token embedding and lm_head (devnotes, "How OpenVINO MTP Speculative
+Decoding Works Internally", "Shared embeddings reduce duplication"). Every call
+recomputes the whole prefix from scratch, so the logits for a given prefix are
+bit-identical however the prefix was reached; plain greedy decoding and greedy
+speculative decoding therefore must emit the same tokens (same page,
+"Correctness before performance").
+
+Its hidden state is the last decoder layer's output before the final norm, the
+residual-stream tensor that the MTP head consumes (same page, "hidden_states").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .mtp_oracle import (argmax_lowest, as_float, rmsnorm, rope, rope_tables, silu)
+
+
+class TinyTarget:
+    def __init__(self, cfg, tw: dict, embed: np.ndarray, lm_head: np.ndarray, dt=np.float32):
+        self.cfg, self.dt = cfg, dt
+        st = cfg.dtype
+        self.layers = [{k: as_float(v, st, dt) for k, v in lw.items()} for lw in tw["layers"]]
+        self.g_final = as_float(tw["g_final"], st, dt)
+        self.embed = as_float(embed, st, dt)
+        self.lm_head = as_float(lm_head, st, dt)
+
+    def forward(self, tokens) -> tuple[np.ndarray, np.ndarray]:
+        """tokens [n] -> (hidden [n, H] before the final norm, logits [n, V])."""
+        cfg, dt = self.cfg, self.dt
+        nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
+        grp = nq // nkv
+        t = np.asarray(tokens, np.int64)
+        n = t.shape[0]
+        x = self.embed[t]
+        tabs = [rope_tables(p, d, cfg.rope_theta, dt) for p in range(n)]
+        scale = dt(1.0 / np.sqrt(d))
+        for lw in self.layers:
+            a = rmsnorm(x, lw["g_attn"], cfg.rms_eps)
+            q = (a @ lw["w_q"].T).reshape(n, nq, d)
+            k = (a @ lw["w_k"].T).reshape(n, nkv, d)
+            v = (a @ lw["w_v"].T).reshape(n, nkv, d)
+            for p in range(n):
+                q[p] = rope(q[p], *tabs[p])
+                k[p] = rope(k[p], *tabs[p])
+            o = np.empty((n, nq, d), dt)
+            for h in range(nq):
+                kk, vv = k[:, h // grp, :], v[:, h // grp, :]
+                for p in range(n):
+                    s = (kk[:p + 1] @ q[p, h]) * scale
+                    s = s - s.max()
+                    w = np.exp(s)
+                    o[p, h] = (w / w.sum()) @ vv[:p + 1]
+            x = x + o.reshape(n, nq * d) @ lw["w_o"].T
+            m = rmsnorm(x, lw["g_mlp"], cfg.rms_eps)
+            x = x + (silu(m @ lw["w_gate"].T) * (m @ lw["w_up"].T)) @ lw["w_down"].T
+        logits = rmsnorm(x, self.g_final, cfg.rms_eps) @ self.lm_head.T
+        return x, logits
+
+    def next_token(self, tokens) -> int:
+        return int(argmax_lowest(self.forward(tokens)[1][-1]))
+
+    def greedy(self, prompt, n_new: int) -> list[int]:
+        """Plain greedy decoding: one full forward per emitted token."""
+        seq = [int(x) for x in prompt]
+        for _ in range(n_new):
+            seq.append(self.next_token(seq))
+        return seq[len(prompt):]
+
+
+def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_fn,
+                       rollback_fn, K: int):
+    """Greedy speculative decoding driven by a draft head.
+
+    draft_fn(hidden [H], last_token, K, committed) -> K draft tokens (the head keeps
+    its cache and advances it by K; committed is the sequence so far);
+    verify_fn(target_logits [K+1, V], drafts) -> (a, next); rollback_fn(a) cuts the head's cache back.  Target rows are the last-position
+    logits of full forwards over the committed prefix extended by j drafts.
+    Returns (emitted tokens, list of accepted lengths).
+    """
+    seq = [int(x) for x in prompt]
+    hid, lg = target.forward(seq)
+    seq.append(int(argmax_lowest(lg[-1])))
+    h = hid[-1]
+    accepted = []
+    while len(seq) - len(prompt) < n_new:
+        d = [int(x) for x in draft_fn(h, seq[-1], K, list(seq))]
+        rows, hids = [], []
+        for j in range(K + 1):
+            hj, lj = target.forward(seq + d[:j])
+            rows.append(lj[-1])
+            hids.append(hj[-1])
+        a, nxt = verify_fn(np.stack(rows), d)
+        a, nxt = int(a), int(nxt)
+        rollback_fn(a)
+        accepted.append(a)
+        seq += d[:a] + [nxt]
+        h = hids[a]
+    return seq[len(prompt):len(prompt) + n_new], accepted

@@ -1,0 +1,404 @@
+"""Pins for the oracle: it is checked against values the pages print, closed forms,
+library routines (torch, transformers), invariants and brute force — never against
+a retyped copy of itself.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import mtp_synth as S
+from oracle import mtp_oracle as O
+from oracle.tiny_target import TinyTarget, speculative_greedy
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_cfg(**kw):
+    base = dict(name="pin", cid=20, hidden=64, n_q=4, n_kv=2, head_dim=16, ffn=96, vocab=50,
+                batch=2, K=3, ctx_lo=5, ctx_hi=None, agree_lo=0.8, agree_hi=None, dtype="f32")
+    base.update(kw)
+    return S.Config(**base)
+
+
+# ----------------------------------------------------------------------------- step weights
+
+def test_step_weights_match_printed_values():
+    g = json.load(open(os.path.join(GOLDEN, "step_weights.json")))
+    a = O.step_weights(g["beta"], g["K"])
+    assert np.allclose(np.round(a, g["decimals"]), g["printed"], atol=0)
+
+
+def test_step_weights_closed_form():
+    # beta = 3/5: weights are 25/49, 15/49, 9/49.
+    assert np.allclose(O.step_weights(0.6, 3), [25 / 49, 15 / 49, 9 / 49], rtol=1e-14)
+    for beta, K in [(0.3, 5), (0.9, 7), (0.6, 1)]:
+        a = O.step_weights(beta, K)
+        assert abs(a.sum() - 1) < 1e-14 and np.all(np.diff(a) < 0) or K == 1
+        assert np.allclose(a[1:] / a[:-1], beta)
+    assert np.allclose(O.step_weights(1.0, 4), 0.25)
+
+
+# ----------------------------------------------------------------------------- verify
+
+def test_verify_golden_cases():
+    g = json.load(open(os.path.join(GOLDEN, "verify_cases.json")))
+    for c in g["cases"]:
+        t = np.array(c["logits"], np.float32)[None]
+        d = np.array(c["drafts"], np.int64).reshape(1, c["K"])
+        a, n = O.verify(t, d)
+        assert (int(a[0]), int(n[0])) == (c["accepted_len"], c["next_token"]), c["name"]
+
+
+def _verify_by_definition(t, d):
+    """Largest n <= K with d_i == argmax(row i-1) for every i <= n; bonus = argmax(row n)."""
+    K = len(d)
+    g = [int(np.flatnonzero(r == r.max())[0]) for r in t]
+    best = max(n for n in range(K + 1) if all(d[i] == g[i] for i in range(n)))
+    return best, g[best]
+
+
+def test_verify_brute_force_small_vocab():
+    rng = np.random.default_rng(1)
+    Vs, K = 5, 3
+    for trial in range(6):
+        t = rng.integers(0, 4, size=(K + 1, Vs)).astype(np.float32)  # integer logits: many ties
+        for d in itertools.product(range(Vs), repeat=K):
+            a, n = O.verify(t[None], np.array(d)[None])
+            assert (int(a[0]), int(n[0])) == _verify_by_definition(t, d)
+
+
+def test_verify_bounds_forced_agreement_and_k0():
+    rng = np.random.default_rng(2)
+    B, K, V = 7, 5, 300
+    d = rng.integers(0, V, size=(B, K))
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    a, n = O.verify(t, d)
+    tok = O.tokens_per_iteration(a)
+    assert np.all((tok >= 1) & (tok <= K + 1))
+    # Target forced to agree with every draft: all K accepted, K+1 tokens per iteration.
+    t2 = t.copy()
+    for b in range(B):
+        for j in range(K):
+            t2[b, j, d[b, j]] += 1e3
+    a2, n2 = O.verify(t2, d)
+    assert np.all(a2 == K) and np.all(O.tokens_per_iteration(a2) == K + 1)
+    assert np.all(n2 == np.argmax(t2[:, K], axis=1))
+    # K = 0: verification is the target's own greedy token of row 0.
+    a0, n0 = O.verify(t[:, :1], np.zeros((B, 0), np.int64))
+    assert np.all(a0 == 0) and np.all(n0 == np.argmax(t[:, 0], axis=1))
+
+
+@pytest.mark.parametrize("name,K,p,agree_hi,B,V,iters", [
+    ("tiny-like", 3, 0.8, None, 1, 4096, 2500),
+    ("b32-like", 3, 0.6, None, 32, 2048, 100),
+    ("q8b-like", 5, 0.9, None, 1, 4096, 2500),
+    ("q32b-like", 5, 0.5, 0.95, 8, 2048, 300),
+])
+def test_planted_acceptance_closed_form(name, K, p, agree_hi, B, V, iters):
+    """With planted agreement p per position, E[tokens / iteration] = 1 + sum_{n=1..K} p^n
+    (up to the 1/V chance agreement and the rare bump failure)."""
+    cfg = small_cfg(cid=30 + K, batch=B, vocab=V, K=K, agree_lo=p, agree_hi=agree_hi)
+    pb = S.agreement(cfg)
+    rng = np.random.default_rng(3)
+    tot = []
+    for it in range(iters):
+        d = rng.integers(0, V, size=(B, K))
+        t = S.plant_target_logits(cfg, d, it)
+        a, _ = O.verify(t, d)
+        tot.append(O.tokens_per_iteration(a))
+    tot = np.concatenate(tot).astype(np.float64)
+    expect = np.mean([1 + sum(q ** n for n in range(1, K + 1)) for q in pb])
+    se = tot.std() / math.sqrt(tot.size)
+    assert abs(tot.mean() - expect) < 4 * se + 2e-3, (tot.mean(), expect, se)
+
+
+# ----------------------------------------------------------------------------- building blocks
+
+def test_rmsnorm_and_silu_match_torch():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 256)).astype(np.float32) * 3
+    g = (1 + 0.02 * rng.standard_normal(256)).astype(np.float32)
+    ref = F.rms_norm(torch.from_numpy(x), (256,), torch.from_numpy(g), eps=1e-6).numpy()
+    assert np.max(np.abs(O.rmsnorm(x, g, 1e-6) - ref)) < 2e-6
+    ref = F.silu(torch.from_numpy(x)).numpy()
+    assert np.max(np.abs(O.silu(x) - ref)) < 2e-6
+
+
+def test_attention_matches_torch_sdpa_gqa():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    nq, nkv, d, T = 8, 2, 64, 37
+    q = rng.standard_normal((nq, d)).astype(np.float32)
+    k = rng.standard_normal((nkv, T, d)).astype(np.float32)
+    v = rng.standard_normal((nkv, T, d)).astype(np.float32)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        enable_gqa=True)[0, :, 0].numpy()
+    assert np.max(np.abs(O.gqa_attention(q, k, v) - ref)) < 2e-6
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((4, 16)).astype(np.float32)
+    k = rng.standard_normal((2, 1, 16)).astype(np.float32)
+    v = rng.standard_normal((2, 1, 16)).astype(np.float32)
+    o = O.gqa_attention(q, k, v)          # one slot: output is that slot's value
+    assert np.array_equal(o[:2], np.repeat(v[0], 2, 0)) and np.array_equal(o[2:], np.repeat(v[1], 2, 0))
+    k = np.repeat(rng.standard_normal((2, 1, 16)).astype(np.float32), 9, axis=1)
+    v = rng.standard_normal((2, 9, 16)).astype(np.float32)
+    o = O.gqa_attention(q, k, v)          # identical keys: uniform weights, mean of V
+    assert np.allclose(o[0], v[0].mean(0), atol=1e-6) and np.allclose(o[3], v[1].mean(0), atol=1e-6)
+
+
+def test_rope_invariants_and_transformers_tables():
+    d, theta = 128, 1e6
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, d)).astype(np.float64)
+    c0, s0 = O.rope_tables(0, d, theta, np.float64)
+    assert np.array_equal(O.rope(x, c0, s0), x)
+    for p1, p2 in [(1, 2), (17, 4096), (30000, 2768)]:
+        c1, s1 = O.rope_tables(p1, d, theta, np.float64)
+        c2, s2 = O.rope_tables(p2, d, theta, np.float64)
+        c3, s3 = O.rope_tables(p1 + p2, d, theta, np.float64)
+        y = O.rope(O.rope(x, c1, s1), c2, s2)
+        assert np.allclose(y, O.rope(x, c3, s3), atol=1e-9)
+        r = O.rope(x, c1, s1)
+        h = d // 2
+        assert np.allclose(r[:, :h] ** 2 + r[:, h:] ** 2, x[:, :h] ** 2 + x[:, h:] ** 2)
+    # Element i of the first half pairs with element i + d/2 at frequency theta^(-2i/d).
+    c, s = O.rope_tables(3, d, theta, np.float64)
+    assert np.isclose(c[0], math.cos(3.0)) and np.isclose(s[1], math.sin(3.0 * theta ** (-2 / d)))
+    torch = pytest.importorskip("torch")
+    tr = pytest.importorskip("transformers.models.llama.modeling_llama")
+    lc = tr.LlamaConfig(hidden_size=1024, num_attention_heads=8, head_dim=d, rope_theta=theta)
+    cos, sin = tr.LlamaRotaryEmbedding(lc)(torch.zeros(1, 1, 1), torch.tensor([[5, 100]]))
+    for i, p in enumerate([5, 100]):
+        c, s = O.rope_tables(p, d, theta)
+        assert np.allclose(cos[0, i, :h].numpy(), c, atol=2e-5)
+        assert np.allclose(sin[0, i, h:].numpy(), s, atol=2e-5)
+
+
+# ----------------------------------------------------------------------------- whole step
+
+def _inputs(cfg, cap=None):
+    return S.make_inputs(cfg, capacity=cap)
+
+
+def test_decoder_step_matches_transformers_llama_layer():
+    """Steps 3-9 of one draft step against transformers' Llama decoder layer (a standard
+    pre-norm GQA/RoPE/SwiGLU block with no biases) fed by torch's own RMSNorm / linear."""
+    torch = pytest.importorskip("torch")
+    tr = pytest.importorskip("transformers.models.llama.modeling_llama")
+    from transformers.cache_utils import DynamicCache
+    F = torch.nn.functional
+    cfg = S.get_config("tiny")
+    inp = _inputs(cfg, 140)
+    W = O.OracleWeights(cfg, inp.weights)
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    res = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, 1)
+
+    w = {k: torch.from_numpy(np.asarray(v, np.float32)) for k, v in inp.weights.items()}
+    H, L = cfg.hidden, int(inp.lens[0])
+    h = torch.from_numpy(inp.hidden.astype(np.float32))
+    e = w["embed"][torch.from_numpy(inp.last_tokens.astype(np.int64))]
+    cat = torch.cat([F.rms_norm(h, (H,), w["g_h"], 1e-6), F.rms_norm(e, (H,), w["g_e"], 1e-6)], 1)
+    x = F.linear(cat, w["w_eh"])
+    lc = tr.LlamaConfig(hidden_size=H, intermediate_size=cfg.ffn, num_attention_heads=cfg.n_q,
+                        num_key_value_heads=cfg.n_kv, head_dim=cfg.head_dim, rms_norm_eps=1e-6,
+                        rope_theta=cfg.rope_theta, attention_bias=False, mlp_bias=False,
+                        num_hidden_layers=1, vocab_size=cfg.vocab)
+    lc._attn_implementation = "eager"
+    layer = tr.LlamaDecoderLayer(lc, 0)
+    sd = {"self_attn.q_proj.weight": w["w_q"], "self_attn.k_proj.weight": w["w_k"],
+          "self_attn.v_proj.weight": w["w_v"], "self_attn.o_proj.weight": w["w_o"],
+          "mlp.gate_proj.weight": w["w_gate"], "mlp.up_proj.weight": w["w_up"],
+          "mlp.down_proj.weight": w["w_down"], "input_layernorm.weight": w["g_attn"],
+          "post_attention_layernorm.weight": w["g_mlp"]}
+    layer.load_state_dict(sd)
+    cache = DynamicCache(config=lc)
+    cache.update(torch.from_numpy(inp.k_cache[:, :, :L].copy()),
+                 torch.from_numpy(inp.v_cache[:, :, :L].copy()), 0)
+    P = int(inp.pos[0])
+    cos, sin = tr.LlamaRotaryEmbedding(lc)(x[None], torch.tensor([[P]]))
+    with torch.no_grad():
+        x2 = layer(x[None], position_ids=torch.tensor([[P]]), past_key_values=cache,
+                   use_cache=True, position_embeddings=(cos, sin))[0]
+        logits = F.linear(F.rms_norm(x2, (H,), w["g_final"], 1e-6), w["lm_head"])
+    assert np.max(np.abs(res["hidden_steps"][0] - x2.numpy())) < 1e-4
+    assert np.max(np.abs(res["logits"][0] - logits.numpy())) < 1e-4
+    newk = cache.layers[0].keys[0, :, L].numpy()
+    newv = cache.layers[0].values[0, :, L].numpy()
+    assert np.max(np.abs(kc[0, :, L] - newk)) < 1e-5 and np.max(np.abs(vc[0, :, L] - newv)) < 1e-6
+    assert int(res["draft_tokens"][0, 0]) == int(torch.argmax(logits[0]))
+
+
+def test_identity_projection_pins():
+    """W_eh = [I, 0] / [0, I] and zero W_o, W_d make the step's hidden output the
+    normalised verifier state / normalised embedding: pins the concat order, the
+    separate gains and both residual paths."""
+    cfg = small_cfg()
+    inp = _inputs(cfg, 20)
+    H = cfg.hidden
+    for half in (0, 1):
+        w = dict(inp.weights)
+        eye = np.zeros((H, 2 * H), np.float32)
+        eye[:, half * H:(half + 1) * H] = np.eye(H, dtype=np.float32)
+        w["w_eh"] = eye
+        w["w_o"] = np.zeros_like(w["w_o"])
+        w["w_down"] = np.zeros_like(w["w_down"])
+        W = O.OracleWeights(cfg, w)
+        r = O.draft(cfg, W, inp.hidden, inp.last_tokens, inp.k_cache.copy(), inp.v_cache.copy(),
+                    inp.lens, inp.pos, 1)
+        src = inp.hidden if half == 0 else w["embed"][inp.last_tokens]
+        g = w["g_h"] if half == 0 else w["g_e"]
+        ms = np.mean(src.astype(np.float64) ** 2, axis=1, keepdims=True)
+        expect = src / np.sqrt(ms + 1e-6) * g
+        assert np.max(np.abs(r["hidden_steps"][0] - expect)) < 1e-5
+
+
+def test_recursion_consumes_previous_token_and_hidden():
+    """Step k+1 equals a fresh 1-step draft started from (h^(k), d_k) at pos+k, len+k."""
+    cfg = small_cfg()
+    inp = _inputs(cfg, 20)
+    W = O.OracleWeights(cfg, inp.weights)
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, 3)
+    kc2, vc2 = inp.k_cache.copy(), inp.v_cache.copy()
+    r1 = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc2, vc2, inp.lens, inp.pos, 1)
+    r2 = O.draft(cfg, W, r1["hidden_steps"][0], r1["draft_tokens"][:, 0], kc2, vc2,
+                 r1["lens"], r1["pos"], 2)
+    assert np.array_equal(r["draft_tokens"][:, 1:], r2["draft_tokens"])
+    assert np.allclose(r["hidden_steps"][1:], r2["hidden_steps"], atol=1e-6)
+    assert np.array_equal(kc, kc2)
+
+
+def test_fp64_rerun_bounds_oracle_rounding():
+    cfg = S.get_config("tiny")
+    inp = _inputs(cfg, 140)
+    r32 = O.draft(cfg, O.OracleWeights(cfg, inp.weights), inp.hidden, inp.last_tokens,
+                  inp.k_cache.copy(), inp.v_cache.copy(), inp.lens, inp.pos, 3,
+                  force_tokens=None)
+    r64 = O.draft(cfg, O.OracleWeights(cfg, inp.weights, np.float64), inp.hidden, inp.last_tokens,
+                  inp.k_cache.copy(), inp.v_cache.copy(), inp.lens, inp.pos, 3,
+                  force_tokens=r32["draft_tokens"])
+    assert np.max(np.abs(r32["hidden_steps"] - r64["hidden_steps"])) < 1e-5
+    assert np.max(np.abs(r32["logits"] - r64["logits"])) < 1e-5
+
+
+def test_rollback_is_truncation():
+    """Drafting K steps then rolling back to accepted length a leaves the cache state a
+    min(a+1, K)-step draft would have left; pos moves to the last verified input."""
+    cfg = small_cfg(K=4)
+    inp = _inputs(cfg, 30)
+    W = O.OracleWeights(cfg, inp.weights)
+    K = 4
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, K)
+    for a in range(K + 1):
+        acc = np.full(cfg.batch, a)
+        ln, ps = O.kv_rollback(r["lens"], r["pos"], acc, K)
+        assert np.all(ln - inp.lens == min(a + 1, K)) and np.all(ps - inp.pos == a + 1)
+        kt, vt = inp.k_cache.copy(), inp.v_cache.copy()
+        rt = O.draft(cfg, W, inp.hidden, inp.last_tokens, kt, vt, inp.lens, inp.pos, min(a + 1, K))
+        assert np.array_equal(rt["lens"], ln)
+        for b in range(cfg.batch):
+            assert np.array_equal(kc[b, :, :ln[b]], kt[b, :, :ln[b]])
+            assert np.array_equal(vc[b, :, :ln[b]], vt[b, :, :ln[b]])
+    ln0, ps0 = O.kv_rollback(inp.lens, inp.pos, np.zeros(cfg.batch), 0)
+    assert np.array_equal(ln0, inp.lens) and np.array_equal(ps0, inp.pos + 1)
+
+
+def test_poisoned_stale_slots_do_not_leak():
+    cfg = small_cfg()
+    inp = _inputs(cfg, 20)
+    W = O.OracleWeights(cfg, inp.weights)
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    for b in range(cfg.batch):
+        kc[b, :, inp.lens[b]:] = np.nan
+        vc[b, :, inp.lens[b]:] = np.nan
+    r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, 3)
+    r0 = O.draft(cfg, W, inp.hidden, inp.last_tokens, inp.k_cache.copy(), inp.v_cache.copy(),
+                 inp.lens, inp.pos, 3)
+    assert np.all(np.isfinite(r["hidden_steps"]))
+    assert np.array_equal(r["hidden_steps"], r0["hidden_steps"])
+
+
+def test_bf16_cache_entries_are_rounded_on_write():
+    cfg = small_cfg(dtype="bf16")
+    inp = _inputs(cfg, 20)
+    W = O.OracleWeights(cfg, inp.weights)
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, 2)
+    assert kc.dtype == np.uint16
+    w = O.OracleWeights(cfg, inp.weights, np.float64)
+    r64 = O.draft(cfg, w, inp.hidden, inp.last_tokens, inp.k_cache.copy(), inp.v_cache.copy(),
+                  inp.lens, inp.pos, 2, force_tokens=r["draft_tokens"])
+    assert np.max(np.abs(r["hidden_steps"] - r64["hidden_steps"])) < 2e-3
+
+
+# ----------------------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("vocab,cache_len", [(4096, 0), (8, 0), (8, 8)])
+def test_speculative_equals_greedy(vocab, cache_len):
+    """Greedy speculative decoding with the oracle head emits exactly the target's plain
+    greedy tokens (a tiny random 2-layer target sharing E and W_lm with the head)."""
+    cfg = small_cfg(cid=40 + vocab + cache_len, batch=1, vocab=vocab, ctx_lo=cache_len, K=3)
+    inp = _inputs(cfg, 256)
+    W = O.OracleWeights(cfg, inp.weights)
+    tgt = TinyTarget(cfg, S.target_weights(cfg, 2), inp.weights["embed"], inp.weights["lm_head"])
+    prompt = S.prompt_tokens(cfg, 6)
+    n_new = 40
+    ref = tgt.greedy(prompt, n_new)
+    st = {"kc": inp.k_cache.copy(), "vc": inp.v_cache.copy(),
+          "len": np.array([cache_len]), "pos": np.array([len(prompt) - 1])}
+
+    def draft_fn(h, last, K, _seq):
+        r = O.draft(cfg, W, np.asarray(h, np.float32)[None], np.array([last]), st["kc"], st["vc"],
+                    st["len"], st["pos"], K)
+        st["len"], st["pos"] = r["lens"], r["pos"]
+        return r["draft_tokens"][0]
+
+    def rollback_fn(a):
+        st["len"], st["pos"] = O.kv_rollback(st["len"], st["pos"], np.array([a]), 3)
+
+    def verify_fn(rows, d):
+        a, n = O.verify(rows[None], np.asarray(d)[None])
+        return a[0], n[0]
+
+    out, acc = speculative_greedy(tgt, prompt, n_new, draft_fn, verify_fn, rollback_fn, 3)
+    assert out == ref
+    assert all(0 <= a <= 3 for a in acc)
+
+
+def test_speculative_equals_greedy_with_scripted_drafts():
+    """A drafter that proposes the target's own greedy continuation with one planted
+    error at index i (or none) must be accepted for exactly i tokens, and the output
+    must still equal plain greedy decoding."""
+    cfg = small_cfg(cid=60, batch=1, vocab=16, K=4)
+    inp = _inputs(cfg, 64)
+    tgt = TinyTarget(cfg, S.target_weights(cfg, 2), inp.weights["embed"], inp.weights["lm_head"])
+    prompt = S.prompt_tokens(cfg, 5)
+    ref = tgt.greedy(prompt, 30)
+    K = 4
+    it = {"n": 0}
+
+    def draft_fn(h, last, K_, seq):
+        cont = tgt.greedy(seq, K_)
+        bad = it["n"] % (K_ + 1)
+        it["n"] += 1
+        if bad < K_:
+            cont[bad] = (cont[bad] + 1) % cfg.vocab
+        return cont
+
+    def verify_fn(rows, d):
+        a, n = O.verify(rows[None], np.asarray(d)[None])
+        return a[0], n[0]
+
+    out, acc = speculative_greedy(tgt, prompt, 30, draft_fn, verify_fn, lambda a: None, K)
+    assert out == ref
+    assert acc == [i % (K + 1) for i in range(len(acc))]
