@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the MTP draft / verify / rollback path on one MI355X.
+
+One step = one speculative iteration over the batch: K recursive draft steps
+(mtp_draft), greedy verification against target logits (mtp_verify) and the MTP
+cache rollback (mtp_kv_rollback). Inputs are seeded and synthetic. The target
+logits of every iteration are planted from the drafts of an untimed recording
+pass and are resident in HBM before the timed pass replays the identical chain
+(the kernels are deterministic; the replay is checked against the recording).
+
+Prints one JSON line: draft-steps/s (value), verified tokens/s, the HBM roofline
+fraction of the whole iteration and of the lm_head kernel (HIP events on the
+library's stream), and the oracle timed on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MTP draft-steps/s + verified tok/s at 1 GPU; % of HBM roofline"
+LMHEAD_BIT = 1 << 6
+DESCR = {
+    "tiny": "tiny fp32 MTP head: H=256, 4/2 heads x 64, FFN 768, V=4096, B=1, L=128, K=3",
+    "q8b": "Qwen3-8B-shaped MTP head, bf16: H=4096, 32/8 heads x 128, FFN 12288, V=151936, "
+           "B=1, KV context 4096, K=5, planted agreement 0.9",
+    "q8b-b32": "Qwen3-8B-shaped MTP head, bf16, B=32 ragged KV context U{512..8192}, K=3, "
+               "planted agreement 0.6",
+    "q32b": "Qwen3-32B-shaped MTP head, bf16: H=5120, 64/8 heads x 128, FFN 25600, V=151936, "
+            "B=8, KV context 32768, K=5",
+    "wide": "wide dense MTP head, bf16: H=7168, 56/8 heads x 128, FFN 18432, V=129280, B=64, "
+            "KV context 4096, K=1",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, lens0, K: int, acc_sum_rows: int) -> dict:
+    """Bytes one iteration must move at least: every weight once per draft step, the
+    gathered embedding rows, the KV cache read (including the new slot) and written,
+    and the target-logit rows verification needs."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    H, F, V, d = cfg.hidden, cfg.ffn, cfg.vocab, cfg.head_dim
+    qd, kvd = cfg.n_q * d, cfg.n_kv * d
+    B = cfg.batch
+    w_layer = (2 * H * H + qd * H + 2 * kvd * H + H * qd + 3 * F * H + 5 * H) * s
+    lm = V * H * s
+    per_step_w = w_layer + lm
+    kv_read = sum(2 * kvd * (int(L) + k + 1) * s for L in lens0 for k in range(K))
+    kv_write = B * K * 2 * kvd * s
+    emb = B * K * H * s
+    io = B * H * s + B * 4 * (2 + K)
+    verify = acc_sum_rows * V * 4
+    return {"per_step_weights": per_step_w, "lm_head": lm + H * s + B * H * 4 + B * 8,
+            "iteration": K * per_step_w + kv_read + kv_write + emb + io + verify}
+
+
+def cpu_baseline(cfg, inp, K: int, reps: int = 3) -> dict:
+    """The oracle (plain NumPy) on the host cores: one speculative iteration of the same
+    workload (K draft steps + verify + rollback), 1 warm-up then the median of `reps`."""
+    import numpy as np
+
+    import mtp_synth as S
+    from oracle import mtp_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    W = O.OracleWeights(cfg, inp.weights)
+    times = []
+    for rep in range(reps + 1):
+        kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+        t0 = time.perf_counter()
+        r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, K)
+        t1 = time.perf_counter()
+        tl = S.plant_target_logits(cfg, r["draft_tokens"], 0)
+        t2 = time.perf_counter()
+        a, n = O.verify(tl, r["draft_tokens"])
+        O.kv_rollback(r["lens"], r["pos"], a, K)
+        t3 = time.perf_counter()
+        if rep:
+            times.append((t1 - t0) + (t3 - t2))
+        log(f"cpu oracle iteration {rep}: {(t1 - t0) + (t3 - t2):.2f} s")
+    t = statistics.median(times)
+    return {"value": round(K / t, 4), "unit": "draft-steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} timed iterations (after 1 warm-up) of {K} draft steps + verify "
+                      f"+ rollback for the same workload, median {t:.3f} s per iteration; "
+                      f"float32 NumPy, {cores} BLAS threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="q8b", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="extra untimed pass with HIP events around every kernel class")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+                                   "(the path shards by sequence with no exchange step)"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mtp_synth as S
+    from mtp_self_speculative_amd import MtpCache, MtpHead
+
+    dev = torch.device("cuda:0")
+    cfg = S.get_config(args.config)
+    B, K = cfg.batch, cfg.K
+    iters = args.warmup + args.steps
+    lens0 = S.cache_lengths(cfg)
+    cap = int(lens0.max()) + (iters + 2) * K + 8
+    t0 = time.time()
+    inp = S.make_inputs(cfg, capacity=cap)
+    log(f"generated {args.config} inputs in {time.time() - t0:.1f} s")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    w = {k: up(v) for k, v in inp.weights.items()}
+    head = MtpHead(hidden=cfg.hidden, n_q_heads=cfg.n_q, n_kv_heads=cfg.n_kv,
+                   head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, weights=w, max_batch=B,
+                   max_k=K, max_capacity=cap, rope_theta=cfg.rope_theta, rms_eps=cfg.rms_eps,
+                   dtype=tdt)
+    cache = MtpCache(up(inp.k_cache), up(inp.v_cache), torch.from_numpy(inp.lens).to(dev),
+                     torch.from_numpy(inp.pos).to(dev))
+    hidden = torch.stack([up(S.hidden_states(cfg, it)) for it in range(iters)])
+    last0 = torch.from_numpy(inp.last_tokens).to(dev)
+    len0, pos0 = cache.len.clone(), cache.pos.clone()
+    drafts = torch.empty((iters, B, K), dtype=torch.int32, device=dev)
+    acc = torch.empty((iters, B), dtype=torch.int32, device=dev)
+    nxt = torch.empty((iters, B), dtype=torch.int32, device=dev)
+    log("inputs resident on the device")
+
+    # Recording pass: plant each iteration's target logits from the drafts it produced.
+    logits = []
+    last = last0
+    for it in range(iters):
+        head.draft(hidden[it], last, cache, K, out=drafts[it])
+        tl = S.plant_target_logits(cfg, drafts[it].cpu().numpy(), it)
+        logits.append(torch.from_numpy(tl).to(dev))
+        head.verify(logits[it], drafts[it], acc[it], nxt[it])
+        head.rollback(cache, acc[it], K)
+        last = nxt[it]
+    torch.cuda.synchronize()
+    rec_drafts, rec_acc = drafts.clone(), acc.clone()
+    assert head.get_error() == 0
+    log("recording pass done")
+
+    def run(it, last):
+        head.draft(hidden[it], last, cache, K, out=drafts[it])
+        head.verify(logits[it], drafts[it], acc[it], nxt[it])
+        head.rollback(cache, acc[it], K)
+        return nxt[it]
+
+    def replay(mask: int):
+        cache.len.copy_(len0)
+        cache.pos.copy_(pos0)
+        last = last0
+        head.set_profiling(0)
+        for it in range(args.warmup):
+            last = run(it, last)
+        torch.cuda.synchronize()
+        head.set_profiling(mask)
+        t0 = time.perf_counter()
+        for it in range(args.warmup, iters):
+            last = run(it, last)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        head.set_profiling(0)
+        return t1 - t0, head.get_profile()
+
+    elapsed, prof = replay(LMHEAD_BIT)
+    if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
+        raise RuntimeError("timed replay diverged from the recording pass")
+    log(f"timed pass: {args.steps} iterations in {elapsed * 1e3:.2f} ms")
+
+    kernel_us = None
+    if args.breakdown:
+        _, bprof = replay((1 << 9) - 1)
+        kernel_us = {k: round(ms * 1e3 / n, 2) for k, (ms, n) in bprof.items() if n}
+        log(f"per-kernel us/launch: {kernel_us}")
+
+    acc_np = acc[args.warmup:].cpu().numpy().astype(np.int64)
+    tokens = int((acc_np + 1).sum())
+    rows = int((acc_np + 1).sum())
+    ab = algorithmic_bytes(cfg, lens0, K, rows // max(1, args.steps))
+    it_s = elapsed / args.steps
+    lm_ms, lm_n = prof["lm_head_argmax"]
+    lm_avg_s = lm_ms / 1e3 / lm_n
+    lm_gbs = ab["lm_head"] / lm_avg_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(K * args.steps / elapsed, 3),
+        "unit": "draft-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(it_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": DESCR[args.config], "name": args.config, "batch": B, "K": K},
+        "verified_tok_per_s": round(tokens / elapsed, 2),
+        "tokens_per_iteration": round(tokens / (args.steps * B), 4),
+        "hbm_roofline_frac": round(ab["iteration"] / it_s / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_iteration": int(ab["iteration"]),
+        "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
+                     "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n,
+                     "algorithmic_bytes_per_launch": int(ab["lm_head"])},
+    }
+    if kernel_us:
+        out["kernel_us_per_launch"] = kernel_us
+    head.close()
+    del w, cache, hidden, logits
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, K)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,193 @@
+/*
+ * mtp.h — C ABI of the MI355X (gfx950) Multi-Token-Prediction draft / verify / rollback path.
+ *
+ * One MTP draft step (speculators user guide, "MTP (Multi-Token Prediction)",
+ * How It Works > Architecture): the verifier's hidden state and the shared token
+ * embedding are RMS-normalised separately, concatenated, projected 2H -> H, run
+ * through one standard decoder layer (attention over the MTP layer's own
+ * single-layer KV cache + SwiGLU MLP), and a final norm plus the shared lm_head
+ * gives the draft token by argmax. The layer output feeds the next step, K times.
+ * Greedy verification (OpenVINO GenAI docs, "Speculative Decoding", Overview)
+ * accepts the longest prefix of drafts that the target's own argmax tokens
+ * reproduce and takes the target's token at the first mismatch as the bonus.
+ * The MTP cache is then cut back to the committed prefix (devnotes, "How
+ * OpenVINO MTP Speculative Decoding Works Internally", "Stateful execution").
+ *
+ * Conventions
+ *  - Every pointer argument that names a tensor is DEVICE memory owned by the
+ *    caller. The library keeps no reference past a call, except the weight
+ *    pointers, which must stay valid and unchanged for the handle's lifetime.
+ *  - Matrices are row-major [out, in]; y = W x. Weights, gains, embedding,
+ *    hidden states and the KV cache use the configuration's dtype
+ *    (MTP_F32: float, MTP_BF16: bfloat16 bit patterns). Accumulation is fp32.
+ *  - `stream` is a hipStream_t passed as void*. NULL means the default stream.
+ *    The three hot calls only enqueue work on it: no host synchronisation and
+ *    no device-to-host copy. Calls on one handle must be ordered on one stream.
+ *  - Argument problems that the host can see are reported synchronously, before
+ *    anything is enqueued. Conditions only the device can see (a token id
+ *    outside [0, vocab), a cache that would overflow its capacity, an accepted
+ *    length outside [0, K]) set a device error word and the kernels stay in
+ *    bounds (clamping the offending value); mtp_get_error() reports it.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef MTP_H
+#define MTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_INVALID_ARG = 1, /* null pointer, null handle, bad enum value            */
+  MTP_ERR_SHAPE = 2,       /* inconsistent or non-positive dimensions               */
+  MTP_ERR_DTYPE = 3,       /* unknown dtype                                         */
+  MTP_ERR_CAPACITY = 4,    /* B > max_batch, K > max_k, workspace or cache too small */
+  MTP_ERR_UNSUPPORTED = 5, /* a shape the kernels do not handle (see mtp_create)     */
+  MTP_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed             */
+  MTP_ERR_DEVICE = 7       /* the device error word was set (see mtp_get_error)      */
+} mtp_status;
+
+typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
+
+/* Device error-word bits reported by mtp_get_error(). */
+#define MTP_DEVERR_TOKEN 1u    /* a last_tokens entry was outside [0, vocab)            */
+#define MTP_DEVERR_CAPACITY 2u /* len + K exceeded the cache capacity                   */
+#define MTP_DEVERR_ACCEPT 4u   /* an accepted_len entry was outside [0, K]              */
+
+/* Shape of the MTP head. rope_theta: RoPE base; rms_eps: RMSNorm epsilon. */
+typedef struct {
+  int32_t hidden;     /* H                                            */
+  int32_t n_q_heads;  /* query heads                                  */
+  int32_t n_kv_heads; /* key/value heads (n_q_heads % n_kv_heads == 0) */
+  int32_t head_dim;   /* d: 64 or 128                                  */
+  int32_t ffn;        /* SwiGLU inner size F                          */
+  int32_t vocab;      /* V, shared with the verifier                  */
+  float rope_theta;
+  float rms_eps;
+  int32_t dtype;      /* mtp_dtype                                    */
+} mtp_config;
+
+/*
+ * Weights (device pointers, configuration dtype, row-major [out, in]):
+ *   g_h, g_e      [H]        gains of the two separate input RMSNorms (hidden, embedding)
+ *   w_eh          [H, 2H]    projection of concat(norm(h), norm(e)); columns 0..H-1 take norm(h)
+ *   g_attn        [H]        pre-attention RMSNorm gain
+ *   w_q           [n_q*d, H], w_k, w_v [n_kv*d, H], w_o [H, n_q*d]
+ *   g_mlp         [H]        pre-MLP RMSNorm gain
+ *   w_gate, w_up  [F, H],    w_down [H, F]
+ *   g_final       [H]        final RMSNorm gain (feeds the lm_head only)
+ *   embed         [V, H]     the verifier's token embedding (read-only, shared)
+ *   lm_head       [V, H]     the verifier's output projection (read-only, shared)
+ */
+typedef struct {
+  const void *g_h, *g_e, *w_eh, *g_attn, *w_q, *w_k, *w_v, *w_o, *g_mlp, *w_gate, *w_up, *w_down,
+      *g_final, *embed, *lm_head;
+} mtp_weights;
+
+/*
+ * The MTP layer's own single-layer cache (devnotes page, "KV cache").
+ *   k, v  [batch, n_kv, capacity, d] configuration dtype; keys are stored after RoPE.
+ *   len   [batch] int32 device: valid slots per sequence (slots 0..len-1 are attended).
+ *   pos   [batch] int32 device: RoPE position of the hidden state handed to the next draft.
+ */
+typedef struct {
+  void *k, *v;
+  int32_t *len, *pos;
+  int32_t batch, capacity;
+} mtp_kv;
+
+typedef struct mtp_handle mtp_handle;
+
+/* Bytes of device workspace a handle needs for up to max_batch sequences, up to
+ * max_k steps per call and caches of up to max_capacity slots. Host only. */
+mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
+                              int32_t max_capacity, size_t* bytes);
+
+/* Create a handle. `workspace` is caller-owned device memory of at least
+ * mtp_workspace_size() bytes, 256-byte aligned, used only by this handle; it is
+ * zeroed here (synchronously). Supported shapes: head_dim 64 or 128,
+ * n_q_heads / n_kv_heads <= 8, hidden and ffn multiples of 8, max_k <= 100.
+ * On success *out receives the handle; on failure *out is NULL. */
+mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
+                      int32_t max_k, int32_t max_capacity, void* workspace, size_t workspace_bytes,
+                      mtp_handle** out);
+
+/*
+ * K recursive draft steps for B sequences (speculators page, Architecture;
+ * forceinjection "MTP 深度解析", 4.4: each step consumes the token drafted before it).
+ *   hidden       [B, H] config dtype: verifier hidden state at position pos[b]
+ *   last_tokens  [B] int32: the latest committed token (input of step 1)
+ *   kv           cache; step k (1-based) writes slot len[b]+k-1 at RoPE position pos[b]+k-1
+ *                and attends over slots 0..len[b]+k-1. On return len and pos are advanced by K.
+ *   draft_tokens [B, K] int32 output.
+ * 0 <= K <= max_k (K = 0 enqueues nothing), 1 <= B <= min(max_batch, kv->batch),
+ * kv->capacity <= max_capacity. Must be followed by exactly one mtp_kv_rollback with the same K.
+ */
+mtp_status mtp_draft(mtp_handle* h, const void* hidden, const int32_t* last_tokens, mtp_kv* kv,
+                     int32_t B, int32_t K, int32_t* draft_tokens, void* stream);
+
+/*
+ * Same kernels as mtp_draft, with diagnostic outputs (any may be NULL):
+ *   hidden_out   [K, B, H] fp32: each step's layer output h^(k) (before the final norm)
+ *   max_logit_out[K, B]    fp32: the largest logit of each step (the drafted token's)
+ *   logits_out   [K, B, V] fp32: every logit of each step
+ */
+mtp_status mtp_draft_debug(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                           mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
+                           float* hidden_out, float* max_logit_out, float* logits_out,
+                           void* stream);
+
+/*
+ * Greedy verification (OpenVINO GenAI "Speculative Decoding", Overview).
+ *   target_logits [B, K+1, vocab] fp32: row j scores the token after input j of
+ *                 [last_token, d_1 .. d_K].
+ *   draft_tokens  [B, K] int32 (ignored when K = 0)
+ *   accepted_len  [B] int32 out: a = largest n <= K with d_i == argmax(row i-1) for all i <= n
+ *   next_token    [B] int32 out: argmax(row a) — the bonus token. Ties take the lowest index.
+ * Tokens per iteration are a + 1 ("Measuring Effectiveness" on the same page).
+ */
+mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* draft_tokens,
+                      int32_t B, int32_t K, int32_t* accepted_len, int32_t* next_token,
+                      void* stream);
+
+/*
+ * Cut the MTP cache back to the committed prefix after a K-step draft:
+ *   len[b] += min(a+1, K) - K,  pos[b] += a + 1 - K,  a = accepted_len[b] (device).
+ * Slot k was computed from the token committed iff k <= a+1; no KV data moves.
+ */
+mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,
+                           int32_t K, void* stream);
+
+/* Synchronise `stream`, read and clear the device error word. *bits receives the
+ * MTP_DEVERR_* bits (may be NULL). Returns MTP_ERR_DEVICE when any bit was set. */
+mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits);
+
+/*
+ * Kernel timing with HIP events, for measurement only. Bit i of `mask` brackets every
+ * launch of kernel class i on the caller's stream with a pair of events:
+ *   0 embedding gather + norms + eh_proj   1 attention norm + QKV   2 attention
+ *   3 O projection                         4 MLP norm + gate/up      5 down projection
+ *   6 final norm + lm_head + argmax        7 verify                  8 rollback
+ * mask = 0 (the default) records nothing. Not for use under stream capture.
+ */
+mtp_status mtp_set_profiling(mtp_handle* h, uint32_t mask);
+
+/* Synchronise on the recorded events and return, per kernel class (arrays of `n`
+ * entries, n <= 16), the summed duration in milliseconds and the number of launches
+ * since the previous call; then forget the records. */
+mtp_status mtp_get_profile(mtp_handle* h, float* total_ms, int32_t* launches, int32_t n);
+
+/* Release the handle (host memory only; the workspace belongs to the caller). */
+void mtp_destroy(mtp_handle* h);
+
+/* Static description of a status code. */
+const char* mtp_status_string(mtp_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTP_H */

@@ -1,0 +1,10 @@
+"""MI355X-native Multi-Token-Prediction draft / verify / rollback path.
+
+The work happens in ``libmtp.so`` (hand-written gfx950 HIP kernels behind the C ABI
+of ``include/mtp.h``); ``_lib`` binds that ABI with ctypes and ``head`` wraps it for
+PyTorch device tensors and streams.
+"""
+from ._lib import (LIB_PATH, MtpError, mtp_config, mtp_create, mtp_destroy, mtp_draft,  # noqa: F401
+                   mtp_draft_debug, mtp_get_error, mtp_kv, mtp_kv_rollback, mtp_status_string,
+                   mtp_verify, mtp_weights, mtp_workspace_size)
+from .head import MtpCache, MtpHead  # noqa: F401

@@ -1,0 +1,105 @@
+// Launch interfaces of the gfx950 kernels (internal to libmtp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+// Prologue: how a workgroup builds the fp32 input vector(s) it multiplies.
+enum Pro : int {
+  PRO_PLAIN = 0,  // x as given
+  PRO_RMS = 1,    // RMSNorm(x) * gain
+  PRO_EH = 2,     // [RMSNorm(h) * g_h ; RMSNorm(embed[tok]) * g_e]   (length 2H)
+};
+// Epilogue: what happens to each dot product y of logical row r, batch row b.
+enum Epi : int {
+  EPI_STORE = 0,   // out[b, r] = y
+  EPI_RESID = 1,   // out[b, r] = res[b, r] + y
+  EPI_SWIGLU = 2,  // rows come in (gate, up) pairs: out[b, r] = silu(y_gate) * y_up
+  EPI_ARGMAX = 3,  // argmax over r per b, finished by the last workgroup
+};
+
+struct GemvParams {
+  // Logical rows r in [0, nrows). Segments: r < seg1 -> w0, r < seg2 -> w1, else w2
+  // (local row index r - segment start). For EPI_SWIGLU, pair r reads w0[r] and w1[r].
+  const void* w0;
+  const void* w1;
+  const void* w2;
+  int seg1, seg2;
+  int nrows;
+  int ncols;
+  int B;
+  int col_block;  // columns staged in LDS at a time (multiple of 64 * elements per 16 B)
+  // Input
+  const float* x;  // [B, ldx] fp32 (PRO_PLAIN, PRO_RMS)
+  int ldx;
+  const void* gain;   // RMS gain (PRO_RMS) or g_h (PRO_EH), weight dtype
+  const void* gain2;  // g_e (PRO_EH)
+  float eps;
+  const void* h;  // PRO_EH hidden state: fp32 [B, H] if h_is_f32 else weight dtype
+  int h_is_f32;
+  int ldh;
+  const void* embed;   // PRO_EH embedding table [vocab, H]
+  const int* tok;      // PRO_EH token of batch row b at tok[b * tok_stride]
+  int tok_stride;
+  int vocab;
+  unsigned* err;
+  // Output
+  float* out;
+  int ldo;
+  const float* res;
+  float* dbg;  // optional second copy of out (EPI_RESID), [B, dbg_ld]
+  int dbg_ld;
+  // EPI_ARGMAX
+  unsigned long long* keys;  // [B], zero on entry, left zero on exit
+  unsigned* counter;         // zero on entry, left zero on exit
+  int* tok_out;              // token of b written to tok_out[b * tok_out_stride]
+  int tok_out_stride;
+  float* maxlogit;  // [B] or null
+  float* logits;    // [B, logits_ld] or null
+  int logits_ld;
+  int* len;  // when advance > 0 the last workgroup adds it to len[b] and pos[b]
+  int* pos;
+  int advance;
+};
+
+hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int max_grid,
+                       hipStream_t s);
+
+struct AttnParams {
+  const float* qkv;  // [B, ldqkv] fp32: q (n_q*d) | k (n_kv*d) | v (n_kv*d), before RoPE
+  int ldqkv;
+  void* kc;  // [Bc, n_kv, capacity, d] cache dtype
+  void* vc;
+  int n_q, n_kv, d;
+  int capacity;
+  const int* len;  // start-of-call values
+  const int* pos;
+  int step;   // 0-based step index: slot len+step, position pos+step
+  int chunk;  // positions per workgroup (multiple of 64)
+  int nsplit;
+  float theta;
+  float scale;
+  float* part_o;   // [B, n_q, nsplit, d]
+  float* part_ml;  // [B, n_q, nsplit, 2]
+  unsigned* counters;  // [B * n_kv]
+  float* o;            // [B, n_q * d]
+  unsigned* err;
+};
+hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
+
+struct VerifyParams {
+  const float* logits;  // [B, K+1, V]
+  const int* draft;     // [B, K]
+  int K, V, chunk, nchunk;
+  unsigned long long* keys;  // [B * (K+1)] zero on entry/exit
+  unsigned* counters;        // [B]
+  int* accepted;
+  int* next;
+};
+hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s);
+
+hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
+                           hipStream_t s);
+
+}  // namespace mtp

@@ -1,0 +1,457 @@
+// Host side of the C ABI declared in include/mtp.h: argument validation, workspace
+// layout, kernel selection and the launch sequence of one speculative iteration.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "mtp.h"
+
+namespace {
+
+using namespace mtp;
+
+constexpr int kMaxSplits = 256;
+constexpr int kMinChunk = 64;
+constexpr int kMaxChunk = 1024;
+constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
+constexpr int kMaxK = 100;
+constexpr int kMaxGroupHeads = 8;
+constexpr int kVerifyChunk = 4096;
+constexpr size_t kGemvLdsBudget = 32 * 1024;
+constexpr int kGemvMaxGrid = 2048;
+
+struct Layout {
+  size_t x, x1, h, qkv, o, act, part_o, part_ml, lm_keys, lm_cnt, attn_cnt, v_keys, v_cnt, err;
+  size_t total;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t B = (size_t)max_batch, H = (size_t)c.hidden, d = (size_t)c.head_dim;
+  const size_t nq = (size_t)c.n_q_heads, nkv = (size_t)c.n_kv_heads;
+  L.x = take(B * H * 4);
+  L.x1 = take(B * H * 4);
+  L.h = take(B * H * 4);
+  L.qkv = take(B * (nq + 2 * nkv) * d * 4);
+  L.o = take(B * nq * d * 4);
+  L.act = take(B * (size_t)c.ffn * 4);
+  L.part_o = take(B * nq * kMaxSplits * d * 4);
+  L.part_ml = take(B * nq * kMaxSplits * 2 * 4);
+  L.lm_keys = take(B * 8);
+  L.lm_cnt = take(4);
+  L.attn_cnt = take(B * nkv * 4);
+  L.v_keys = take(B * (size_t)(max_k + 1) * 8);
+  L.v_cnt = take(B * 4);
+  L.err = take(4);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+mtp_status check_config(const mtp_config* c) {
+  if (!c) return MTP_ERR_INVALID_ARG;
+  if (c->dtype != MTP_F32 && c->dtype != MTP_BF16) return MTP_ERR_DTYPE;
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn <= 0 || c->vocab <= 0)
+    return MTP_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads != 0) return MTP_ERR_SHAPE;
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return MTP_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return MTP_ERR_UNSUPPORTED;
+  if (c->n_q_heads / c->n_kv_heads > kMaxGroupHeads) return MTP_ERR_UNSUPPORTED;
+  if (c->hidden % 8 != 0 || c->ffn % 8 != 0) return MTP_ERR_UNSUPPORTED;
+  return MTP_OK;
+}
+
+mtp_status check_limits(int max_batch, int max_k, int max_capacity) {
+  if (max_batch < 1 || max_k < 0 || max_capacity < 1) return MTP_ERR_SHAPE;
+  if (max_k > kMaxK || max_capacity > kMaxCapacity) return MTP_ERR_CAPACITY;
+  return MTP_OK;
+}
+
+int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
+int col_block_for(int ncols, int B, int dtype) {
+  const int step = 64 * (dtype == MTP_F32 ? 4 : 8);
+  const int nb = nb_for(B);
+  int cb = (int)(kGemvLdsBudget / (4 * (size_t)nb)) / step * step;
+  if (cb < step) cb = step;
+  const int full = (ncols + step - 1) / step * step;
+  return cb < full ? cb : full;
+}
+
+}  // namespace
+
+struct ProfRec {
+  int id;
+  hipEvent_t a, b;
+};
+
+struct mtp_handle {
+  mtp_config cfg;
+  mtp_weights w;
+  int max_batch, max_k, max_cap;
+  char* ws;
+  size_t ws_bytes;
+  Layout L;
+  uint32_t prof_mask = 0;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  template <class T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(ws + off);
+  }
+};
+
+namespace {
+
+enum KernelClass { KC_EH = 0, KC_QKV, KC_ATTN, KC_OPROJ, KC_GATEUP, KC_DOWN, KC_LMHEAD, KC_VERIFY,
+                   KC_ROLLBACK, KC_COUNT };
+
+hipEvent_t take_event(mtp_handle* h) {
+  if (!h->pool.empty()) {
+    hipEvent_t e = h->pool.back();
+    h->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `f` and, when kernel class `id` is being profiled, bracket it with events.
+template <class Fn>
+hipError_t timed(mtp_handle* h, int id, hipStream_t s, Fn&& f) {
+  if (!((h->prof_mask >> id) & 1u)) return f();
+  hipEvent_t a = take_event(h), b = take_event(h);
+  if (!a || !b) return hipErrorOutOfMemory;
+  (void)hipEventRecord(a, s);
+  hipError_t e = f();
+  (void)hipEventRecord(b, s);
+  h->recs.push_back({id, a, b});
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtp_status_string(mtp_status s) {
+  switch (s) {
+    case MTP_OK: return "ok";
+    case MTP_ERR_INVALID_ARG: return "invalid argument";
+    case MTP_ERR_SHAPE: return "inconsistent or non-positive shape";
+    case MTP_ERR_DTYPE: return "unknown dtype";
+    case MTP_ERR_CAPACITY: return "capacity exceeded (batch, K, workspace or cache)";
+    case MTP_ERR_UNSUPPORTED: return "shape not supported by the kernels";
+    case MTP_ERR_HIP: return "HIP runtime error";
+    case MTP_ERR_DEVICE: return "device-side error (see mtp_get_error bits)";
+  }
+  return "unknown status";
+}
+
+mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
+                              int32_t max_capacity, size_t* bytes) {
+  if (!bytes) return MTP_ERR_INVALID_ARG;
+  mtp_status st = check_config(cfg);
+  if (st != MTP_OK) return st;
+  st = check_limits(max_batch, max_k, max_capacity);
+  if (st != MTP_OK) return st;
+  *bytes = make_layout(*cfg, max_batch, max_k).total;
+  return MTP_OK;
+}
+
+mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
+                      int32_t max_k, int32_t max_capacity, void* workspace, size_t workspace_bytes,
+                      mtp_handle** out) {
+  if (!out) return MTP_ERR_INVALID_ARG;
+  *out = nullptr;
+  mtp_status st = check_config(cfg);
+  if (st != MTP_OK) return st;
+  st = check_limits(max_batch, max_k, max_capacity);
+  if (st != MTP_OK) return st;
+  if (!w || !workspace) return MTP_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->g_h, w->g_e, w->w_eh, w->g_attn, w->w_q, w->w_k, w->w_v, w->w_o,
+                        w->g_mlp, w->w_gate, w->w_up, w->w_down, w->g_final, w->embed, w->lm_head};
+  for (const void* p : ptrs)
+    if (!p || !aligned(p, 16)) return MTP_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MTP_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg, max_batch, max_k);
+  if (workspace_bytes < L.total) return MTP_ERR_CAPACITY;
+  if (hipMemset(workspace, 0, L.total) != hipSuccess) return MTP_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;
+  mtp_handle* h = new (std::nothrow) mtp_handle();
+  if (!h) return MTP_ERR_CAPACITY;
+  h->cfg = *cfg;
+  h->w = *w;
+  h->max_batch = max_batch;
+  h->max_k = max_k;
+  h->max_cap = max_capacity;
+  h->ws = static_cast<char*>(workspace);
+  h->ws_bytes = workspace_bytes;
+  h->L = L;
+  *out = h;
+  return MTP_OK;
+}
+
+void mtp_destroy(mtp_handle* h) {
+  if (!h) return;
+  for (auto& r : h->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  delete h;
+}
+
+mtp_status mtp_set_profiling(mtp_handle* h, uint32_t mask) {
+  if (!h) return MTP_ERR_INVALID_ARG;
+  h->prof_mask = mask;
+  return MTP_OK;
+}
+
+mtp_status mtp_get_profile(mtp_handle* h, float* total_ms, int32_t* launches, int32_t n) {
+  if (!h || !total_ms || !launches || n < 0 || n > 16) return MTP_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.f;
+    launches[i] = 0;
+  }
+  mtp_status st = MTP_OK;
+  if (!h->recs.empty() && hipEventSynchronize(h->recs.back().b) != hipSuccess) st = MTP_ERR_HIP;
+  for (auto& r : h->recs) {
+    float ms = 0.f;
+    if (st == MTP_OK && hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) st = MTP_ERR_HIP;
+    if (r.id < n) {
+      total_ms[r.id] += ms;
+      launches[r.id] += 1;
+    }
+    h->pool.push_back(r.a);
+    h->pool.push_back(r.b);
+  }
+  h->recs.clear();
+  return st;
+}
+
+static mtp_status check_kv(const mtp_handle* h, const mtp_kv* kv, int B) {
+  if (!kv || !kv->k || !kv->v || !kv->len || !kv->pos) return MTP_ERR_INVALID_ARG;
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return MTP_ERR_INVALID_ARG;
+  if (kv->batch < 1 || kv->capacity < 1) return MTP_ERR_SHAPE;
+  if (B > kv->batch) return MTP_ERR_SHAPE;
+  if (kv->capacity > h->max_cap) return MTP_ERR_CAPACITY;
+  return MTP_OK;
+}
+
+static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                             mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
+                             float* hidden_out, float* max_logit_out, float* logits_out,
+                             void* stream) {
+  if (!h || !hidden || !last_tokens) return MTP_ERR_INVALID_ARG;
+  if (K < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  mtp_status st = check_kv(h, kv, B);
+  if (st != MTP_OK) return st;
+  if (K == 0) return MTP_OK;
+  if (!draft_tokens) return MTP_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mtp_config& c = h->cfg;
+  const mtp_weights& w = h->w;
+  const Layout& L = h->L;
+  const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, F = c.ffn;
+  const int V = c.vocab, qkvd = (nq + 2 * nkv) * d;
+  float* x = h->at<float>(L.x);
+  float* x1 = h->at<float>(L.x1);
+  float* hb = h->at<float>(L.h);
+  float* qkv = h->at<float>(L.qkv);
+  float* o = h->at<float>(L.o);
+  float* act = h->at<float>(L.act);
+  unsigned* err = h->at<unsigned>(L.err);
+
+  int chunk = (kv->capacity + kMaxSplits - 1) / kMaxSplits;
+  chunk = (chunk + kMinChunk - 1) / kMinChunk * kMinChunk;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  const int nsplit = (kv->capacity + chunk - 1) / chunk;
+
+  for (int k = 0; k < K; ++k) {
+    hipError_t e;
+    // 1. embedding gather + separate RMSNorms + concat + eh_proj
+    GemvParams g{};
+    g.w0 = g.w1 = g.w2 = w.w_eh;
+    g.nrows = g.seg1 = g.seg2 = H;
+    g.ncols = 2 * H;
+    g.B = B;
+    g.col_block = col_block_for(2 * H, B, c.dtype);
+    g.gain = w.g_h;
+    g.gain2 = w.g_e;
+    g.eps = c.rms_eps;
+    g.h = k == 0 ? hidden : (const void*)hb;
+    g.h_is_f32 = (k > 0 || c.dtype == MTP_F32) ? 1 : 0;
+    g.ldh = H;
+    g.embed = w.embed;
+    g.tok = k == 0 ? last_tokens : draft_tokens + (k - 1);
+    g.tok_stride = k == 0 ? 1 : K;
+    g.vocab = V;
+    g.err = err;
+    g.out = x;
+    g.ldo = H;
+    if ((e = timed(h, KC_EH, s, [&] { return launch_gemv(c.dtype, PRO_EH, EPI_STORE, g, kGemvMaxGrid, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+
+    // 2. attention RMSNorm + fused QKV projection
+    g = GemvParams{};
+    g.w0 = w.w_q; g.w1 = w.w_k; g.w2 = w.w_v;
+    g.seg1 = nq * d; g.seg2 = (nq + nkv) * d; g.nrows = qkvd;
+    g.ncols = H; g.B = B; g.col_block = col_block_for(H, B, c.dtype);
+    g.x = x; g.ldx = H; g.gain = w.g_attn; g.eps = c.rms_eps;
+    g.out = qkv; g.ldo = qkvd;
+    if ((e = timed(h, KC_QKV, s, [&] { return launch_gemv(c.dtype, PRO_RMS, EPI_STORE, g, kGemvMaxGrid, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+
+    // 3. RoPE + cache append + split decode attention + merge
+    AttnParams a{};
+    a.qkv = qkv; a.ldqkv = qkvd;
+    a.kc = kv->k; a.vc = kv->v;
+    a.n_q = nq; a.n_kv = nkv; a.d = d; a.capacity = kv->capacity;
+    a.len = kv->len; a.pos = kv->pos; a.step = k;
+    a.chunk = chunk; a.nsplit = nsplit;
+    a.theta = c.rope_theta;
+    a.scale = 1.0f / sqrtf((float)d);
+    a.part_o = h->at<float>(L.part_o);
+    a.part_ml = h->at<float>(L.part_ml);
+    a.counters = h->at<unsigned>(L.attn_cnt);
+    a.o = o;
+    a.err = err;
+    if ((e = timed(h, KC_ATTN, s, [&] { return launch_attention(c.dtype, a, B, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+
+    // 4. O projection + residual
+    g = GemvParams{};
+    g.w0 = g.w1 = g.w2 = w.w_o;
+    g.nrows = g.seg1 = g.seg2 = H;
+    g.ncols = nq * d; g.B = B; g.col_block = col_block_for(nq * d, B, c.dtype);
+    g.x = o; g.ldx = nq * d;
+    g.out = x1; g.ldo = H; g.res = x;
+    if ((e = timed(h, KC_OPROJ, s, [&] { return launch_gemv(c.dtype, PRO_PLAIN, EPI_RESID, g, kGemvMaxGrid, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+
+    // 5. MLP RMSNorm + gate/up + SiLU * up
+    g = GemvParams{};
+    g.w0 = w.w_gate; g.w1 = w.w_up; g.w2 = w.w_up;
+    g.nrows = g.seg1 = g.seg2 = F;
+    g.ncols = H; g.B = B; g.col_block = col_block_for(H, B, c.dtype);
+    g.x = x1; g.ldx = H; g.gain = w.g_mlp; g.eps = c.rms_eps;
+    g.out = act; g.ldo = F;
+    if ((e = timed(h, KC_GATEUP, s, [&] { return launch_gemv(c.dtype, PRO_RMS, EPI_SWIGLU, g, kGemvMaxGrid, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+
+    // 6. down projection + residual -> h^(k)
+    g = GemvParams{};
+    g.w0 = g.w1 = g.w2 = w.w_down;
+    g.nrows = g.seg1 = g.seg2 = H;
+    g.ncols = F; g.B = B; g.col_block = col_block_for(F, B, c.dtype);
+    g.x = act; g.ldx = F;
+    g.out = hb; g.ldo = H; g.res = x1;
+    g.dbg = hidden_out ? hidden_out + (size_t)k * B * H : nullptr;
+    g.dbg_ld = H;
+    if ((e = timed(h, KC_DOWN, s, [&] { return launch_gemv(c.dtype, PRO_PLAIN, EPI_RESID, g, kGemvMaxGrid, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+
+    // 7. final RMSNorm + shared lm_head + argmax -> draft token
+    g = GemvParams{};
+    g.w0 = g.w1 = g.w2 = w.lm_head;
+    g.nrows = g.seg1 = g.seg2 = V;
+    g.ncols = H; g.B = B; g.col_block = col_block_for(H, B, c.dtype);
+    g.x = hb; g.ldx = H; g.gain = w.g_final; g.eps = c.rms_eps;
+    g.keys = h->at<unsigned long long>(L.lm_keys);
+    g.counter = h->at<unsigned>(L.lm_cnt);
+    g.tok_out = draft_tokens + k;
+    g.tok_out_stride = K;
+    g.maxlogit = max_logit_out ? max_logit_out + (size_t)k * B : nullptr;
+    g.logits = logits_out ? logits_out + (size_t)k * B * V : nullptr;
+    g.logits_ld = V;
+    g.len = kv->len; g.pos = kv->pos;
+    g.advance = (k == K - 1) ? K : 0;
+    if ((e = timed(h, KC_LMHEAD, s, [&] { return launch_gemv(c.dtype, PRO_RMS, EPI_ARGMAX, g, kGemvMaxGrid, s); })) != hipSuccess)
+      return MTP_ERR_HIP;
+  }
+  return MTP_OK;
+}
+
+mtp_status mtp_draft(mtp_handle* h, const void* hidden, const int32_t* last_tokens, mtp_kv* kv,
+                     int32_t B, int32_t K, int32_t* draft_tokens, void* stream) {
+  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, nullptr, nullptr, nullptr,
+                    stream);
+}
+
+mtp_status mtp_draft_debug(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                           mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
+                           float* hidden_out, float* max_logit_out, float* logits_out,
+                           void* stream) {
+  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out,
+                    logits_out, stream);
+}
+
+mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* draft_tokens,
+                      int32_t B, int32_t K, int32_t* accepted_len, int32_t* next_token,
+                      void* stream) {
+  if (!h || !target_logits || !accepted_len || !next_token) return MTP_ERR_INVALID_ARG;
+  if (K < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  if (K > 0 && !draft_tokens) return MTP_ERR_INVALID_ARG;
+  VerifyParams p{};
+  p.logits = target_logits;
+  p.draft = draft_tokens;
+  p.K = K;
+  p.V = h->cfg.vocab;
+  p.chunk = kVerifyChunk;
+  p.nchunk = (p.V + kVerifyChunk - 1) / kVerifyChunk;
+  p.keys = h->at<unsigned long long>(h->L.v_keys);
+  p.counters = h->at<unsigned>(h->L.v_cnt);
+  p.accepted = accepted_len;
+  p.next = next_token;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(h, KC_VERIFY, s, [&] { return launch_verify(p, B, s); }) == hipSuccess ? MTP_OK
+                                                                                      : MTP_ERR_HIP;
+}
+
+mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,
+                           int32_t K, void* stream) {
+  if (!h || !accepted_len) return MTP_ERR_INVALID_ARG;
+  if (K < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  mtp_status st = check_kv(h, kv, B);
+  if (st != MTP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(h, KC_ROLLBACK, s, [&] {
+           return launch_rollback(kv->len, kv->pos, accepted_len, B, K,
+                                  h->at<unsigned>(h->L.err), s);
+         }) == hipSuccess
+             ? MTP_OK
+             : MTP_ERR_HIP;
+}
+
+mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits) {
+  if (!h) return MTP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MTP_ERR_HIP;
+  unsigned v = 0;
+  unsigned* dev = h->at<unsigned>(h->L.err);
+  if (hipMemcpy(&v, dev, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MTP_ERR_HIP;
+  if (v && hipMemset(dev, 0, sizeof(v)) != hipSuccess) return MTP_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;
+  if (bits) *bits = v;
+  return v ? MTP_ERR_DEVICE : MTP_OK;
+}
+
+}  // extern "C"

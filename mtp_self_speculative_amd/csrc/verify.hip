@@ -1,0 +1,83 @@
+// Greedy verification and MTP-cache rollback.
+//
+// Verify: grid (vocabulary chunk, row j = 0..K, sequence b). Each workgroup reduces its
+// chunk of target-logit row (b, j) to a packed (value, index) key — larger value wins,
+// lowest index on ties — and folds it into a per-row key with an atomic max, which is
+// order independent and hence deterministic. The last workgroup of sequence b turns the
+// K+1 keys into the target's tokens, scans the longest prefix of drafts that match them
+// and writes accepted_len and the bonus token.
+// Rollback: one lane per sequence moves len/pos to the committed prefix.
+#include "common.h"
+#include "kernels.h"
+
+namespace mtp {
+
+constexpr int kVerifyThreads = 256;
+
+__global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) {
+  __shared__ unsigned long long kred[kVerifyThreads / kWave];
+  __shared__ int flag;
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* row = p.logits + ((long)b * (p.K + 1) + j) * p.V;
+  const int lo = c * p.chunk, hi = min(lo + p.chunk, p.V);
+  unsigned long long best = 0ull;
+  for (int i = lo + threadIdx.x; i < hi; i += kVerifyThreads) {
+    const unsigned long long k = pack_key(__builtin_nontemporal_load(row + i), (uint32_t)i);
+    best = k > best ? k : best;
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) kred[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kVerifyThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
+    if (best) atomic_max_key(p.keys + (long)b * (p.K + 1) + j, best);
+  }
+  if (last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) {
+    __threadfence();
+    if (threadIdx.x == 0) {
+      unsigned long long* kb = p.keys + (long)b * (p.K + 1);
+      int a = 0;
+      while (a < p.K) {
+        const int gtok = (int)key_index(__hip_atomic_load(kb + a, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT));
+        if (p.draft[(long)b * p.K + a] != gtok) break;
+        ++a;
+      }
+      const int next =
+          (int)key_index(__hip_atomic_load(kb + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      for (int q = 0; q <= p.K; ++q)
+        __hip_atomic_store(kb + q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      p.accepted[b] = a;
+      p.next[b] = next;
+    }
+  }
+}
+
+__global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, int K,
+                                unsigned* err) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int a = accepted[b];
+  if (a < 0 || a > K) {
+    set_error(err, 4u);
+    a = a < 0 ? 0 : K;
+  }
+  const int keep = (a + 1 < K) ? a + 1 : K;
+  len[b] += keep - K;
+  pos[b] += a + 1 - K;
+}
+
+hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s) {
+  hipLaunchKernelGGL(verify_kernel, dim3(p.nchunk, p.K + 1, B), dim3(kVerifyThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(rollback_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, pos, accepted,
+                     B, K, err);
+  return hipGetLastError();
+}
+
+}  // namespace mtp

@@ -1,0 +1,89 @@
+"""The C-ABI library loads, exports every symbol include/mtp.h declares, and rejects bad
+arguments on the host before touching a device. No compute call is made here."""
+import ctypes
+import subprocess
+
+import pytest
+
+from mtp_self_speculative_amd import _lib as L
+
+
+def cfg(**kw):
+    base = dict(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288, vocab=151936,
+                rope_theta=1e6, rms_eps=1e-6, dtype=L.MTP_BF16)
+    base.update(kw)
+    return L.make_config(**base)
+
+
+def test_every_declared_symbol_is_exported():
+    names = L.declared_symbols()
+    assert {"mtp_draft", "mtp_verify", "mtp_kv_rollback"} <= set(names)
+    for n in names:
+        assert hasattr(L.LIB, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for s in range(8):
+        assert L.mtp_status_string(s)
+    assert "unknown" in L.mtp_status_string(99)
+
+
+def _ws_status(c, mb=1, mk=5, cap=4416):
+    n = ctypes.c_size_t(0)
+    return L.LIB.mtp_workspace_size(ctypes.byref(c) if c is not None else None, mb, mk, cap,
+                                    ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,mb,mk,cap,status", [
+    (dict(), 1, 5, 4416, 0),
+    (dict(dtype=7), 1, 5, 4416, 3),
+    (dict(head_dim=96), 1, 5, 4416, 5),
+    (dict(n_q_heads=30), 1, 5, 4416, 2),
+    (dict(n_q_heads=64, n_kv_heads=4), 1, 5, 4416, 5),   # 16 query heads per KV head
+    (dict(hidden=4100), 1, 5, 4416, 5),
+    (dict(hidden=0), 1, 5, 4416, 2),
+    (dict(rms_eps=0.0), 1, 5, 4416, 1),
+    (dict(), 0, 5, 4416, 2),
+    (dict(), 1, 101, 4416, 4),
+    (dict(), 1, 5, 1 << 20, 4),
+    (dict(), 1, -1, 4416, 2),
+])
+def test_workspace_size_validation(kw, mb, mk, cap, status):
+    st, n = _ws_status(cfg(**kw), mb, mk, cap)
+    assert st == status
+    if status == 0:
+        assert n > 0
+
+
+def test_workspace_grows_with_batch_and_k():
+    sizes = [L.mtp_workspace_size(cfg(), b, k, 4416) for b, k in [(1, 5), (8, 5), (8, 100)]]
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert all(s % 256 == 0 for s in sizes)
+
+
+def test_null_arguments_rejected_before_any_device_call():
+    h = ctypes.c_void_p(0)
+    w = L.mtp_weights()
+    c = cfg()
+    assert L.LIB.mtp_create(ctypes.byref(c), ctypes.byref(w), 1, 5, 4416, None, 0,
+                            ctypes.byref(h)) == 1
+    assert h.value is None
+    assert L.LIB.mtp_create(None, ctypes.byref(w), 1, 5, 4416, None, 0, ctypes.byref(h)) == 1
+    kv = L.mtp_kv()
+    assert L.LIB.mtp_draft(None, None, None, ctypes.byref(kv), 1, 1, None, None) == 1
+    assert L.LIB.mtp_draft_debug(None, None, None, ctypes.byref(kv), 1, 1, None, None, None,
+                                 None, None) == 1
+    assert L.LIB.mtp_verify(None, None, None, 1, 1, None, None, None) == 1
+    assert L.LIB.mtp_kv_rollback(None, ctypes.byref(kv), None, 1, 1, None) == 1
+    assert L.LIB.mtp_get_error(None, None, None) == 1
+    L.LIB.mtp_destroy(None)
+
+
+def test_python_wrapper_raises_mtp_error():
+    with pytest.raises(L.MtpError) as e:
+        L.mtp_workspace_size(cfg(head_dim=32), 1, 1, 16)
+    assert e.value.status == 5
