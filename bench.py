@@ -189,10 +189,13 @@ def main() -> int:
         head.set_profiling(0)
         return t1 - t0, head.get_profile()
 
-    elapsed, prof = replay(LMHEAD_BIT)
+    elapsed, _ = replay(0)
     if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
         raise RuntimeError("timed replay diverged from the recording pass")
     log(f"timed pass: {args.steps} iterations in {elapsed * 1e3:.2f} ms")
+    # Same replay with HIP events around every lm_head launch (on the library's stream).
+    el_ev, prof = replay(LMHEAD_BIT)
+    log(f"lm_head-event pass: {args.steps} iterations in {el_ev * 1e3:.2f} ms")
 
     kernel_us = None
     if args.breakdown:

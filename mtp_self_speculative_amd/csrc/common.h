@@ -23,6 +23,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+__device__ __forceinline__ void load8_f32(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void store8_lds(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+
 // Element type tags: storage of weights / activations in memory.
 struct F32 {
   using T = float;
@@ -34,6 +45,8 @@ struct F32 {
     o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
   }
   __device__ static void put(T* p, long i, float f) { p[i] = f; }
+  // 8 consecutive elements (16-byte aligned) as floats.
+  __device__ static void load8(const T* p, float* o) { load8_f32(p, o); }
 };
 struct BF16 {
   using T = uint16_t;
@@ -44,6 +57,9 @@ struct BF16 {
     o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
   }
   __device__ static void put(T* p, long i, float f) { p[i] = f32_to_bf16(f); }
+  __device__ static void load8(const T* p, float* o) {
+    unpack(*reinterpret_cast<const u32x4*>(p), o);
+  }
 };
 
 // ---------------------------------------------------------------- wave reductions
@@ -106,29 +122,41 @@ __device__ __forceinline__ float key_value(unsigned long long k) {
   return from_orderable((uint32_t)(k >> 32));
 }
 
-__device__ __forceinline__ void atomic_max_key(unsigned long long* p, unsigned long long k) {
-  __hip_atomic_fetch_max(p, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Publish a key; returns the previous value so that callers can wait for completion.
+__device__ __forceinline__ unsigned long long atomic_max_key(unsigned long long* p,
+                                                             unsigned long long k) {
+  return __hip_atomic_fetch_max(p, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Completion counter: every workgroup calls this once after its global writes;
-// returns true in exactly one workgroup, the last to arrive, which then sees all
-// other workgroups' writes. That workgroup resets the counter to zero.
+// Completion counter for workgroups that publish their results only through
+// device-scope atomic read-modify-writes (which are performed at the device's
+// coherence point). Each thread waits until its own atomics have returned, the
+// workgroup synchronises, and one thread bumps the counter; exactly one workgroup,
+// the last to arrive, gets true and resets the counter. No cache-wide release or
+// acquire fence is needed: the last workgroup reads the published values back with
+// atomic read-modify-writes as well.
 __device__ __forceinline__ bool last_to_arrive(unsigned int* counter, unsigned int total,
                                                int* flag_lds) {
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    unsigned int prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (prev == total - 1);
-    if (last) {
-      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
-    }
+    const unsigned int prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (prev == total - 1);
+    if (last) __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag_lds = last;
   }
   __syncthreads();
   return *flag_lds != 0;
+}
+
+// Force a returned atomic value to be materialised, so that the atomic is issued in
+// its returning form and the wait before the completion counter covers it.
+__device__ __forceinline__ void keep_alive(unsigned long long v) { asm volatile("" ::"v"(v)); }
+
+// Read a published key and reset it to zero in one atomic step.
+__device__ __forceinline__ unsigned long long take_key(unsigned long long* p) {
+  return __hip_atomic_exchange(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void set_error(unsigned int* err, unsigned int bit) {

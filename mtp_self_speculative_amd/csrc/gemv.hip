@@ -253,16 +253,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
       const int b = b0 + threadIdx.x;
       unsigned long long k = 0ull;
       for (int w = 0; w < kWavesPerBlock; ++w) k = kred[w][threadIdx.x] > k ? kred[w][threadIdx.x] : k;
-      if (b < p.B && k) atomic_max_key(p.keys + b, k);
+      if (b < p.B && k) keep_alive(atomic_max_key(p.keys + b, k));
     }
     if (last_to_arrive(p.counter, gridDim.x * gridDim.y, &flag)) {
-      __threadfence();
       for (int b = threadIdx.x; b < p.B; b += kThreads) {
-        const unsigned long long k =
-            __hip_atomic_load(p.keys + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long k = take_key(p.keys + b);
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
         if (p.maxlogit) p.maxlogit[b] = key_value(k);
-        __hip_atomic_store(p.keys + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (p.advance > 0) {
           p.len[b] += p.advance;
           p.pos[b] += p.advance;
@@ -306,6 +303,9 @@ static hipError_t launch_dt(Pro pro, Epi epi, const GemvParams& p, int max_grid,
 
 hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int max_grid,
                        hipStream_t s) {
+  const int step = 64 * (wdtype == 0 ? F32::kVec : BF16::kVec);
+  if (p.col_block < step || p.col_block % step != 0 || p.ncols < 1 || p.nrows < 1)
+    return hipErrorInvalidValue;
   return wdtype == 0 ? launch_dt<F32>(pro, epi, p, max_grid, s)
                      : launch_dt<BF16>(pro, epi, p, max_grid, s);
 }

@@ -63,8 +63,19 @@ struct GemvParams {
   int advance;
 };
 
+// Column-blocked GEMV for any batch (batch rows in blockIdx.y tiles of up to 8).
 hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int max_grid,
                        hipStream_t s);
+// Persistent pipelined GEMV for batch 1-2 when the input vectors fit in LDS.
+bool gemv_pipe_fits(int ncols, int B);
+int gemv_pipe_grid(int nrows, int num_cu);
+hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, int grid,
+                            hipStream_t s);
+
+// RoPE tables of K consecutive steps: tab[k][b][0..d/2) = cos, tab[k][b][d/2..d) = sin of
+// (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded to fp32.
+hipError_t launch_rope_tables(float* tab, const int* pos, int B, int K, int d, float theta,
+                              hipStream_t s);
 
 struct AttnParams {
   const float* qkv;  // [B, ldqkv] fp32: q (n_q*d) | k (n_kv*d) | v (n_kv*d), before RoPE
@@ -78,14 +89,14 @@ struct AttnParams {
   int step;   // 0-based step index: slot len+step, position pos+step
   int chunk;  // positions per workgroup (multiple of 64)
   int nsplit;
-  float theta;
+  const float* rope;  // [B, d]: cos then sin of the step's position
   float scale;
   float* part_o;   // [B, n_q, nsplit, d]
   float* part_ml;  // [B, n_q, nsplit, 2]
-  unsigned* counters;  // [B * n_kv]
-  float* o;            // [B, n_q * d]
+  float* o;  // [B, n_q * d]
   unsigned* err;
 };
+// Attention (partials per split) followed by the split merge into o.
 hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
 
 struct VerifyParams {

@@ -24,7 +24,8 @@ constexpr size_t kGemvLdsBudget = 32 * 1024;
 constexpr int kGemvMaxGrid = 2048;
 
 struct Layout {
-  size_t x, x1, h, qkv, o, act, part_o, part_ml, lm_keys, lm_cnt, attn_cnt, v_keys, v_cnt, err;
+  size_t x, x1, h, qkv, o, act, rope, part_o, part_ml, lm_keys, lm_cnt, v_keys, v_cnt,
+      err;
   size_t total;
 };
 
@@ -46,11 +47,11 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   L.qkv = take(B * (nq + 2 * nkv) * d * 4);
   L.o = take(B * nq * d * 4);
   L.act = take(B * (size_t)c.ffn * 4);
+  L.rope = take((size_t)(max_k > 0 ? max_k : 1) * B * d * 4);
   L.part_o = take(B * nq * kMaxSplits * d * 4);
   L.part_ml = take(B * nq * kMaxSplits * 2 * 4);
   L.lm_keys = take(B * 8);
   L.lm_cnt = take(4);
-  L.attn_cnt = take(B * nkv * 4);
   L.v_keys = take(B * (size_t)(max_k + 1) * 8);
   L.v_cnt = take(B * 4);
   L.err = take(4);
@@ -105,6 +106,7 @@ struct mtp_handle {
   char* ws;
   size_t ws_bytes;
   Layout L;
+  int num_cu = 256;
   uint32_t prof_mask = 0;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
@@ -141,6 +143,15 @@ hipError_t timed(mtp_handle* h, int id, hipStream_t s, Fn&& f) {
   (void)hipEventRecord(b, s);
   h->recs.push_back({id, a, b});
   return e;
+}
+
+// Pick the pipelined kernel when the batch's input vectors fit in LDS, else the
+// column-blocked one.
+hipError_t run_gemv(const mtp_handle* h, Pro pro, Epi epi, GemvParams& g, hipStream_t s) {
+  if (gemv_pipe_fits(g.ncols, g.B))
+    return launch_gemv_pipe(h->cfg.dtype, pro, epi, g, gemv_pipe_grid(g.nrows, h->num_cu), s);
+  g.col_block = col_block_for(g.ncols, g.B, h->cfg.dtype);
+  return launch_gemv(h->cfg.dtype, pro, epi, g, kGemvMaxGrid, s);
 }
 
 }  // namespace
@@ -201,6 +212,11 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
   h->ws = static_cast<char*>(workspace);
   h->ws_bytes = workspace_bytes;
   h->L = L;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      ncu > 0)
+    h->num_cu = ncu;
   *out = h;
   return MTP_OK;
 }
@@ -257,6 +273,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
                              float* hidden_out, float* max_logit_out, float* logits_out,
                              void* stream) {
   if (!h || !hidden || !last_tokens) return MTP_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16)) return MTP_ERR_INVALID_ARG;
   if (K < 0 || B < 1) return MTP_ERR_SHAPE;
   if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
   mtp_status st = check_kv(h, kv, B);
@@ -278,11 +295,18 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   float* act = h->at<float>(L.act);
   unsigned* err = h->at<unsigned>(L.err);
 
-  int chunk = (kv->capacity + kMaxSplits - 1) / kMaxSplits;
-  chunk = (chunk + kMinChunk - 1) / kMinChunk * kMinChunk;
-  if (chunk < kMinChunk) chunk = kMinChunk;
+  // Attention splits: aim for about four workgroups per CU over (split, kv head, sequence),
+  // with chunks of 128..1024 cache positions (multiples of 64) and at most kMaxSplits.
+  long want = ((long)kv->capacity * B * nkv + 4L * h->num_cu - 1) / (4L * h->num_cu);
+  int chunk = (int)((want + kMinChunk - 1) / kMinChunk * kMinChunk);
+  if (chunk < 2 * kMinChunk) chunk = 2 * kMinChunk;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  const int min_chunk = (kv->capacity + kMaxSplits - 1) / kMaxSplits;
+  if (chunk < min_chunk) chunk = (min_chunk + kMinChunk - 1) / kMinChunk * kMinChunk;
   const int nsplit = (kv->capacity + chunk - 1) / chunk;
 
+  if (launch_rope_tables(h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, s) != hipSuccess)
+    return MTP_ERR_HIP;
   for (int k = 0; k < K; ++k) {
     hipError_t e;
     // 1. embedding gather + separate RMSNorms + concat + eh_proj
@@ -291,7 +315,6 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.nrows = g.seg1 = g.seg2 = H;
     g.ncols = 2 * H;
     g.B = B;
-    g.col_block = col_block_for(2 * H, B, c.dtype);
     g.gain = w.g_h;
     g.gain2 = w.g_e;
     g.eps = c.rms_eps;
@@ -305,17 +328,17 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.err = err;
     g.out = x;
     g.ldo = H;
-    if ((e = timed(h, KC_EH, s, [&] { return launch_gemv(c.dtype, PRO_EH, EPI_STORE, g, kGemvMaxGrid, s); })) != hipSuccess)
+    if ((e = timed(h, KC_EH, s, [&] { return run_gemv(h, PRO_EH, EPI_STORE, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
     // 2. attention RMSNorm + fused QKV projection
     g = GemvParams{};
     g.w0 = w.w_q; g.w1 = w.w_k; g.w2 = w.w_v;
     g.seg1 = nq * d; g.seg2 = (nq + nkv) * d; g.nrows = qkvd;
-    g.ncols = H; g.B = B; g.col_block = col_block_for(H, B, c.dtype);
+    g.ncols = H; g.B = B;
     g.x = x; g.ldx = H; g.gain = w.g_attn; g.eps = c.rms_eps;
     g.out = qkv; g.ldo = qkvd;
-    if ((e = timed(h, KC_QKV, s, [&] { return launch_gemv(c.dtype, PRO_RMS, EPI_STORE, g, kGemvMaxGrid, s); })) != hipSuccess)
+    if ((e = timed(h, KC_QKV, s, [&] { return run_gemv(h, PRO_RMS, EPI_STORE, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
     // 3. RoPE + cache append + split decode attention + merge
@@ -325,11 +348,10 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     a.n_q = nq; a.n_kv = nkv; a.d = d; a.capacity = kv->capacity;
     a.len = kv->len; a.pos = kv->pos; a.step = k;
     a.chunk = chunk; a.nsplit = nsplit;
-    a.theta = c.rope_theta;
+    a.rope = h->at<float>(L.rope) + (size_t)k * B * d;
     a.scale = 1.0f / sqrtf((float)d);
     a.part_o = h->at<float>(L.part_o);
     a.part_ml = h->at<float>(L.part_ml);
-    a.counters = h->at<unsigned>(L.attn_cnt);
     a.o = o;
     a.err = err;
     if ((e = timed(h, KC_ATTN, s, [&] { return launch_attention(c.dtype, a, B, s); })) != hipSuccess)
@@ -339,39 +361,39 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g = GemvParams{};
     g.w0 = g.w1 = g.w2 = w.w_o;
     g.nrows = g.seg1 = g.seg2 = H;
-    g.ncols = nq * d; g.B = B; g.col_block = col_block_for(nq * d, B, c.dtype);
+    g.ncols = nq * d; g.B = B;
     g.x = o; g.ldx = nq * d;
     g.out = x1; g.ldo = H; g.res = x;
-    if ((e = timed(h, KC_OPROJ, s, [&] { return launch_gemv(c.dtype, PRO_PLAIN, EPI_RESID, g, kGemvMaxGrid, s); })) != hipSuccess)
+    if ((e = timed(h, KC_OPROJ, s, [&] { return run_gemv(h, PRO_PLAIN, EPI_RESID, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
     // 5. MLP RMSNorm + gate/up + SiLU * up
     g = GemvParams{};
     g.w0 = w.w_gate; g.w1 = w.w_up; g.w2 = w.w_up;
     g.nrows = g.seg1 = g.seg2 = F;
-    g.ncols = H; g.B = B; g.col_block = col_block_for(H, B, c.dtype);
+    g.ncols = H; g.B = B;
     g.x = x1; g.ldx = H; g.gain = w.g_mlp; g.eps = c.rms_eps;
     g.out = act; g.ldo = F;
-    if ((e = timed(h, KC_GATEUP, s, [&] { return launch_gemv(c.dtype, PRO_RMS, EPI_SWIGLU, g, kGemvMaxGrid, s); })) != hipSuccess)
+    if ((e = timed(h, KC_GATEUP, s, [&] { return run_gemv(h, PRO_RMS, EPI_SWIGLU, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
     // 6. down projection + residual -> h^(k)
     g = GemvParams{};
     g.w0 = g.w1 = g.w2 = w.w_down;
     g.nrows = g.seg1 = g.seg2 = H;
-    g.ncols = F; g.B = B; g.col_block = col_block_for(F, B, c.dtype);
+    g.ncols = F; g.B = B;
     g.x = act; g.ldx = F;
     g.out = hb; g.ldo = H; g.res = x1;
     g.dbg = hidden_out ? hidden_out + (size_t)k * B * H : nullptr;
     g.dbg_ld = H;
-    if ((e = timed(h, KC_DOWN, s, [&] { return launch_gemv(c.dtype, PRO_PLAIN, EPI_RESID, g, kGemvMaxGrid, s); })) != hipSuccess)
+    if ((e = timed(h, KC_DOWN, s, [&] { return run_gemv(h, PRO_PLAIN, EPI_RESID, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
     // 7. final RMSNorm + shared lm_head + argmax -> draft token
     g = GemvParams{};
     g.w0 = g.w1 = g.w2 = w.lm_head;
     g.nrows = g.seg1 = g.seg2 = V;
-    g.ncols = H; g.B = B; g.col_block = col_block_for(H, B, c.dtype);
+    g.ncols = H; g.B = B;
     g.x = hb; g.ldx = H; g.gain = w.g_final; g.eps = c.rms_eps;
     g.keys = h->at<unsigned long long>(L.lm_keys);
     g.counter = h->at<unsigned>(L.lm_cnt);
@@ -382,7 +404,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.logits_ld = V;
     g.len = kv->len; g.pos = kv->pos;
     g.advance = (k == K - 1) ? K : 0;
-    if ((e = timed(h, KC_LMHEAD, s, [&] { return launch_gemv(c.dtype, PRO_RMS, EPI_ARGMAX, g, kGemvMaxGrid, s); })) != hipSuccess)
+    if ((e = timed(h, KC_LMHEAD, s, [&] { return run_gemv(h, PRO_RMS, EPI_ARGMAX, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
   }
   return MTP_OK;

@@ -31,23 +31,23 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) 
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kVerifyThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
-    if (best) atomic_max_key(p.keys + (long)b * (p.K + 1) + j, best);
+    if (best) keep_alive(atomic_max_key(p.keys + (long)b * (p.K + 1) + j, best));
   }
   if (last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) {
-    __threadfence();
+    // Take (and reset) the K+1 row keys and scan for the first mismatch.
     if (threadIdx.x == 0) {
       unsigned long long* kb = p.keys + (long)b * (p.K + 1);
-      int a = 0;
-      while (a < p.K) {
-        const int gtok = (int)key_index(__hip_atomic_load(kb + a, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT));
-        if (p.draft[(long)b * p.K + a] != gtok) break;
-        ++a;
+      int a = 0, next = -1;
+      for (int q = 0; q <= p.K; ++q) {
+        const int t = (int)key_index(take_key(kb + q));
+        if (next < 0) {
+          if (q < p.K && p.draft[(long)b * p.K + q] == t) {
+            ++a;
+          } else {
+            next = t;
+          }
+        }
       }
-      const int next =
-          (int)key_index(__hip_atomic_load(kb + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      for (int q = 0; q <= p.K; ++q)
-        __hip_atomic_store(kb + q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       p.accepted[b] = a;
       p.next[b] = next;
     }

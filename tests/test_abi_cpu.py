@@ -26,6 +26,12 @@ def test_every_declared_symbol_is_exported():
     assert set(names) <= exported
 
 
+def test_no_unresolved_internal_symbols():
+    out = subprocess.run(["nm", "-D", "--undefined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "mtp" not in out, out
+
+
 def test_status_strings():
     for s in range(8):
         assert L.mtp_status_string(s)

@@ -99,6 +99,9 @@ def test_draft_k1_and_k0():
 
 
 def test_determinism_and_batch_independence():
+    """Reruns are bit-identical; a sequence's result does not depend on the rest of the
+    batch (bit-exact between batch sizes served by the same kernels, within the parity
+    tolerance across kernel families)."""
     cfg = CASES["small-bf16-b9-empty"].with_(ctx_lo=20, ctx_hi=90)
     inp = S.make_inputs(cfg, capacity=100)
     a = run_draft(cfg, inp, cfg.K)
@@ -107,8 +110,15 @@ def test_determinism_and_batch_independence():
     assert np.array_equal(a["hidden"], b["hidden"])
     assert np.array_equal(a["k"], b["k"]) and np.array_equal(a["v"], b["v"])
     one = run_draft(cfg, inp, cfg.K, B=1)
-    assert np.array_equal(one["tokens"][0], a["tokens"][0])
-    assert np.array_equal(one["hidden"][:, 0], a["hidden"][:, 0])
+    two = run_draft(cfg, inp, cfg.K, B=2)
+    assert np.array_equal(one["tokens"][0], two["tokens"][0])
+    assert np.array_equal(one["hidden"][:, 0], two["hidden"][:, 0])
+    r = oracle_forced(cfg, inp, cfg.K, a["tokens"])
+    for k in range(cfg.K):
+        if r["margin"][k, 0] > MARGIN:
+            assert one["tokens"][0, k] == a["tokens"][0, k]
+    if np.array_equal(one["tokens"][0], a["tokens"][0]):
+        assert np.max(np.abs(one["hidden"][:, 0] - a["hidden"][:, 0])) < TOL[cfg.dtype]
 
 
 def test_poisoned_stale_slots_do_not_leak():
