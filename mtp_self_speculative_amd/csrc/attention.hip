@@ -19,28 +19,33 @@
 
 namespace mtp {
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kAttnWaves = 8;  // waves per workgroup
+constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kMaxGroup = 8;
-constexpr int kRowBatch = 8;  // rows per lane in flight in phases 1 and 3
+constexpr int kJ1 = 4;   // phase 1: rows per lane per batch (lane groups of LPR lanes)
+constexpr int kJ3 = 16;  // phase 3: rows per wave per batch (one row per wave instruction)
+
+// Positions per workgroup must be a multiple of this.
+int attn_chunk_quantum() { return kAttnWaves * kJ3; }
 
 size_t attn_lds_bytes(int d, int chunk) {
   return sizeof(float) * ((size_t)kMaxGroup * d + 2 * d + (size_t)kMaxGroup * chunk +
                           (size_t)kAttnWaves * kMaxGroup * d);
 }
 
-template <class CT, int D>
+template <class CT, int D, int GP>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   using T = typename CT::T;
   constexpr int VEC = CT::kVec;
-  constexpr int LPR = D / VEC;      // lanes per cache row
-  constexpr int PPW = kWave / LPR;  // rows per wave instruction
+  constexpr int LPR = D / VEC;      // phase 1: lanes per cache row
+  constexpr int PPW = kWave / LPR;  // phase 1: rows per wave instruction
   constexpr int HALF = D / 2;
-  constexpr int RSTEP = kAttnWaves * PPW;  // rows per workgroup instruction
+  constexpr int DPL = D / kWave;    // phase 3: dimensions per lane
+  constexpr int R1 = kAttnWaves * PPW;  // phase 1: rows per workgroup instruction
   extern __shared__ __align__(16) float sm[];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPR, dl = (lane % LPR) * VEC;
   const int G = p.n_q / p.n_kv;
   const int chunk = p.chunk;
@@ -52,183 +57,209 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
 
   const int slot = p.len[b] + p.step;
   const bool overflow = slot >= p.capacity;
-  if (overflow && s == 0 && g == 0 && threadIdx.x == 0) set_error(p.err, 2u);
+  if (overflow && s == 0 && g == 0 && tid == 0) set_error(p.err, 2u);
   const int T_valid = overflow ? p.capacity : slot + 1;
   const int t0 = s * chunk;
   const int t1 = min(t0 + chunk, T_valid);
+  if (t0 >= t1) return;  // nothing cached in this split (the merge skips it)
   const long kv_base = ((long)b * p.n_kv + g) * p.capacity;
   T* kc = static_cast<T*>(p.kc);
   T* vc = static_cast<T*>(p.vc);
-  const int nj = t1 > t0 ? (t1 - t0 + RSTEP - 1) / RSTEP : 0;  // row iterations per lane
-  auto row_of = [&](int j) { return t0 + j * RSTEP + wave * PPW + sub; };
+  const int n = t1 - t0;
 
-  if (t0 < t1) {
-    u32x4 kr[kRowBatch], vr[kRowBatch];
-    auto load_rows = [&](u32x4 (&buf)[kRowBatch], const T* base, int j0) {
+  // ---- set-up operands first (small, cache-resident): q pairs, new k/v, cos/sin. Every
+  // thread loads (threads past HALF duplicate), so no load sits behind a branch.
+  float qa[GP], qb[GP];
+  const float* qkv = p.qkv + (long)b * p.ldqkv;
+  const int ti = tid % HALF;
 #pragma unroll
-      for (int jj = 0; jj < kRowBatch; ++jj) {
-        const int t = row_of(j0 + jj);
-        buf[jj] = (j0 + jj < nj && t < t1 && t != slot)
-                      ? __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4*>(base + (kv_base + t) * D + dl))
-                      : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    load_rows(kr, kc, 0);
-    load_rows(vr, vc, 0);
+  for (int h = 0; h < GP; ++h) {
+    const int hh = g * G + (h < G ? h : G - 1);
+    qa[h] = qkv[(long)hh * D + ti];
+    qb[h] = qkv[(long)hh * D + ti + HALF];
+  }
+  const float k1 = qkv[(long)p.n_q * D + g * D + ti];
+  const float k2 = qkv[(long)p.n_q * D + g * D + ti + HALF];
+  const float v1 = qkv[(long)(p.n_q + p.n_kv) * D + g * D + ti];
+  const float v2 = qkv[(long)(p.n_q + p.n_kv) * D + g * D + ti + HALF];
+  const float cs = p.rope[(long)b * D + ti];
+  const float sn = p.rope[(long)b * D + HALF + ti];
+  __builtin_amdgcn_sched_barrier(0);  // set-up loads stay ahead of the K/V stream
 
-    // ---- q (G heads) and the new k, v; RoPE from the step's table; round to cache dtype
-    const float* qkv = p.qkv + (long)b * p.ldqkv;
-    for (int i = threadIdx.x; i < G * D; i += kAttnThreads) q_l[i] = qkv[(long)g * G * D + i];
-    for (int i = threadIdx.x; i < D; i += kAttnThreads) {
-      kn[i] = qkv[(long)p.n_q * D + g * D + i];
-      vn[i] = qkv[(long)(p.n_q + p.n_kv) * D + g * D + i];
+  // ---- first batches of K rows (16-byte lane groups) and V rows (lane owns DPL dims)
+  const int nj1 = (n + R1 - 1) / R1;          // phase-1 row iterations per lane
+  const int nj3 = (n + kAttnWaves - 1) / kAttnWaves;  // phase-3 rows per wave
+  auto row1 = [&](int j) { return t0 + j * R1 + wave * PPW + sub; };
+  auto row3 = [&](int j) { return t0 + j * kAttnWaves + wave; };
+  // Rows past the chunk are clamped to its last row (loaded, then ignored); the new
+  // slot's row is loaded too (stale) and replaced by the values computed here.
+  u32x4 kr[kJ1];
+  auto load_k = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < kJ1; ++jj) {
+      int t = row1(j0 + jj);
+      t = t < t1 ? t : t1 - 1;
+      kr[jj] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kc + (kv_base + t) * D + dl));
     }
-    __syncthreads();
-    const float* tab = p.rope + (long)b * D;  // [HALF] cos, then [HALF] sin
-    for (int i = threadIdx.x; i < HALF; i += kAttnThreads) {
-      const float c = tab[i], sn = tab[HALF + i];
-      for (int h = 0; h < G; ++h) {
-        const float x1 = q_l[h * D + i], x2 = q_l[h * D + i + HALF];
-        q_l[h * D + i] = x1 * c - x2 * sn;
-        q_l[h * D + i + HALF] = x2 * c + x1 * sn;
-      }
-      const float x1 = kn[i], x2 = kn[i + HALF];
-      T b1, b2, v1, v2;
-      CT::put(&b1, 0, x1 * c - x2 * sn);
-      CT::put(&b2, 0, x2 * c + x1 * sn);
-      CT::put(&v1, 0, vn[i]);
-      CT::put(&v2, 0, vn[i + HALF]);
-      kn[i] = CT::get(&b1, 0);
-      kn[i + HALF] = CT::get(&b2, 0);
-      vn[i] = CT::get(&v1, 0);
-      vn[i + HALF] = CT::get(&v2, 0);
-      if (!overflow && slot >= t0 && slot < t0 + chunk) {
-        const long o = (kv_base + slot) * D;
-        kc[o + i] = b1;
-        kc[o + i + HALF] = b2;
-        vc[o + i] = v1;
-        vc[o + i + HALF] = v2;
+  };
+  using VT = typename CT::template Vec<DPL>;
+  VT vr[kJ3];
+  auto load_v = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < kJ3; ++jj) {
+      int t = row3(j0 + jj);
+      t = t < t1 ? t : t1 - 1;
+      vr[jj] = CT::template load_vec<DPL>(vc + (kv_base + t) * D + lane * DPL);
+    }
+  };
+  load_k(0);
+  load_v(0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- RoPE (rotate-half) on q and the new key; round k, v to the cache dtype
+  if (tid < HALF) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      if (h < G) {
+        q_l[h * D + tid] = qa[h] * cs - qb[h] * sn;
+        q_l[h * D + tid + HALF] = qb[h] * cs + qa[h] * sn;
       }
     }
-    __syncthreads();
+    T b1, b2, w1, w2;
+    CT::put(&b1, 0, k1 * cs - k2 * sn);
+    CT::put(&b2, 0, k2 * cs + k1 * sn);
+    CT::put(&w1, 0, v1);
+    CT::put(&w2, 0, v2);
+    kn[tid] = CT::get(&b1, 0);
+    kn[tid + HALF] = CT::get(&b2, 0);
+    vn[tid] = CT::get(&w1, 0);
+    vn[tid + HALF] = CT::get(&w2, 0);
+  }
+  __syncthreads();
 
-    // ---- phase 1: scores
-    {
-      float qr[kMaxGroup][VEC];
+  // ---- phase 1: scores s[h][t] = q_h . k_t * scale (GP >= G heads; the padding heads
+  // compute scores that are never stored)
+  {
+    float qr[GP][VEC];
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h)
+    for (int h = 0; h < GP; ++h)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) qr[h][e] = (h < G) ? q_l[h * D + dl + e] : 0.f;
-      for (int j0 = 0; j0 < nj; j0 += kRowBatch) {
-        if (j0 > 0) load_rows(kr, kc, j0);
+      for (int e = 0; e < VEC; ++e) qr[h][e] = q_l[(h < G ? h : 0) * D + dl + e];
+    float knr[VEC];
 #pragma unroll
-        for (int jj = 0; jj < kRowBatch; ++jj) {
-          if (j0 + jj >= nj) break;
-          const int t = row_of(j0 + jj);
-          float kv[VEC];
-          CT::unpack(kr[jj], kv);
-          if (t == slot) {
+    for (int e = 0; e < VEC; ++e) knr[e] = kn[dl + e];
+    for (int j0 = 0; j0 < nj1; j0 += kJ1) {
+      if (j0 > 0) load_k(j0);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) kv[e] = kn[dl + e];
-          }
+      for (int jj = 0; jj < kJ1; ++jj) {
+        const int t = row1(j0 + jj);
+        const bool is_new = t == slot;
+        float kv[VEC];
+        CT::unpack(kr[jj], kv);
 #pragma unroll
-          for (int h = 0; h < kMaxGroup; ++h) {
-            if (h < G) {
-              float part = 0.f;
+        for (int e = 0; e < VEC; ++e) kv[e] = is_new ? knr[e] : kv[e];
+        float part[GP];
 #pragma unroll
-              for (int e = 0; e < VEC; ++e) part = fmaf(qr[h][e], kv[e], part);
-              part = group_sum<LPR>(part);
-              if ((lane % LPR) == 0 && t < t1) sc[h * chunk + (t - t0)] = part * p.scale;
-            }
+        for (int h = 0; h < GP; ++h) {
+          part[h] = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) part[h] = fmaf(qr[h][e], kv[e], part[h]);
+        }
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          if constexpr (LPR <= 16) {
+            part[h] = dpp_group_sum<LPR>(part[h]);
+          } else {
+            part[h] = dpp_group_sum<16>(part[h]);
+            part[h] += __shfl_xor(part[h], 16, kWave);
           }
         }
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 2: per-head max, exp, sum over the chunk
-    const int n = t1 - t0;
-    const long hbase = (long)b * p.n_q + g * G;
-    for (int h = wave; h < G; h += kAttnWaves) {
-      float m = -INFINITY;
-      for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[h * chunk + i]);
-      m = wave_max(m);
-      float l = 0.f;
-      for (int i = lane; i < n; i += kWave) {
-        const float e = expf(sc[h * chunk + i] - m);
-        sc[h * chunk + i] = e;
-        l += e;
-      }
-      l = wave_sum(l);
-      if (lane == 0) {
-        p.part_ml[((hbase + h) * p.nsplit + s) * 2 + 0] = m;
-        p.part_ml[((hbase + h) * p.nsplit + s) * 2 + 1] = l;
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 3: unnormalised P.V
-    {
-      float acc[kMaxGroup][VEC];
+        if ((lane % LPR) == 0 && t < t1) {
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
-      for (int j0 = 0; j0 < nj; j0 += kRowBatch) {
-        if (j0 > 0) load_rows(vr, vc, j0);
-#pragma unroll
-        for (int jj = 0; jj < kRowBatch; ++jj) {
-          if (j0 + jj >= nj) break;
-          const int t = row_of(j0 + jj);
-          if (t >= t1) continue;
-          float vv[VEC];
-          CT::unpack(vr[jj], vv);
-          if (t == slot) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) vv[e] = vn[dl + e];
-          }
-#pragma unroll
-          for (int h = 0; h < kMaxGroup; ++h) {
-            if (h < G) {
-              const float pr = sc[h * chunk + (t - t0)];
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(pr, vv[e], acc[h][e]);
-            }
-          }
+          for (int h = 0; h < GP; ++h)
+            if (h < G) sc[h * chunk + (t - t0)] = part[h] * p.scale;
         }
-      }
-      // reduce over the PPW row groups of the wave (lanes with the same dl)
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < G) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            float v = acc[h][e];
-#pragma unroll
-            for (int m = LPR; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-            acc[h][e] = v;
-          }
-        }
-      }
-      if (sub == 0) {
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h)
-          if (h < G)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) ored[(wave * kMaxGroup + h) * D + dl + e] = acc[h][e];
-      }
-      __syncthreads();
-      for (int i = threadIdx.x; i < G * D; i += kAttnThreads) {
-        const int h = i / D, dd = i % D;
-        float o = 0.f;
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) o += ored[(w * kMaxGroup + h) * D + dd];
-        p.part_o[((hbase + h) * p.nsplit + s) * D + dd] = o;
       }
     }
   }
+  __syncthreads();
 
+  // ---- phase 2: per-head max, exp, sum over the chunk
+  const long hbase = (long)b * p.n_q + g * G;
+  for (int h = wave; h < G; h += kAttnWaves) {
+    float m = -INFINITY;
+    for (int i = lane; i < n; i += kWave) m = fmaxf(m, sc[h * chunk + i]);
+    m = wave_max_fast(m);
+    float l = 0.f;
+    for (int i = lane; i < n; i += kWave) {
+      const float e = expf(sc[h * chunk + i] - m);
+      sc[h * chunk + i] = e;
+      l += e;
+    }
+    l = wave_sum_fast(l);
+    if (lane == 0) {
+      p.part_ml[((hbase + h) * p.nsplit + s) * 2 + 0] = m;
+      p.part_ml[((hbase + h) * p.nsplit + s) * 2 + 1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: unnormalised P.V; lane owns dims lane*DPL .. +DPL-1, waves own rows.
+  // Branch-free: rows past the chunk get weight 0, the new slot's row is selected from LDS.
+  {
+    float acc[GP][DPL];
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    float vnr[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vnr[e] = vn[lane * DPL + e];
+    for (int j0 = 0; j0 < nj3; j0 += kJ3) {
+      if (j0 > 0) load_v(j0);
+      float pr[kJ3][GP];
+#pragma unroll
+      for (int jj = 0; jj < kJ3; ++jj) {
+        const int t = row3(j0 + jj);
+        const int tc = (t < t1 ? t : t1 - 1) - t0;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) pr[jj][h] = sc[(h < G ? h : 0) * chunk + tc];
+      }
+#pragma unroll
+      for (int jj = 0; jj < kJ3; ++jj) {
+        const int t = row3(j0 + jj);
+        const bool live = t < t1;
+        float vv[DPL];
+        CT::template unpack_vec<DPL>(vr[jj], vv);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vv[e] = live ? (t == slot ? vnr[e] : vv[e]) : 0.f;
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pr[jj][h], vv[e], acc[h][e]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+      if (h < G)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ored[(wave * kMaxGroup + h) * D + lane * DPL + e] = acc[h][e];
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kAttnThreads) {
+      const int h = i / D, dd = i % D;
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) o += ored[(w * kMaxGroup + h) * D + dd];
+      p.part_o[((hbase + h) * p.nsplit + s) * D + dd] = o;
+    }
+  }
+  // ---- the workgroup whose chunk holds the new slot appends it to the cache
+  if (!overflow && slot >= t0 && slot < t0 + chunk && tid < D) {
+    const long o = (kv_base + slot) * D + tid;
+    CT::put(kc, o, kn[tid]);
+    CT::put(vc, o, vn[tid]);
+  }
 }
 
 // Merge the splits of one (query head, sequence): o = sum_q w_q o_q with
@@ -265,7 +296,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
   float L = 0.f;
   for (int i = 0; i < D / kWave; ++i) L += red[i];
   const float* po = p.part_o + hb * p.nsplit * D + t;
-  constexpr int UB = 16;
+  constexpr int UB = 32;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < nvalid; q0 += UB) {
     float v[UB];
@@ -278,31 +309,56 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
   p.o[hb * D + t] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / L;
 }
 
-__global__ void rope_tables_kernel(float* tab, const int* pos, int B, int K, int d,
-                                   float theta) {
+// Per-call set-up: RoPE tables of the K steps (tab[k][b][0..d/2) = cos, [d/2..d) = sin of
+// (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded to fp32) and the verifier
+// hidden state widened to fp32 (the first step's input).
+template <class CT>
+__global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int d, float theta,
+                                   const void* hidden, float* hf, int H) {
   const int half = d / 2;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= K * B * half) return;
-  const int i = e % half, kb = e / half, b = kb % B, k = kb / B;
-  const double inv = pow((double)theta, -2.0 * (double)i / (double)d);
-  const double ang = (double)(pos[b] + k) * inv;
-  tab[(long)kb * d + i] = (float)cos(ang);
-  tab[(long)kb * d + half + i] = (float)sin(ang);
+  if (e < K * B * half) {
+    const int i = e % half, kb = e / half, b = kb % B, k = kb / B;
+    const double inv = pow((double)theta, -2.0 * (double)i / (double)d);
+    const double ang = (double)(pos[b] + k) * inv;
+    tab[(long)kb * d + i] = (float)cos(ang);
+    tab[(long)kb * d + half + i] = (float)sin(ang);
+  }
+  if (e < B * H) hf[e] = CT::get(static_cast<const typename CT::T*>(hidden), e);
 }
 
-hipError_t launch_rope_tables(float* tab, const int* pos, int B, int K, int d, float theta,
-                              hipStream_t s) {
-  const int n = K * B * (d / 2);
-  hipLaunchKernelGGL(rope_tables_kernel, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos, B, K,
-                     d, theta);
+hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
+                              float theta, const void* hidden, float* hf, int H, hipStream_t s) {
+  const int n1 = K * B * (d / 2), n2 = B * H;
+  const int n = n1 > n2 ? n1 : n2;
+  if (dtype == 0)
+    hipLaunchKernelGGL(draft_setup_kernel<F32>, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos,
+                       B, K, d, theta, hidden, hf, H);
+  else
+    hipLaunchKernelGGL(draft_setup_kernel<BF16>, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos,
+                       B, K, d, theta, hidden, hf, H);
+  return hipGetLastError();
+}
+
+template <class CT, int D, int GP>
+static hipError_t launch_attn_g(const AttnParams& p, int B, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<CT, D, GP>), dim3(p.nsplit, p.n_kv, B), dim3(kAttnThreads),
+                     attn_lds_bytes(D, p.chunk), s, p);
   return hipGetLastError();
 }
 
 template <class CT, int D>
 static hipError_t launch_attn_t(const AttnParams& p, int B, hipStream_t s) {
-  if (p.nsplit > 256 || p.nsplit < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<CT, D>), dim3(p.nsplit, p.n_kv, B), dim3(kAttnThreads),
-                     attn_lds_bytes(D, p.chunk), s, p);
+  if (p.nsplit > 256 || p.nsplit < 1 || p.chunk % attn_chunk_quantum() != 0)
+    return hipErrorInvalidValue;
+  const int G = p.n_q / p.n_kv;
+  hipError_t e0;
+  if (G <= 1) e0 = launch_attn_g<CT, D, 1>(p, B, s);
+  else if (G <= 2) e0 = launch_attn_g<CT, D, 2>(p, B, s);
+  else if (G <= 4) e0 = launch_attn_g<CT, D, 4>(p, B, s);
+  else if (G <= 8) e0 = launch_attn_g<CT, D, 8>(p, B, s);
+  else return hipErrorInvalidValue;
+  if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(p.n_q, B), dim3(D), 0, s, p);

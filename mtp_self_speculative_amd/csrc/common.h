@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mtp {
 
 constexpr int kWave = 64;
@@ -47,6 +49,28 @@ struct F32 {
   __device__ static void put(T* p, long i, float f) { p[i] = f; }
   // 8 consecutive elements (16-byte aligned) as floats.
   __device__ static void load8(const T* p, float* o) { load8_f32(p, o); }
+  // N consecutive elements (N = 1 or 2) loaded as one naturally aligned access.
+  template <int N>
+  struct VecT { float v[N]; };
+  template <int N>
+  using Vec = VecT<N>;
+  template <int N>
+  __device__ static Vec<N> load_vec(const T* p) {
+    Vec<N> r;
+    if constexpr (N == 2) {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+      r.v[0] = t.x; r.v[1] = t.y;
+    } else {
+      r.v[0] = __builtin_nontemporal_load(p);
+    }
+    return r;
+  }
+  template <int N>
+  __device__ static void unpack_vec(const Vec<N>& r, float* o) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] = r.v[i];
+  }
 };
 struct BF16 {
   using T = uint16_t;
@@ -60,7 +84,66 @@ struct BF16 {
   __device__ static void load8(const T* p, float* o) {
     unpack(*reinterpret_cast<const u32x4*>(p), o);
   }
+  // N consecutive elements (N = 1 or 2) loaded as one naturally aligned access.
+  template <int N>
+  using Vec = typename std::conditional<N == 2, uint32_t, uint16_t>::type;
+  template <int N>
+  __device__ static Vec<N> load_vec(const T* p) {
+    if constexpr (N == 2) {
+      return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    } else {
+      return __builtin_nontemporal_load(p);
+    }
+  }
+  template <int N>
+  __device__ static void unpack_vec(const Vec<N>& r, float* o) {
+    if constexpr (N == 2) {
+      o[0] = bf16_lo(r);
+      o[1] = bf16_hi(r);
+    } else {
+      o[0] = bf16_to_f32(r);
+    }
+  }
 };
+
+// ---------------------------------------------------------------- DPP lane movement
+// gfx9 DPP controls: quad_perm(a,b,c,d) = a | b<<2 | c<<4 | d<<6, row_mirror = 0x140,
+// row_half_mirror = 0x141. Rows are groups of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of W lanes (W = 2, 4, 8 or 16) with DPP; every lane of the
+// group ends with the group's sum.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group of 2..16 lanes");
+  v += dpp<0xB1>(v);                      // lane ^ 1
+  if constexpr (W >= 4) v += dpp<0x4E>(v);  // lane ^ 2
+  if constexpr (W >= 8) v += dpp<0x141>(v); // mirror within 8 lanes
+  if constexpr (W >= 16) v += dpp<0x140>(v); // mirror within 16 lanes
+  return v;
+}
+// Sum over the 64-lane wave, result uniform in every lane.
+__device__ __forceinline__ float wave_sum_fast(float v) {
+  v = dpp_group_sum<16>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+__device__ __forceinline__ float wave_max_fast(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
 
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_sum(float v) {
@@ -92,7 +175,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 // Sum of `v` over the workgroup; `red` holds >= blockDim/64 floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = wave_sum(v);
+  v = wave_sum_fast(v);
   __syncthreads();
   if (lane == 0) red[w] = v;
   __syncthreads();

@@ -3,11 +3,13 @@
 // Each wave owns the logical rows gw, gw + nw, ... (nw = waves in the grid) and walks
 // them in stages of CH 16-byte chunks per lane (CH KiB of one row per wave instruction
 // group). Two register buffers alternate: while one stage is consumed the next is in
-// flight, so every wave keeps up to 2*CH KiB requested; the grid is sized to a few
-// workgroups per CU so that the whole chip streams without re-staging the input. The
-// first two stages are requested before the prologue (token gather, RMS reductions,
-// staging of the fp32 input vector into LDS), hiding the prologue behind the first
-// HBM round trip. Weight loads are non-temporal: each byte is used once.
+// flight. Every load is unconditional (addresses past the end are clamped to valid
+// data and meet zeros in the LDS copy of the input), so the compiler can count
+// outstanding loads exactly and wait only for the buffer being consumed. The grid is
+// sized to a few workgroups per CU so that the whole chip streams without re-staging
+// the input. The input-vector loads of the prologue go out first, then the first two
+// weight stages, so the norm reduction and the staging of the fp32 input vector into
+// LDS overlap the first HBM round trip. Weight loads are non-temporal (used once).
 //
 // A logical row has P parts read with the same input vector: P = 2 streams the gate
 // and up rows of one SwiGLU unit together. The epilogues are those of the general
@@ -17,34 +19,35 @@
 
 namespace mtp {
 
-template <class WT>
-__device__ __forceinline__ float ld_h(const void* p, long i, int is_f32) {
-  return is_f32 ? static_cast<const float*>(p)[i]
-                : WT::get(static_cast<const typename WT::T*>(p), i);
-}
+constexpr int kPipeWPB = 4;
+constexpr int kPipeCH = 4;
+constexpr size_t kPipeMaxLds = 64 * 1024;
 
 template <class WT, int NB, int P, int CH, int WPB, int PRO, int EPI>
 __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
   using T = typename WT::T;
   constexpr int VEC = WT::kVec;
   constexpr int SW = CH * kWave * VEC;  // columns per stage
-  extern __shared__ __align__(16) float xs[];  // [NB][ncols]
+  constexpr int NT = WPB * kWave;
+  constexpr int SLOTS = 2;              // prologue: 8-element groups per thread per batch
+  constexpr int NPART = (PRO == PRO_EH) ? 2 : 1;
+  extern __shared__ __align__(16) float xs[];  // [NB][ldl], zero beyond ncols
   __shared__ float red[WPB];
   __shared__ unsigned long long kred[WPB][NB];
   __shared__ int tok_s[NB];
   __shared__ int flag;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nthreads = WPB * kWave;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncols = p.ncols;
   const int nw = gridDim.x * WPB;
   const int gw = blockIdx.x * WPB + wave;
   const int S = (ncols + SW - 1) / SW;
+  const int ldl = S * SW;
   const int nrows_w = gw < p.nrows ? (p.nrows - 1 - gw) / nw + 1 : 0;
   const int items = nrows_w * S;
   const int B = p.B;
 
-  // Row base pointers of part q of logical row r.
+  // Row base pointer of part q of logical row r.
   auto row_ptr = [&](int r, int q) -> const T* {
     if constexpr (P == 2) {
       return static_cast<const T*>(q ? p.w1 : p.w0) + (long)r * ncols;
@@ -54,154 +57,146 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
       return static_cast<const T*>(p.w2) + (long)(r - p.seg2) * ncols;
     }
   };
-
   u32x4 A[P][CH], Bf[P][CH];
   auto load = [&](u32x4 (&buf)[P][CH], int it) {
-    const bool ok = it < items;
-    const int r = ok ? gw + (it / S) * nw : 0;
-    const int c0 = ok ? (it % S) * SW : 0;
+    const int itc = it < items ? it : (items > 0 ? items - 1 : 0);
+    const int r = items > 0 ? gw + (itc / S) * nw : 0;
+    const int c0 = (itc % S) * SW;
 #pragma unroll
     for (int q = 0; q < P; ++q) {
-      const T* rp = row_ptr(r, q) + c0 + lane * VEC;
+      const T* rp = row_ptr(r, q);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const int col = c0 + c * kWave * VEC + lane * VEC;
-        buf[q][c] = (ok && col < ncols)
-                        ? __builtin_nontemporal_load(
-                              reinterpret_cast<const u32x4*>(rp + c * kWave * VEC))
-                        : u32x4{0u, 0u, 0u, 0u};
+        int col = c0 + c * kWave * VEC + lane * VEC;
+        col = col < ncols ? col : ncols - VEC;
+        buf[q][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + col));
       }
     }
   };
-
-  load(A, 0);
-  load(Bf, 1);
 
   // ---- residual operands of this wave's first rows: lane l holds row gw + l*nw
   float resv[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) resv[i] = 0.f;
   if constexpr (EPI == EPI_RESID) {
-    if (lane < nrows_w) {
+    const int rr = lane < nrows_w ? gw + lane * nw : 0;
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < B) resv[i] = p.res[(long)i * p.ldo + gw + lane * nw];
-    }
+    for (int i = 0; i < NB; ++i) resv[i] = p.res[(long)(i < B ? i : 0) * p.ldo + rr];
   }
 
-  // ---- prologue: fp32 input vectors (normalised where needed) into LDS. Every thread
-  // owns 8-element groups c = (slot * nthreads + tid) * 8; all loads of a batch are in
-  // flight together and the values stay in registers between the reduction and staging.
-  constexpr int SLOTS = 2;
-  const int per_batch = nthreads * 8 * SLOTS;
-  const T* gain = static_cast<const T*>(p.gain);
-  const T* gain2 = static_cast<const T*>(p.gain2);
+  // ---- prologue loads: thread owns 8-element groups c = (slot * NT + tid) * 8
   if constexpr (PRO == PRO_EH) {
-    if (threadIdx.x < NB) {
-      const int b = threadIdx.x;
+    if (tid < NB) {
       int t = 0;
-      if (b < B) {
-        t = p.tok[(long)b * p.tok_stride];
+      if (tid < B) {
+        t = p.tok[(long)tid * p.tok_stride];
         if (t < 0 || t >= p.vocab) {
           if (blockIdx.x == 0) set_error(p.err, 1u);
           t = 0;
         }
       }
-      tok_s[b] = t;
+      tok_s[tid] = t;
     }
     __syncthreads();
   }
   const int Hh = (PRO == PRO_EH) ? ncols / 2 : ncols;  // length of one normalised part
+  const int per_batch = NT * 8 * SLOTS;
+  float v[NB][NPART][SLOTS][8];
+  float gv[NPART][SLOTS][8];
+  const T* gains[2] = {static_cast<const T*>(p.gain), static_cast<const T*>(p.gain2)};
+  auto fetch = [&](int i, int q, int base) {
+    const int ib = i < B ? i : 0;
+#pragma unroll
+    for (int sl = 0; sl < SLOTS; ++sl) {
+      int c = base + (sl * NT + tid) * 8;
+      c = c < Hh ? c : Hh - 8;
+      if constexpr (PRO != PRO_PLAIN) {
+        if (i == 0) WT::load8(gains[q] + c, gv[q][sl]);
+      }
+      if constexpr (PRO == PRO_PLAIN || PRO == PRO_RMS) {
+        load8_f32(p.x + (long)ib * p.ldx + c, v[i][q][sl]);
+      } else if (q == 0) {
+        load8_f32(static_cast<const float*>(p.h) + (long)ib * p.ldh + c, v[i][q][sl]);
+      } else {
+        WT::load8(static_cast<const T*>(p.embed) + (long)tok_s[ib] * Hh + c, v[i][q][sl]);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int q = 0; q < NPART; ++q) fetch(i, q, 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the input loads ahead of the weight stream
+
+  load(A, 0);
+  load(Bf, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- prologue: fp32 input vectors (normalised where needed) into LDS
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    float* dst = xs + i * ncols;
-    if (i >= B) {
-      for (int c = threadIdx.x; c < ncols; c += nthreads) dst[c] = 0.f;
-      continue;
-    }
+    float* dst = xs + (long)i * ldl;
+    const bool live = i < B;
+    float rsq[NPART];
     if constexpr (PRO == PRO_PLAIN) {
-      const float* xb = p.x + (long)i * p.ldx;
-      for (int base = 0; base < ncols; base += per_batch) {
-        float v[SLOTS][8];
-#pragma unroll
-        for (int sl = 0; sl < SLOTS; ++sl) {
-          const int c = base + (sl * nthreads + threadIdx.x) * 8;
-          if (c < ncols) load8_f32(xb + c, v[sl]);
-        }
-#pragma unroll
-        for (int sl = 0; sl < SLOTS; ++sl) {
-          const int c = base + (sl * nthreads + threadIdx.x) * 8;
-          if (c < ncols) store8_lds(dst + c, v[sl]);
-        }
-      }
+      rsq[0] = 1.f;
     } else {
-      // One or two parts of length Hh, each RMS-normalised with its own gain.
-      constexpr int NPART = (PRO == PRO_EH) ? 2 : 1;
       float ssum[NPART];
 #pragma unroll
       for (int q = 0; q < NPART; ++q) ssum[q] = 0.f;
-      const bool one_batch = Hh <= per_batch;
-      float v[NPART][SLOTS][8];
-      auto fetch = [&](int q, int base) {
-#pragma unroll
-        for (int sl = 0; sl < SLOTS; ++sl) {
-          const int c = base + (sl * nthreads + threadIdx.x) * 8;
-          if (c < Hh) {
-            if constexpr (PRO == PRO_RMS) {
-              load8_f32(p.x + (long)i * p.ldx + c, v[q][sl]);
-            } else if (q == 0) {
-              if (p.h_is_f32)
-                load8_f32(static_cast<const float*>(p.h) + (long)i * p.ldh + c, v[q][sl]);
-              else
-                WT::load8(static_cast<const T*>(p.h) + (long)i * p.ldh + c, v[q][sl]);
-            } else {
-              WT::load8(static_cast<const T*>(p.embed) + (long)tok_s[i] * Hh + c, v[q][sl]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[q][sl][e] = 0.f;
-          }
-        }
-      };
       for (int base = 0; base < Hh; base += per_batch) {
+        if (base > 0) {
 #pragma unroll
-        for (int q = 0; q < NPART; ++q) fetch(q, base);
+          for (int q = 0; q < NPART; ++q) fetch(i, q, base);
+        }
 #pragma unroll
         for (int q = 0; q < NPART; ++q)
 #pragma unroll
-          for (int sl = 0; sl < SLOTS; ++sl)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ssum[q] = fmaf(v[q][sl][e], v[q][sl][e], ssum[q]);
-      }
-      float tot[NPART];
-#pragma unroll
-      for (int q = 0; q < NPART; ++q) tot[q] = block_sum(ssum[q], red);
-      float rsq[NPART];
-#pragma unroll
-      for (int q = 0; q < NPART; ++q) rsq[q] = 1.0f / sqrtf(tot[q] / (float)Hh + p.eps);
-      for (int base = 0; base < Hh; base += per_batch) {
-        if (!one_batch) {
-#pragma unroll
-          for (int q = 0; q < NPART; ++q) fetch(q, base);
-        }
-#pragma unroll
-        for (int q = 0; q < NPART; ++q) {
-          const T* gq = q == 0 ? gain : gain2;
-#pragma unroll
           for (int sl = 0; sl < SLOTS; ++sl) {
-            const int c = base + (sl * nthreads + threadIdx.x) * 8;
-            if (c < Hh) {
-              float gv[8];
-              WT::load8(gq + c, gv);
-              float o[8];
+            const bool in = base + (sl * NT + tid) * 8 < Hh;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) o[e] = v[q][sl][e] * rsq[q] * gv[e];
-              store8_lds(dst + q * Hh + c, o);
+            for (int e = 0; e < 8; ++e) {
+              const float x = in ? v[i][q][sl][e] : 0.f;
+              ssum[q] = fmaf(x, x, ssum[q]);
             }
+          }
+      }
+#pragma unroll
+      for (int q = 0; q < NPART; ++q) {
+        const float tot = block_sum(ssum[q], red);
+        rsq[q] = 1.0f / sqrtf(tot / (float)Hh + p.eps);
+      }
+    }
+    for (int base = 0; base < Hh; base += per_batch) {
+      if (base > 0 && (PRO == PRO_PLAIN || Hh > per_batch)) {
+#pragma unroll
+        for (int q = 0; q < NPART; ++q) fetch(i, q, base);
+      }
+#pragma unroll
+      for (int q = 0; q < NPART; ++q) {
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) {
+          const int c = base + (sl * NT + tid) * 8;
+          if (c < Hh) {
+            float o[8];
+            if constexpr (PRO == PRO_PLAIN) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] = live ? v[i][q][sl][e] : 0.f;
+            } else {
+              if (base > 0) {
+                const int cc = c < Hh ? c : Hh - 8;
+                WT::load8(gains[q] + cc, gv[q][sl]);
+              }
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                o[e] = live ? v[i][q][sl][e] * rsq[q] * gv[q][sl][e] : 0.f;
+            }
+            store8_lds(dst + q * Hh + c, o);
           }
         }
       }
     }
+    for (int c = ncols + tid; c < ldl; c += NT) dst[c] = 0.f;
   }
   __syncthreads();
 
@@ -220,23 +215,21 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int col = c0 + c * kWave * VEC + lane * VEC;
-      if (col < ncols) {
-        float wf[P][VEC];
+      float wf[P][VEC];
 #pragma unroll
-        for (int q = 0; q < P; ++q) WT::unpack(buf[q][c], wf[q]);
+      for (int q = 0; q < P; ++q) WT::unpack(buf[q][c], wf[q]);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          float xv[VEC];
+      for (int i = 0; i < NB; ++i) {
+        float xv[VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; e += 4) {
-            const float4 t4 = *reinterpret_cast<const float4*>(xs + i * ncols + col + e);
-            xv[e] = t4.x; xv[e + 1] = t4.y; xv[e + 2] = t4.z; xv[e + 3] = t4.w;
-          }
-#pragma unroll
-          for (int q = 0; q < P; ++q)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[q][i] = fmaf(wf[q][e], xv[e], acc[q][i]);
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 t4 = *reinterpret_cast<const float4*>(xs + (long)i * ldl + col + e);
+          xv[e] = t4.x; xv[e + 1] = t4.y; xv[e + 2] = t4.z; xv[e + 3] = t4.w;
         }
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[q][i] = fmaf(wf[q][e], xv[e], acc[q][i]);
       }
     }
     if (it % S == S - 1) {
@@ -245,7 +238,7 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
 #pragma unroll
       for (int q = 0; q < P; ++q)
 #pragma unroll
-        for (int i = 0; i < NB; ++i) acc[q][i] = wave_sum(acc[q][i]);
+        for (int i = 0; i < NB; ++i) acc[q][i] = wave_sum_fast(acc[q][i]);
       float rvv[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) rvv[i] = j < kWave ? __shfl(resv[i], j, kWave) : 0.f;
@@ -261,9 +254,9 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
             p.out[o] = acc[0][i];
           } else if constexpr (EPI == EPI_RESID) {
             const float rv = j < kWave ? rvv[i] : p.res[o];
-            const float v = rv + acc[0][i];
-            p.out[o] = v;
-            if (p.dbg) p.dbg[(long)i * p.dbg_ld + r] = v;
+            const float y = rv + acc[0][i];
+            p.out[o] = y;
+            if (p.dbg) p.dbg[(long)i * p.dbg_ld + r] = y;
           } else {
             const unsigned long long k = pack_key(acc[0][i], (uint32_t)r);
             best[i] = k > best[i] ? k : best[i];
@@ -292,13 +285,13 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
       for (int i = 0; i < NB; ++i) kred[wave][i] = best[i];
     }
     __syncthreads();
-    if (threadIdx.x < NB && (int)threadIdx.x < B) {
+    if (tid < NB && tid < B) {
       unsigned long long k = 0ull;
-      for (int w = 0; w < WPB; ++w) k = kred[w][threadIdx.x] > k ? kred[w][threadIdx.x] : k;
-      if (k) keep_alive(atomic_max_key(p.keys + threadIdx.x, k));
+      for (int w = 0; w < WPB; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
+      if (k) keep_alive(atomic_max_key(p.keys + tid, k));
     }
     if (last_to_arrive(p.counter, gridDim.x, &flag)) {
-      for (int b = threadIdx.x; b < B; b += nthreads) {
+      for (int b = tid; b < B; b += NT) {
         const unsigned long long k = take_key(p.keys + b);
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
         if (p.maxlogit) p.maxlogit[b] = key_value(k);
@@ -311,17 +304,19 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
   }
 }
 
-constexpr int kPipeWPB = 4;
-constexpr int kPipeCH = 4;
-constexpr size_t kPipeMaxLds = 64 * 1024;
+static int pipe_stage_cols(int wdtype) { return kPipeCH * kWave * (wdtype == 0 ? 4 : 8); }
 
-bool gemv_pipe_fits(int ncols, int B) {
-  return B >= 1 && B <= 2 && (size_t)B * ncols * sizeof(float) <= kPipeMaxLds;
+bool gemv_pipe_fits(int ncols, int B, int wdtype) {
+  const int sw = pipe_stage_cols(wdtype);
+  const size_t ldl = (size_t)(ncols + sw - 1) / sw * sw;
+  return B >= 1 && B <= 2 && ncols >= 8 && ldl * B * sizeof(float) <= kPipeMaxLds;
 }
 
 template <class WT, int NB, int P, int PRO, int EPI>
 static hipError_t pipe_one(const GemvParams& p, int grid, hipStream_t s) {
-  const size_t lds = (size_t)NB * p.ncols * sizeof(float);
+  const int sw = kPipeCH * kWave * WT::kVec;
+  const size_t ldl = (size_t)(p.ncols + sw - 1) / sw * sw;
+  const size_t lds = (size_t)NB * ldl * sizeof(float);
   hipLaunchKernelGGL((gemv_pipe_kernel<WT, NB, P, kPipeCH, kPipeWPB, PRO, EPI>), dim3(grid),
                      dim3(kPipeWPB * 64), lds, s, p);
   return hipGetLastError();
@@ -344,18 +339,24 @@ static hipError_t pipe_dt(Pro pro, Epi epi, const GemvParams& p, int grid, hipSt
   return hipErrorInvalidValue;
 }
 
-int gemv_pipe_grid(int nrows, int num_cu) {
-  // Huge matrices: a few persistent workgroups per CU stream best. Smaller ones: about
-  // one logical row per wave, capped at eight workgroups per CU.
-  if (nrows >= 64 * 1024) return 2 * num_cu;
-  int g = (nrows + kPipeWPB - 1) / kPipeWPB;
-  const int cap = 8 * num_cu;
-  return g < cap ? (g < 1 ? 1 : g) : cap;
+int gemv_pipe_grid(int nrows, int ncols, int wdtype, int num_cu) {
+  // Measured on MI355X at batch 1: matrices with many rows or long rows (two or more
+  // stages per row) stream best with two workgroups per CU; short-row matrices with a
+  // few thousand rows want about one row per wave, four workgroups per CU.
+  const int sw = pipe_stage_cols(wdtype);
+  const int stages = (ncols + sw - 1) / sw;
+  const int per_cu = (nrows >= 64 * 1024 || stages >= 2) ? 2 : 4;
+  int g = per_cu * num_cu;
+  const int rows_cap = (nrows + kPipeWPB - 1) / kPipeWPB;
+  if (g > rows_cap) g = rows_cap;
+  return g < 1 ? 1 : g;
 }
 
 hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, int grid,
                             hipStream_t s) {
-  if (!gemv_pipe_fits(p.ncols, p.B)) return hipErrorInvalidValue;
+  if (!gemv_pipe_fits(p.ncols, p.B, wdtype) || p.ncols % 8 != 0 || p.nrows < 1 || grid < 1)
+    return hipErrorInvalidValue;
+  if (pro == PRO_EH && !p.h_is_f32) return hipErrorInvalidValue;
   return wdtype == 0 ? pipe_dt<F32>(pro, epi, p, grid, s) : pipe_dt<BF16>(pro, epi, p, grid, s);
 }
 

@@ -67,15 +67,16 @@ struct GemvParams {
 hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int max_grid,
                        hipStream_t s);
 // Persistent pipelined GEMV for batch 1-2 when the input vectors fit in LDS.
-bool gemv_pipe_fits(int ncols, int B);
-int gemv_pipe_grid(int nrows, int num_cu);
+bool gemv_pipe_fits(int ncols, int B, int wdtype);
+int gemv_pipe_grid(int nrows, int ncols, int wdtype, int num_cu);
 hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, int grid,
                             hipStream_t s);
 
-// RoPE tables of K consecutive steps: tab[k][b][0..d/2) = cos, tab[k][b][d/2..d) = sin of
-// (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded to fp32.
-hipError_t launch_rope_tables(float* tab, const int* pos, int B, int K, int d, float theta,
-                              hipStream_t s);
+// Per-call set-up: RoPE tables of K consecutive steps (tab[k][b][0..d/2) = cos,
+// tab[k][b][d/2..d) = sin of (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded
+// to fp32) and hidden [B, H] (weight dtype) widened to fp32 into hf.
+hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
+                              float theta, const void* hidden, float* hf, int H, hipStream_t s);
 
 struct AttnParams {
   const float* qkv;  // [B, ldqkv] fp32: q (n_q*d) | k (n_kv*d) | v (n_kv*d), before RoPE
@@ -96,7 +97,9 @@ struct AttnParams {
   float* o;  // [B, n_q * d]
   unsigned* err;
 };
-// Attention (partials per split) followed by the split merge into o.
+// Attention (partials per split) followed by the split merge into o. p.chunk must be a
+// positive multiple of attn_chunk_quantum().
+int attn_chunk_quantum();
 hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
 
 struct VerifyParams {

@@ -15,7 +15,7 @@ using namespace mtp;
 
 constexpr int kMaxSplits = 256;
 constexpr int kMinChunk = 64;
-constexpr int kMaxChunk = 1024;
+constexpr int kMaxChunk = 512;
 constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
 constexpr int kMaxK = 100;
 constexpr int kMaxGroupHeads = 8;
@@ -148,8 +148,8 @@ hipError_t timed(mtp_handle* h, int id, hipStream_t s, Fn&& f) {
 // Pick the pipelined kernel when the batch's input vectors fit in LDS, else the
 // column-blocked one.
 hipError_t run_gemv(const mtp_handle* h, Pro pro, Epi epi, GemvParams& g, hipStream_t s) {
-  if (gemv_pipe_fits(g.ncols, g.B))
-    return launch_gemv_pipe(h->cfg.dtype, pro, epi, g, gemv_pipe_grid(g.nrows, h->num_cu), s);
+  if (gemv_pipe_fits(g.ncols, g.B, h->cfg.dtype))
+    return launch_gemv_pipe(h->cfg.dtype, pro, epi, g, gemv_pipe_grid(g.nrows, g.ncols, h->cfg.dtype, h->num_cu), s);
   g.col_block = col_block_for(g.ncols, g.B, h->cfg.dtype);
   return launch_gemv(h->cfg.dtype, pro, epi, g, kGemvMaxGrid, s);
 }
@@ -295,17 +295,19 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   float* act = h->at<float>(L.act);
   unsigned* err = h->at<unsigned>(L.err);
 
-  // Attention splits: aim for about four workgroups per CU over (split, kv head, sequence),
-  // with chunks of 128..1024 cache positions (multiples of 64) and at most kMaxSplits.
-  long want = ((long)kv->capacity * B * nkv + 4L * h->num_cu - 1) / (4L * h->num_cu);
-  int chunk = (int)((want + kMinChunk - 1) / kMinChunk * kMinChunk);
-  if (chunk < 2 * kMinChunk) chunk = 2 * kMinChunk;
+  // Attention splits: aim for about two workgroups per CU over (split, kv head, sequence),
+  // with chunks of q..1024 cache positions (q = the kernel's quantum) and <= kMaxSplits.
+  const int q = attn_chunk_quantum();
+  long want = ((long)kv->capacity * B * nkv + 2L * h->num_cu - 1) / (2L * h->num_cu);
+  int chunk = (int)((want + q - 1) / q * q);
+  if (chunk < q) chunk = q;
   if (chunk > kMaxChunk) chunk = kMaxChunk;
   const int min_chunk = (kv->capacity + kMaxSplits - 1) / kMaxSplits;
-  if (chunk < min_chunk) chunk = (min_chunk + kMinChunk - 1) / kMinChunk * kMinChunk;
+  if (chunk < min_chunk) chunk = (min_chunk + q - 1) / q * q;
   const int nsplit = (kv->capacity + chunk - 1) / chunk;
 
-  if (launch_rope_tables(h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, s) != hipSuccess)
+  if (launch_draft_setup(c.dtype, h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, hidden,
+                         hb, H, s) != hipSuccess)
     return MTP_ERR_HIP;
   for (int k = 0; k < K; ++k) {
     hipError_t e;
@@ -318,8 +320,8 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.gain = w.g_h;
     g.gain2 = w.g_e;
     g.eps = c.rms_eps;
-    g.h = k == 0 ? hidden : (const void*)hb;
-    g.h_is_f32 = (k > 0 || c.dtype == MTP_F32) ? 1 : 0;
+    g.h = hb;  // the set-up kernel widened the step-1 hidden state into hb
+    g.h_is_f32 = 1;
     g.ldh = H;
     g.embed = w.embed;
     g.tok = k == 0 ? last_tokens : draft_tokens + (k - 1);
