@@ -189,22 +189,34 @@ def _inputs(cfg, cap=None):
     return S.make_inputs(cfg, capacity=cap)
 
 
-def test_decoder_step_matches_transformers_llama_layer():
+@pytest.mark.parametrize("case", ["tiny", "bf16"])
+def test_decoder_step_matches_transformers_llama_layer(case):
     """Steps 3-9 of one draft step against transformers' Llama decoder layer (a standard
-    pre-norm GQA/RoPE/SwiGLU block with no biases) fed by torch's own RMSNorm / linear."""
+    pre-norm GQA/RoPE/SwiGLU block with no biases) fed by torch's own RMSNorm / linear.
+    For a bf16 head the new cache entries must be torch's round-to-nearest-even bf16 of
+    the layer's rotated keys and values."""
     torch = pytest.importorskip("torch")
     tr = pytest.importorskip("transformers.models.llama.modeling_llama")
     from transformers.cache_utils import DynamicCache
     F = torch.nn.functional
-    cfg = S.get_config("tiny")
-    inp = _inputs(cfg, 140)
+    if case == "tiny":
+        cfg = S.get_config("tiny")
+        cap = 140
+    else:
+        cfg = small_cfg(cid=70, hidden=128, n_q=4, n_kv=2, head_dim=64, ffn=256, vocab=300,
+                        batch=1, K=1, ctx_lo=37, dtype="bf16")
+        cap = 48
+    inp = _inputs(cfg, cap)
     W = O.OracleWeights(cfg, inp.weights)
     kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
     res = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, 1)
 
-    w = {k: torch.from_numpy(np.asarray(v, np.float32)) for k, v in inp.weights.items()}
+    def f32(a):
+        return torch.from_numpy(O.as_float(a, cfg.dtype).copy())
+
+    w = {k: f32(v) for k, v in inp.weights.items()}
     H, L = cfg.hidden, int(inp.lens[0])
-    h = torch.from_numpy(inp.hidden.astype(np.float32))
+    h = f32(inp.hidden)
     e = w["embed"][torch.from_numpy(inp.last_tokens.astype(np.int64))]
     cat = torch.cat([F.rms_norm(h, (H,), w["g_h"], 1e-6), F.rms_norm(e, (H,), w["g_e"], 1e-6)], 1)
     x = F.linear(cat, w["w_eh"])
@@ -221,20 +233,31 @@ def test_decoder_step_matches_transformers_llama_layer():
           "post_attention_layernorm.weight": w["g_mlp"]}
     layer.load_state_dict(sd)
     cache = DynamicCache(config=lc)
-    cache.update(torch.from_numpy(inp.k_cache[:, :, :L].copy()),
-                 torch.from_numpy(inp.v_cache[:, :, :L].copy()), 0)
+    cache.update(f32(inp.k_cache[:, :, :L]), f32(inp.v_cache[:, :, :L]), 0)
     P = int(inp.pos[0])
     cos, sin = tr.LlamaRotaryEmbedding(lc)(x[None], torch.tensor([[P]]))
     with torch.no_grad():
         x2 = layer(x[None], position_ids=torch.tensor([[P]]), past_key_values=cache,
                    use_cache=True, position_embeddings=(cos, sin))[0]
         logits = F.linear(F.rms_norm(x2, (H,), w["g_final"], 1e-6), w["lm_head"])
-    assert np.max(np.abs(res["hidden_steps"][0] - x2.numpy())) < 1e-4
-    assert np.max(np.abs(res["logits"][0] - logits.numpy())) < 1e-4
-    newk = cache.layers[0].keys[0, :, L].numpy()
-    newv = cache.layers[0].values[0, :, L].numpy()
-    assert np.max(np.abs(kc[0, :, L] - newk)) < 1e-5 and np.max(np.abs(vc[0, :, L] - newv)) < 1e-6
-    assert int(res["draft_tokens"][0, 0]) == int(torch.argmax(logits[0]))
+    newk = cache.layers[0].keys[0, :, L]
+    newv = cache.layers[0].values[0, :, L]
+    if cfg.dtype == "f32":
+        # The pinned cache attends to the new entry in fp32; the layer's output matches.
+        assert np.max(np.abs(res["hidden_steps"][0] - x2.numpy())) < 1e-4
+        assert np.max(np.abs(res["logits"][0] - logits.numpy())) < 1e-4
+        assert np.max(np.abs(kc[0, :, L] - newk.numpy())) < 1e-5
+        assert np.max(np.abs(vc[0, :, L] - newv.numpy())) < 1e-6
+        assert int(res["draft_tokens"][0, 0]) == int(torch.argmax(logits[0]))
+    else:
+        # bf16 cache: the oracle attends to rounded entries, the layer to fp32 ones; the
+        # written entries are the nearest bf16 (ties to even) of the layer's values.
+        for mine, ref in ((kc[0, :, L], newk), (vc[0, :, L], newv)):
+            want = ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            same = np.mean(mine == want)
+            ulp = np.abs(mine.astype(np.int32) - want.astype(np.int32))
+            assert same > 0.98 and ulp.max() <= 1, (same, ulp.max())
+        assert np.max(np.abs(res["hidden_steps"][0] - x2.numpy())) < 2e-2
 
 
 def test_identity_projection_pins():
