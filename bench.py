@@ -26,6 +26,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "lm_head_argmax_q8b_counters.md")
+LMHEAD_SOURCES = ("mtp_self_speculative_amd/csrc/gemv_pipe.hip",
+                  "mtp_self_speculative_amd/csrc/common.h",
+                  "mtp_self_speculative_amd/csrc/kernels.h")
 METRIC = "MTP draft-steps/s + verified tok/s at 1 GPU; % of HBM roofline"
 LMHEAD_BIT = 1 << 6
 DESCR = {
@@ -63,6 +67,48 @@ def algorithmic_bytes(cfg, lens0, K: int, acc_sum_rows: int) -> dict:
     verify = acc_sum_rows * V * 4
     return {"per_step_weights": per_step_w, "lm_head": lm + H * s + B * H * 4 + B * 8,
             "iteration": K * per_step_w + kv_read + kv_write + emb + io + verify}
+
+
+def lmhead_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in LMHEAD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str):
+    """HBM bytes per lm_head launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), or None when the
+    summary is missing, is for another workload, or the kernel source changed since."""
+    if config != "q8b" or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != lmhead_source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
+    """A plain device-to-device copy of known size, run under rocprofv3 --pmc to scale
+    FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(cfg, inp, K: int, reps: int = 3) -> dict:
@@ -108,7 +154,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="extra untimed pass with HIP events around every kernel class")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
                                    "(the path shards by sequence with no exchange step)"}))
@@ -231,7 +282,8 @@ def main() -> int:
         "algorithmic_bytes_per_iteration": int(ab["iteration"]),
         "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
                      "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.config),
                      "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n,
                      "algorithmic_bytes_per_launch": int(ab["lm_head"])},
     }

@@ -187,6 +187,16 @@ void mtp_destroy(mtp_handle* h);
 /* Static description of a status code. */
 const char* mtp_status_string(mtp_status s);
 
+/*
+ * Training-loss weights of the K MTP steps, speculators user guide "MTP (Multi-Token
+ * Prediction)", Step Weight Formula: out[k-1] = beta^(k-1) / sum_{j=1..K} beta^(j-1)
+ * for k = 1..K (beta = 0.6, K = 3 gives 0.51, 0.31, 0.18). A host function: `out` is
+ * caller-owned host memory with room for K floats; evaluated in double precision.
+ * Errors: MTP_ERR_INVALID_ARG for a NULL `out` or a beta that is not finite and > 0;
+ * MTP_ERR_SHAPE for K < 1 or K > 100. Nothing is written on error.
+ */
+mtp_status mtp_step_weights(float beta, int32_t K, float* out);
+
 #ifdef __cplusplus
 }
 #endif

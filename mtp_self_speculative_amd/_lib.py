@@ -70,6 +70,7 @@ _SIGS = {
     "mtp_get_profile": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I), _I]),
     "mtp_destroy": (None, [_P]),
     "mtp_status_string": (ctypes.c_char_p, [_I]),
+    "mtp_step_weights": (_I, [ctypes.c_float, _I, ctypes.POINTER(ctypes.c_float)]),
 }
 
 
@@ -199,3 +200,10 @@ def mtp_destroy(handle: int) -> None:
 
 def mtp_status_string(st: int) -> str:
     return status_string(st)
+
+
+def mtp_step_weights(beta: float, K: int) -> list:
+    """Training-loss weights of the K MTP steps (host computation in the library)."""
+    out = (ctypes.c_float * max(int(K), 1))()
+    _check(LIB.mtp_step_weights(float(beta), int(K), out), "mtp_step_weights")
+    return [float(out[i]) for i in range(int(K))]

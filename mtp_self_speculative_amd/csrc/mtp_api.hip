@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/mtp.h: argument validation, workspace
 // layout, kernel selection and the launch sequence of one speculative iteration.
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -19,7 +20,7 @@ constexpr int kMaxChunk = 512;
 constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
 constexpr int kMaxK = 100;
 constexpr int kMaxGroupHeads = 8;
-constexpr int kVerifyChunk = 4096;
+constexpr int kVerifyChunk = 2048;
 constexpr size_t kGemvLdsBudget = 32 * 1024;
 constexpr int kGemvMaxGrid = 2048;
 
@@ -170,6 +171,16 @@ const char* mtp_status_string(mtp_status s) {
     case MTP_ERR_DEVICE: return "device-side error (see mtp_get_error bits)";
   }
   return "unknown status";
+}
+
+mtp_status mtp_step_weights(float beta, int32_t K, float* out) {
+  if (!out || !(beta > 0.f) || !(beta < INFINITY)) return MTP_ERR_INVALID_ARG;
+  if (K < 1 || K > kMaxK) return MTP_ERR_SHAPE;
+  double total = 0.0, w = 1.0;
+  for (int k = 0; k < K; ++k, w *= beta) total += w;
+  w = 1.0;
+  for (int k = 0; k < K; ++k, w *= beta) out[k] = (float)(w / total);
+  return MTP_OK;
 }
 
 mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,

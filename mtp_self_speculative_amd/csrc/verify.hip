@@ -13,6 +13,7 @@
 namespace mtp {
 
 constexpr int kVerifyThreads = 256;
+constexpr int kVerifyPer = 8;  // logits per lane; a workgroup covers kVerifyThreads * kVerifyPer
 
 __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) {
   __shared__ unsigned long long kred[kVerifyThreads / kWave];
@@ -21,10 +22,20 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* row = p.logits + ((long)b * (p.K + 1) + j) * p.V;
   const int lo = c * p.chunk, hi = min(lo + p.chunk, p.V);
+  // All loads are issued before any is used; indexes past the row end are clamped to its
+  // last element, whose key then only repeats.
+  int idx[kVerifyPer];
+  float v[kVerifyPer];
+#pragma unroll
+  for (int k = 0; k < kVerifyPer; ++k) {
+    idx[k] = min(lo + (int)threadIdx.x + k * kVerifyThreads, hi - 1);
+    v[k] = __builtin_nontemporal_load(row + idx[k]);
+  }
   unsigned long long best = 0ull;
-  for (int i = lo + threadIdx.x; i < hi; i += kVerifyThreads) {
-    const unsigned long long k = pack_key(__builtin_nontemporal_load(row + i), (uint32_t)i);
-    best = k > best ? k : best;
+#pragma unroll
+  for (int k = 0; k < kVerifyPer; ++k) {
+    const unsigned long long key = pack_key(v[k], (uint32_t)idx[k]);
+    best = key > best ? key : best;
   }
   best = wave_max_u64(best);
   if (lane == 0) kred[wave] = best;
@@ -69,6 +80,9 @@ __global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, 
 }
 
 hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s) {
+  if (p.chunk != kVerifyThreads * kVerifyPer || (long)p.nchunk * p.chunk < p.V ||
+      (long)(p.nchunk - 1) * p.chunk >= p.V)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(verify_kernel, dim3(p.nchunk, p.K + 1, B), dim3(kVerifyThreads), 0, s, p);
   return hipGetLastError();
 }

@@ -1,7 +1,10 @@
 """The C-ABI library loads, exports every symbol include/mtp.h declares, and rejects bad
-arguments on the host before touching a device. No compute call is made here."""
+arguments on the host before touching a device. No device call is made here; the one
+host-only computation (the step weights) is checked against its printed values."""
 import ctypes
 import subprocess
+
+import numpy as np
 
 import pytest
 
@@ -93,3 +96,24 @@ def test_python_wrapper_raises_mtp_error():
     with pytest.raises(L.MtpError) as e:
         L.mtp_workspace_size(cfg(head_dim=32), 1, 1, 16)
     assert e.value.status == 5
+
+
+def test_step_weights_entry_point():
+    """The library's host helper against the printed values and the closed form
+    (speculators user guide, "MTP (Multi-Token Prediction)", Step Weight Formula)."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "step_weights.json")))
+    w = L.mtp_step_weights(0.6, 3)
+    assert [round(x, 2) for x in w] == [0.51, 0.31, 0.18]
+    assert [round(x, 2) for x in w] == gold["printed"]
+    assert np.allclose(w, [25 / 49, 15 / 49, 9 / 49], rtol=0, atol=1e-7)
+    assert np.allclose(L.mtp_step_weights(1.0, 4), [0.25] * 4, atol=1e-7)
+    w = L.mtp_step_weights(0.3, 100)
+    assert abs(sum(w) - 1.0) < 1e-5 and all(a > b for a, b in zip(w, w[1:]) if b > 0)
+    out = (ctypes.c_float * 4)(*([7.0] * 4))
+    for beta, K, st in [(0.0, 3, 1), (-1.0, 3, 1), (float("nan"), 3, 1), (float("inf"), 3, 1),
+                        (0.6, 0, 2), (0.6, 101, 2)]:
+        assert L.LIB.mtp_step_weights(beta, K, out) == st
+    assert list(out) == [7.0] * 4
+    assert L.LIB.mtp_step_weights(0.6, 3, None) == 1
