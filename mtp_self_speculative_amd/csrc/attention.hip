@@ -306,7 +306,12 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
     for (int j = 0; j < UB; ++j)
       if (q0 + j < nvalid) acc[j & 3] = fmaf(v[j], w[q0 + j], acc[j & 3]);
   }
-  p.o[hb * D + t] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / L;
+  const float r = ((acc[0] + acc[1]) + (acc[2] + acc[3])) / L;
+  if (p.o_bf16) {
+    const long i = (long)b * p.ld_o_bf16 + hq * D + t;
+    split_bf16(r, p.o_bf16[i], p.o_bf16_lo[i]);
+  } else
+    p.o[hb * D + t] = r;
 }
 
 // Per-call set-up: RoPE tables of the K steps (tab[k][b][0..d/2) = cos, [d/2..d) = sin of

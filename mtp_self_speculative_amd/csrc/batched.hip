@@ -1,0 +1,140 @@
+// Row-wise steps of the batched draft path, one workgroup per sequence.
+//
+// The MFMA contraction writes fp32 partial sums per K split. Each kernel here adds the
+// splits in a fixed order (deterministic), applies the step's epilogue (residual add,
+// SwiGLU, plain store) and, where the next contraction starts with an RMSNorm, also
+// produces that contraction's bf16 operand row: the whole row is in this workgroup, so
+// the norm needs no second pass over memory. Operand rows are written as bf16 hi / lo
+// planes, so the contraction sees the fp32 values to about 16 bits. PREP_EH builds the eh_proj operand
+// [RMSNorm(h) * g_h ; RMSNorm(embed[tok]) * g_e] (speculators user guide, "MTP
+// (Multi-Token Prediction)", How It Works > Architecture: both inputs are normalised
+// separately, then concatenated).
+#include "common.h"
+#include "kernels.h"
+
+namespace mtp {
+
+constexpr int kRedThreads = 512;
+constexpr int kRedVPT = 4;  // float4 groups per thread in the norm modes
+
+int red_max_cols() { return 4 * kRedVPT * kRedThreads; }
+
+// Four values as bf16 hi / lo planes (see split_bf16).
+__device__ __forceinline__ void store4_split(uint16_t* hi, uint16_t* lo, float a, float b, float c,
+                                             float d) {
+  uint16_t h[4], l[4];
+  split_bf16(a, h[0], l[0]);
+  split_bf16(b, h[1], l[1]);
+  split_bf16(c, h[2], l[2]);
+  split_bf16(d, h[3], l[3]);
+  *reinterpret_cast<uint2*>(hi) = uint2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+  *reinterpret_cast<uint2*>(lo) = uint2{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
+}
+__device__ __forceinline__ float4 load4_bf16(const uint16_t* src) {
+  const uint2 u = *reinterpret_cast<const uint2*>(src);
+  return float4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+}
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return float4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+}
+__device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+
+template <int MODE>
+__global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
+  __shared__ float red[kRedThreads / kWave];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = p.n;
+  auto sum_part = [&](int c) -> float4 {
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.nsplit; ++s)
+      v = add4(v, *reinterpret_cast<const float4*>(p.part + ((long)s * p.bp + b) * p.n_part + c));
+    return v;
+  };
+
+  if constexpr (MODE == RED_QKV) {
+    for (int c = 4 * tid; c < n; c += 4 * kRedThreads)
+      *reinterpret_cast<float4*>(p.out + (long)b * n + c) = sum_part(c);
+  } else if constexpr (MODE == RED_SWIGLU) {
+    for (int c = 4 * tid; c < n; c += 4 * kRedThreads) {
+      const float4 g = sum_part(c), u = sum_part(n + c);
+      const long o = (long)b * p.ldq + c;
+      store4_split(p.xq + o, p.xq_lo + o, g.x / (1.0f + expf(-g.x)) * u.x,
+                  g.y / (1.0f + expf(-g.y)) * u.y, g.z / (1.0f + expf(-g.z)) * u.z,
+                  g.w / (1.0f + expf(-g.w)) * u.w);
+    }
+  } else {
+    // Norm modes: the row stays in registers between the sum of squares and the scaling.
+    constexpr int NPART = (MODE == PREP_EH) ? 2 : 1;
+    int t = 0;
+    if constexpr (MODE == PREP_EH) {
+      t = p.tok[(long)b * p.tok_stride];
+      if (t < 0 || t >= p.vocab) {
+        if (tid == 0) set_error(p.err, 1u);
+        t = 0;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NPART; ++q) {
+      float4 v[kRedVPT];
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < kRedVPT; ++j) {
+        const int c = 4 * (tid + j * kRedThreads);
+        v[j] = float4{0.f, 0.f, 0.f, 0.f};
+        if (c < n) {
+          if constexpr (MODE == PREP_EH) {
+            v[j] = q == 0 ? *reinterpret_cast<const float4*>(p.h + (long)b * n + c)
+                          : load4_bf16(p.embed + (long)t * n + c);
+          } else {
+            v[j] = sum_part(c);
+            if constexpr (MODE == RED_RESID)
+              v[j] = add4(*reinterpret_cast<const float4*>(p.res + (long)b * n + c), v[j]);
+            *reinterpret_cast<float4*>(p.out + (long)b * n + c) = v[j];
+            if (MODE == RED_RESID && p.dbg)
+              *reinterpret_cast<float4*>(p.dbg + (long)b * p.dbg_ld + c) = v[j];
+          }
+          ss += dot4(v[j]);
+        }
+      }
+      const float tot = block_sum(ss, red);
+      const float r = 1.0f / sqrtf(tot / (float)n + p.eps);
+      const uint16_t* g = q == 0 ? p.gain : p.gain2;
+#pragma unroll
+      for (int j = 0; j < kRedVPT; ++j) {
+        const int c = 4 * (tid + j * kRedThreads);
+        if (c < n) {
+          const float4 gv = load4_bf16(g + c);
+          const long o = (long)b * p.ldq + q * n + c;
+          store4_split(p.xq + o, p.xq_lo + o, v[j].x * r * gv.x, v[j].y * r * gv.y,
+                       v[j].z * r * gv.z, v[j].w * r * gv.w);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s) {
+  if (B < 1 || p.n < 4 || p.n % 4 != 0 || p.ldq % 4 != 0) return hipErrorInvalidValue;
+  if ((mode != RED_QKV && (!p.xq || !p.xq_lo)) || (mode != RED_SWIGLU && mode != PREP_EH && !p.out))
+    return hipErrorInvalidValue;
+  const bool norm = mode == RED_EH || mode == RED_RESID || mode == PREP_EH;
+  if (norm && (p.n > red_max_cols() || !p.gain || p.ldq < (mode == PREP_EH ? 2 : 1) * p.n))
+    return hipErrorInvalidValue;
+  if (mode == PREP_EH && (!p.gain2 || !p.h || !p.embed || !p.tok || !p.err))
+    return hipErrorInvalidValue;
+  if (mode == RED_RESID && !p.res) return hipErrorInvalidValue;
+  if (mode != PREP_EH && (!p.part || p.nsplit < 1 || p.bp < B || p.n_part % 4 != 0))
+    return hipErrorInvalidValue;
+  const dim3 g(B), t(kRedThreads);
+  switch (mode) {
+    case RED_EH: hipLaunchKernelGGL(red_kernel<RED_EH>, g, t, 0, s, p); break;
+    case RED_QKV: hipLaunchKernelGGL(red_kernel<RED_QKV>, g, t, 0, s, p); break;
+    case RED_RESID: hipLaunchKernelGGL(red_kernel<RED_RESID>, g, t, 0, s, p); break;
+    case RED_SWIGLU: hipLaunchKernelGGL(red_kernel<RED_SWIGLU>, g, t, 0, s, p); break;
+    case PREP_EH: hipLaunchKernelGGL(red_kernel<PREP_EH>, g, t, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mtp

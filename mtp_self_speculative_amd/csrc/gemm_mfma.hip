@@ -1,0 +1,285 @@
+// Weight-streaming bf16 contraction on the matrix cores, for batches of 3..64 sequences.
+//
+// At these batch sizes every projection is still HBM-bound (each weight byte feeds B
+// multiply-adds), but a VALU dot product per sequence would be compute-bound from about
+// B = 20 on, so the multiply-adds go to v_mfma_f32_16x16x32_bf16: a 16-row slice of W
+// (A operand, one 16-byte load per lane: row lane%16, columns 8*(lane/16)..+7 of a
+// 32-column step) against 16 sequences of the input (B operand, same column mapping).
+// The input arrives as two bf16 planes hi + lo of its fp32 values and both are
+// multiplied (two MFMAs per step into one fp32 accumulator): rounding the input to one
+// bf16 would cost several hundredths in the hidden state at these sizes.
+//
+// Work is split into items of (64-row tile, K split). A workgroup of four waves takes
+// items in turn (a persistent grid); wave w owns rows 16w..16w+15 of the tile. Each item
+// is walked in chunks of 256 columns: per chunk a wave streams 16 rows x 512 bytes of W
+// (eight 16-byte non-temporal loads per lane, so every row piece is a full 64-byte
+// segment) and runs 16 x NB MFMAs. The input rows (both planes) of the chunk are staged
+// once per workgroup in LDS (double-buffered) and read from there by all four waves. W stages
+// are double-buffered in registers; all loads are unconditional (indexes past the end
+// are clamped), so the compiler can wait for exactly the buffer being consumed.
+//
+// Epilogues: EPI_STORE writes the fp32 partial sums of the item's K split (a row-wise
+// reduction kernel adds the splits in a fixed order, so results are deterministic);
+// EPI_ARGMAX (one split) folds each row's value into a packed (value, index) key per
+// sequence and finishes with the last-workgroup protocol of the GEMV.
+#include "common.h"
+#include "kernels.h"
+
+namespace mtp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMmWaves = 4;
+constexpr int kMmThreads = kMmWaves * kWave;
+constexpr int kMmTileRows = 16 * kMmWaves;
+constexpr int kMmChunk = 256;               // columns per stage
+constexpr int kMmKSteps = kMmChunk / 32;    // MFMA k-steps per stage
+constexpr int kMmLdsRow = kMmChunk + 8;     // bf16 per LDS row: 16-byte pad against bank conflicts
+constexpr int kMmMaxNB = 4;
+
+__host__ __device__ int mm_chunks(int ncols) { return (ncols + kMmChunk - 1) / kMmChunk; }
+int mm_batch_pad(int B) { return (B + 15) / 16 * 16; }
+
+// K splits: enough items to occupy the chip (about 1024), while the partial sums stay
+// below an eighth of the weight bytes (nsplit * 16NB * 4 B per row <= ncols * 2 B / 8).
+int mm_split(int nrows, int ncols, int B) {
+  const int ntiles = (nrows + kMmTileRows - 1) / kMmTileRows;
+  const int nch = mm_chunks(ncols);
+  int want = 1024 / ntiles;
+  const int cap = ncols / (16 * mm_batch_pad(B));
+  if (want > cap) want = cap;
+  if (want > nch) want = nch;
+  int best = 1;
+  for (int s = 1; s <= want; ++s)
+    if (nch % s == 0) best = s;
+  return best;
+}
+
+// LDS: [2 buffers][2 planes][16 NB rows][kMmLdsRow] bf16
+static size_t mm_lds_bytes(int nb) { return (size_t)4 * 16 * nb * kMmLdsRow * sizeof(uint16_t); }
+
+int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
+  const long items = (long)((nrows + kMmTileRows - 1) / kMmTileRows) * nsplit;
+  const int nb = mm_batch_pad(B) / 16;
+  const int per_cu = nb >= 3 ? 1 : nb == 2 ? 2 : 4;  // resident workgroups (LDS, registers)
+  long g = (long)per_cu * num_cu;
+  if (g > items) g = items;
+  (void)ncols;
+  return (int)(g < 1 ? 1 : g);
+}
+
+template <int NB, int EPI>
+__global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
+  constexpr int BP = 16 * NB;
+  constexpr int XPASS = BP / 8;  // 16-byte input loads per thread, plane and stage
+  extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][kMmLdsRow]
+  __shared__ unsigned long long kred[kMmWaves][BP];
+  __shared__ int flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = p.nrows, Kd = p.ncols;
+  const int C = mm_chunks(Kd) / p.nsplit;  // chunks per item
+  const int ntiles = (N + kMmTileRows - 1) / kMmTileRows;
+  const int nitems = ntiles * p.nsplit;
+  const int G = gridDim.x;
+  const int my_items = (int)blockIdx.x < nitems ? (nitems - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const int stages = my_items * C;
+
+  auto clampit = [&](int it) { return it < stages ? it : (stages > 0 ? stages - 1 : 0); };
+  auto item_of = [&](int it) { return (int)blockIdx.x + (it / C) * G; };
+  auto chunk_of = [&](int it) { return (item_of(it) % p.nsplit) * C + it % C; };
+
+  auto row_ptr = [&](int r) -> const uint16_t* {
+    if (r < p.seg1) return static_cast<const uint16_t*>(p.w0) + (long)r * Kd;
+    if (r < p.seg2) return static_cast<const uint16_t*>(p.w1) + (long)(r - p.seg1) * Kd;
+    return static_cast<const uint16_t*>(p.w2) + (long)(r - p.seg2) * Kd;
+  };
+
+  u32x4 A[kMmKSteps], Bf[kMmKSteps];
+  // Stages past the workgroup's last one are prefetched from the dummy region (16 rows
+  // of 256 bf16), never consumed.
+  auto wload = [&](u32x4 (&buf)[kMmKSteps], int it) {
+    const bool live = it < stages;
+    int r = (item_of(it) / p.nsplit) * kMmTileRows + wave * 16 + (lane & 15);
+    r = r < N ? r : N - 1;
+    const uint16_t* rp = live ? row_ptr(r)
+                              : static_cast<const uint16_t*>(p.dummy) + (lane & 15) * kMmChunk;
+    const int c0 = live ? chunk_of(it) * kMmChunk + (lane >> 4) * 8 : (lane >> 4) * 8;
+#pragma unroll
+    for (int s = 0; s < kMmKSteps; ++s) {
+      int col = c0 + s * 32;
+      col = (col < Kd || !live) ? col : Kd - 8;
+      buf[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + col));
+    }
+  };
+
+  u32x4 xr[2][XPASS];
+  auto xload = [&](int it) {
+    const int c0 = chunk_of(clampit(it)) * kMmChunk;
+#pragma unroll
+    for (int j = 0; j < XPASS; ++j) {
+      const int q = tid + j * kMmThreads;
+      const int row = q >> 5, col = c0 + (q & 31) * 8;
+      const int rr = row < p.B ? row : p.B - 1;
+      const int cc = col < Kd ? col : Kd - 8;
+      const long o = (long)rr * p.ldx + cc;
+      xr[0][j] = *reinterpret_cast<const u32x4*>(p.x + o);
+      xr[1][j] = *reinterpret_cast<const u32x4*>(p.x_lo + o);
+    }
+  };
+  auto xstore = [&](int it, int bufi) {
+    const int c0 = chunk_of(clampit(it)) * kMmChunk;
+#pragma unroll
+    for (int j = 0; j < XPASS; ++j) {
+      const int q = tid + j * kMmThreads;
+      const int row = q >> 5, cp = q & 31;
+      const bool live = row < p.B && c0 + cp * 8 < Kd;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+        *reinterpret_cast<u32x4*>(xl + ((long)(2 * bufi + pl) * BP + row) * kMmLdsRow + cp * 8) =
+            live ? xr[pl][j] : z;
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned long long best[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) best[nb] = 0ull;
+
+  auto consume = [&](u32x4 (&buf)[kMmKSteps], int it) {
+    const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * kMmLdsRow + (lane & 15) * kMmLdsRow +
+                         (lane >> 4) * 8;
+#pragma unroll
+    for (int s = 0; s < kMmKSteps; ++s) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, buf[s]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kMmLdsRow + s * 32);
+        const u32x4 bl =
+            *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * kMmLdsRow + s * 32);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh),
+                                                          acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl),
+                                                          acc[nb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Lane l holds rows 4*(l/16)+i (i < 4) of the wave's 16-row slice for sequence
+  // 16*nb + l%16.
+  auto finish_item = [&](int it) {
+    const int item = item_of(it);
+    const int tile = item / p.nsplit, split = item % p.nsplit;
+    const int r0 = tile * kMmTileRows + wave * 16 + (lane >> 4) * 4;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = nb * 16 + (lane & 15);
+      if constexpr (EPI == EPI_STORE) {
+        float* dst = p.part + ((long)split * BP + b) * N + r0;
+        if (r0 + 3 < N && (N & 3) == 0) {
+          *reinterpret_cast<float4*>(dst) = float4{acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + i < N) dst[i] = acc[nb][i];
+        }
+      } else {
+        unsigned long long k = 0ull;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (r0 + i < N) {
+            const unsigned long long ki = pack_key(acc[nb][i], (uint32_t)(r0 + i));
+            k = ki > k ? ki : k;
+            if (p.logits && b < p.B) p.logits[(long)b * p.logits_ld + r0 + i] = acc[nb][i];
+          }
+        }
+        unsigned long long o = __shfl_xor(k, 16, kWave);
+        k = o > k ? o : k;
+        o = __shfl_xor(k, 32, kWave);
+        k = o > k ? o : k;
+        best[nb] = k > best[nb] ? k : best[nb];
+      }
+      acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  auto stage = [&](u32x4 (&buf)[kMmKSteps], int it) {
+    xload(it + 1);
+    consume(buf, it);
+    wload(buf, it + 2);
+    if (it % C == C - 1) finish_item(it);
+    xstore(it + 1, (it + 1) & 1);
+    __syncthreads();
+  };
+
+  xload(0);
+  wload(A, 0);
+  wload(Bf, 1);
+  xstore(0, 0);
+  __syncthreads();
+  for (int it = 0; it < stages; it += 2) {
+    stage(A, it);
+    if (it + 1 >= stages) break;
+    stage(Bf, it + 1);
+  }
+
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (lane < 16) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) kred[wave][nb * 16 + lane] = best[nb];
+    }
+    __syncthreads();
+    if (tid < BP && tid < p.B) {
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int w = 0; w < kMmWaves; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
+      if (k) keep_alive(atomic_max_key(p.keys + tid, k));
+    }
+    if (last_to_arrive(p.counter, gridDim.x, &flag)) {
+      for (int b = tid; b < p.B; b += kMmThreads) {
+        const unsigned long long k = take_key(p.keys + b);
+        p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
+        if (p.maxlogit) p.maxlogit[b] = key_value(k);
+        if (p.advance > 0) {
+          p.len[b] += p.advance;
+          p.pos[b] += p.advance;
+        }
+      }
+    }
+  }
+}
+
+template <int NB>
+static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
+  const size_t lds = mm_lds_bytes(NB);
+  if (epi == EPI_ARGMAX)
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX>), dim3(grid), dim3(kMmThreads), lds, s, p);
+  else
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE>), dim3(grid), dim3(kMmThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
+  if (epi != EPI_STORE && epi != EPI_ARGMAX) return hipErrorInvalidValue;
+  if (p.B < 1 || p.B > 16 * kMmMaxNB || p.nrows < 1 || p.ncols < 8 || p.ncols % 8 != 0 ||
+      p.ldx < p.ncols || p.ldx % 8 != 0 || !p.x || !p.x_lo || p.nsplit < 1 || mm_chunks(p.ncols) % p.nsplit != 0 ||
+      grid < 1)
+    return hipErrorInvalidValue;
+  if (epi == EPI_ARGMAX && (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
+    return hipErrorInvalidValue;
+  if (epi == EPI_STORE && !p.part) return hipErrorInvalidValue;
+  static_assert(16 * kMmChunk * 2 <= kDummyBytes, "dummy region too small");
+  if (!p.dummy) return hipErrorInvalidValue;
+  switch (mm_batch_pad(p.B) / 16) {
+    case 1: return mm_nb<1>(epi, p, grid, s);
+    case 2: return mm_nb<2>(epi, p, grid, s);
+    case 3: return mm_nb<3>(epi, p, grid, s);
+    default: return mm_nb<4>(epi, p, grid, s);
+  }
+}
+
+}  // namespace mtp

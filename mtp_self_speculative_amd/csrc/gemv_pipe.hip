@@ -58,17 +58,19 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
     }
   };
   u32x4 A[P][CH], Bf[P][CH];
+  // Stages past the wave's last one are prefetched from the small dummy region (the
+  // loads stay unconditional, but re-read no weights from HBM).
   auto load = [&](u32x4 (&buf)[P][CH], int it) {
-    const int itc = it < items ? it : (items > 0 ? items - 1 : 0);
-    const int r = items > 0 ? gw + (itc / S) * nw : 0;
-    const int c0 = (itc % S) * SW;
+    const bool live = it < items;
+    const int r = live ? gw + (it / S) * nw : 0;
+    const int c0 = live ? (it % S) * SW : 0;
 #pragma unroll
     for (int q = 0; q < P; ++q) {
-      const T* rp = row_ptr(r, q);
+      const T* rp = live ? row_ptr(r, q) : static_cast<const T*>(p.dummy);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         int col = c0 + c * kWave * VEC + lane * VEC;
-        col = col < ncols ? col : ncols - VEC;
+        col = (col < ncols || !live) ? col : ncols - VEC;
         buf[q][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + col));
       }
     }
@@ -357,6 +359,8 @@ hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, i
   if (!gemv_pipe_fits(p.ncols, p.B, wdtype) || p.ncols % 8 != 0 || p.nrows < 1 || grid < 1)
     return hipErrorInvalidValue;
   if (pro == PRO_EH && !p.h_is_f32) return hipErrorInvalidValue;
+  static_assert(kPipeCH * kWave * 16 <= kDummyBytes, "dummy region too small");
+  if (!p.dummy) return hipErrorInvalidValue;
   return wdtype == 0 ? pipe_dt<F32>(pro, epi, p, grid, s) : pipe_dt<BF16>(pro, epi, p, grid, s);
 }
 

@@ -61,7 +61,11 @@ struct GemvParams {
   int* len;  // when advance > 0 the last workgroup adds it to len[b] and pos[b]
   int* pos;
   int advance;
+  // >= kDummyBytes of readable device memory: the target of the pipelined kernel's
+  // prefetches past a wave's last stage, which are issued but never consumed
+  const void* dummy;
 };
+constexpr int kDummyBytes = 16 * 1024;
 
 // Column-blocked GEMV for any batch (batch rows in blockIdx.y tiles of up to 8).
 hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int max_grid,
@@ -95,12 +99,85 @@ struct AttnParams {
   float* part_o;   // [B, n_q, nsplit, d]
   float* part_ml;  // [B, n_q, nsplit, 2]
   float* o;  // [B, n_q * d]
+  uint16_t* o_bf16;  // when set, the merge writes o as bf16 planes hi / lo (o_bf16, o_bf16_lo,
+  uint16_t* o_bf16_lo;  // [b * ld_o_bf16 + ...]) instead of fp32
+  int ld_o_bf16;
   unsigned* err;
 };
 // Attention (partials per split) followed by the split merge into o. p.chunk must be a
 // positive multiple of attn_chunk_quantum().
 int attn_chunk_quantum();
 hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
+
+// ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions
+
+// y[b, r] = sum_c W[r, c] * x[b, c] for r < nrows, with W bf16 rows (segments as in
+// GemvParams) and x a bf16 operand [16*NB, ldx]. Work items are (64-row tile, K split);
+// EPI_STORE writes fp32 partial sums per split, EPI_ARGMAX (nsplit == 1) finishes an
+// argmax over r per batch row as the GEMV does.
+struct MmParams {
+  const void* w0;
+  const void* w1;
+  const void* w2;
+  int seg1, seg2;
+  int nrows, ncols;
+  // The fp32 input rows as two bf16 planes, x = hi + lo (lo = the rounding residue of hi),
+  // each [>= B rows, ldx]; the contraction runs on both, so the input keeps ~16 bits.
+  const uint16_t* x;
+  const uint16_t* x_lo;
+  int ldx;
+  int B;
+  int nsplit;   // divides mm_chunks(ncols)
+  float* part;  // EPI_STORE: [nsplit][16*NB][nrows]
+  unsigned long long* keys;  // EPI_ARGMAX, as GemvParams
+  unsigned* counter;
+  int* tok_out;
+  int tok_out_stride;
+  float* maxlogit;
+  float* logits;
+  int logits_ld;
+  int* len;
+  int* pos;
+  int advance;
+  const void* dummy;  // as GemvParams::dummy
+};
+__host__ __device__ int mm_chunks(int ncols);  // K chunks of the contraction
+int mm_batch_pad(int B);                           // 16 * NB for batch B
+int mm_split(int nrows, int ncols, int B);         // K splits used for these sizes
+int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu);
+hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s);
+
+// Row-wise steps between contractions, one workgroup per sequence b:
+//   RED_EH:   x = sum(part) -> out (fp32); xq = split(RMSNorm(x) * gain)
+//   RED_QKV:  out = sum(part)
+//   RED_RESID: y = res + sum(part) -> out (and dbg); xq = split(RMSNorm(y) * gain)
+//   RED_SWIGLU: xq = split(silu(sum(part[gate rows])) * sum(part[up rows]))  (n = nrows/2)
+//   PREP_EH:  xq = [split(RMSNorm(h) * g_h), split(RMSNorm(embed[tok]) * g_e)]
+// where split(v) writes the bf16 planes hi = bf16(v), lo = bf16(v - hi).
+enum RedMode : int { RED_EH = 0, RED_QKV = 1, RED_RESID = 2, RED_SWIGLU = 3, PREP_EH = 4 };
+struct RedParams {
+  const float* part;  // [nsplit][bp][n_part]
+  int nsplit, bp, n_part;
+  int n;              // outputs per row
+  const float* res;   // [B, n] (RED_RESID)
+  float* out;         // [B, n] fp32 (RED_EH, RED_QKV, RED_RESID)
+  float* dbg;         // optional copy of out (RED_RESID), [B, dbg_ld]
+  int dbg_ld;
+  const uint16_t* gain;   // bf16 [n]
+  const uint16_t* gain2;  // PREP_EH: g_e
+  float eps;
+  uint16_t* xq;       // bf16 planes [B, ldq]: hi = bf16(v) in xq, lo = bf16(v - hi) in xq_lo
+  uint16_t* xq_lo;
+  int ldq;
+  const float* h;     // PREP_EH hidden [B, n] fp32
+  const uint16_t* embed;
+  const int* tok;
+  int tok_stride;
+  int vocab;
+  unsigned* err;
+};
+int red_max_cols();  // largest n the norm modes accept
+hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s);
 
 struct VerifyParams {
   const float* logits;  // [B, K+1, V]

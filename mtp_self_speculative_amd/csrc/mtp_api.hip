@@ -27,8 +27,32 @@ constexpr int kGemvMaxGrid = 2048;
 struct Layout {
   size_t x, x1, h, qkv, o, act, rope, part_o, part_ml, lm_keys, lm_cnt, v_keys, v_cnt,
       err;
+  size_t dummy;        // zeroed target of never-consumed tail prefetches
+  size_t xq, xq_lo, mm_part;  // batched path: bf16 operand planes, K-split partial sums
+  int ldq;
   size_t total;
 };
+
+// Batched (MFMA) path: bf16 weights, 3..64 sequences, rows short enough for the
+// row-wise norm kernels.
+constexpr int kMmMinBatch = 3;
+constexpr int kMmMaxBatch = 64;
+bool mm_eligible(const mtp_config& c) {
+  return c.dtype == MTP_BF16 && c.hidden <= red_max_cols();
+}
+bool use_mm(const mtp_config& c, int B) {
+  return mm_eligible(c) && B >= kMmMinBatch && B <= kMmMaxBatch;
+}
+
+// The contractions of one draft step that end in K-split partial sums: (rows, columns).
+void mm_shapes(const mtp_config& c, int shapes[5][2]) {
+  const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  const int v[5][2] = {{H, 2 * H}, {qd + 2 * kvd, H}, {H, qd}, {2 * c.ffn, H}, {H, c.ffn}};
+  for (int i = 0; i < 5; ++i) {
+    shapes[i][0] = v[i][0];
+    shapes[i][1] = v[i][1];
+  }
+}
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -56,6 +80,27 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   L.v_keys = take(B * (size_t)(max_k + 1) * 8);
   L.v_cnt = take(B * 4);
   L.err = take(4);
+  L.dummy = take(kDummyBytes);
+  L.ldq = 0;
+  L.xq = L.xq_lo = L.mm_part = off;
+  if (mm_eligible(c) && max_batch >= kMmMinBatch) {
+    const int bmax = max_batch < kMmMaxBatch ? max_batch : kMmMaxBatch;
+    int w = 2 * c.hidden;
+    if (c.ffn > w) w = c.ffn;
+    if (c.n_q_heads * c.head_dim > w) w = c.n_q_heads * c.head_dim;
+    L.ldq = (w + 7) / 8 * 8;
+    L.xq = take((size_t)mm_batch_pad(bmax) * L.ldq * 2);
+    L.xq_lo = take((size_t)mm_batch_pad(bmax) * L.ldq * 2);
+    int shapes[5][2];
+    mm_shapes(c, shapes);
+    size_t part = 0;
+    for (int b = kMmMinBatch; b <= bmax; ++b)
+      for (auto& sh : shapes) {
+        const size_t e = (size_t)mm_split(sh[0], sh[1], b) * mm_batch_pad(b) * sh[0];
+        if (e > part) part = e;
+      }
+    L.mm_part = take(part * 4);
+  }
   L.total = off;
   return L;
 }
@@ -149,6 +194,7 @@ hipError_t timed(mtp_handle* h, int id, hipStream_t s, Fn&& f) {
 // Pick the pipelined kernel when the batch's input vectors fit in LDS, else the
 // column-blocked one.
 hipError_t run_gemv(const mtp_handle* h, Pro pro, Epi epi, GemvParams& g, hipStream_t s) {
+  g.dummy = h->ws + h->L.dummy;
   if (gemv_pipe_fits(g.ncols, g.B, h->cfg.dtype))
     return launch_gemv_pipe(h->cfg.dtype, pro, epi, g, gemv_pipe_grid(g.nrows, g.ncols, h->cfg.dtype, h->num_cu), s);
   g.col_block = col_block_for(g.ncols, g.B, h->cfg.dtype);
@@ -279,6 +325,150 @@ static mtp_status check_kv(const mtp_handle* h, const mtp_kv* kv, int B) {
   return MTP_OK;
 }
 
+// Attention parameters of step k (shared by both paths).
+static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int chunk,
+                              int nsplit) {
+  const mtp_config& c = h->cfg;
+  const Layout& L = h->L;
+  AttnParams a{};
+  a.qkv = h->at<float>(L.qkv);
+  a.ldqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  a.kc = kv->k; a.vc = kv->v;
+  a.n_q = c.n_q_heads; a.n_kv = c.n_kv_heads; a.d = c.head_dim; a.capacity = kv->capacity;
+  a.len = kv->len; a.pos = kv->pos; a.step = k;
+  a.chunk = chunk; a.nsplit = nsplit;
+  a.rope = h->at<float>(L.rope) + (size_t)k * B * c.head_dim;
+  a.scale = 1.0f / sqrtf((float)c.head_dim);
+  a.part_o = h->at<float>(L.part_o);
+  a.part_ml = h->at<float>(L.part_ml);
+  a.o = h->at<float>(L.o);
+  a.err = h->at<unsigned>(L.err);
+  return a;
+}
+
+// The K draft steps for 3..64 sequences with bf16 weights: each projection is an MFMA
+// contraction into K-split partials followed by a row-wise kernel that adds the splits,
+// applies the epilogue and writes the next contraction's normalised bf16 operand.
+static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_kv* kv,
+                                 int32_t B, int32_t K, int32_t* draft_tokens, float* hidden_out,
+                                 float* max_logit_out, float* logits_out, int chunk, int nsplit,
+                                 hipStream_t s) {
+  const mtp_config& c = h->cfg;
+  const mtp_weights& w = h->w;
+  const Layout& L = h->L;
+  const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, F = c.ffn;
+  const int V = c.vocab, qkvd = (nq + 2 * nkv) * d;
+  const int bp = mm_batch_pad(B);
+  float* x = h->at<float>(L.x);
+  float* x1 = h->at<float>(L.x1);
+  float* hb = h->at<float>(L.h);
+  float* part = h->at<float>(L.mm_part);
+  uint16_t* xq = h->at<uint16_t>(L.xq);
+  uint16_t* xq_lo = h->at<uint16_t>(L.xq_lo);
+  unsigned* err = h->at<unsigned>(L.err);
+  auto g16 = [&](const void* p) { return static_cast<const uint16_t*>(p); };
+
+  // One contraction (rows r of w0|w1|w2 against xq) into partials; returns the splits.
+  auto mm = [&](const void* w0, const void* w1, const void* w2, int seg1, int seg2, int N,
+                int Kd, int* ns) -> hipError_t {
+    MmParams m{};
+    m.w0 = w0; m.w1 = w1; m.w2 = w2; m.seg1 = seg1; m.seg2 = seg2;
+    m.nrows = N; m.ncols = Kd; m.x = xq; m.x_lo = xq_lo; m.ldx = L.ldq; m.B = B;
+    m.nsplit = mm_split(N, Kd, B);
+    m.part = part;
+    m.dummy = h->ws + L.dummy;
+    *ns = m.nsplit;
+    return launch_mm(EPI_STORE, m, mm_grid(N, Kd, B, m.nsplit, h->num_cu), s);
+  };
+  auto red = [&](RedMode mode, int ns, int n_part, int n, const float* res, float* out,
+                 float* dbg, const void* gain) -> hipError_t {
+    RedParams r{};
+    r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = n_part; r.n = n;
+    r.res = res; r.out = out; r.dbg = dbg; r.dbg_ld = H;
+    r.gain = g16(gain); r.eps = c.rms_eps;
+    r.xq = mode == RED_QKV ? nullptr : xq;
+    r.xq_lo = mode == RED_QKV ? nullptr : xq_lo;
+    r.ldq = L.ldq;
+    return launch_red(mode, r, B, s);
+  };
+
+  for (int k = 0; k < K; ++k) {
+    hipError_t e;
+    int ns = 1;
+    // 1. gather + separate RMSNorms + concat, then eh_proj
+    e = timed(h, KC_EH, s, [&] {
+      RedParams r{};
+      r.n = H; r.gain = g16(w.g_h); r.gain2 = g16(w.g_e); r.eps = c.rms_eps;
+      r.xq = xq; r.xq_lo = xq_lo; r.ldq = L.ldq; r.h = hb; r.embed = g16(w.embed);
+      r.tok = k == 0 ? last_tokens : draft_tokens + (k - 1);
+      r.tok_stride = k == 0 ? 1 : K;
+      r.vocab = V; r.err = err;
+      hipError_t e2 = launch_red(PREP_EH, r, B, s);
+      if (e2 == hipSuccess) e2 = mm(w.w_eh, w.w_eh, w.w_eh, H, H, H, 2 * H, &ns);
+      if (e2 == hipSuccess) e2 = red(RED_EH, ns, H, H, nullptr, x, nullptr, w.g_attn);
+      return e2;
+    });
+    if (e != hipSuccess) return MTP_ERR_HIP;
+    // 2. QKV (the attention norm was applied by the previous row kernel)
+    e = timed(h, KC_QKV, s, [&] {
+      hipError_t e2 = mm(w.w_q, w.w_k, w.w_v, nq * d, (nq + nkv) * d, qkvd, H, &ns);
+      if (e2 == hipSuccess) e2 = red(RED_QKV, ns, qkvd, qkvd, nullptr, h->at<float>(L.qkv), nullptr, nullptr);
+      return e2;
+    });
+    if (e != hipSuccess) return MTP_ERR_HIP;
+    // 3. RoPE + cache append + attention; the merge writes o as the next bf16 operand
+    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit);
+    a.o_bf16 = xq;
+    a.o_bf16_lo = xq_lo;
+    a.ld_o_bf16 = L.ldq;
+    if (timed(h, KC_ATTN, s, [&] { return launch_attention(c.dtype, a, B, s); }) != hipSuccess)
+      return MTP_ERR_HIP;
+    // 4. O projection + residual; writes RMSNorm(x1) * g_mlp
+    e = timed(h, KC_OPROJ, s, [&] {
+      hipError_t e2 = mm(w.w_o, w.w_o, w.w_o, H, H, H, nq * d, &ns);
+      if (e2 == hipSuccess) e2 = red(RED_RESID, ns, H, H, x, x1, nullptr, w.g_mlp);
+      return e2;
+    });
+    if (e != hipSuccess) return MTP_ERR_HIP;
+    // 5. gate / up + SwiGLU
+    e = timed(h, KC_GATEUP, s, [&] {
+      hipError_t e2 = mm(w.w_gate, w.w_up, w.w_up, F, 2 * F, 2 * F, H, &ns);
+      if (e2 == hipSuccess) e2 = red(RED_SWIGLU, ns, 2 * F, F, nullptr, nullptr, nullptr, nullptr);
+      return e2;
+    });
+    if (e != hipSuccess) return MTP_ERR_HIP;
+    // 6. down + residual -> h^(k); writes RMSNorm(h^(k)) * g_final
+    e = timed(h, KC_DOWN, s, [&] {
+      hipError_t e2 = mm(w.w_down, w.w_down, w.w_down, H, H, H, F, &ns);
+      if (e2 == hipSuccess)
+        e2 = red(RED_RESID, ns, H, H, x1, hb, hidden_out ? hidden_out + (size_t)k * B * H : nullptr,
+                 w.g_final);
+      return e2;
+    });
+    if (e != hipSuccess) return MTP_ERR_HIP;
+    // 7. shared lm_head + argmax -> draft token
+    e = timed(h, KC_LMHEAD, s, [&] {
+      MmParams m{};
+      m.w0 = m.w1 = m.w2 = w.lm_head;
+      m.seg1 = m.seg2 = V;
+      m.nrows = V; m.ncols = H; m.x = xq; m.x_lo = xq_lo; m.ldx = L.ldq; m.B = B; m.nsplit = 1;
+      m.keys = h->at<unsigned long long>(L.lm_keys);
+      m.counter = h->at<unsigned>(L.lm_cnt);
+      m.tok_out = draft_tokens + k;
+      m.tok_out_stride = K;
+      m.maxlogit = max_logit_out ? max_logit_out + (size_t)k * B : nullptr;
+      m.logits = logits_out ? logits_out + (size_t)k * B * V : nullptr;
+      m.logits_ld = V;
+      m.len = kv->len; m.pos = kv->pos;
+      m.advance = (k == K - 1) ? K : 0;
+      m.dummy = h->ws + L.dummy;
+      return launch_mm(EPI_ARGMAX, m, mm_grid(V, H, B, 1, h->num_cu), s);
+    });
+    if (e != hipSuccess) return MTP_ERR_HIP;
+  }
+  return MTP_OK;
+}
+
 static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                              mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
                              float* hidden_out, float* max_logit_out, float* logits_out,
@@ -320,6 +510,9 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   if (launch_draft_setup(c.dtype, h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, hidden,
                          hb, H, s) != hipSuccess)
     return MTP_ERR_HIP;
+  if (use_mm(c, B))
+    return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out,
+                          logits_out, chunk, nsplit, s);
   for (int k = 0; k < K; ++k) {
     hipError_t e;
     // 1. embedding gather + separate RMSNorms + concat + eh_proj
@@ -355,18 +548,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
       return MTP_ERR_HIP;
 
     // 3. RoPE + cache append + split decode attention + merge
-    AttnParams a{};
-    a.qkv = qkv; a.ldqkv = qkvd;
-    a.kc = kv->k; a.vc = kv->v;
-    a.n_q = nq; a.n_kv = nkv; a.d = d; a.capacity = kv->capacity;
-    a.len = kv->len; a.pos = kv->pos; a.step = k;
-    a.chunk = chunk; a.nsplit = nsplit;
-    a.rope = h->at<float>(L.rope) + (size_t)k * B * d;
-    a.scale = 1.0f / sqrtf((float)d);
-    a.part_o = h->at<float>(L.part_o);
-    a.part_ml = h->at<float>(L.part_ml);
-    a.o = o;
-    a.err = err;
+    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit);
     if ((e = timed(h, KC_ATTN, s, [&] { return launch_attention(c.dtype, a, B, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 

@@ -47,8 +47,24 @@ import numpy as np
 # ----------------------------------------------------------------------------- dtypes
 
 def widen_bf16(bits: np.ndarray) -> np.ndarray:
-    """bfloat16 bit patterns -> float32 (exact)."""
-    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    """bfloat16 bit patterns -> float32 (exact): the 16 bits become the high half.
+
+    Large tables are converted in slices on a few threads (the result is the same)."""
+    b = np.ascontiguousarray(bits, np.uint16)
+    out = np.empty(b.shape, np.uint32)
+    fb, fo = b.reshape(-1), out.reshape(-1)
+    step = 1 << 22
+
+    def part(i):
+        np.left_shift(fb[i:i + step], 16, out=fo[i:i + step], dtype=np.uint32)
+
+    if fb.size <= step:
+        part(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(16) as ex:
+            list(ex.map(part, range(0, fb.size, step)))
+    return out.view(np.float32)
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

@@ -66,6 +66,16 @@ CASES = {
     # bf16, B = 9 (two batch tiles), G = 4, empty caches (len 0), K = 5
     "small-bf16-b9-empty": small(name="b9", cid=102, hidden=512, n_q=8, n_kv=2, head_dim=128,
                                  ffn=1536, vocab=7777, batch=9, K=5, ctx_lo=0, ctx_hi=None),
+    # bf16 batched path (MFMA contraction): B = 16, 17, 33, 64 cover one to four 16-sequence
+    # tiles, full and partial; ragged K chunks (H = 640, F = 1800), ragged vocab tile
+    "mm-b16": small(name="mm16", cid=104, hidden=640, n_q=10, n_kv=2, head_dim=64, ffn=1800,
+                    vocab=6007, batch=16, K=3, ctx_lo=1, ctx_hi=200),
+    "mm-b17": small(name="mm17", cid=105, hidden=512, n_q=4, n_kv=4, head_dim=128, ffn=1536,
+                    vocab=4099, batch=17, K=2, ctx_lo=0, ctx_hi=150),
+    "mm-b33": small(name="mm33", cid=106, hidden=512, n_q=8, n_kv=1, head_dim=64, ffn=2048,
+                    vocab=5000, batch=33, K=2, ctx_lo=30, ctx_hi=300),
+    "mm-b64": small(name="mm64", cid=107, hidden=768, n_q=6, n_kv=2, head_dim=128, ffn=2304,
+                    vocab=8192, batch=64, K=2, ctx_lo=1, ctx_hi=120),
     # bf16, B = 2, a cache long enough for several attention splits (len 3000..3100)
     "small-bf16-long": small(name="long", cid=103, hidden=256, n_q=4, n_kv=4, head_dim=128,
                              ffn=512, vocab=2048, batch=2, K=3, ctx_lo=3000, ctx_hi=3100),
@@ -265,6 +275,32 @@ def test_q8b_full_size_parity():
     n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"])
     assert n >= 4
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
+
+
+@pytest.mark.parametrize("name,sample", [("q8b-b32", None), ("q32b", (0, 5)), ("wide", (0, 31, 63))])
+def test_batched_full_size_sampled_parity(name, sample):
+    """The batched workloads at their real sizes, in the launch configuration the
+    benchmark times: every sequence of the batch runs on the GPU, the oracle recomputes a
+    sample of them (sequences are independent: the shortest and longest caches of the
+    ragged batch, else the listed ones)."""
+    cfg = S.get_config(name)
+    lens = S.cache_lengths(cfg)
+    inp = S.make_inputs(cfg, capacity=int(lens.max()) + cfg.K + 8)
+    g = run_draft(cfg, inp, cfg.K, want_logits=False)
+    idx = np.array(sample if sample else (int(np.argmin(lens)), int(np.argmax(lens))))
+    W = O.OracleWeights(cfg, inp.weights)
+    kc, vc = inp.k_cache[idx].copy(), inp.v_cache[idx].copy()
+    r = O.draft(cfg, W, inp.hidden[idx], inp.last_tokens[idx], kc, vc, inp.lens[idx],
+                inp.pos[idx], cfg.K, force_tokens=g["tokens"][idx])
+    n = compare_draft(cfg, r, g["tokens"][idx], g["hidden"][:, idx], g["max"][:, idx])
+    assert n >= len(idx) * cfg.K // 2
+    assert np.array_equal(g["len"], inp.lens + cfg.K) and np.array_equal(g["pos"], inp.pos + cfg.K)
+    for j, b in enumerate(idx):
+        L0 = int(inp.lens[b])
+        for name_, oc in (("k", kc), ("v", vc)):
+            new_g = O.as_float(g[name_][b, :, L0:L0 + cfg.K], cfg.dtype)
+            new_o = O.as_float(oc[j, :, L0:L0 + cfg.K], cfg.dtype)
+            assert np.allclose(new_g, new_o, rtol=1e-2, atol=TOL[cfg.dtype])
 
 
 def test_speculative_decoding_with_gpu_head_equals_greedy():
