@@ -110,7 +110,8 @@ mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t 
 /* Create a handle. `workspace` is caller-owned device memory of at least
  * mtp_workspace_size() bytes, 256-byte aligned, used only by this handle; it is
  * zeroed here (synchronously). Supported shapes: head_dim 64 or 128,
- * n_q_heads / n_kv_heads <= 8, hidden and ffn multiples of 8, max_k <= 100.
+ * n_q_heads / n_kv_heads <= 8, hidden and ffn multiples of 8, max_k <= 100,
+ * max_capacity <= 262144 (256 attention splits of up to 1024 slots).
  * On success *out receives the handle; on failure *out is NULL. */
 mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
                       int32_t max_k, int32_t max_capacity, void* workspace, size_t workspace_bytes,

@@ -9,7 +9,11 @@
 // new key/value are rounded to the cache dtype, and the workgroup whose chunk holds the
 // new slot writes them; every workgroup takes that slot's values from LDS, so none
 // depends on another's cache write.
-// Phase 1: scores (lane groups of LPR lanes reduce one row per head) into LDS.
+// K and V rows stream in double-buffered batches of 16-byte loads (the first V batches
+// are in flight while the softmax runs); the new slot is never read back from the cache.
+// Phase 1: scores into LDS. With a bf16 cache they come from the matrix cores: 16-row
+// tiles of K against the group's query heads (q as bf16 hi/lo planes); with an fp32
+// cache, lane groups of LPR lanes reduce one row per head on the VALU.
 // Phase 2: per-head max / exp / sum over the chunk.
 // Phase 3: P.V with the same row layout, reduced across row groups and waves.
 // Each split writes (max, sum, unnormalised o); the merge kernel (one workgroup per
@@ -22,26 +26,30 @@ namespace mtp {
 constexpr int kAttnWaves = 8;  // waves per workgroup
 constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kMaxGroup = 8;
-constexpr int kJ1 = 4;   // phase 1: rows per lane per batch (lane groups of LPR lanes)
-constexpr int kJ3 = 16;  // phase 3: rows per wave per batch (one row per wave instruction)
+constexpr int kAttnJ = 4;  // cache rows per lane per batch (K and V alike)
 
 // Positions per workgroup must be a multiple of this.
-int attn_chunk_quantum() { return kAttnWaves * kJ3; }
+int attn_chunk_quantum() { return 128; }
 
 size_t attn_lds_bytes(int d, int chunk) {
   return sizeof(float) * ((size_t)kMaxGroup * d + 2 * d + (size_t)kMaxGroup * chunk +
                           (size_t)kAttnWaves * kMaxGroup * d);
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <class CT, int D, int GP>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   using T = typename CT::T;
-  constexpr int VEC = CT::kVec;
-  constexpr int LPR = D / VEC;      // phase 1: lanes per cache row
-  constexpr int PPW = kWave / LPR;  // phase 1: rows per wave instruction
+  constexpr bool kMfma = sizeof(T) == 2;   // bf16 cache: scores on the matrix cores
+  constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte load
+  constexpr int LPR = D / VEC;              // lanes per cache row
+  constexpr int PPW = kWave / LPR;          // rows per wave instruction
   constexpr int HALF = D / 2;
-  constexpr int DPL = D / kWave;    // phase 3: dimensions per lane
-  constexpr int R1 = kAttnWaves * PPW;  // phase 1: rows per workgroup instruction
+  constexpr int R1 = kAttnWaves * PPW;      // rows per workgroup instruction
+  constexpr int RB = R1 * kAttnJ;           // rows per batch
+  constexpr int KS = D / 32;                // MFMA k-steps per 16-slot score tile
   extern __shared__ __align__(16) float sm[];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -62,10 +70,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   const int t0 = s * chunk;
   const int t1 = min(t0 + chunk, T_valid);
   if (t0 >= t1) return;  // nothing cached in this split (the merge skips it)
+  // Cached rows [t0, te) are streamed from memory; the new slot (when it falls in this
+  // chunk) is handled from LDS, so every streamed row is real, finite cache data.
+  const bool has_new = !overflow && slot >= t0 && slot < t1;
+  const int te = has_new ? slot : t1;
+  const int ns = te - t0;  // streamed rows (0 when the chunk holds only the new slot)
   const long kv_base = ((long)b * p.n_kv + g) * p.capacity;
   T* kc = static_cast<T*>(p.kc);
   T* vc = static_cast<T*>(p.vc);
   const int n = t1 - t0;
+  const int nbat = (ns + RB - 1) / RB;  // V batches
+  const int ntile = (ns + 15) / 16;     // score tiles (matrix-core path)
+  const int last = ns > 0 ? te - 1 : t0;  // clamp target of rows past the stream (real data
+                                          // whenever anything is streamed)
 
   // ---- set-up operands first (small, cache-resident): q pairs, new k/v, cos/sin. Every
   // thread loads (threads past HALF duplicate), so no load sits behind a branch.
@@ -86,35 +103,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   const float sn = p.rope[(long)b * D + HALF + ti];
   __builtin_amdgcn_sched_barrier(0);  // set-up loads stay ahead of the K/V stream
 
-  // ---- first batches of K rows (16-byte lane groups) and V rows (lane owns DPL dims)
-  const int nj1 = (n + R1 - 1) / R1;          // phase-1 row iterations per lane
-  const int nj3 = (n + kAttnWaves - 1) / kAttnWaves;  // phase-3 rows per wave
-  auto row1 = [&](int j) { return t0 + j * R1 + wave * PPW + sub; };
-  auto row3 = [&](int j) { return t0 + j * kAttnWaves + wave; };
-  // Rows past the chunk are clamped to its last row (loaded, then ignored); the new
-  // slot's row is loaded too (stale) and replaced by the values computed here.
-  u32x4 kr[kJ1];
-  auto load_k = [&](int j0) {
+  // ---- K stream. Matrix-core path: wave w takes 16-row tiles w, w + 8, ...; lane l reads
+  // 16 bytes of row (tile * 16 + l % 16) at dims 8 * (l / 16) + 32 * k. VALU path: lane
+  // (sub, dl) reads elements dl..dl+VEC-1 of row t0 + batch * RB + jj * R1 + w * PPW + sub.
+  auto row_of = [&](int bt, int jj) { return t0 + bt * RB + jj * R1 + wave * PPW + sub; };
+  auto clamp_row = [&](int t) { return t < te ? t : last; };
+  u32x4 kt0[KS], kt1[KS];
+  auto load_tile = [&](u32x4 (&buf)[KS], int j) {
+    const int t = clamp_row(t0 + (wave + j * kAttnWaves) * 16 + (lane & 15));
 #pragma unroll
-    for (int jj = 0; jj < kJ1; ++jj) {
-      int t = row1(j0 + jj);
-      t = t < t1 ? t : t1 - 1;
-      kr[jj] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(kc + (kv_base + t) * D + dl));
+    for (int k = 0; k < KS; ++k)
+      buf[k] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kc + (kv_base + t) * D + k * 32 + (lane >> 4) * 8));
+  };
+  u32x4 buf0[kAttnJ], buf1[kAttnJ];
+  auto load_batch = [&](const T* base, u32x4 (&buf)[kAttnJ], int bt) {
+#pragma unroll
+    for (int jj = 0; jj < kAttnJ; ++jj) {
+      const int t = clamp_row(row_of(bt, jj));
+      buf[jj] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(base + (kv_base + t) * D + dl));
     }
   };
-  using VT = typename CT::template Vec<DPL>;
-  VT vr[kJ3];
-  auto load_v = [&](int j0) {
-#pragma unroll
-    for (int jj = 0; jj < kJ3; ++jj) {
-      int t = row3(j0 + jj);
-      t = t < t1 ? t : t1 - 1;
-      vr[jj] = CT::template load_vec<DPL>(vc + (kv_base + t) * D + lane * DPL);
-    }
-  };
-  load_k(0);
-  load_v(0);
+  if constexpr (kMfma) {
+    load_tile(kt0, 0);
+    load_tile(kt1, 1);
+  } else {
+    load_batch(kc, buf0, 0);
+    load_batch(kc, buf1, 1);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- RoPE (rotate-half) on q and the new key; round k, v to the cache dtype
@@ -138,27 +155,62 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // ---- phase 1: scores s[h][t] = q_h . k_t * scale (GP >= G heads; the padding heads
-  // compute scores that are never stored)
-  {
+  // ---- phase 1: scores s[h][t] = q_h . k_t * scale into LDS
+  if constexpr (kMfma) {
+    // S^T (16 rows x 16 heads) = K (16 x D) . Q^T (D x 16): q enters as bf16 planes
+    // hi + lo (two MFMAs per k-step), so it keeps ~16 bits; heads >= G are zero.
+    const int hq = lane & 15;
+    bf16x8 qh[KS], qlo[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = hq < G ? q_l[hq * D + k * 32 + (lane >> 4) * 8 + e] : 0.f;
+        uint16_t hi, lo;
+        split_bf16(v, hi, lo);
+        qh[k][e] = __builtin_bit_cast(__bf16, hi);
+        qlo[k][e] = __builtin_bit_cast(__bf16, lo);
+      }
+    }
+    auto score_tile = [&](u32x4 (&buf)[KS], int j) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 kk = __builtin_bit_cast(bf16x8, buf[k]);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qh[k], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qlo[k], a, 0, 0, 0);
+      }
+      // lane l holds rows 4 * (l / 16) + i of the tile for head l % 16
+      const int r0 = (wave + j * kAttnWaves) * 16 + (lane >> 4) * 4;
+      if (hq < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < ns) sc[hq * chunk + r0 + i] = a[i] * p.scale;
+      }
+    };
+    const int my_tiles = wave < ntile ? (ntile - 1 - wave) / kAttnWaves + 1 : 0;
+    for (int j = 0; j < my_tiles; j += 2) {
+      score_tile(kt0, j);
+      load_tile(kt0, j + 2);
+      if (j + 1 >= my_tiles) break;
+      score_tile(kt1, j + 1);
+      load_tile(kt1, j + 3);
+    }
+    // the first V batches go out before the softmax
+    load_batch(vc, buf0, 0);
+    load_batch(vc, buf1, 1);
+  } else {
     float qr[GP][VEC];
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qr[h][e] = q_l[(h < G ? h : 0) * D + dl + e];
-    float knr[VEC];
+    auto scores = [&](u32x4 (&buf)[kAttnJ], int bt) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) knr[e] = kn[dl + e];
-    for (int j0 = 0; j0 < nj1; j0 += kJ1) {
-      if (j0 > 0) load_k(j0);
-#pragma unroll
-      for (int jj = 0; jj < kJ1; ++jj) {
-        const int t = row1(j0 + jj);
-        const bool is_new = t == slot;
+      for (int jj = 0; jj < kAttnJ; ++jj) {
+        const int t = row_of(bt, jj);
         float kv[VEC];
-        CT::unpack(kr[jj], kv);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) kv[e] = is_new ? knr[e] : kv[e];
+        CT::unpack(buf[jj], kv);
         float part[GP];
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
@@ -175,17 +227,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
             part[h] += __shfl_xor(part[h], 16, kWave);
           }
         }
-        if ((lane % LPR) == 0 && t < t1) {
+        if ((lane % LPR) == 0 && t < te) {
 #pragma unroll
           for (int h = 0; h < GP; ++h)
             if (h < G) sc[h * chunk + (t - t0)] = part[h] * p.scale;
         }
       }
+    };
+    for (int bt = 0; bt < nbat; bt += 2) {
+      scores(buf0, bt);
+      load_batch(kc, buf0, bt + 2);
+      if (bt + 1 >= nbat) break;
+      scores(buf1, bt + 1);
+      load_batch(kc, buf1, bt + 3);
+    }
+    load_batch(vc, buf0, 0);
+    load_batch(vc, buf1, 1);
+  }
+  // the new slot's score, from LDS (q and the rounded new key)
+  if (has_new && wave == 0) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      if (h < G) {
+        float d0 = 0.f;
+        for (int e = lane; e < D; e += kWave) d0 = fmaf(q_l[h * D + e], kn[e], d0);
+        d0 = wave_sum_fast(d0);
+        if (lane == 0) sc[h * chunk + (slot - t0)] = d0 * p.scale;
+      }
     }
   }
   __syncthreads();
 
-  // ---- phase 2: per-head max, exp, sum over the chunk
+  // ---- phase 2: per-head max, exp, sum over the chunk (the first V batches are in flight)
   const long hbase = (long)b * p.n_q + g * G;
   for (int h = wave; h < G; h += kAttnWaves) {
     float m = -INFINITY;
@@ -205,46 +278,64 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   }
   __syncthreads();
 
-  // ---- phase 3: unnormalised P.V; lane owns dims lane*DPL .. +DPL-1, waves own rows.
-  // Branch-free: rows past the chunk get weight 0, the new slot's row is selected from LDS.
+  // ---- phase 3: unnormalised P.V over the streamed rows (rows past the stream get weight
+  // 0; their clamped values are real data), then the new slot's row from LDS. Partial sums
+  // are reduced over the PPW rows of a wave instruction (lane shuffles) and over the waves
+  // (LDS).
   {
-    float acc[GP][DPL];
+    float acc[GP][VEC];
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-    float vnr[DPL];
+      for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+    auto pv = [&](u32x4 (&buf)[kAttnJ], int bt) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) vnr[e] = vn[lane * DPL + e];
-    for (int j0 = 0; j0 < nj3; j0 += kJ3) {
-      if (j0 > 0) load_v(j0);
-      float pr[kJ3][GP];
+      for (int jj = 0; jj < kAttnJ; ++jj) {
+        const int t = row_of(bt, jj);
+        const bool live = t < te;
+        const int tc = (live ? t : last) - t0;
+        float pr[GP];
 #pragma unroll
-      for (int jj = 0; jj < kJ3; ++jj) {
-        const int t = row3(j0 + jj);
-        const int tc = (t < t1 ? t : t1 - 1) - t0;
-#pragma unroll
-        for (int h = 0; h < GP; ++h) pr[jj][h] = sc[(h < G ? h : 0) * chunk + tc];
-      }
-#pragma unroll
-      for (int jj = 0; jj < kJ3; ++jj) {
-        const int t = row3(j0 + jj);
-        const bool live = t < t1;
-        float vv[DPL];
-        CT::template unpack_vec<DPL>(vr[jj], vv);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) vv[e] = live ? (t == slot ? vnr[e] : vv[e]) : 0.f;
+        for (int h = 0; h < GP; ++h) pr[h] = live ? sc[(h < G ? h : 0) * chunk + tc] : 0.f;
+        float vv[VEC];
+        CT::unpack(buf[jj], vv);
 #pragma unroll
         for (int h = 0; h < GP; ++h)
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pr[jj][h], vv[e], acc[h][e]);
+          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(pr[h], vv[e], acc[h][e]);
       }
+    };
+    for (int bt = 0; bt < nbat; bt += 2) {
+      pv(buf0, bt);
+      load_batch(vc, buf0, bt + 2);
+      if (bt + 1 >= nbat) break;
+      pv(buf1, bt + 1);
+      load_batch(vc, buf1, bt + 3);
     }
 #pragma unroll
     for (int h = 0; h < GP; ++h)
-      if (h < G)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) ored[(wave * kMaxGroup + h) * D + lane * DPL + e] = acc[h][e];
+      for (int e = 0; e < VEC; ++e) {
+        float v = acc[h][e];
+#pragma unroll
+        for (int m = LPR; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+        acc[h][e] = v;
+      }
+    if (has_new && wave == 0 && lane < LPR) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        const float pn = sc[(h < G ? h : 0) * chunk + (slot - t0)];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(pn, vn[dl + e], acc[h][e]);
+      }
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+        if (h < G)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ored[(wave * kMaxGroup + h) * D + dl + e] = acc[h][e];
+    }
     __syncthreads();
     for (int i = tid; i < G * D; i += kAttnThreads) {
       const int h = i / D, dd = i % D;
@@ -255,7 +346,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     }
   }
   // ---- the workgroup whose chunk holds the new slot appends it to the cache
-  if (!overflow && slot >= t0 && slot < t0 + chunk && tid < D) {
+  if (has_new && tid < D) {
     const long o = (kv_base + slot) * D + tid;
     CT::put(kc, o, kn[tid]);
     CT::put(vc, o, vn[tid]);

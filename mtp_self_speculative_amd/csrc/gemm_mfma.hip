@@ -9,11 +9,11 @@
 // multiplied (two MFMAs per step into one fp32 accumulator): rounding the input to one
 // bf16 would cost several hundredths in the hidden state at these sizes.
 //
-// Work is split into items of (64-row tile, K split). A workgroup of four waves takes
-// items in turn (a persistent grid); wave w owns rows 16w..16w+15 of the tile. Each item
-// is walked in chunks of 256 columns: per chunk a wave streams 16 rows x 512 bytes of W
-// (eight 16-byte non-temporal loads per lane, so every row piece is a full 64-byte
-// segment) and runs 16 x NB MFMAs. The input rows (both planes) of the chunk are staged
+// Work is split into items of (128-row tile, K split). A workgroup of four waves takes
+// items in turn (a persistent grid); wave w owns two 16-row slices of the tile, which
+// share every input fragment it reads from LDS. Each item is walked in chunks of 256
+// columns: per chunk a wave streams 32 rows x 512 bytes of W (sixteen 16-byte loads per
+// lane, so every row piece is a full 64-byte segment) and runs 32 x NB MFMAs. The input rows (both planes) of the chunk are staged
 // once per workgroup in LDS (double-buffered) and read from there by all four waves. W stages
 // are double-buffered in registers; all loads are unconditional (indexes past the end
 // are clamped), so the compiler can wait for exactly the buffer being consumed.
@@ -32,21 +32,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMmWaves = 4;
 constexpr int kMmThreads = kMmWaves * kWave;
-constexpr int kMmTileRows = 16 * kMmWaves;
-constexpr int kMmChunk = 256;               // columns per stage
-constexpr int kMmKSteps = kMmChunk / 32;    // MFMA k-steps per stage
-constexpr int kMmLdsRow = kMmChunk + 8;     // bf16 per LDS row: 16-byte pad against bank conflicts
+constexpr int kMmMT = 2;                          // 16-row slices per wave
+constexpr int kMmTileRows = 16 * kMmMT * kMmWaves;  // 128
+constexpr int kMmChunk = 256;                     // columns per stage
+constexpr int kMmKSteps = kMmChunk / 32;          // MFMA k-steps per stage
+constexpr int kMmLdsRow = kMmChunk + 8;           // bf16 per LDS row: 16-byte pad against bank conflicts
 constexpr int kMmMaxNB = 4;
 
 __host__ __device__ int mm_chunks(int ncols) { return (ncols + kMmChunk - 1) / kMmChunk; }
 int mm_batch_pad(int B) { return (B + 15) / 16 * 16; }
 
-// K splits: enough items to occupy the chip (about 1024), while the partial sums stay
+// K splits: enough items to occupy the chip (about 512), while the partial sums stay
 // below an eighth of the weight bytes (nsplit * 16NB * 4 B per row <= ncols * 2 B / 8).
 int mm_split(int nrows, int ncols, int B) {
   const int ntiles = (nrows + kMmTileRows - 1) / kMmTileRows;
   const int nch = mm_chunks(ncols);
-  int want = 1024 / ntiles;
+  int want = 512 / ntiles;
   const int cap = ncols / (16 * mm_batch_pad(B));
   if (want > cap) want = cap;
   if (want > nch) want = nch;
@@ -62,7 +63,7 @@ static size_t mm_lds_bytes(int nb) { return (size_t)4 * 16 * nb * kMmLdsRow * si
 int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
   const long items = (long)((nrows + kMmTileRows - 1) / kMmTileRows) * nsplit;
   const int nb = mm_batch_pad(B) / 16;
-  const int per_cu = nb >= 3 ? 1 : nb == 2 ? 2 : 4;  // resident workgroups (LDS, registers)
+  const int per_cu = nb >= 3 ? 1 : 2;  // resident workgroups (LDS, registers)
   long g = (long)per_cu * num_cu;
   if (g > items) g = items;
   (void)ncols;
@@ -89,6 +90,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
   auto clampit = [&](int it) { return it < stages ? it : (stages > 0 ? stages - 1 : 0); };
   auto item_of = [&](int it) { return (int)blockIdx.x + (it / C) * G; };
   auto chunk_of = [&](int it) { return (item_of(it) % p.nsplit) * C + it % C; };
+  // first row of slice m of this wave in the tile of stage it
+  auto slice_row = [&](int it, int m) {
+    return (item_of(it) / p.nsplit) * kMmTileRows + (wave * kMmMT + m) * 16;
+  };
 
   auto row_ptr = [&](int r) -> const uint16_t* {
     if (r < p.seg1) return static_cast<const uint16_t*>(p.w0) + (long)r * Kd;
@@ -96,21 +101,24 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
     return static_cast<const uint16_t*>(p.w2) + (long)(r - p.seg2) * Kd;
   };
 
-  u32x4 A[kMmKSteps], Bf[kMmKSteps];
+  u32x4 A[kMmMT][kMmKSteps], Bf[kMmMT][kMmKSteps];
   // Stages past the workgroup's last one are prefetched from the dummy region (16 rows
-  // of 256 bf16), never consumed.
-  auto wload = [&](u32x4 (&buf)[kMmKSteps], int it) {
+  // of 256 bf16) and never consumed.
+  auto wload = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
     const bool live = it < stages;
-    int r = (item_of(it) / p.nsplit) * kMmTileRows + wave * 16 + (lane & 15);
-    r = r < N ? r : N - 1;
-    const uint16_t* rp = live ? row_ptr(r)
-                              : static_cast<const uint16_t*>(p.dummy) + (lane & 15) * kMmChunk;
     const int c0 = live ? chunk_of(it) * kMmChunk + (lane >> 4) * 8 : (lane >> 4) * 8;
 #pragma unroll
-    for (int s = 0; s < kMmKSteps; ++s) {
-      int col = c0 + s * 32;
-      col = (col < Kd || !live) ? col : Kd - 8;
-      buf[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + col));
+    for (int m = 0; m < kMmMT; ++m) {
+      int r = slice_row(it, m) + (lane & 15);
+      r = r < N ? r : N - 1;
+      const uint16_t* rp = live ? row_ptr(r)
+                                : static_cast<const uint16_t*>(p.dummy) + (lane & 15) * kMmChunk;
+#pragma unroll
+      for (int k = 0; k < kMmKSteps; ++k) {
+        int col = c0 + k * 32;
+        col = (col < Kd || !live) ? col : Kd - 8;
+        buf[m][k] = *reinterpret_cast<const u32x4*>(rp + col);
+      }
     }
   };
 
@@ -143,71 +151,78 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
     }
   };
 
-  f32x4 acc[NB];
+  f32x4 acc[kMmMT][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < kMmMT; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   unsigned long long best[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) best[nb] = 0ull;
 
-  auto consume = [&](u32x4 (&buf)[kMmKSteps], int it) {
+  // Each input fragment read from LDS serves both 16-row slices of the wave.
+  auto consume = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
     const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * kMmLdsRow + (lane & 15) * kMmLdsRow +
                          (lane >> 4) * 8;
 #pragma unroll
-    for (int s = 0; s < kMmKSteps; ++s) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, buf[s]);
+    for (int k = 0; k < kMmKSteps; ++k) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 bh = *reinterpret_cast<const u32x4*>(xb + nb * 16 * kMmLdsRow + s * 32);
-        const u32x4 bl =
-            *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * kMmLdsRow + s * 32);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh),
-                                                          acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl),
-                                                          acc[nb], 0, 0, 0);
+        const bf16x8 bh = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + nb * 16 * kMmLdsRow + k * 32));
+        const bf16x8 bl = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * kMmLdsRow + k * 32));
+#pragma unroll
+        for (int m = 0; m < kMmMT; ++m) {
+          const bf16x8 w = __builtin_bit_cast(bf16x8, buf[m][k]);
+          acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bh, acc[m][nb], 0, 0, 0);
+          acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bl, acc[m][nb], 0, 0, 0);
+        }
       }
     }
   };
 
-  // Lane l holds rows 4*(l/16)+i (i < 4) of the wave's 16-row slice for sequence
-  // 16*nb + l%16.
+  // Lane l holds rows 4*(l/16)+i (i < 4) of slice m for sequence 16*nb + l%16.
   auto finish_item = [&](int it) {
-    const int item = item_of(it);
-    const int tile = item / p.nsplit, split = item % p.nsplit;
-    const int r0 = tile * kMmTileRows + wave * 16 + (lane >> 4) * 4;
+    const int split = item_of(it) % p.nsplit;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int b = nb * 16 + (lane & 15);
-      if constexpr (EPI == EPI_STORE) {
-        float* dst = p.part + ((long)split * BP + b) * N + r0;
-        if (r0 + 3 < N && (N & 3) == 0) {
-          *reinterpret_cast<float4*>(dst) = float4{acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]};
-        } else {
+    for (int m = 0; m < kMmMT; ++m) {
+      const int r0 = slice_row(it, m) + (lane >> 4) * 4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (r0 + i < N) dst[i] = acc[nb][i];
-        }
-      } else {
-        unsigned long long k = 0ull;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = nb * 16 + (lane & 15);
+        if constexpr (EPI == EPI_STORE) {
+          float* dst = p.part + ((long)split * BP + b) * N + r0;
+          if (r0 + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<float4*>(dst) =
+                float4{acc[m][nb][0], acc[m][nb][1], acc[m][nb][2], acc[m][nb][3]};
+          } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (r0 + i < N) {
-            const unsigned long long ki = pack_key(acc[nb][i], (uint32_t)(r0 + i));
-            k = ki > k ? ki : k;
-            if (p.logits && b < p.B) p.logits[(long)b * p.logits_ld + r0 + i] = acc[nb][i];
+            for (int i = 0; i < 4; ++i)
+              if (r0 + i < N) dst[i] = acc[m][nb][i];
           }
+        } else {
+          unsigned long long k = 0ull;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (r0 + i < N) {
+              const unsigned long long ki = pack_key(acc[m][nb][i], (uint32_t)(r0 + i));
+              k = ki > k ? ki : k;
+              if (p.logits && b < p.B) p.logits[(long)b * p.logits_ld + r0 + i] = acc[m][nb][i];
+            }
+          }
+          unsigned long long o = __shfl_xor(k, 16, kWave);
+          k = o > k ? o : k;
+          o = __shfl_xor(k, 32, kWave);
+          k = o > k ? o : k;
+          best[nb] = k > best[nb] ? k : best[nb];
         }
-        unsigned long long o = __shfl_xor(k, 16, kWave);
-        k = o > k ? o : k;
-        o = __shfl_xor(k, 32, kWave);
-        k = o > k ? o : k;
-        best[nb] = k > best[nb] ? k : best[nb];
+        acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
-  auto stage = [&](u32x4 (&buf)[kMmKSteps], int it) {
+  auto stage = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
     xload(it + 1);
     consume(buf, it);
     wload(buf, it + 2);
@@ -266,8 +281,8 @@ static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   if (epi != EPI_STORE && epi != EPI_ARGMAX) return hipErrorInvalidValue;
   if (p.B < 1 || p.B > 16 * kMmMaxNB || p.nrows < 1 || p.ncols < 8 || p.ncols % 8 != 0 ||
-      p.ldx < p.ncols || p.ldx % 8 != 0 || !p.x || !p.x_lo || p.nsplit < 1 || mm_chunks(p.ncols) % p.nsplit != 0 ||
-      grid < 1)
+      p.ldx < p.ncols || p.ldx % 8 != 0 || !p.x || !p.x_lo || p.nsplit < 1 ||
+      mm_chunks(p.ncols) % p.nsplit != 0 || grid < 1)
     return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX && (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
     return hipErrorInvalidValue;

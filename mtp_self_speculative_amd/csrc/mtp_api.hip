@@ -16,7 +16,7 @@ using namespace mtp;
 
 constexpr int kMaxSplits = 256;
 constexpr int kMinChunk = 64;
-constexpr int kMaxChunk = 512;
+constexpr int kMaxChunk = 1024;
 constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
 constexpr int kMaxK = 100;
 constexpr int kMaxGroupHeads = 8;

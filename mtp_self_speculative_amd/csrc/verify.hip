@@ -6,6 +6,7 @@
 // order independent and hence deterministic. The last workgroup of sequence b turns the
 // K+1 keys into the target's tokens, scans the longest prefix of drafts that match them
 // and writes accepted_len and the bonus token.
+// Rows of a length divisible by 4 take a variant with 16-byte loads and larger chunks.
 // Rollback: one lane per sequence moves len/pos to the committed prefix.
 #include "common.h"
 #include "kernels.h"
@@ -65,6 +66,67 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) 
   }
 }
 
+// Same reduction for rows whose length is a multiple of 4 (16-byte aligned rows): each
+// lane keeps kVerifyVecPer float4 loads in flight, a workgroup covers kVerifyVecChunk
+// logits, so far fewer workgroups (and same-address atomics) are needed per row.
+constexpr int kVerifyVecPer = 8;
+constexpr int kVerifyVecChunk = kVerifyThreads * kVerifyVecPer * 4;
+
+__global__ __launch_bounds__(kVerifyThreads) void verify_vec_kernel(VerifyParams p) {
+  __shared__ unsigned long long kred[kVerifyThreads / kWave];
+  __shared__ int flag;
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const f32x4v* row = reinterpret_cast<const f32x4v*>(p.logits + ((long)b * (p.K + 1) + j) * p.V);
+  const int lo = c * (kVerifyVecChunk / 4), hi = min(lo + kVerifyVecChunk / 4, p.V / 4);
+  int idx[kVerifyVecPer];
+  f32x4v v[kVerifyVecPer];
+#pragma unroll
+  for (int k = 0; k < kVerifyVecPer; ++k) {
+    idx[k] = min(lo + (int)threadIdx.x + k * kVerifyThreads, hi - 1);
+    v[k] = __builtin_nontemporal_load(row + idx[k]);
+  }
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int k = 0; k < kVerifyVecPer; ++k) {
+    const uint32_t i0 = (uint32_t)idx[k] * 4;
+    unsigned long long key = pack_key(v[k].x, i0);
+    unsigned long long t = pack_key(v[k].y, i0 + 1);
+    key = t > key ? t : key;
+    t = pack_key(v[k].z, i0 + 2);
+    key = t > key ? t : key;
+    t = pack_key(v[k].w, i0 + 3);
+    key = t > key ? t : key;
+    best = key > best ? key : best;
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) kred[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kVerifyThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
+    if (best) keep_alive(atomic_max_key(p.keys + (long)b * (p.K + 1) + j, best));
+  }
+  if (last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) {
+    if (threadIdx.x == 0) {
+      unsigned long long* kb = p.keys + (long)b * (p.K + 1);
+      int a = 0, next = -1;
+      for (int q = 0; q <= p.K; ++q) {
+        const int t = (int)key_index(take_key(kb + q));
+        if (next < 0) {
+          if (q < p.K && p.draft[(long)b * p.K + q] == t) {
+            ++a;
+          } else {
+            next = t;
+          }
+        }
+      }
+      p.accepted[b] = a;
+      p.next[b] = next;
+    }
+  }
+}
+
 __global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, int K,
                                 unsigned* err) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -80,6 +142,12 @@ __global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, 
 }
 
 hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s) {
+  if (p.V < 1 || p.K < 0 || B < 1) return hipErrorInvalidValue;
+  if (p.V % 4 == 0 && ((uintptr_t)p.logits & 15) == 0) {
+    const int nchunk = (p.V + kVerifyVecChunk - 1) / kVerifyVecChunk;
+    hipLaunchKernelGGL(verify_vec_kernel, dim3(nchunk, p.K + 1, B), dim3(kVerifyThreads), 0, s, p);
+    return hipGetLastError();
+  }
   if (p.chunk != kVerifyThreads * kVerifyPer || (long)p.nchunk * p.chunk < p.V ||
       (long)(p.nchunk - 1) * p.chunk >= p.V)
     return hipErrorInvalidValue;
