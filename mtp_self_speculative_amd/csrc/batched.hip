@@ -16,6 +16,7 @@ namespace mtp {
 
 constexpr int kRedThreads = 512;
 constexpr int kRedVPT = 4;  // float4 groups per thread in the norm modes
+constexpr int kRedMaxSplit = 16;
 
 int red_max_cols() { return 4 * kRedVPT * kRedThreads; }
 
@@ -44,10 +45,19 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
   __shared__ float red[kRedThreads / kWave];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int n = p.n;
+  // All split partials of a column group are requested at once (indexes past nsplit
+  // repeat the last split and are not added), then added in split order.
   auto sum_part = [&](int c) -> float4 {
-    float4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.nsplit; ++s)
-      v = add4(v, *reinterpret_cast<const float4*>(p.part + ((long)s * p.bp + b) * p.n_part + c));
+    float4 t[kRedMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kRedMaxSplit; ++s) {
+      const int sc = s < p.nsplit ? s : p.nsplit - 1;
+      t[s] = *reinterpret_cast<const float4*>(p.part + ((long)sc * p.bp + b) * p.n_part + c);
+    }
+    float4 v = t[0];
+#pragma unroll
+    for (int s = 1; s < kRedMaxSplit; ++s)
+      if (s < p.nsplit) v = add4(v, t[s]);
     return v;
   };
 
@@ -123,7 +133,8 @@ hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s) {
   if (mode == PREP_EH && (!p.gain2 || !p.h || !p.embed || !p.tok || !p.err))
     return hipErrorInvalidValue;
   if (mode == RED_RESID && !p.res) return hipErrorInvalidValue;
-  if (mode != PREP_EH && (!p.part || p.nsplit < 1 || p.bp < B || p.n_part % 4 != 0))
+  if (mode != PREP_EH &&
+      (!p.part || p.nsplit < 1 || p.nsplit > kRedMaxSplit || p.bp < B || p.n_part % 4 != 0))
     return hipErrorInvalidValue;
   const dim3 g(B), t(kRedThreads);
   switch (mode) {

@@ -38,16 +38,18 @@ constexpr int kMmChunk = 256;                     // columns per stage
 constexpr int kMmKSteps = kMmChunk / 32;          // MFMA k-steps per stage
 constexpr int kMmLdsRow = kMmChunk + 8;           // bf16 per LDS row: 16-byte pad against bank conflicts
 constexpr int kMmMaxNB = 4;
+constexpr int kMmMaxSplit = 16;  // the row-wise reductions add at most this many splits
 
 __host__ __device__ int mm_chunks(int ncols) { return (ncols + kMmChunk - 1) / kMmChunk; }
 int mm_batch_pad(int B) { return (B + 15) / 16 * 16; }
 
-// K splits: enough items to occupy the chip (about 512), while the partial sums stay
-// below an eighth of the weight bytes (nsplit * 16NB * 4 B per row <= ncols * 2 B / 8).
+// K splits: enough items to occupy the chip (about 512), at most 16, while the partial
+// sums stay below an eighth of the weight bytes (nsplit * 16NB * 4 B per row <= ncols * 2 B / 8).
 int mm_split(int nrows, int ncols, int B) {
   const int ntiles = (nrows + kMmTileRows - 1) / kMmTileRows;
   const int nch = mm_chunks(ncols);
   int want = 512 / ntiles;
+  if (want > kMmMaxSplit) want = kMmMaxSplit;
   const int cap = ncols / (16 * mm_batch_pad(B));
   if (want > cap) want = cap;
   if (want > nch) want = nch;
