@@ -271,6 +271,29 @@ def verify(target_logits: np.ndarray, draft_tokens: np.ndarray):
     return acc, nxt
 
 
+def verify_from_hidden(cfg, target_hidden: np.ndarray, target_norm: np.ndarray,
+                       lm_head: np.ndarray, draft_tokens: np.ndarray, dt=np.float32):
+    """Greedy verification from the target's hidden states.  [OVSD] Overview;
+    [SPEC] Architecture (the LM head is shared with the verifier).
+
+    target_hidden [B, K+1, H] (storage dtype): the target's last-layer outputs before
+    its final norm at the K+1 verified inputs [last_token, d_1 .. d_K]; target_norm [H]
+    is the target's final-norm gain; lm_head [V, H] is the shared head. The target's
+    logits are lm_head . RMSNorm(h; target_norm), and verification then proceeds as in
+    ``verify``. Returns accepted_len [B], next_token [B], and the top-1 minus top-2
+    margin [B, K+1] of each row (for near-tie aware comparisons).
+    """
+    st = cfg.dtype
+    th = as_float(target_hidden, st, dt)
+    g = as_float(target_norm, st, dt)
+    w = as_float(lm_head, st, dt)
+    logits = rmsnorm(th, g, cfg.rms_eps) @ w.T
+    V = logits.shape[-1]
+    srt = np.partition(logits, V - 2, axis=-1)[..., V - 2:]
+    acc, nxt = verify(logits, draft_tokens)
+    return acc, nxt, srt[..., 1] - srt[..., 0]
+
+
 def kv_rollback(lens: np.ndarray, pos: np.ndarray, accepted_len: np.ndarray, K: int):
     """Cut the MTP cache back to the committed prefix.  [OVMTP] Stateful execution;
     [OVSD] Overview (drafting resumes after the first divergent token).

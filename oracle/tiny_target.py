@@ -73,13 +73,16 @@ class TinyTarget:
 
 
 def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_fn,
-                       rollback_fn, K: int):
+                       rollback_fn, K: int, from_hidden: bool = False):
     """Greedy speculative decoding driven by a draft head.
 
     draft_fn(hidden [H], last_token, K, committed) -> K draft tokens (the head keeps
     its cache and advances it by K; committed is the sequence so far);
-    verify_fn(target_logits [K+1, V], drafts) -> (a, next); rollback_fn(a) cuts the head's cache back.  Target rows are the last-position
-    logits of full forwards over the committed prefix extended by j drafts.
+    verify_fn(target_rows [K+1, X], drafts) -> (a, next); rollback_fn(a) cuts the
+    head's cache back.  Target rows are taken at the last position of full forwards
+    over the committed prefix extended by j drafts: its logits (X = V), or with
+    from_hidden its hidden states before the final norm (X = H), which verify_fn turns
+    into tokens through the target's final norm and the shared lm_head.
     Returns (emitted tokens, list of accepted lengths).
     """
     seq = [int(x) for x in prompt]
@@ -94,7 +97,7 @@ def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_
             hj, lj = target.forward(seq + d[:j])
             rows.append(lj[-1])
             hids.append(hj[-1])
-        a, nxt = verify_fn(np.stack(rows), d)
+        a, nxt = verify_fn(np.stack(hids if from_hidden else rows), d)
         a, nxt = int(a), int(nxt)
         rollback_fn(a)
         accepted.append(a)

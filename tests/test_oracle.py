@@ -398,6 +398,40 @@ def test_speculative_equals_greedy(vocab, cache_len):
     assert all(0 <= a <= 3 for a in acc)
 
 
+@pytest.mark.parametrize("vocab,cache_len", [(4096, 0), (8, 8)])
+def test_speculative_from_hidden_states_equals_greedy(vocab, cache_len):
+    """Verification from the target's hidden states (its final norm and the shared
+    lm_head applied by the verifier) also reproduces plain greedy decoding exactly."""
+    cfg = small_cfg(cid=70 + vocab + cache_len, batch=1, vocab=vocab, ctx_lo=cache_len, K=3)
+    inp = _inputs(cfg, 256)
+    W = O.OracleWeights(cfg, inp.weights)
+    tw = S.target_weights(cfg, 2)
+    tgt = TinyTarget(cfg, tw, inp.weights["embed"], inp.weights["lm_head"])
+    prompt = S.prompt_tokens(cfg, 6)
+    ref = tgt.greedy(prompt, 40)
+    st = {"kc": inp.k_cache.copy(), "vc": inp.v_cache.copy(),
+          "len": np.array([cache_len]), "pos": np.array([len(prompt) - 1])}
+
+    def draft_fn(h, last, K, _seq):
+        r = O.draft(cfg, W, np.asarray(h, np.float32)[None], np.array([last]), st["kc"], st["vc"],
+                    st["len"], st["pos"], K)
+        st["len"], st["pos"] = r["lens"], r["pos"]
+        return r["draft_tokens"][0]
+
+    def rollback_fn(a):
+        st["len"], st["pos"] = O.kv_rollback(st["len"], st["pos"], np.array([a]), 3)
+
+    def verify_fn(hid_rows, d):
+        a, n, _ = O.verify_from_hidden(cfg, hid_rows[None], tw["g_final"], inp.weights["lm_head"],
+                                       np.asarray(d)[None])
+        return a[0], n[0]
+
+    out, acc = speculative_greedy(tgt, prompt, 40, draft_fn, verify_fn, rollback_fn, 3,
+                                  from_hidden=True)
+    assert out == ref
+    assert all(0 <= a <= 3 for a in acc)
+
+
 def test_speculative_equals_greedy_with_scripted_drafts():
     """A drafter that proposes the target's own greedy continuation with one planted
     error at index i (or none) must be accepted for exactly i tokens, and the output
