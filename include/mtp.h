@@ -163,6 +163,25 @@ mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* 
 mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,
                            int32_t K, void* stream);
 
+/*
+ * Greedy verification from the target's hidden states instead of its logits
+ * (OpenVINO GenAI "Speculative Decoding", Overview; speculators "MTP (Multi-Token
+ * Prediction)", Architecture: the LM head is shared with the verifier). For every
+ * sequence b and verified input j (0..K) the target's token is
+ *   argmax_v (lm_head . RMSNorm(target_hidden[b, j]; target_norm))_v, lowest index on ties,
+ * computed by the fused norm + lm_head + argmax kernels without writing logits; drafts are
+ * then accepted as in mtp_verify.
+ *   target_hidden [B, K+1, hidden] config dtype, 16-byte aligned: the target's last-layer
+ *                 outputs before its final norm at inputs [last_token, d_1 .. d_K]
+ *   target_norm   [hidden] config dtype, 16-byte aligned: the target's final-norm gain
+ *   draft_tokens, accepted_len, next_token: as mtp_verify.
+ * Rows are processed in groups of up to 64 (each group streams the lm_head once).
+ * Errors: as mtp_verify.
+ */
+mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,
+                             const int32_t* draft_tokens, int32_t B, int32_t K,
+                             int32_t* accepted_len, int32_t* next_token, void* stream);
+
 /* Synchronise `stream`, read and clear the device error word. *bits receives the
  * MTP_DEVERR_* bits (may be NULL). Returns MTP_ERR_DEVICE when any bit was set. */
 mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits);

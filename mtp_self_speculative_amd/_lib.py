@@ -64,6 +64,7 @@ _SIGS = {
     "mtp_draft": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, _P, _P]),
     "mtp_draft_debug": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, _P, _P, _P, _P, _P]),
     "mtp_verify": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
+    "mtp_verify_hidden": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "mtp_kv_rollback": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P]),
     "mtp_get_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "mtp_set_profiling": (_I, [_P, ctypes.c_uint32]),
@@ -159,6 +160,13 @@ def mtp_verify(handle: int, target_logits: int, draft_tokens: int | None, B: int
                accepted_len: int, next_token: int, stream: int | None) -> None:
     _check(LIB.mtp_verify(handle, target_logits, draft_tokens, B, K, accepted_len, next_token,
                           stream), "mtp_verify")
+
+
+def mtp_verify_hidden(handle: int, target_hidden: int, target_norm: int,
+                      draft_tokens: int | None, B: int, K: int, accepted_len: int,
+                      next_token: int, stream: int | None) -> None:
+    _check(LIB.mtp_verify_hidden(handle, target_hidden, target_norm, draft_tokens, B, K,
+                                 accepted_len, next_token, stream), "mtp_verify_hidden")
 
 
 def mtp_kv_rollback(handle: int, kv: mtp_kv, accepted_len: int, B: int, K: int,

@@ -92,7 +92,10 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
         const int c = 4 * (tid + j * kRedThreads);
         v[j] = float4{0.f, 0.f, 0.f, 0.f};
         if (c < n) {
-          if constexpr (MODE == PREP_EH) {
+          if constexpr (MODE == PREP_NORM) {
+            v[j] = p.h16 ? load4_bf16(p.h16 + (long)b * n + c)
+                         : *reinterpret_cast<const float4*>(p.h + (long)b * n + c);
+          } else if constexpr (MODE == PREP_EH) {
             v[j] = q == 0 ? *reinterpret_cast<const float4*>(p.h + (long)b * n + c)
                           : load4_bf16(p.embed + (long)t * n + c);
           } else {
@@ -125,15 +128,17 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
 
 hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s) {
   if (B < 1 || p.n < 4 || p.n % 4 != 0 || p.ldq % 4 != 0) return hipErrorInvalidValue;
-  if ((mode != RED_QKV && (!p.xq || !p.xq_lo)) || (mode != RED_SWIGLU && mode != PREP_EH && !p.out))
+  if ((mode != RED_QKV && (!p.xq || !p.xq_lo)) ||
+      (mode != RED_SWIGLU && mode != PREP_EH && mode != PREP_NORM && !p.out))
     return hipErrorInvalidValue;
-  const bool norm = mode == RED_EH || mode == RED_RESID || mode == PREP_EH;
+  const bool norm = mode == RED_EH || mode == RED_RESID || mode == PREP_EH || mode == PREP_NORM;
   if (norm && (p.n > red_max_cols() || !p.gain || p.ldq < (mode == PREP_EH ? 2 : 1) * p.n))
     return hipErrorInvalidValue;
   if (mode == PREP_EH && (!p.gain2 || !p.h || !p.embed || !p.tok || !p.err))
     return hipErrorInvalidValue;
   if (mode == RED_RESID && !p.res) return hipErrorInvalidValue;
-  if (mode != PREP_EH &&
+  if (mode == PREP_NORM && !p.h && !p.h16) return hipErrorInvalidValue;
+  if (mode != PREP_EH && mode != PREP_NORM &&
       (!p.part || p.nsplit < 1 || p.nsplit > kRedMaxSplit || p.bp < B || p.n_part % 4 != 0))
     return hipErrorInvalidValue;
   const dim3 g(B), t(kRedThreads);
@@ -143,8 +148,47 @@ hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s) {
     case RED_RESID: hipLaunchKernelGGL(red_kernel<RED_RESID>, g, t, 0, s, p); break;
     case RED_SWIGLU: hipLaunchKernelGGL(red_kernel<RED_SWIGLU>, g, t, 0, s, p); break;
     case PREP_EH: hipLaunchKernelGGL(red_kernel<PREP_EH>, g, t, 0, s, p); break;
+    case PREP_NORM: hipLaunchKernelGGL(red_kernel<PREP_NORM>, g, t, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+__global__ void widen_kernel(const uint16_t* src16, const float* src32, float* dst, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    dst[i] = src16 ? bf16_to_f32(src16[i]) : src32[i];
+}
+
+hipError_t launch_widen(int dtype, const void* src, float* dst, long n, hipStream_t s) {
+  if (!src || !dst || n < 0) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(widen_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     dtype == 1 ? static_cast<const uint16_t*>(src) : nullptr,
+                     dtype == 1 ? nullptr : static_cast<const float*>(src), dst, n);
+  return hipGetLastError();
+}
+
+// One lane per sequence: accept drafts while they equal the target's tokens; the first
+// mismatch (or row K) gives the next token (OpenVINO GenAI, Speculative Decoding,
+// Overview).
+__global__ void accept_kernel(const int* tokens, const int* draft, int B, int K, int* accepted,
+                              int* next) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int a = 0;
+  while (a < K && draft[(long)b * K + a] == tokens[(long)b * (K + 1) + a]) ++a;
+  accepted[b] = a;
+  next[b] = tokens[(long)b * (K + 1) + a];
+}
+
+hipError_t launch_accept(const int* tokens, const int* draft, int B, int K, int* accepted,
+                         int* next, hipStream_t s) {
+  if (!tokens || (K > 0 && !draft) || !accepted || !next || B < 1 || K < 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accept_kernel, dim3((B + 255) / 256), dim3(256), 0, s, tokens, draft, B, K,
+                     accepted, next);
   return hipGetLastError();
 }
 

@@ -154,7 +154,9 @@ hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s);
 //   RED_SWIGLU: xq = split(silu(sum(part[gate rows])) * sum(part[up rows]))  (n = nrows/2)
 //   PREP_EH:  xq = [split(RMSNorm(h) * g_h), split(RMSNorm(embed[tok]) * g_e)]
 // where split(v) writes the bf16 planes hi = bf16(v), lo = bf16(v - hi).
-enum RedMode : int { RED_EH = 0, RED_QKV = 1, RED_RESID = 2, RED_SWIGLU = 3, PREP_EH = 4 };
+//   PREP_NORM: xq = split(RMSNorm(h) * gain), h read from h16 (bf16) or h (fp32)
+enum RedMode : int { RED_EH = 0, RED_QKV = 1, RED_RESID = 2, RED_SWIGLU = 3, PREP_EH = 4,
+                     PREP_NORM = 5 };
 struct RedParams {
   const float* part;  // [nsplit][bp][n_part]
   int nsplit, bp, n_part;
@@ -169,7 +171,8 @@ struct RedParams {
   uint16_t* xq;       // bf16 planes [B, ldq]: hi = bf16(v) in xq, lo = bf16(v - hi) in xq_lo
   uint16_t* xq_lo;
   int ldq;
-  const float* h;     // PREP_EH hidden [B, n] fp32
+  const float* h;     // PREP_EH / PREP_NORM hidden [B, n] fp32
+  const uint16_t* h16;  // PREP_NORM hidden [B, n] bf16 (used instead of h when set)
   const uint16_t* embed;
   const int* tok;
   int tok_stride;
@@ -192,5 +195,12 @@ hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s);
 
 hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
                            hipStream_t s);
+
+// dst[i] = src[i] widened to fp32 (src in weight dtype), i < n.
+hipError_t launch_widen(int dtype, const void* src, float* dst, long n, hipStream_t s);
+// Prefix scan of verification from per-row target tokens: tokens[b * (K+1) + j] is the
+// target's token after input j; accepted[b] / next[b] as launch_verify writes them.
+hipError_t launch_accept(const int* tokens, const int* draft, int B, int K, int* accepted,
+                         int* next, hipStream_t s);
 
 }  // namespace mtp

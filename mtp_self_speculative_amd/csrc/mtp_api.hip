@@ -30,12 +30,16 @@ struct Layout {
   size_t dummy;        // zeroed target of never-consumed tail prefetches
   size_t xq, xq_lo, mm_part;  // batched path: bf16 operand planes, K-split partial sums
   int ldq;
+  // verification from hidden states: one group of up to kVhGroup rows at a time
+  size_t vh_x, vh_q, vh_q_lo, vh_keys, vh_cnt, vh_tok;
+  int vh_rows, vh_ld;
   size_t total;
 };
 
 // Batched (MFMA) path: bf16 weights, 3..64 sequences, rows short enough for the
 // row-wise norm kernels.
 constexpr int kMmMinBatch = 3;
+constexpr int kVhGroup = 64;  // rows of target hidden states per lm_head pass
 constexpr int kMmMaxBatch = 64;
 bool mm_eligible(const mtp_config& c) {
   return c.dtype == MTP_BF16 && c.hidden <= red_max_cols();
@@ -100,6 +104,21 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
         if (e > part) part = e;
       }
     L.mm_part = take(part * 4);
+  }
+  // verification from the target's hidden states
+  {
+    const long rows_all = (long)max_batch * (max_k + 1);
+    L.vh_rows = (int)(rows_all < kVhGroup ? rows_all : kVhGroup);
+    L.vh_ld = (c.hidden + 7) / 8 * 8;
+    L.vh_x = take((size_t)L.vh_rows * c.hidden * 4);
+    L.vh_q = L.vh_q_lo = off;
+    if (mm_eligible(c)) {
+      L.vh_q = take((size_t)mm_batch_pad(L.vh_rows) * L.vh_ld * 2);
+      L.vh_q_lo = take((size_t)mm_batch_pad(L.vh_rows) * L.vh_ld * 2);
+    }
+    L.vh_keys = take((size_t)L.vh_rows * 8);
+    L.vh_cnt = take(4);
+    L.vh_tok = take((size_t)rows_all * 4);
   }
   L.total = off;
   return L;
@@ -640,6 +659,69 @@ mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed(h, KC_VERIFY, s, [&] { return launch_verify(p, B, s); }) == hipSuccess ? MTP_OK
                                                                                       : MTP_ERR_HIP;
+}
+
+mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,
+                             const int32_t* draft_tokens, int32_t B, int32_t K,
+                             int32_t* accepted_len, int32_t* next_token, void* stream) {
+  if (!h || !target_hidden || !target_norm || !accepted_len || !next_token)
+    return MTP_ERR_INVALID_ARG;
+  if (!aligned(target_hidden, 16) || !aligned(target_norm, 16)) return MTP_ERR_INVALID_ARG;
+  if (K < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  if (K > 0 && !draft_tokens) return MTP_ERR_INVALID_ARG;
+  const mtp_config& c = h->cfg;
+  const Layout& L = h->L;
+  const int H = c.hidden, V = c.vocab;
+  const int R = B * (K + 1);
+  const size_t esz = c.dtype == MTP_BF16 ? 2 : 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* tok = h->at<int>(L.vh_tok);
+  auto run = [&]() -> hipError_t {
+    hipError_t e = hipSuccess;
+    for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.vh_rows) {
+      const int rows = R - r0 < L.vh_rows ? R - r0 : L.vh_rows;
+      const char* src = static_cast<const char*>(target_hidden) + (size_t)r0 * H * esz;
+      if (mm_eligible(c) && rows >= kMmMinBatch) {
+        RedParams r{};
+        r.n = H; r.gain = static_cast<const uint16_t*>(target_norm); r.eps = c.rms_eps;
+        r.xq = h->at<uint16_t>(L.vh_q); r.xq_lo = h->at<uint16_t>(L.vh_q_lo); r.ldq = L.vh_ld;
+        r.h16 = reinterpret_cast<const uint16_t*>(src);
+        e = launch_red(PREP_NORM, r, rows, s);
+        if (e != hipSuccess) break;
+        MmParams m{};
+        m.w0 = m.w1 = m.w2 = h->w.lm_head;
+        m.seg1 = m.seg2 = V;
+        m.nrows = V; m.ncols = H;
+        m.x = h->at<uint16_t>(L.vh_q); m.x_lo = h->at<uint16_t>(L.vh_q_lo); m.ldx = L.vh_ld;
+        m.B = rows; m.nsplit = 1;
+        m.keys = h->at<unsigned long long>(L.vh_keys);
+        m.counter = h->at<unsigned>(L.vh_cnt);
+        m.tok_out = tok + r0; m.tok_out_stride = 1;
+        m.dummy = h->ws + L.dummy;
+        e = launch_mm(EPI_ARGMAX, m, mm_grid(V, H, rows, 1, h->num_cu), s);
+      } else {
+        const float* x = reinterpret_cast<const float*>(src);
+        if (c.dtype == MTP_BF16) {
+          e = launch_widen(c.dtype, src, h->at<float>(L.vh_x), (long)rows * H, s);
+          x = h->at<float>(L.vh_x);
+          if (e != hipSuccess) break;
+        }
+        GemvParams g{};
+        g.w0 = g.w1 = g.w2 = h->w.lm_head;
+        g.nrows = g.seg1 = g.seg2 = V;
+        g.ncols = H; g.B = rows;
+        g.x = x; g.ldx = H; g.gain = target_norm; g.eps = c.rms_eps;
+        g.keys = h->at<unsigned long long>(L.vh_keys);
+        g.counter = h->at<unsigned>(L.vh_cnt);
+        g.tok_out = tok + r0; g.tok_out_stride = 1;
+        e = run_gemv(h, PRO_RMS, EPI_ARGMAX, g, s);
+      }
+    }
+    if (e == hipSuccess) e = launch_accept(tok, draft_tokens, B, K, accepted_len, next_token, s);
+    return e;
+  };
+  return timed(h, KC_VERIFY, s, run) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
 mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,

@@ -112,6 +112,23 @@ class MtpHead:
                      accepted.data_ptr(), next_token.data_ptr(), _stream(stream))
         return accepted, next_token
 
+    def verify_hidden(self, target_hidden: torch.Tensor, target_norm: torch.Tensor,
+                      draft_tokens: torch.Tensor | None, accepted: torch.Tensor | None = None,
+                      next_token: torch.Tensor | None = None, stream=None):
+        """Greedy verification from the target's pre-norm hidden states [B, K+1, H]
+        through its final-norm gain [H] and the shared lm_head."""
+        B, K1, _ = target_hidden.shape
+        dev = target_hidden.device
+        if accepted is None:
+            accepted = torch.empty(B, dtype=torch.int32, device=dev)
+        if next_token is None:
+            next_token = torch.empty(B, dtype=torch.int32, device=dev)
+        th = target_hidden.contiguous()
+        L.mtp_verify_hidden(self.handle, th.data_ptr(), target_norm.data_ptr(),
+                            _ptr(draft_tokens), B, K1 - 1, accepted.data_ptr(),
+                            next_token.data_ptr(), _stream(stream))
+        return accepted, next_token
+
     def rollback(self, cache: MtpCache, accepted: torch.Tensor, K: int, stream=None) -> None:
         L.mtp_kv_rollback(self.handle, cache.kv, accepted.data_ptr(), accepted.shape[0], K,
                           _stream(stream))

@@ -21,6 +21,9 @@ chunk), so the values depend neither on the thread count nor on the machine.
     stream 10 small synthetic target decoder: projections, N(0, 0.02)
     stream 11 small synthetic target decoder: norm gains, N(1, 0.02)
     stream 12 prompts for the synthetic target
+    stream 13 target hidden states for verification from hidden states, N(0, 1)
+              (sub = iteration)
+    stream 14 the target's final-norm gain, N(1, 0.02)
 
 bf16 configurations draw in fp32 and round to bf16 (round to nearest even);
 bf16 arrays are carried as their uint16 bit patterns.
@@ -154,6 +157,17 @@ def hidden_states(cfg: Config, it: int = 0) -> np.ndarray:
     """Verifier hidden state handed to the draft at iteration `it`, [B, H] storage dtype."""
     return normal(cfg.cid, 3, it, cfg.batch * cfg.hidden, 0.0, 1.0, cfg.dtype).reshape(
         cfg.batch, cfg.hidden)
+
+
+def target_hidden(cfg: Config, K: int, it: int = 0) -> np.ndarray:
+    """The target's pre-norm hidden states at the K+1 verified inputs, [B, K+1, H]."""
+    return normal(cfg.cid, 13, it, cfg.batch * (K + 1) * cfg.hidden, 0.0, 1.0,
+                  cfg.dtype).reshape(cfg.batch, K + 1, cfg.hidden)
+
+
+def target_norm(cfg: Config) -> np.ndarray:
+    """The target's final-norm gain, [H]."""
+    return normal(cfg.cid, 14, 0, cfg.hidden, 1.0, 0.02, cfg.dtype)
 
 
 def last_tokens(cfg: Config) -> np.ndarray:
