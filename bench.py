@@ -254,6 +254,25 @@ def main() -> int:
         kernel_us = {k: round(ms * 1e3 / n, 2) for k, (ms, n) in bprof.items() if n}
         log(f"per-kernel us/launch: {kernel_us}")
 
+    # Verification from the target's hidden states (the alternative to mtp_verify that
+    # never materialises target logits): one call per recorded iteration's drafts.
+    th = up(S.target_hidden(cfg, K))
+    tn = up(S.target_norm(cfg))
+    vacc = torch.empty(B, dtype=torch.int32, device=dev)
+    vnxt = torch.empty(B, dtype=torch.int32, device=dev)
+    for it in range(3):
+        head.verify_hidden(th, tn, drafts[it], vacc, vnxt)
+    torch.cuda.synchronize()
+    t0v = time.perf_counter()
+    for it in range(args.steps):
+        head.verify_hidden(th, tn, drafts[args.warmup + it], vacc, vnxt)
+    torch.cuda.synchronize()
+    vh_us = (time.perf_counter() - t0v) / args.steps * 1e6
+    vh_passes = -(-(B * (K + 1)) // 64)
+    vh_bytes = vh_passes * cfg.vocab * cfg.hidden * (2 if cfg.dtype == "bf16" else 4) + \
+        B * (K + 1) * cfg.hidden * (2 if cfg.dtype == "bf16" else 4)
+    log(f"verify from hidden states: {vh_us:.2f} us per call")
+
     acc_np = acc[args.warmup:].cpu().numpy().astype(np.int64)
     tokens = int((acc_np + 1).sum())
     rows = int((acc_np + 1).sum())
@@ -287,6 +306,9 @@ def main() -> int:
                      "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n,
                      "algorithmic_bytes_per_launch": int(ab["lm_head"])},
     }
+    out["verify_from_hidden"] = {"us_per_call": round(vh_us, 2), "rows": B * (K + 1),
+                                 "algorithmic_bytes": int(vh_bytes),
+                                 "hbm_frac": round(vh_bytes / (vh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if kernel_us:
         out["kernel_us_per_launch"] = kernel_us
     head.close()

@@ -208,6 +208,19 @@ void mtp_destroy(mtp_handle* h);
 const char* mtp_status_string(mtp_status s);
 
 /*
+ * Speculative length for the next iteration from the last one's accepted lengths (OpenVINO
+ * GenAI "Speculative Decoding", Backend Differences: the stateful backend adapts
+ * num_assistant_tokens per step from recent acceptance and backs off when it is low).
+ * A sequence that accepted all K drafts asks for K + 1, one that accepted a < K asks for
+ * a + 1; *k_next is the largest request clipped to [k_min, k_max]. Host function:
+ * accepted_len is host memory [B] (values 0..K). Errors: MTP_ERR_INVALID_ARG for NULL
+ * pointers or an accepted length outside 0..K, MTP_ERR_SHAPE for B < 1, K < 0,
+ * k_min < 0, k_max < k_min or k_max > 100. Nothing is written on error.
+ */
+mtp_status mtp_adapt_k(const int32_t* accepted_len, int32_t B, int32_t K, int32_t k_min,
+                       int32_t k_max, int32_t* k_next);
+
+/*
  * Training-loss weights of the K MTP steps, speculators user guide "MTP (Multi-Token
  * Prediction)", Step Weight Formula: out[k-1] = beta^(k-1) / sum_{j=1..K} beta^(j-1)
  * for k = 1..K (beta = 0.6, K = 3 gives 0.51, 0.31, 0.18). A host function: `out` is

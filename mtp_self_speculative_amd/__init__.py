@@ -4,7 +4,7 @@ The work happens in ``libmtp.so`` (hand-written gfx950 HIP kernels behind the C 
 of ``include/mtp.h``); ``_lib`` binds that ABI with ctypes and ``head`` wraps it for
 PyTorch device tensors and streams.
 """
-from ._lib import (LIB_PATH, MtpError, mtp_config, mtp_create, mtp_destroy, mtp_draft,  # noqa: F401
+from ._lib import (LIB_PATH, MtpError, mtp_adapt_k, mtp_config, mtp_create, mtp_destroy, mtp_draft,  # noqa: F401
                    mtp_draft_debug, mtp_get_error, mtp_kv, mtp_kv_rollback, mtp_status_string,
                    mtp_step_weights, mtp_verify, mtp_verify_hidden, mtp_weights,
                    mtp_workspace_size)

@@ -72,6 +72,7 @@ _SIGS = {
     "mtp_destroy": (None, [_P]),
     "mtp_status_string": (ctypes.c_char_p, [_I]),
     "mtp_step_weights": (_I, [ctypes.c_float, _I, ctypes.POINTER(ctypes.c_float)]),
+    "mtp_adapt_k": (_I, [ctypes.POINTER(_I), _I, _I, _I, _I, ctypes.POINTER(_I)]),
 }
 
 
@@ -208,6 +209,16 @@ def mtp_destroy(handle: int) -> None:
 
 def mtp_status_string(st: int) -> str:
     return status_string(st)
+
+
+def mtp_adapt_k(accepted_len, K: int, k_min: int, k_max: int) -> int:
+    """Next speculative length from the accepted lengths (host sequence of ints)."""
+    a = [int(x) for x in accepted_len]
+    arr = (_I * max(len(a), 1))(*a)
+    out = _I(0)
+    _check(LIB.mtp_adapt_k(arr, len(a), int(K), int(k_min), int(k_max), ctypes.byref(out)),
+           "mtp_adapt_k")
+    return int(out.value)
 
 
 def mtp_step_weights(beta: float, K: int) -> list:

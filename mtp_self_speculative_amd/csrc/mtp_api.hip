@@ -248,6 +248,21 @@ mtp_status mtp_step_weights(float beta, int32_t K, float* out) {
   return MTP_OK;
 }
 
+mtp_status mtp_adapt_k(const int32_t* accepted_len, int32_t B, int32_t K, int32_t k_min,
+                       int32_t k_max, int32_t* k_next) {
+  if (!accepted_len || !k_next) return MTP_ERR_INVALID_ARG;
+  if (B < 1 || K < 0 || k_min < 0 || k_max < k_min || k_max > kMaxK) return MTP_ERR_SHAPE;
+  int want = 0;
+  for (int b = 0; b < B; ++b) {
+    const int a = accepted_len[b];
+    if (a < 0 || a > K) return MTP_ERR_INVALID_ARG;
+    const int w = a == K ? K + 1 : a + 1;
+    want = w > want ? w : want;
+  }
+  *k_next = want < k_min ? k_min : want > k_max ? k_max : want;
+  return MTP_OK;
+}
+
 mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
                               int32_t max_capacity, size_t* bytes) {
   if (!bytes) return MTP_ERR_INVALID_ARG;

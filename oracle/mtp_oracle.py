@@ -309,6 +309,19 @@ def kv_rollback(lens: np.ndarray, pos: np.ndarray, accepted_len: np.ndarray, K: 
     return lens, pos
 
 
+def adapt_k(accepted_len, K: int, k_min: int, k_max: int) -> int:
+    """Speculative length for the next iteration.  [OVSD] Backend Differences (the
+    stateful backend adapts num_assistant_tokens per step from recent acceptance and
+    backs off when it is low); [FI] 7.3 (depth adapted to the live acceptance rate).
+
+    Reading: a sequence that accepted all K drafts asks for K + 1, one that accepted a < K
+    asks for a + 1; the batch takes the largest request, clipped to [k_min, k_max].
+    """
+    a = np.asarray(accepted_len, np.int64).reshape(-1)
+    want = np.where(a >= K, K + 1, a + 1)
+    return int(min(max(int(want.max()), k_min), k_max))
+
+
 def step_weights(beta: float, K: int) -> np.ndarray:
     """Normalised exponential-decay step weights alpha_k = beta^(k-1) / sum_j beta^(j-1).
     [SPEC] Step Weight Formula."""

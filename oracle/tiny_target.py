@@ -73,7 +73,7 @@ class TinyTarget:
 
 
 def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_fn,
-                       rollback_fn, K: int, from_hidden: bool = False):
+                       rollback_fn, K: int, from_hidden: bool = False, next_k=None):
     """Greedy speculative decoding driven by a draft head.
 
     draft_fn(hidden [H], last_token, K, committed) -> K draft tokens (the head keeps
@@ -83,6 +83,8 @@ def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_
     over the committed prefix extended by j drafts: its logits (X = V), or with
     from_hidden its hidden states before the final norm (X = H), which verify_fn turns
     into tokens through the target's final norm and the shared lm_head.
+    With next_k, the speculative length of the next iteration is next_k(a, K) (K is
+    the first iteration's length).
     Returns (emitted tokens, list of accepted lengths).
     """
     seq = [int(x) for x in prompt]
@@ -103,4 +105,6 @@ def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_
         accepted.append(a)
         seq += d[:a] + [nxt]
         h = hids[a]
+        if next_k is not None:
+            K = int(next_k(a, K))
     return seq[len(prompt):len(prompt) + n_new], accepted

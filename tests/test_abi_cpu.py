@@ -118,3 +118,20 @@ def test_step_weights_entry_point():
         assert L.LIB.mtp_step_weights(beta, K, out) == st
     assert list(out) == [7.0] * 4
     assert L.LIB.mtp_step_weights(0.6, 3, None) == 1
+
+
+def test_adapt_k_entry_point():
+    """The library's host rule against the hand-worked cases and the oracle."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "adapt_k_cases.json")))
+    for c in gold["cases"]:
+        assert L.mtp_adapt_k(c["accepted"], c["K"], c["k_min"], c["k_max"]) == c["k_next"], c
+    out = ctypes.c_int32(-7)
+    arr = (ctypes.c_int32 * 2)(1, 6)
+    assert L.LIB.mtp_adapt_k(arr, 2, 5, 1, 8, ctypes.byref(out)) == 1  # accepted > K
+    assert L.LIB.mtp_adapt_k(None, 2, 5, 1, 8, ctypes.byref(out)) == 1
+    assert L.LIB.mtp_adapt_k(arr, 0, 5, 1, 8, ctypes.byref(out)) == 2
+    assert L.LIB.mtp_adapt_k(arr, 2, 5, 4, 3, ctypes.byref(out)) == 2
+    assert L.LIB.mtp_adapt_k(arr, 2, 5, 1, 101, ctypes.byref(out)) == 2
+    assert out.value == -7

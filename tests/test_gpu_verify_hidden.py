@@ -111,3 +111,41 @@ def test_speculative_decoding_from_hidden_states_on_gpu_equals_greedy():
     assert out == tgt.greedy(prompt, 32)
     assert head.get_error() == 0
     head.close()
+
+
+def test_speculative_decoding_with_adaptive_k_on_gpu_equals_greedy():
+    """The GPU head drafts with a length that the library's adaptive rule changes every
+    iteration; verification and rollback follow; output equals plain greedy decoding."""
+    from mtp_self_speculative_amd import mtp_adapt_k
+    from oracle.tiny_target import TinyTarget, speculative_greedy
+    cfg = small(name="e2ek", cid=142, hidden=128, n_q=4, n_kv=2, head_dim=64, ffn=256, vocab=8,
+                batch=1, K=6, ctx_lo=8, ctx_hi=None, dtype="f32")
+    inp = S.make_inputs(cfg, capacity=256)
+    head, cache = make_head(cfg, inp, max_k=6)
+    tgt = TinyTarget(cfg, S.target_weights(cfg, 2), inp.weights["embed"], inp.weights["lm_head"])
+    prompt = S.prompt_tokens(cfg, 6)
+    cache.pos.fill_(len(prompt) - 1)
+    st = {"ks": []}
+
+    def draft_fn(h, last, K, _seq):
+        st["K"] = K
+        st["ks"].append(K)
+        out = head.draft(torch.from_numpy(np.asarray(h, np.float32)[None]).cuda(),
+                         torch.tensor([last], dtype=torch.int32, device="cuda"), cache, K)
+        st["d"] = out
+        return out[0].cpu().numpy()
+
+    def verify_fn(rows, d):
+        a, n = head.verify(torch.from_numpy(rows[None].astype(np.float32)).cuda(), st["d"])
+        st["a"] = a
+        return int(a[0]), int(n[0])
+
+    def rollback_fn(a):
+        head.rollback(cache, st["a"], st["K"])
+
+    out, _ = speculative_greedy(tgt, prompt, 48, draft_fn, verify_fn, rollback_fn, 2,
+                                next_k=lambda a, K: mtp_adapt_k([a], K, 1, 6))
+    assert out == tgt.greedy(prompt, 48)
+    assert len(set(st["ks"])) > 1
+    assert head.get_error() == 0
+    head.close()

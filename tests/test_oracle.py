@@ -432,6 +432,48 @@ def test_speculative_from_hidden_states_equals_greedy(vocab, cache_len):
     assert all(0 <= a <= 3 for a in acc)
 
 
+def test_adapt_k_golden_cases():
+    """The adaptive-length rule against hand-worked cases (cited in the fixture)."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "adapt_k_cases.json")))
+    for c in gold["cases"]:
+        assert O.adapt_k(c["accepted"], c["K"], c["k_min"], c["k_max"]) == c["k_next"], c
+
+
+def test_speculative_with_adaptive_k_equals_greedy():
+    """Changing K every iteration (draft, verify and rollback all follow it) keeps greedy
+    speculative decoding exactly equal to plain greedy decoding, and K moves."""
+    cfg = small_cfg(cid=80, batch=1, vocab=8, ctx_lo=4, K=3)
+    inp = _inputs(cfg, 512)
+    W = O.OracleWeights(cfg, inp.weights)
+    tgt = TinyTarget(cfg, S.target_weights(cfg, 2), inp.weights["embed"], inp.weights["lm_head"])
+    prompt = S.prompt_tokens(cfg, 6)
+    ref = tgt.greedy(prompt, 60)
+    st = {"kc": inp.k_cache.copy(), "vc": inp.v_cache.copy(),
+          "len": np.array([4]), "pos": np.array([len(prompt) - 1]), "K": 2, "ks": []}
+
+    def draft_fn(h, last, K, _seq):
+        st["K"] = K
+        st["ks"].append(K)
+        r = O.draft(cfg, W, np.asarray(h, np.float32)[None], np.array([last]), st["kc"], st["vc"],
+                    st["len"], st["pos"], K)
+        st["len"], st["pos"] = r["lens"], r["pos"]
+        return r["draft_tokens"][0]
+
+    def rollback_fn(a):
+        st["len"], st["pos"] = O.kv_rollback(st["len"], st["pos"], np.array([a]), st["K"])
+
+    def verify_fn(rows, d):
+        a, n = O.verify(rows[None], np.asarray(d)[None])
+        return a[0], n[0]
+
+    out, acc = speculative_greedy(tgt, prompt, 60, draft_fn, verify_fn, rollback_fn, 2,
+                                  next_k=lambda a, K: O.adapt_k([a], K, 1, 6))
+    assert out == ref
+    assert len(set(st["ks"])) > 1
+
+
 def test_speculative_equals_greedy_with_scripted_drafts():
     """A drafter that proposes the target's own greedy continuation with one planted
     error at index i (or none) must be accepted for exactly i tokens, and the output
