@@ -309,6 +309,54 @@ def kv_rollback(lens: np.ndarray, pos: np.ndarray, accepted_len: np.ndarray, K: 
     return lens, pos
 
 
+def kv_catchup(cfg, W: OracleWeights, target_hidden: np.ndarray, draft_tokens: np.ndarray,
+               accepted_len: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+               lens: np.ndarray, pos: np.ndarray, K: int):
+    """Commit the MTP cache exactly after verification.  [OVMTP] Stateful execution
+    (the MTP cache holds the MTP layer's K/V of the committed positions, built from the
+    verifier's hidden states); [SPEC] Architecture (the layer's input at a position is
+    the projection of the normalised hidden state and next-token embedding).
+
+    On entry lens/pos are the values after a K-step draft. Draft step k wrote slot
+    lens-K+k-1 from (h^(k-1), tok_{k-1}); for k >= 2 that hidden state was the head's own,
+    and with a = K the pair (h_{t+K}, d_K) was never processed. Here every committed
+    pair j = 1..a, (target_hidden[b, j-1], d_j) at position pos-K+j, is run through the
+    layer's input side (eh_proj, attention norm, K/V projections, RoPE) and written to
+    slot lens-K+j in the cache dtype. target_hidden [B, K+1, H] (storage dtype) are the
+    target's pre-norm hidden states at the verified inputs [last_token, d_1 .. d_K].
+    Returns lens, pos advanced to the committed prefix: lens-K+a+1, pos-K+a+1.
+    """
+    dt = W.dt
+    w = W.w
+    nkv, d = cfg.n_kv, cfg.head_dim
+    eps = cfg.rms_eps
+    th = as_float(target_hidden, cfg.dtype, dt)
+    dtok = np.asarray(draft_tokens, np.int64).reshape(th.shape[0], -1)
+    acc = np.asarray(accepted_len, np.int64)
+    lens = np.asarray(lens, np.int64)
+    pos = np.asarray(pos, np.int64)
+    for b in range(th.shape[0]):
+        for j in range(1, int(acc[b]) + 1):
+            h = th[b, j - 1][None]
+            e = W.embed_rows(dtok[b, j - 1:j])
+            x = np.concatenate([rmsnorm(h, w["g_h"], eps), rmsnorm(e, w["g_e"], eps)],
+                               axis=1) @ w["w_eh"].T
+            a = rmsnorm(x, w["g_attn"], eps)
+            kn = (a @ w["w_k"].T).reshape(nkv, d)
+            vn = (a @ w["w_v"].T).reshape(nkv, d)
+            p = int(pos[b]) - K + j
+            slot = int(lens[b]) - K + j
+            cos, sin = rope_tables(p, d, cfg.rope_theta, dt)
+            kb = rope(kn, cos, sin)
+            if cfg.dtype == "bf16":
+                k_cache[b, :, slot, :] = _store_bf16(kb)
+                v_cache[b, :, slot, :] = _store_bf16(vn)
+            else:
+                k_cache[b, :, slot, :] = kb.astype(np.float32)
+                v_cache[b, :, slot, :] = vn.astype(np.float32)
+    return lens - K + acc + 1, pos - K + acc + 1
+
+
 def adapt_k(accepted_len, K: int, k_min: int, k_max: int) -> int:
     """Speculative length for the next iteration.  [OVSD] Backend Differences (the
     stateful backend adapts num_assistant_tokens per step from recent acceptance and

@@ -474,6 +474,82 @@ def test_speculative_with_adaptive_k_equals_greedy():
     assert len(set(st["ks"])) > 1
 
 
+def _catchup_run(cfg, inp, W, tgt, prompt, n_new, K0, next_k, bad_at):
+    """Greedy speculative decoding with exact catch-up. The head runs every draft step
+    (writing its cache) teacher-forced on the target's own greedy continuation with one
+    planted error at index bad_at(iteration, K) (none when that is K, so all K drafts are
+    accepted). Returns the emitted tokens, accepted lengths and the head's cache state."""
+    st = {"kc": np.zeros_like(inp.k_cache), "vc": np.zeros_like(inp.v_cache),
+          "len": np.array([0]), "pos": np.array([len(prompt) - 1]), "it": 0}
+
+    def draft_fn(h, last, K, seq):
+        cont = tgt.greedy(seq, K)
+        bad = bad_at(st["it"], K)
+        st["it"] += 1
+        if bad < K:
+            cont[bad] = (cont[bad] + 1) % cfg.vocab
+        st["K"] = K
+        r = O.draft(cfg, W, np.asarray(h, np.float32)[None], np.array([last]), st["kc"], st["vc"],
+                    st["len"], st["pos"], K, force_tokens=np.array([cont]))
+        st["len"], st["pos"], st["d"] = r["lens"], r["pos"], np.array([cont])
+        return cont
+
+    def verify_fn(hid_rows, d):
+        st["hid"] = hid_rows
+        a, n, _ = O.verify_from_hidden(cfg, hid_rows[None], tgt_norm, inp.weights["lm_head"],
+                                       np.asarray(d)[None])
+        return a[0], n[0]
+
+    def commit_fn(a):
+        st["len"], st["pos"] = O.kv_catchup(cfg, W, st["hid"][None], st["d"], np.array([a]),
+                                            st["kc"], st["vc"], st["len"], st["pos"], st["K"])
+
+    tgt_norm = tgt.g_final_store
+    out, acc = speculative_greedy(tgt, prompt, n_new, draft_fn, verify_fn, commit_fn, K0,
+                                  from_hidden=True, next_k=next_k)
+    return out, acc, st
+
+
+def test_exact_catchup_cache_is_independent_of_the_speculation_schedule():
+    """With exact catch-up every committed slot holds the layer's K/V of (the verifier's
+    hidden state, the next committed token) at its position, so the cache over the
+    committed prefix depends only on the committed tokens: two different speculative
+    schedules leave identical caches, both equal to slots written one position at a time
+    by single-step drafts from the target's own hidden states, and the output is still
+    plain greedy decoding."""
+    cfg = small_cfg(cid=90, batch=1, vocab=16, ctx_lo=0, K=4)
+    inp = _inputs(cfg, 256)
+    W = O.OracleWeights(cfg, inp.weights)
+    tw = S.target_weights(cfg, 2)
+    tgt = TinyTarget(cfg, tw, inp.weights["embed"], inp.weights["lm_head"])
+    tgt.g_final_store = tw["g_final"]
+    prompt = S.prompt_tokens(cfg, 6)
+    n_new = 40
+    ref = tgt.greedy(prompt, n_new)
+    out1, acc1, s1 = _catchup_run(cfg, inp, W, tgt, prompt, n_new, 3, None,
+                                  lambda it, K: it % (K + 1))
+    out2, acc2, s2 = _catchup_run(cfg, inp, W, tgt, prompt, n_new, 2,
+                                  lambda a, K: O.adapt_k([a], K, 1, 5),
+                                  lambda it, K: K if it % 3 else it % K)
+    assert out1 == ref and out2 == ref
+    assert 3 in acc1 and 0 in acc1 and len(set(acc2)) > 1  # includes the a = K gap
+    n = min(int(s1["len"][0]), int(s2["len"][0]))
+    assert n > 20
+    assert np.array_equal(s1["kc"][:, :, :n], s2["kc"][:, :, :n])
+    assert np.array_equal(s1["vc"][:, :, :n], s2["vc"][:, :, :n])
+    # reference: slot s is written by a one-step draft at position len(prompt)-1+s from
+    # the target's hidden state there and the token after it
+    seq = list(prompt) + ref
+    hid, _ = tgt.forward(seq)
+    kc, vc = np.zeros_like(inp.k_cache), np.zeros_like(inp.v_cache)
+    for slot in range(n):
+        p = len(prompt) - 1 + slot
+        O.draft(cfg, W, hid[p][None], np.array([seq[p + 1]]), kc, vc, np.array([slot]),
+                np.array([p]), 1)
+    assert np.allclose(s1["kc"][:, :, :n], kc[:, :, :n], rtol=0, atol=1e-5)
+    assert np.allclose(s1["vc"][:, :, :n], vc[:, :, :n], rtol=0, atol=1e-5)
+
+
 def test_speculative_equals_greedy_with_scripted_drafts():
     """A drafter that proposes the target's own greedy continuation with one planted
     error at index i (or none) must be accepted for exactly i tokens, and the output
