@@ -182,6 +182,28 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
                              const int32_t* draft_tokens, int32_t B, int32_t K,
                              int32_t* accepted_len, int32_t* next_token, void* stream);
 
+/*
+ * Exact MTP-cache catch-up, used instead of mtp_kv_rollback after verification (devnotes
+ * "How OpenVINO MTP Speculative Decoding Works Internally", Stateful execution; speculators
+ * "MTP (Multi-Token Prediction)", Architecture). Draft step k >= 2 wrote its slot from the
+ * head's own hidden state, and with all K drafts accepted the pair (h_{t+K}, d_K) was never
+ * processed. For every sequence b and committed pair j = 1..a_b this runs
+ * (target_hidden[b, j-1], d_j) through the layer's input side (embedding gather, separate
+ * RMSNorms, eh_proj, attention RMSNorm, K/V projections, RoPE at position pos - K + j) and
+ * writes slot len - K + j in the cache dtype; then len and pos advance to the committed
+ * prefix: len += a + 1 - K, pos += a + 1 - K (values on entry: after the K-step draft).
+ *   target_hidden [B, K+1, hidden] config dtype, 16-byte aligned: the target's last-layer
+ *                 outputs before its final norm at inputs [last_token, d_1 .. d_K]
+ *   draft_tokens [B, K], accepted_len [B] device int32 (accepted_len from mtp_verify /
+ *                 mtp_verify_hidden).
+ * Requires 1 <= K <= max_k. Device conditions: a slot outside the capacity sets
+ * MTP_DEVERR_CAPACITY (the slot is skipped); an accepted length outside 0..K sets
+ * MTP_DEVERR_ACCEPT and is clamped. Other errors: as mtp_kv_rollback.
+ */
+mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
+                          const int32_t* draft_tokens, const int32_t* accepted_len, int32_t B,
+                          int32_t K, void* stream);
+
 /* Synchronise `stream`, read and clear the device error word. *bits receives the
  * MTP_DEVERR_* bits (may be NULL). Returns MTP_ERR_DEVICE when any bit was set. */
 mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits);

@@ -65,6 +65,7 @@ _SIGS = {
     "mtp_draft_debug": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, _P, _P, _P, _P, _P]),
     "mtp_verify": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
     "mtp_verify_hidden": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "mtp_kv_catchup": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _P, _P, _I, _I, _P]),
     "mtp_kv_rollback": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P]),
     "mtp_get_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "mtp_set_profiling": (_I, [_P, ctypes.c_uint32]),
@@ -168,6 +169,12 @@ def mtp_verify_hidden(handle: int, target_hidden: int, target_norm: int,
                       next_token: int, stream: int | None) -> None:
     _check(LIB.mtp_verify_hidden(handle, target_hidden, target_norm, draft_tokens, B, K,
                                  accepted_len, next_token, stream), "mtp_verify_hidden")
+
+
+def mtp_kv_catchup(handle: int, kv: mtp_kv, target_hidden: int, draft_tokens: int,
+                   accepted_len: int, B: int, K: int, stream: int | None) -> None:
+    _check(LIB.mtp_kv_catchup(handle, ctypes.byref(kv), target_hidden, draft_tokens,
+                              accepted_len, B, K, stream), "mtp_kv_catchup")
 
 
 def mtp_kv_rollback(handle: int, kv: mtp_kv, accepted_len: int, B: int, K: int,

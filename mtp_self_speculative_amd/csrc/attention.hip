@@ -415,10 +415,7 @@ __global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e < K * B * half) {
     const int i = e % half, kb = e / half, b = kb % B, k = kb / B;
-    const double inv = pow((double)theta, -2.0 * (double)i / (double)d);
-    const double ang = (double)(pos[b] + k) * inv;
-    tab[(long)kb * d + i] = (float)cos(ang);
-    tab[(long)kb * d + half + i] = (float)sin(ang);
+    rope_cs(pos[b] + k, i, d, theta, tab[(long)kb * d + i], tab[(long)kb * d + half + i]);
   }
   if (e < B * H) hf[e] = CT::get(static_cast<const typename CT::T*>(hidden), e);
 }

@@ -192,4 +192,84 @@ hipError_t launch_accept(const int* tokens, const int* draft, int B, int K, int*
   return hipGetLastError();
 }
 
+__global__ void gather_rows_kernel(const uint16_t* src16, const float* src32, float* dst, int r0,
+                                   int rows, int K, int H) {
+  const int i = blockIdx.y;
+  const int r = r0 + i;
+  const long srow = (long)(r / K) * (K + 1) + r % K;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < H; c += gridDim.x * blockDim.x)
+    dst[(long)i * H + c] = src16 ? bf16_to_f32(src16[srow * H + c]) : src32[srow * H + c];
+}
+
+hipError_t launch_gather_rows(int dtype, const void* src, float* dst, int r0, int rows, int K,
+                              int H, hipStream_t s) {
+  if (!src || !dst || rows < 1 || K < 1 || H < 1 || r0 < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((H + 255) / 256, rows), dim3(256), 0, s,
+                     dtype == 1 ? static_cast<const uint16_t*>(src) : nullptr,
+                     dtype == 1 ? nullptr : static_cast<const float*>(src), dst, r0, rows, K, H);
+  return hipGetLastError();
+}
+
+// Grid (row, kv head); thread i handles the rotate-half pair (i, i + d/2).
+template <class CT>
+__global__ void catchup_write_kernel(CatchupParams p) {
+  using T = typename CT::T;
+  const int i = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int half = p.d / 2;
+  const int r = p.r0 + i;
+  const int b = r / p.K, j = r % p.K + 1;
+  int a = p.accepted[b];
+  a = a < 0 ? 0 : a > p.K ? p.K : a;
+  if (j > a || t >= half) return;
+  const int slot = p.len[b] - p.K + j;
+  const int position = p.pos[b] - p.K + j;
+  if (slot < 0 || slot >= p.capacity) {
+    if (t == 0) set_error(p.err, 2u);
+    return;
+  }
+  float c, sn;
+  rope_cs(position, t, p.d, p.theta, c, sn);
+  const float* kr = p.kvrows + (long)i * p.ld + g * p.d;
+  const float* vr = kr + p.n_kv * p.d;
+  const float k1 = kr[t], k2 = kr[t + half];
+  const long o = (((long)b * p.n_kv + g) * p.capacity + slot) * p.d;
+  CT::put(static_cast<T*>(p.kc), o + t, k1 * c - k2 * sn);
+  CT::put(static_cast<T*>(p.kc), o + t + half, k2 * c + k1 * sn);
+  CT::put(static_cast<T*>(p.vc), o + t, vr[t]);
+  CT::put(static_cast<T*>(p.vc), o + t + half, vr[t + half]);
+}
+
+hipError_t launch_catchup_write(int cdtype, const CatchupParams& p, hipStream_t s) {
+  if (!p.kvrows || !p.kc || !p.vc || !p.len || !p.pos || !p.accepted || p.K < 1 || p.rows < 1 ||
+      p.d < 2 || p.d > 1024 || p.d % 2 != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid(p.rows, p.n_kv), block((p.d / 2 + 63) / 64 * 64);
+  if (cdtype == 1)
+    hipLaunchKernelGGL(catchup_write_kernel<BF16>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(catchup_write_kernel<F32>, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+__global__ void catchup_commit_kernel(int* len, int* pos, const int* accepted, int B, int K,
+                                      unsigned* err) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int a = accepted[b];
+  if (a < 0 || a > K) {
+    set_error(err, 4u);
+    a = a < 0 ? 0 : K;
+  }
+  len[b] += a + 1 - K;
+  pos[b] += a + 1 - K;
+}
+
+hipError_t launch_catchup_commit(int* len, int* pos, const int* accepted, int B, int K,
+                                 unsigned* err, hipStream_t s) {
+  if (!len || !pos || !accepted || B < 1 || K < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(catchup_commit_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, pos,
+                     accepted, B, K, err);
+  return hipGetLastError();
+}
+
 }  // namespace mtp

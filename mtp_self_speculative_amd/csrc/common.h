@@ -191,6 +191,17 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// ---------------------------------------------------------------- RoPE
+// cos / sin of position * theta^(-2i/d) for rotate-half pair i (0 <= i < d/2), evaluated
+// in double precision from the integer position and rounded to fp32.
+__device__ __forceinline__ void rope_cs(int position, int i, int d, float theta, float& c,
+                                        float& s) {
+  const double inv = pow((double)theta, -2.0 * (double)i / (double)d);
+  const double ang = (double)position * inv;
+  c = (float)cos(ang);
+  s = (float)sin(ang);
+}
+
 // ---------------------------------------------------------------- argmax keys
 // A logit and its index packed so that a larger key means a larger value and,
 // among equal values, a smaller index. Key 0 is below every finite logit.

@@ -198,6 +198,33 @@ hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K
 
 // dst[i] = src[i] widened to fp32 (src in weight dtype), i < n.
 hipError_t launch_widen(int dtype, const void* src, float* dst, long n, hipStream_t s);
+// dst[i, :] = fp32(src[(r / K) * (K + 1) + r % K, :]) for r = r0 + i, i < rows: the
+// verified-input rows j - 1 = r % K of sequence r / K (src [B, K+1, H], weight dtype).
+hipError_t launch_gather_rows(int dtype, const void* src, float* dst, int r0, int rows, int K,
+                              int H, hipStream_t s);
+
+// Exact cache catch-up, write side. kv rows [rows, 2 * n_kv * d] fp32 hold k (before RoPE)
+// then v of candidate rows r = r0 + i, sequence b = r / K, committed pair j = r % K + 1.
+// Rows with j <= accepted[b] are rotated at position pos[b] - K + j and written to slot
+// len[b] - K + j in the cache dtype (len / pos: values after the K-step draft).
+struct CatchupParams {
+  const float* kvrows;
+  int ld;  // floats per kv row
+  void* kc;
+  void* vc;
+  int n_kv, d, capacity;
+  const int* len;
+  const int* pos;
+  const int* accepted;
+  int K, r0, rows;
+  float theta;
+  unsigned* err;
+};
+hipError_t launch_catchup_write(int cdtype, const CatchupParams& p, hipStream_t s);
+// len[b] += a + 1 - K and pos[b] += a + 1 - K (a clamped to 0..K, error bit 4 if not).
+hipError_t launch_catchup_commit(int* len, int* pos, const int* accepted, int B, int K,
+                                 unsigned* err, hipStream_t s);
+
 // Prefix scan of verification from per-row target tokens: tokens[b * (K+1) + j] is the
 // target's token after input j; accepted[b] / next[b] as launch_verify writes them.
 hipError_t launch_accept(const int* tokens, const int* draft, int B, int K, int* accepted,

@@ -33,6 +33,9 @@ struct Layout {
   // verification from hidden states: one group of up to kVhGroup rows at a time
   size_t vh_x, vh_q, vh_q_lo, vh_keys, vh_cnt, vh_tok;
   int vh_rows, vh_ld;
+  // exact cache catch-up: one group of up to kVhGroup candidate rows at a time
+  size_t cu_h, cu_x, cu_kv, cu_q, cu_q_lo, cu_part;
+  int cu_rows, cu_ld;
   size_t total;
 };
 
@@ -119,6 +122,30 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
     L.vh_keys = take((size_t)L.vh_rows * 8);
     L.vh_cnt = take(4);
     L.vh_tok = take((size_t)rows_all * 4);
+  }
+  // exact cache catch-up
+  {
+    const long rows_all = (long)max_batch * max_k;
+    L.cu_rows = (int)(rows_all < kVhGroup ? rows_all : kVhGroup);
+    L.cu_ld = (2 * c.hidden + 7) / 8 * 8;
+    const int kvd2 = 2 * c.n_kv_heads * c.head_dim;
+    const int rr = L.cu_rows > 0 ? L.cu_rows : 1;
+    L.cu_h = take((size_t)rr * c.hidden * 4);
+    L.cu_x = take((size_t)rr * c.hidden * 4);
+    L.cu_kv = take((size_t)rr * kvd2 * 4);
+    L.cu_q = L.cu_q_lo = L.cu_part = off;
+    if (mm_eligible(c) && L.cu_rows >= kMmMinBatch) {
+      L.cu_q = take((size_t)mm_batch_pad(L.cu_rows) * L.cu_ld * 2);
+      L.cu_q_lo = take((size_t)mm_batch_pad(L.cu_rows) * L.cu_ld * 2);
+      size_t part = 0;
+      for (int b = kMmMinBatch; b <= L.cu_rows; ++b) {
+        const size_t e1 = (size_t)mm_split(c.hidden, 2 * c.hidden, b) * mm_batch_pad(b) * c.hidden;
+        const size_t e2 = (size_t)mm_split(kvd2, c.hidden, b) * mm_batch_pad(b) * kvd2;
+        part = e1 > part ? e1 : part;
+        part = e2 > part ? e2 : part;
+      }
+      L.cu_part = take(part * 4);
+    }
   }
   L.total = off;
   return L;
@@ -737,6 +764,96 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
     return e;
   };
   return timed(h, KC_VERIFY, s, run) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
+}
+
+mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
+                          const int32_t* draft_tokens, const int32_t* accepted_len, int32_t B,
+                          int32_t K, void* stream) {
+  if (!h || !target_hidden || !draft_tokens || !accepted_len) return MTP_ERR_INVALID_ARG;
+  if (!aligned(target_hidden, 16)) return MTP_ERR_INVALID_ARG;
+  if (K < 1 || B < 1) return MTP_ERR_SHAPE;
+  if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  mtp_status st = check_kv(h, kv, B);
+  if (st != MTP_OK) return st;
+  const mtp_config& c = h->cfg;
+  const mtp_weights& w = h->w;
+  const Layout& L = h->L;
+  const int H = c.hidden, kvd = c.n_kv_heads * c.head_dim;
+  const int R = B * K;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned* err = h->at<unsigned>(L.err);
+  float* hrows = h->at<float>(L.cu_h);
+  float* xrows = h->at<float>(L.cu_x);
+  float* kvrows = h->at<float>(L.cu_kv);
+  auto run = [&]() -> hipError_t {
+    hipError_t e = hipSuccess;
+    for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.cu_rows) {
+      const int rows = R - r0 < L.cu_rows ? R - r0 : L.cu_rows;
+      e = launch_gather_rows(c.dtype, target_hidden, hrows, r0, rows, K, H, s);
+      if (e != hipSuccess) break;
+      if (mm_eligible(c) && rows >= kMmMinBatch) {
+        uint16_t* q = h->at<uint16_t>(L.cu_q);
+        uint16_t* qlo = h->at<uint16_t>(L.cu_q_lo);
+        float* part = h->at<float>(L.cu_part);
+        const int bp = mm_batch_pad(rows);
+        RedParams r{};
+        r.n = H; r.gain = static_cast<const uint16_t*>(w.g_h);
+        r.gain2 = static_cast<const uint16_t*>(w.g_e); r.eps = c.rms_eps;
+        r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld; r.h = hrows;
+        r.embed = static_cast<const uint16_t*>(w.embed);
+        r.tok = draft_tokens + r0; r.tok_stride = 1; r.vocab = c.vocab; r.err = err;
+        if ((e = launch_red(PREP_EH, r, rows, s)) != hipSuccess) break;
+        auto mm = [&](const void* w0, const void* w1, int seg1, int N, int Kd, int* ns) {
+          MmParams m{};
+          m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
+          m.nrows = N; m.ncols = Kd; m.x = q; m.x_lo = qlo; m.ldx = L.cu_ld; m.B = rows;
+          m.nsplit = mm_split(N, Kd, rows);
+          m.part = part;
+          m.dummy = h->ws + L.dummy;
+          *ns = m.nsplit;
+          return launch_mm(EPI_STORE, m, mm_grid(N, Kd, rows, m.nsplit, h->num_cu), s);
+        };
+        int ns = 1;
+        if ((e = mm(w.w_eh, w.w_eh, H, H, 2 * H, &ns)) != hipSuccess) break;
+        r = RedParams{};
+        r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = H; r.n = H;
+        r.out = xrows; r.gain = static_cast<const uint16_t*>(w.g_attn); r.eps = c.rms_eps;
+        r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld;
+        if ((e = launch_red(RED_EH, r, rows, s)) != hipSuccess) break;
+        if ((e = mm(w.w_k, w.w_v, kvd, 2 * kvd, H, &ns)) != hipSuccess) break;
+        r = RedParams{};
+        r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = 2 * kvd; r.n = 2 * kvd;
+        r.out = kvrows; r.ldq = L.cu_ld;
+        if ((e = launch_red(RED_QKV, r, rows, s)) != hipSuccess) break;
+      } else {
+        GemvParams g{};
+        g.w0 = g.w1 = g.w2 = w.w_eh;
+        g.nrows = g.seg1 = g.seg2 = H;
+        g.ncols = 2 * H; g.B = rows;
+        g.gain = w.g_h; g.gain2 = w.g_e; g.eps = c.rms_eps;
+        g.h = hrows; g.h_is_f32 = 1; g.ldh = H;
+        g.embed = w.embed; g.tok = draft_tokens + r0; g.tok_stride = 1; g.vocab = c.vocab;
+        g.err = err; g.out = xrows; g.ldo = H;
+        if ((e = run_gemv(h, PRO_EH, EPI_STORE, g, s)) != hipSuccess) break;
+        g = GemvParams{};
+        g.w0 = w.w_k; g.w1 = w.w_v; g.w2 = w.w_v;
+        g.seg1 = kvd; g.seg2 = 2 * kvd; g.nrows = 2 * kvd;
+        g.ncols = H; g.B = rows;
+        g.x = xrows; g.ldx = H; g.gain = w.g_attn; g.eps = c.rms_eps;
+        g.out = kvrows; g.ldo = 2 * kvd;
+        if ((e = run_gemv(h, PRO_RMS, EPI_STORE, g, s)) != hipSuccess) break;
+      }
+      CatchupParams cp{};
+      cp.kvrows = kvrows; cp.ld = 2 * kvd; cp.kc = kv->k; cp.vc = kv->v;
+      cp.n_kv = c.n_kv_heads; cp.d = c.head_dim; cp.capacity = kv->capacity;
+      cp.len = kv->len; cp.pos = kv->pos; cp.accepted = accepted_len;
+      cp.K = K; cp.r0 = r0; cp.rows = rows; cp.theta = c.rope_theta; cp.err = err;
+      e = launch_catchup_write(c.dtype, cp, s);
+    }
+    if (e == hipSuccess) e = launch_catchup_commit(kv->len, kv->pos, accepted_len, B, K, err, s);
+    return e;
+  };
+  return timed(h, KC_ROLLBACK, s, run) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
 mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,

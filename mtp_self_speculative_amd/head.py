@@ -129,6 +129,15 @@ class MtpHead:
                             next_token.data_ptr(), _stream(stream))
         return accepted, next_token
 
+    def catchup(self, cache: MtpCache, target_hidden: torch.Tensor, draft_tokens: torch.Tensor,
+                accepted: torch.Tensor, stream=None) -> None:
+        """Exact cache commit after verification (instead of rollback): rewrites the
+        committed slots from the target's hidden states [B, K+1, H]."""
+        B, K1, _ = target_hidden.shape
+        th = target_hidden.contiguous()
+        L.mtp_kv_catchup(self.handle, cache.kv, th.data_ptr(), draft_tokens.data_ptr(),
+                         accepted.data_ptr(), B, K1 - 1, _stream(stream))
+
     def rollback(self, cache: MtpCache, accepted: torch.Tensor, K: int, stream=None) -> None:
         L.mtp_kv_rollback(self.handle, cache.kv, accepted.data_ptr(), accepted.shape[0], K,
                           _stream(stream))

@@ -89,6 +89,7 @@ def test_null_arguments_rejected_before_any_device_call():
     assert L.LIB.mtp_verify(None, None, None, 1, 1, None, None, None) == 1
     assert L.LIB.mtp_verify_hidden(None, None, None, None, 1, 1, None, None, None) == 1
     assert L.LIB.mtp_kv_rollback(None, ctypes.byref(kv), None, 1, 1, None) == 1
+    assert L.LIB.mtp_kv_catchup(None, ctypes.byref(kv), None, None, None, 1, 1, None) == 1
     assert L.LIB.mtp_get_error(None, None, None) == 1
     L.LIB.mtp_destroy(None)
 
