@@ -272,6 +272,23 @@ def main() -> int:
     vh_bytes = vh_passes * cfg.vocab * cfg.hidden * (2 if cfg.dtype == "bf16" else 4) + \
         B * (K + 1) * cfg.hidden * (2 if cfg.dtype == "bf16" else 4)
     log(f"verify from hidden states: {vh_us:.2f} us per call")
+    # Exact cache catch-up (the alternative to rollback), on the recorded drafts and
+    # accepted lengths, from the state right after a K-step draft.
+    len_k, pos_k = len0 + K, pos0 + K
+    cu_ms = []
+    for it in range(args.steps + 2):
+        cache.len.copy_(len_k)
+        cache.pos.copy_(pos_k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        head.catchup(cache, th, drafts[args.warmup + it % args.steps], acc[args.warmup + it % args.steps])
+        e1.record()
+        e1.synchronize()
+        if it >= 2:
+            cu_ms.append(e0.elapsed_time(e1))
+    cu_us = float(np.median(cu_ms)) * 1e3
+    assert head.get_error() == 0
+    log(f"exact cache catch-up: {cu_us:.2f} us per call")
 
     acc_np = acc[args.warmup:].cpu().numpy().astype(np.int64)
     tokens = int((acc_np + 1).sum())
@@ -309,6 +326,7 @@ def main() -> int:
     out["verify_from_hidden"] = {"us_per_call": round(vh_us, 2), "rows": B * (K + 1),
                                  "algorithmic_bytes": int(vh_bytes),
                                  "hbm_frac": round(vh_bytes / (vh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["kv_catchup"] = {"us_per_call": round(cu_us, 2), "candidate_rows": B * K}
     if kernel_us:
         out["kernel_us_per_launch"] = kernel_us
     head.close()
