@@ -43,6 +43,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .sampling import sample_tokens
+
 
 # ----------------------------------------------------------------------------- dtypes
 
@@ -163,17 +165,19 @@ class OracleWeights:
 
 def draft(cfg, W: OracleWeights, hidden: np.ndarray, last_tokens: np.ndarray,
           k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray, pos: np.ndarray,
-          K: int, force_tokens: np.ndarray | None = None) -> dict:
+          K: int, force_tokens: np.ndarray | None = None, sample: dict | None = None) -> dict:
     """K recursive MTP draft steps for every sequence.  [SPEC] Architecture; [FI] 4.4.
 
     hidden [B, H] (storage dtype); last_tokens [B]; k_cache/v_cache [B, n_kv, S, d]
     (storage dtype, updated in place with slots len..len+K-1); lens/pos [B] (returned
     advanced by K). force_tokens [B, K]: step k+1 consumes force_tokens[:, k] instead
-    of the oracle's own draft (teacher forcing).
+    of the oracle's own draft (teacher forcing). sample = {"T", "seeds", "offset"}: each
+    token is sampled from softmax(logits / T) by ``sampling.sample_tokens`` (row k for
+    step k+1) instead of taken by argmax ([OVSD] Overview, temperature > 0).
 
     Returns draft_tokens [B, K], hidden_steps [K, B, H] (h^(k)), logits [K, B, V],
-    top1 / margin [K, B] (largest logit, and its gap to the second largest),
-    lens, pos.
+    top1 / margin [K, B] (largest logit, and its gap to the second largest; when
+    sampling, the gap between the two largest perturbed keys), lens, pos.
     """
     dt = W.dt
     w = W.w
@@ -229,6 +233,8 @@ def draft(cfg, W: OracleWeights, hidden: np.ndarray, last_tokens: np.ndarray,
         srt = np.partition(lg, V - 2, axis=1)[:, V - 2:]
         top1[k] = srt[:, 1]
         margin[k] = srt[:, 1] - srt[:, 0]
+        if sample is not None:
+            dk, margin[k] = sample_tokens(lg, sample["T"], sample["seeds"], sample["offset"], k)
         drafts[:, k] = dk
         hsteps[k] = x2
         logits_all[k] = lg

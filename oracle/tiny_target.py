@@ -108,3 +108,53 @@ def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_
         if next_k is not None:
             K = int(next_k(a, K))
     return seq[len(prompt):len(prompt) + n_new], accepted
+
+
+def softmax_rows(logits: np.ndarray, T: float) -> np.ndarray:
+    x = np.asarray(logits, np.float64) / T
+    x = np.exp(x - x.max(axis=-1, keepdims=True))
+    return x / x.sum(axis=-1, keepdims=True)
+
+
+def speculative_sample_batch(target: TinyTarget, prompt, n_new: int, first_tokens, draft_fn,
+                             verify_fn, commit_fn, K: int):
+    """B independent sampled generations from one prompt, advanced in lock step.
+
+    first_tokens [B]: the token after the prompt, sampled by the caller from the target.
+    Each iteration i: draft_fn(hidden [B, H], last [B], K, i) -> (drafts [B, K],
+    draft_logits [B, K, V]); verify_fn(target_logits [B, K+1, V], drafts, draft_logits, i)
+    -> (accepted_len [B], next_token [B]); commit_fn(accepted_len) cuts the head's cache.
+    Target rows come from full forwards over each committed prefix extended by j drafts
+    (memoised by prefix). Returns the first n_new emitted tokens per sequence [B, n_new]
+    and the accepted lengths [iterations, B].
+    """
+    memo = {}
+
+    def fwd(seq):
+        key = tuple(seq)
+        if key not in memo:
+            h, lg = target.forward(list(seq))
+            memo[key] = (h[-1], lg[-1])
+        return memo[key]
+
+    B = len(first_tokens)
+    seqs = [[int(x) for x in prompt] + [int(first_tokens[b])] for b in range(B)]
+    accepted = []
+    it = 0
+    while min(len(s) for s in seqs) - len(prompt) < n_new:
+        last = np.array([s[-1] for s in seqs])
+        # the head consumes the hidden state that produced the last committed token
+        hid = np.stack([fwd(s[:-1])[0] for s in seqs])
+        d, dl = draft_fn(hid, last, K, it)
+        d = np.asarray(d, np.int64)
+        rows = np.stack([[fwd(seqs[b] + [int(x) for x in d[b, :j]])[1] for j in range(K + 1)]
+                         for b in range(B)])
+        a, nxt = verify_fn(rows, d, dl, it)
+        a, nxt = np.asarray(a, np.int64), np.asarray(nxt, np.int64)
+        commit_fn(a)
+        accepted.append(a)
+        for b in range(B):
+            seqs[b] += [int(x) for x in d[b, :a[b]]] + [int(nxt[b])]
+        it += 1
+    out = np.array([s[len(prompt):len(prompt) + n_new] for s in seqs])
+    return out, np.array(accepted)
