@@ -54,7 +54,7 @@ typedef enum {
 typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
 
 /* Device error-word bits reported by mtp_get_error(). */
-#define MTP_DEVERR_TOKEN 1u    /* a last_tokens entry was outside [0, vocab)            */
+#define MTP_DEVERR_TOKEN 1u    /* a token id (last_tokens or a draft) was outside [0, vocab) */
 #define MTP_DEVERR_CAPACITY 2u /* len + K exceeded the cache capacity                   */
 #define MTP_DEVERR_ACCEPT 4u   /* an accepted_len entry was outside [0, K]              */
 
@@ -203,6 +203,52 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
 mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
                           const int32_t* draft_tokens, const int32_t* accepted_len, int32_t B,
                           int32_t K, void* stream);
+
+/*
+ * K recursive draft steps that SAMPLE each token at temperature T instead of taking the
+ * argmax (OpenVINO GenAI "Speculative Decoding", Overview: at temperature > 0 the drafts
+ * are verified by the standard sampling scheme, see mtp_verify_sample). Step k+1 draws
+ * d_{k+1} from softmax(z_k / T), z_k = lm_head . RMSNorm(h^(k); g_final), by the
+ * Gumbel-max rule argmax_v (z_k[v] / T + G_v) inside the fused lm_head kernel, and
+ * writes z_k (before the temperature) to draft_logits. Everything else is mtp_draft.
+ *   temperature  > 0 and finite
+ *   seeds [B]    device uint64: each sequence's random stream
+ *   offset       the iteration's counter: every (seed, offset) pair draws fresh numbers
+ *   draft_tokens [B, K] device int32 (out)
+ *   draft_logits [B, K, V] device fp32 (out): row (b, k) holds z_k of sequence b
+ * Random numbers: Philox4x64-10 (Salmon et al., SC'11) with key (seeds[b], 0) and counter
+ * (v >> 2, k, 0, offset); entry v takes word v & 3 as U = ((w >> 40) | 1) * 2^-24 and
+ * G_v = -log(-log U).
+ * Errors: as mtp_draft; a non-positive or non-finite temperature, or a null seeds /
+ * draft_logits with K > 0, returns MTP_ERR_INVALID_ARG.
+ */
+mtp_status mtp_draft_sample(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                            mtp_kv* kv, int32_t B, int32_t K, float temperature,
+                            const uint64_t* seeds, uint64_t offset, int32_t* draft_tokens,
+                            float* draft_logits, void* stream);
+
+/*
+ * Speculative-sampling verification at temperature T (OpenVINO GenAI "Speculative
+ * Decoding", Overview: the standard scheme, whose output follows the target's own
+ * distribution; the first divergent position gets the target's sample). With
+ * p_j = softmax(target_logits[b, j] / T) and q_j = softmax(draft_logits[b, j] / T):
+ *   draft d_{j+1} = draft_tokens[b, j] is accepted iff U_j < p_j(d) / q_j(d) (in the log
+ *   domain), for j = 0, 1, ... until the first rejection; a = number accepted;
+ *   next_token = a sample of max(0, p_a - q_a) (renormalised) if a < K, of p_K if a = K
+ *   (of p_a if rounding leaves no positive residual).
+ *   target_logits [B, K+1, V] device fp32 (finite), draft_logits [B, K, V] device fp32 as
+ *   written by mtp_draft_sample, draft_tokens [B, K] device int32, seeds / offset as for the
+ *   draft of the same iteration; accepted_len [B], next_token [B] device int32 (out).
+ * Random numbers (Philox4x64-10, key (seeds[b], 0)): U_j is word 0 of counter
+ * (0, j, 1, offset); the final draw uses Gumbel noise from counter (v >> 2, a, 2, offset),
+ * word v & 3. Use mtp_kv_rollback (or mtp_kv_catchup) afterwards as with mtp_verify.
+ * Errors: as mtp_verify; a draft token outside [0, V) sets MTP_DEVERR_TOKEN and is
+ * rejected; bad temperature or null seeds returns MTP_ERR_INVALID_ARG.
+ */
+mtp_status mtp_verify_sample(mtp_handle* h, const float* target_logits, const float* draft_logits,
+                             const int32_t* draft_tokens, int32_t B, int32_t K, float temperature,
+                             const uint64_t* seeds, uint64_t offset, int32_t* accepted_len,
+                             int32_t* next_token, void* stream);
 
 /* Synchronise `stream`, read and clear the device error word. *bits receives the
  * MTP_DEVERR_* bits (may be NULL). Returns MTP_ERR_DEVICE when any bit was set. */

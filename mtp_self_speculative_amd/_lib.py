@@ -65,6 +65,10 @@ _SIGS = {
     "mtp_draft_debug": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, _P, _P, _P, _P, _P]),
     "mtp_verify": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
     "mtp_verify_hidden": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "mtp_draft_sample": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, ctypes.c_float, _P,
+                              ctypes.c_uint64, _P, _P, _P]),
+    "mtp_verify_sample": (_I, [_P, _P, _P, _P, _I, _I, ctypes.c_float, _P, ctypes.c_uint64, _P,
+                               _P, _P]),
     "mtp_kv_catchup": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _P, _P, _I, _I, _P]),
     "mtp_kv_rollback": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P]),
     "mtp_get_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -162,6 +166,23 @@ def mtp_verify(handle: int, target_logits: int, draft_tokens: int | None, B: int
                accepted_len: int, next_token: int, stream: int | None) -> None:
     _check(LIB.mtp_verify(handle, target_logits, draft_tokens, B, K, accepted_len, next_token,
                           stream), "mtp_verify")
+
+
+def mtp_draft_sample(handle: int, hidden: int, last_tokens: int, kv: mtp_kv, B: int, K: int,
+                     temperature: float, seeds: int | None, offset: int, draft_tokens: int,
+                     draft_logits: int | None, stream: int | None) -> None:
+    _check(LIB.mtp_draft_sample(handle, hidden, last_tokens, ctypes.byref(kv), B, K, temperature,
+                                seeds, offset, draft_tokens, draft_logits, stream),
+           "mtp_draft_sample")
+
+
+def mtp_verify_sample(handle: int, target_logits: int, draft_logits: int | None,
+                      draft_tokens: int | None, B: int, K: int, temperature: float,
+                      seeds: int | None, offset: int, accepted_len: int, next_token: int,
+                      stream: int | None) -> None:
+    _check(LIB.mtp_verify_sample(handle, target_logits, draft_logits, draft_tokens, B, K,
+                                 temperature, seeds, offset, accepted_len, next_token, stream),
+           "mtp_verify_sample")
 
 
 def mtp_verify_hidden(handle: int, target_hidden: int, target_norm: int,

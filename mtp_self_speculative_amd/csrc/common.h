@@ -191,6 +191,18 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Maximum of `v` over the workgroup; `red` as for block_sum.
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max_fast(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int i = 1; i < nw; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
 // ---------------------------------------------------------------- RoPE
 // cos / sin of position * theta^(-2i/d) for rotate-half pair i (0 <= i < d/2), evaluated
 // in double precision from the integer position and rounded to fp32.
@@ -201,6 +213,56 @@ __device__ __forceinline__ void rope_cs(int position, int i, int d, float theta,
   c = (float)cos(ang);
   s = (float)sin(ang);
 }
+
+// ---------------------------------------------------------------- counter-based random numbers
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1,
+// 2, 3", SC'11): ten rounds of two 64x64->128-bit multiplies with the key bumped by Weyl
+// constants between rounds. Any (counter, key) is evaluated independently, so every
+// vocabulary entry draws its own number wherever and in whatever order it is computed.
+struct Philox4 {
+  uint64_t w[4];
+};
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                 uint64_t c3, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+// Counter layout of the sampling streams: (c0, row, purpose, offset) under key (seed, 0).
+// Vocabulary entry v of a row uses word v & 3 of block c0 = v >> 2.
+enum RngPurpose : uint64_t {
+  RNG_DRAFT = 0,     // the draft's Gumbel noise at draft step `row`
+  RNG_ACCEPT = 1,    // acceptance uniform of draft `row` (c0 = 0, word 0)
+  RNG_RESAMPLE = 2,  // Gumbel noise of the resampled / bonus token (row = accepted length)
+};
+__device__ __forceinline__ Philox4 rng_block(uint64_t seed, uint64_t offset, uint64_t purpose,
+                                             uint64_t row, uint64_t c0) {
+  return philox4x64_10(c0, row, purpose, offset, seed, 0ull);
+}
+__device__ __forceinline__ uint64_t philox_word(const Philox4& b, int i) {
+  return i == 0 ? b.w[0] : i == 1 ? b.w[1] : i == 2 ? b.w[2] : b.w[3];
+}
+// A word as a uniform number in (0, 1): its top 24 bits with the lowest forced to one,
+// times 2^-24 (an odd multiple of 2^-24, exact in fp32).
+__device__ __forceinline__ float rng_uniform(uint64_t w) {
+  return (float)((uint32_t)(w >> 40) | 1u) * 0x1p-24f;
+}
+// Standard Gumbel variate: adding one to each log-weight and taking the argmax samples
+// the categorical distribution of the weights.
+__device__ __forceinline__ float gumbel_of(uint64_t w) { return -logf(-logf(rng_uniform(w))); }
 
 // ---------------------------------------------------------------- argmax keys
 // A logit and its index packed so that a larger key means a larger value and,

@@ -21,7 +21,8 @@
 // Epilogues: EPI_STORE writes the fp32 partial sums of the item's K split (a row-wise
 // reduction kernel adds the splits in a fixed order, so results are deterministic);
 // EPI_ARGMAX (one split) folds each row's value into a packed (value, index) key per
-// sequence and finishes with the last-workgroup protocol of the GEMV.
+// sequence and finishes with the last-workgroup protocol of the GEMV; EPI_SAMPLE does
+// the same with value / temperature + Gumbel noise, which samples softmax(value / T).
 #include "common.h"
 #include "kernels.h"
 
@@ -204,11 +205,22 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
               if (r0 + i < N) dst[i] = acc[m][nb][i];
           }
         } else {
+          // EPI_SAMPLE: the lane's four rows r0..r0+3 (r0 % 4 == 0) take the four words
+          // of one random block as their Gumbel noise.
+          float noise[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (EPI == EPI_SAMPLE) {
+            const Philox4 rb = rng_block(b < p.B ? p.smp.seeds[b] : 0ull, p.smp.offset,
+                                         RNG_DRAFT, (uint64_t)p.smp.row, (uint64_t)(r0 >> 2));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) noise[i] = gumbel_of(rb.w[i]);
+          }
           unsigned long long k = 0ull;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (r0 + i < N) {
-              const unsigned long long ki = pack_key(acc[m][nb][i], (uint32_t)(r0 + i));
+              float val = acc[m][nb][i];
+              if constexpr (EPI == EPI_SAMPLE) val = val / p.smp.temp + noise[i];
+              const unsigned long long ki = pack_key(val, (uint32_t)(r0 + i));
               k = ki > k ? ki : k;
               if (p.logits && b < p.B) p.logits[(long)b * p.logits_ld + r0 + i] = acc[m][nb][i];
             }
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
     stage(Bf, it + 1);
   }
 
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (epi_is_argmax(EPI)) {
     if (lane < 16) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) kred[wave][nb * 16 + lane] = best[nb];
@@ -275,18 +287,21 @@ static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   const size_t lds = mm_lds_bytes(NB);
   if (epi == EPI_ARGMAX)
     hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX>), dim3(grid), dim3(kMmThreads), lds, s, p);
+  else if (epi == EPI_SAMPLE)
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE>), dim3(grid), dim3(kMmThreads), lds, s, p);
   else
     hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE>), dim3(grid), dim3(kMmThreads), lds, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
-  if (epi != EPI_STORE && epi != EPI_ARGMAX) return hipErrorInvalidValue;
+  if (epi != EPI_STORE && !epi_is_argmax(epi)) return hipErrorInvalidValue;
+  if (epi == EPI_SAMPLE && (!(p.smp.temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
   if (p.B < 1 || p.B > 16 * kMmMaxNB || p.nrows < 1 || p.ncols < 8 || p.ncols % 8 != 0 ||
       p.ldx < p.ncols || p.ldx % 8 != 0 || !p.x || !p.x_lo || p.nsplit < 1 ||
       mm_chunks(p.ncols) % p.nsplit != 0 || grid < 1)
     return hipErrorInvalidValue;
-  if (epi == EPI_ARGMAX && (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
+  if (epi_is_argmax(epi) && (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
     return hipErrorInvalidValue;
   if (epi == EPI_STORE && !p.part) return hipErrorInvalidValue;
   static_assert(16 * kMmChunk * 2 <= kDummyBytes, "dummy region too small");

@@ -6,7 +6,8 @@
 // (applying the RMSNorm / embedding-gather prologue on the fly), then each wave streams
 // whole rows with 16-byte loads (64 lanes x 16 B = 1 KiB per instruction, several rows
 // and column chunks in flight) and reduces across the wave. Epilogues fuse the residual
-// add, SwiGLU and the vocabulary argmax, so no [B, V] logits tensor is ever written.
+// add, SwiGLU and the vocabulary argmax (plain, or over logit / temperature + Gumbel
+// noise to sample), so no [B, V] logits tensor has to be written.
 #include "common.h"
 #include "kernels.h"
 
@@ -232,8 +233,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
               const float v = p.res[o] + y;
               p.out[o] = v;
               if (p.dbg) p.dbg[(long)b * p.dbg_ld + lrow[r]] = v;
-            } else {  // EPI_ARGMAX
-              const unsigned long long k = pack_key(y, (uint32_t)lrow[r]);
+            } else {  // EPI_ARGMAX / EPI_SAMPLE
+              float val = y;
+              if constexpr (EPI == EPI_SAMPLE) {
+                const Philox4 rb = rng_block(p.smp.seeds[b], p.smp.offset, RNG_DRAFT,
+                                             (uint64_t)p.smp.row, (uint64_t)(lrow[r] >> 2));
+                val = y / p.smp.temp + gumbel_of(philox_word(rb, lrow[r] & 3));
+              }
+              const unsigned long long k = pack_key(val, (uint32_t)lrow[r]);
               best[i] = k > best[i] ? k : best[i];
               if (p.logits) p.logits[(long)b * p.logits_ld + lrow[r]] = y;
             }
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
     }
   }
 
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (epi_is_argmax(EPI)) {
     if (lane == 0) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) kred[wave][i] = best[i];
@@ -298,6 +305,7 @@ static hipError_t launch_dt(Pro pro, Epi epi, const GemvParams& p, int max_grid,
   if (pro == PRO_PLAIN && epi == EPI_RESID) return launch_nb<WT, PRO_PLAIN, EPI_RESID>(p, max_grid, s);
   if (pro == PRO_RMS && epi == EPI_SWIGLU) return launch_nb<WT, PRO_RMS, EPI_SWIGLU>(p, max_grid, s);
   if (pro == PRO_RMS && epi == EPI_ARGMAX) return launch_nb<WT, PRO_RMS, EPI_ARGMAX>(p, max_grid, s);
+  if (pro == PRO_RMS && epi == EPI_SAMPLE) return launch_nb<WT, PRO_RMS, EPI_SAMPLE>(p, max_grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -306,6 +314,7 @@ hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int ma
   const int step = 64 * (wdtype == 0 ? F32::kVec : BF16::kVec);
   if (p.col_block < step || p.col_block % step != 0 || p.ncols < 1 || p.nrows < 1)
     return hipErrorInvalidValue;
+  if (epi == EPI_SAMPLE && (!(p.smp.temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
   return wdtype == 0 ? launch_dt<F32>(pro, epi, p, max_grid, s)
                      : launch_dt<BF16>(pro, epi, p, max_grid, s);
 }

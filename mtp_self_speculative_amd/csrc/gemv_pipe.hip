@@ -13,7 +13,8 @@
 //
 // A logical row has P parts read with the same input vector: P = 2 streams the gate
 // and up rows of one SwiGLU unit together. The epilogues are those of the general
-// GEMV (store, residual add, SwiGLU, vocabulary argmax with last-workgroup finish).
+// GEMV (store, residual add, SwiGLU, vocabulary argmax with last-workgroup finish, and
+// the sampling argmax over value / temperature + Gumbel noise).
 #include "common.h"
 #include "kernels.h"
 
@@ -209,8 +210,12 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) acc[q][i] = 0.f;
   unsigned long long best[NB];
+  float gum[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) best[i] = 0ull;
+  for (int i = 0; i < NB; ++i) {
+    best[i] = 0ull;
+    gum[i] = 0.f;
+  }
 
   auto consume = [&](u32x4 (&buf)[P][CH], int it) {
     const int c0 = (it % S) * SW;
@@ -244,6 +249,22 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
       float rvv[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) rvv[i] = j < kWave ? __shfl(resv[i], j, kWave) : 0.f;
+      float nz[NB];
+      if constexpr (EPI == EPI_SAMPLE) {
+        // Lane l holds the Gumbel noise of this wave's row 64 * (j / 64) + l, drawn for
+        // 64 rows at once so that the random blocks are computed by all lanes.
+        if ((j & 63) == 0) {
+          const int rl = gw + (j + lane) * nw;  // rows past the end are drawn, never used
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            const Philox4 rb = rng_block(i < B ? p.smp.seeds[i] : 0ull, p.smp.offset, RNG_DRAFT,
+                                         (uint64_t)p.smp.row, (uint64_t)(rl >> 2));
+            gum[i] = gumbel_of(philox_word(rb, rl & 3));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) nz[i] = __shfl(gum[i], j & 63, kWave);
+      }
       if (lane == 0) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -260,7 +281,9 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
             p.out[o] = y;
             if (p.dbg) p.dbg[(long)i * p.dbg_ld + r] = y;
           } else {
-            const unsigned long long k = pack_key(acc[0][i], (uint32_t)r);
+            float val = acc[0][i];
+            if constexpr (EPI == EPI_SAMPLE) val = val / p.smp.temp + nz[i];
+            const unsigned long long k = pack_key(val, (uint32_t)r);
             best[i] = k > best[i] ? k : best[i];
             if (p.logits) p.logits[(long)i * p.logits_ld + r] = acc[0][i];
           }
@@ -281,7 +304,7 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
     load(Bf, it + 3);
   }
 
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (epi_is_argmax(EPI)) {
     if (lane == 0) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) kred[wave][i] = best[i];
@@ -338,6 +361,7 @@ static hipError_t pipe_dt(Pro pro, Epi epi, const GemvParams& p, int grid, hipSt
   if (pro == PRO_PLAIN && epi == EPI_RESID) return pipe_nb<WT, PRO_PLAIN, EPI_RESID>(p, grid, s);
   if (pro == PRO_RMS && epi == EPI_SWIGLU) return pipe_nb<WT, PRO_RMS, EPI_SWIGLU>(p, grid, s);
   if (pro == PRO_RMS && epi == EPI_ARGMAX) return pipe_nb<WT, PRO_RMS, EPI_ARGMAX>(p, grid, s);
+  if (pro == PRO_RMS && epi == EPI_SAMPLE) return pipe_nb<WT, PRO_RMS, EPI_SAMPLE>(p, grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -359,6 +383,7 @@ hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, i
   if (!gemv_pipe_fits(p.ncols, p.B, wdtype) || p.ncols % 8 != 0 || p.nrows < 1 || grid < 1)
     return hipErrorInvalidValue;
   if (pro == PRO_EH && !p.h_is_f32) return hipErrorInvalidValue;
+  if (epi == EPI_SAMPLE && (!(p.smp.temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
   static_assert(kPipeCH * kWave * 16 <= kDummyBytes, "dummy region too small");
   if (!p.dummy) return hipErrorInvalidValue;
   return wdtype == 0 ? pipe_dt<F32>(pro, epi, p, grid, s) : pipe_dt<BF16>(pro, epi, p, grid, s);

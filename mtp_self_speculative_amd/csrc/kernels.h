@@ -17,6 +17,17 @@ enum Epi : int {
   EPI_RESID = 1,   // out[b, r] = res[b, r] + y
   EPI_SWIGLU = 2,  // rows come in (gate, up) pairs: out[b, r] = silu(y_gate) * y_up
   EPI_ARGMAX = 3,  // argmax over r per b, finished by the last workgroup
+  EPI_SAMPLE = 4,  // as EPI_ARGMAX over y / temp + Gumbel noise: a sample of softmax(y / temp)
+};
+constexpr bool epi_is_argmax(int e) { return e == EPI_ARGMAX || e == EPI_SAMPLE; }
+
+// EPI_SAMPLE: the noise of vocabulary row r for batch row b comes from the stream
+// (seed seeds[b], offset, purpose draft, row `row`).
+struct SampleParams {
+  float temp;              // > 0
+  const uint64_t* seeds;   // [B] device
+  uint64_t offset;
+  int row;                 // draft step (0-based)
 };
 
 struct GemvParams {
@@ -64,6 +75,7 @@ struct GemvParams {
   // >= kDummyBytes of readable device memory: the target of the pipelined kernel's
   // prefetches past a wave's last stage, which are issued but never consumed
   const void* dummy;
+  SampleParams smp;  // EPI_SAMPLE
 };
 constexpr int kDummyBytes = 16 * 1024;
 
@@ -140,6 +152,7 @@ struct MmParams {
   int* pos;
   int advance;
   const void* dummy;  // as GemvParams::dummy
+  SampleParams smp;   // EPI_SAMPLE
 };
 __host__ __device__ int mm_chunks(int ncols);  // K chunks of the contraction
 int mm_batch_pad(int B);                           // 16 * NB for batch B
@@ -192,6 +205,27 @@ struct VerifyParams {
   int* next;
 };
 hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s);
+
+// Speculative-sampling verification at temperature temp (two launches, see verify.hip).
+struct VSampleParams {
+  const float* tlog;  // [B, K+1, V] target logits
+  const float* dlog;  // [B, K, V] draft logits (row j produced draft j)
+  const int* draft;   // [B, K]
+  int K, V, nchunk;   // nchunk = vs_chunks(V)
+  float temp;
+  const uint64_t* seeds;     // [B]
+  uint64_t offset;
+  unsigned long long* part;  // [B, 2K+1, nchunk] (max, sum) pairs, left zero
+  float* lse;                // [B, 2] log-sum-exps of the target / draft row a
+  unsigned long long* keys;  // [B, 2] zero on entry/exit
+  unsigned* counters;        // [B] zero on entry/exit
+  int* accepted;
+  int* next;
+  unsigned* err;
+};
+constexpr int kVsMaxK = 100;
+int vs_chunks(int V);
+hipError_t launch_verify_sample(const VSampleParams& p, int B, hipStream_t s);
 
 hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
                            hipStream_t s);

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/mtp.h: argument validation, workspace
 // layout, kernel selection and the launch sequence of one speculative iteration.
 #include <math.h>
+#include <cmath>
 #include <stdlib.h>
 #include <string.h>
 
@@ -19,6 +20,7 @@ constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 1024;
 constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
 constexpr int kMaxK = 100;
+static_assert(kMaxK <= kVsMaxK, "sampling verification holds 2K+1 log-sum-exps in LDS");
 constexpr int kMaxGroupHeads = 8;
 constexpr int kVerifyChunk = 2048;
 constexpr size_t kGemvLdsBudget = 32 * 1024;
@@ -36,6 +38,8 @@ struct Layout {
   // exact cache catch-up: one group of up to kVhGroup candidate rows at a time
   size_t cu_h, cu_x, cu_kv, cu_q, cu_q_lo, cu_part;
   int cu_rows, cu_ld;
+  // sampling verification: (max, sum) pairs per (sequence, row, chunk), row a's lse, keys
+  size_t vs_part, vs_lse, vs_keys;
   size_t total;
 };
 
@@ -147,6 +151,9 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
       L.cu_part = take(part * 4);
     }
   }
+  L.vs_part = take((size_t)max_batch * (2 * max_k + 1) * vs_chunks(c.vocab) * 8);
+  L.vs_lse = take((size_t)max_batch * 2 * 4);
+  L.vs_keys = take((size_t)max_batch * 2 * 8);
   L.total = off;
   return L;
 }
@@ -410,9 +417,17 @@ static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int
 // The K draft steps for 3..64 sequences with bf16 weights: each projection is an MFMA
 // contraction into K-split partials followed by a row-wise kernel that adds the splits,
 // applies the epilogue and writes the next contraction's normalised bf16 operand.
+// Where the lm_head writes logits (optional) and whether it samples instead of argmax.
+struct LmOut {
+  float* logits;       // step k, sequence b at logits + k * step_stride + b * ld
+  size_t step_stride;
+  int ld;
+  const SampleParams* smp;  // null: argmax
+};
+
 static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_kv* kv,
                                  int32_t B, int32_t K, int32_t* draft_tokens, float* hidden_out,
-                                 float* max_logit_out, float* logits_out, int chunk, int nsplit,
+                                 float* max_logit_out, const LmOut& lo, int chunk, int nsplit,
                                  hipStream_t s) {
   const mtp_config& c = h->cfg;
   const mtp_weights& w = h->w;
@@ -518,12 +533,16 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       m.tok_out = draft_tokens + k;
       m.tok_out_stride = K;
       m.maxlogit = max_logit_out ? max_logit_out + (size_t)k * B : nullptr;
-      m.logits = logits_out ? logits_out + (size_t)k * B * V : nullptr;
-      m.logits_ld = V;
+      m.logits = lo.logits ? lo.logits + (size_t)k * lo.step_stride : nullptr;
+      m.logits_ld = lo.ld;
       m.len = kv->len; m.pos = kv->pos;
       m.advance = (k == K - 1) ? K : 0;
       m.dummy = h->ws + L.dummy;
-      return launch_mm(EPI_ARGMAX, m, mm_grid(V, H, B, 1, h->num_cu), s);
+      if (lo.smp) {
+        m.smp = *lo.smp;
+        m.smp.row = k;
+      }
+      return launch_mm(lo.smp ? EPI_SAMPLE : EPI_ARGMAX, m, mm_grid(V, H, B, 1, h->num_cu), s);
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -532,7 +551,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
 
 static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                              mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
-                             float* hidden_out, float* max_logit_out, float* logits_out,
+                             float* hidden_out, float* max_logit_out, const LmOut& lo,
                              void* stream) {
   if (!h || !hidden || !last_tokens) return MTP_ERR_INVALID_ARG;
   if (!aligned(hidden, 16)) return MTP_ERR_INVALID_ARG;
@@ -572,8 +591,8 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
                          hb, H, s) != hipSuccess)
     return MTP_ERR_HIP;
   if (use_mm(c, B))
-    return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out,
-                          logits_out, chunk, nsplit, s);
+    return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out, lo,
+                          chunk, nsplit, s);
   for (int k = 0; k < K; ++k) {
     hipError_t e;
     // 1. embedding gather + separate RMSNorms + concat + eh_proj
@@ -656,11 +675,16 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.tok_out = draft_tokens + k;
     g.tok_out_stride = K;
     g.maxlogit = max_logit_out ? max_logit_out + (size_t)k * B : nullptr;
-    g.logits = logits_out ? logits_out + (size_t)k * B * V : nullptr;
-    g.logits_ld = V;
+    g.logits = lo.logits ? lo.logits + (size_t)k * lo.step_stride : nullptr;
+    g.logits_ld = lo.ld;
     g.len = kv->len; g.pos = kv->pos;
     g.advance = (k == K - 1) ? K : 0;
-    if ((e = timed(h, KC_LMHEAD, s, [&] { return run_gemv(h, PRO_RMS, EPI_ARGMAX, g, s); })) != hipSuccess)
+    if (lo.smp) {
+      g.smp = *lo.smp;
+      g.smp.row = k;
+    }
+    const Epi lm_epi = lo.smp ? EPI_SAMPLE : EPI_ARGMAX;
+    if ((e = timed(h, KC_LMHEAD, s, [&] { return run_gemv(h, PRO_RMS, lm_epi, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
   }
   return MTP_OK;
@@ -668,16 +692,30 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
 
 mtp_status mtp_draft(mtp_handle* h, const void* hidden, const int32_t* last_tokens, mtp_kv* kv,
                      int32_t B, int32_t K, int32_t* draft_tokens, void* stream) {
-  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, nullptr, nullptr, nullptr,
-                    stream);
+  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, nullptr, nullptr,
+                    LmOut{nullptr, 0, 0, nullptr}, stream);
+}
+
+mtp_status mtp_draft_sample(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                            mtp_kv* kv, int32_t B, int32_t K, float temperature,
+                            const uint64_t* seeds, uint64_t offset, int32_t* draft_tokens,
+                            float* draft_logits, void* stream) {
+  if (!h) return MTP_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return MTP_ERR_INVALID_ARG;
+  if (K > 0 && (!seeds || !draft_logits || !aligned(draft_logits, 4))) return MTP_ERR_INVALID_ARG;
+  SampleParams smp{temperature, seeds, offset, 0};
+  const int V = h->cfg.vocab;
+  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, nullptr, nullptr,
+                    LmOut{draft_logits, (size_t)V, K * V, &smp}, stream);
 }
 
 mtp_status mtp_draft_debug(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                            mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
                            float* hidden_out, float* max_logit_out, float* logits_out,
                            void* stream) {
+  if (!h) return MTP_ERR_INVALID_ARG;
   return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out,
-                    logits_out, stream);
+                    LmOut{logits_out, (size_t)B * h->cfg.vocab, h->cfg.vocab, nullptr}, stream);
 }
 
 mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* draft_tokens,
@@ -701,6 +739,38 @@ mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed(h, KC_VERIFY, s, [&] { return launch_verify(p, B, s); }) == hipSuccess ? MTP_OK
                                                                                       : MTP_ERR_HIP;
+}
+
+mtp_status mtp_verify_sample(mtp_handle* h, const float* target_logits, const float* draft_logits,
+                             const int32_t* draft_tokens, int32_t B, int32_t K, float temperature,
+                             const uint64_t* seeds, uint64_t offset, int32_t* accepted_len,
+                             int32_t* next_token, void* stream) {
+  if (!h || !target_logits || !seeds || !accepted_len || !next_token) return MTP_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return MTP_ERR_INVALID_ARG;
+  if (K < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  if (K > 0 && (!draft_tokens || !draft_logits)) return MTP_ERR_INVALID_ARG;
+  VSampleParams p{};
+  p.tlog = target_logits;
+  p.dlog = draft_logits;
+  p.draft = draft_tokens;
+  p.K = K;
+  p.V = h->cfg.vocab;
+  p.nchunk = vs_chunks(p.V);
+  p.temp = temperature;
+  p.seeds = seeds;
+  p.offset = offset;
+  p.part = h->at<unsigned long long>(h->L.vs_part);
+  p.lse = h->at<float>(h->L.vs_lse);
+  p.keys = h->at<unsigned long long>(h->L.vs_keys);
+  p.counters = h->at<unsigned>(h->L.v_cnt);
+  p.accepted = accepted_len;
+  p.next = next_token;
+  p.err = h->at<unsigned>(h->L.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(h, KC_VERIFY, s, [&] { return launch_verify_sample(p, B, s); }) == hipSuccess
+             ? MTP_OK
+             : MTP_ERR_HIP;
 }
 
 mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,

@@ -7,6 +7,7 @@
 // K+1 keys into the target's tokens, scans the longest prefix of drafts that match them
 // and writes accepted_len and the bonus token.
 // Rows of a length divisible by 4 take a variant with 16-byte loads and larger chunks.
+// Sampling verification (temperature > 0) is described above its kernels below.
 // Rollback: one lane per sequence moves len/pos to the committed prefix.
 #include "common.h"
 #include "kernels.h"
@@ -125,6 +126,165 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_vec_kernel(VerifyParams
       p.next[b] = next;
     }
   }
+}
+
+// ---------------------------------------------------------------- sampling verification
+// Speculative sampling at temperature T, in two launches.
+// (1) grid (chunk, row, sequence) over the K+1 target rows and the K draft rows: each
+//     workgroup reduces its chunk of x / T to the pair (max m, sum of exp(x/T - m)) and
+//     publishes it with a returning atomic exchange. The last workgroup of a sequence
+//     merges every row's pairs in chunk order into a log-sum-exp, then runs the
+//     acceptance tests in order: draft d_{j+1} is accepted iff
+//     log U_j < (t_j[d]/T - lse_t[j]) - (z_j[d]/T - lse_z[j]), i.e. U < p/q; it writes the
+//     accepted length a and the two log-sum-exps of row a.
+// (2) grid (chunk, sequence): Gumbel-max draws over row a, one of log(p_a - q_a) where
+//     positive (a < K: the residual distribution) and one of t_a / T (the target's own
+//     distribution: the bonus token when a = K, the fallback when rounding left no
+//     positive residual). Each lane takes four consecutive entries and one random block.
+constexpr int kVsThreads = 256;
+constexpr int kVsPer = 8;
+constexpr int kVsChunk = kVsThreads * kVsPer;  // logits per workgroup and row
+
+int vs_chunks(int V) { return (V + kVsChunk - 1) / kVsChunk; }
+
+__device__ __forceinline__ unsigned long long pack_pair(float m, float sum) {
+  return ((unsigned long long)__float_as_uint(m) << 32) | (unsigned long long)__float_as_uint(sum);
+}
+
+__global__ __launch_bounds__(kVsThreads) void vs_stats_kernel(VSampleParams p) {
+  __shared__ float red[kVsThreads / kWave];
+  __shared__ float lse_s[2 * kVsMaxK + 1];
+  __shared__ int flag;
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int K = p.K, V = p.V, R = 2 * K + 1;
+  const float* row = r <= K ? p.tlog + ((long)b * (K + 1) + r) * V
+                            : p.dlog + ((long)b * K + (r - K - 1)) * V;
+  const int lo = c * kVsChunk;
+  float x[kVsPer];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kVsPer; ++k) {
+    const int idx = lo + (int)threadIdx.x + k * kVsThreads;
+    x[k] = idx < V ? __builtin_nontemporal_load(row + idx) / p.temp : -INFINITY;
+    m = fmaxf(m, x[k]);
+  }
+  m = block_max(m, red);  // finite: every chunk holds at least one entry
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kVsPer; ++k) sum += expf(x[k] - m);
+  sum = block_sum(sum, red);
+  if (threadIdx.x == 0)
+    keep_alive(__hip_atomic_exchange(p.part + ((long)b * R + r) * p.nchunk + c, pack_pair(m, sum),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (!last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) return;
+  // Merge each row's pairs in chunk order (running max, rescaled sum).
+  for (int q = threadIdx.x; q < R; q += kVsThreads) {
+    unsigned long long* pp = p.part + ((long)b * R + q) * p.nchunk;
+    float M = -INFINITY, S = 0.f;
+    for (int cc = 0; cc < p.nchunk; ++cc) {
+      const unsigned long long v = take_key(pp + cc);
+      const float mc = __uint_as_float((uint32_t)(v >> 32));
+      const float sc = __uint_as_float((uint32_t)v);
+      if (mc > M) {
+        S = S * expf(M - mc) + sc;
+        M = mc;
+      } else {
+        S += sc * expf(mc - M);
+      }
+    }
+    lse_s[q] = M + logf(S);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0;
+    for (int j = 0; j < K; ++j) {
+      const int d = p.draft[(long)b * K + j];
+      if (d < 0 || d >= V) {  // an invalid draft token is rejected
+        set_error(p.err, 1u);
+        break;
+      }
+      const float lp = p.tlog[((long)b * (K + 1) + j) * V + d] / p.temp - lse_s[j];
+      const float lq = p.dlog[((long)b * K + j) * V + d] / p.temp - lse_s[K + 1 + j];
+      const Philox4 rb = rng_block(p.seeds[b], p.offset, RNG_ACCEPT, (uint64_t)j, 0ull);
+      if (logf(rng_uniform(rb.w[0])) < lp - lq) {
+        ++a;
+      } else {
+        break;
+      }
+    }
+    p.accepted[b] = a;
+    p.lse[2 * b] = lse_s[a];
+    p.lse[2 * b + 1] = a < K ? lse_s[K + 1 + a] : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p) {
+  __shared__ unsigned long long kred[2][kVsThreads / kWave];
+  __shared__ int flag;
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = p.K, V = p.V;
+  int a = p.accepted[b];
+  a = a < 0 ? 0 : a > K ? K : a;
+  const bool resid = a < K;
+  const float* trow = p.tlog + ((long)b * (K + 1) + a) * V;
+  const float* drow = resid ? p.dlog + ((long)b * K + a) * V : trow;
+  const float lt = p.lse[2 * b], lz = p.lse[2 * b + 1];
+  const uint64_t seed = p.seeds[b];
+  unsigned long long kr = 0ull, kp = 0ull;
+#pragma unroll
+  for (int g = 0; g < kVsPer / 4; ++g) {
+    const int v0 = c * kVsChunk + (g * kVsThreads + (int)threadIdx.x) * 4;
+    if (v0 >= V) continue;
+    const Philox4 rb = rng_block(seed, p.offset, RNG_RESAMPLE, (uint64_t)a, (uint64_t)(v0 >> 2));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = v0 + e;
+      if (v >= V) break;
+      const float tv = trow[v] / p.temp;
+      const float gv = gumbel_of(rb.w[e]);
+      const unsigned long long k1 = pack_key(tv + gv, (uint32_t)v);
+      kp = k1 > kp ? k1 : kp;
+      if (resid) {
+        const float rv = expf(tv - lt) - expf(drow[v] / p.temp - lz);
+        if (rv > 0.f) {
+          const unsigned long long k2 = pack_key(logf(rv) + gv, (uint32_t)v);
+          kr = k2 > kr ? k2 : kr;
+        }
+      }
+    }
+  }
+  kr = wave_max_u64(kr);
+  kp = wave_max_u64(kp);
+  if (lane == 0) {
+    kred[0][wave] = kr;
+    kred[1][wave] = kp;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    unsigned long long k = 0ull;
+    for (int w = 0; w < kVsThreads / kWave; ++w) k = kred[threadIdx.x][w] > k ? kred[threadIdx.x][w] : k;
+    if (k) keep_alive(atomic_max_key(p.keys + 2 * b + threadIdx.x, k));
+  }
+  if (last_to_arrive(p.counters + b, gridDim.x, &flag)) {
+    if (threadIdx.x == 0) {
+      const unsigned long long r = take_key(p.keys + 2 * b);
+      const unsigned long long q = take_key(p.keys + 2 * b + 1);
+      p.next[b] = (int)key_index(r ? r : q);
+    }
+  }
+}
+
+hipError_t launch_verify_sample(const VSampleParams& p, int B, hipStream_t s) {
+  if (p.V < 1 || p.K < 0 || p.K > kVsMaxK || B < 1 || p.nchunk != vs_chunks(p.V) ||
+      !(p.temp > 0.f) || !p.seeds || !p.tlog || (p.K > 0 && (!p.dlog || !p.draft)) || !p.part ||
+      !p.lse || !p.keys || !p.counters || !p.accepted || !p.next || !p.err)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vs_stats_kernel, dim3(p.nchunk, 2 * p.K + 1, B), dim3(kVsThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vs_resample_kernel, dim3(p.nchunk, B), dim3(kVsThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 __global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, int K,

@@ -99,6 +99,36 @@ class MtpHead:
                           out.data_ptr(), hid.data_ptr(), mx.data_ptr(), _ptr(lg), _stream(stream))
         return out, hid, mx, lg
 
+    def draft_sample(self, hidden: torch.Tensor, last_tokens: torch.Tensor, cache: MtpCache,
+                     K: int, temperature: float, seeds: torch.Tensor, offset: int, stream=None):
+        """K draft steps sampling at `temperature`; seeds [B] int64 on the device.
+        Returns (draft tokens [B, K] int32, draft logits [B, K, V] fp32)."""
+        B = hidden.shape[0]
+        dev = hidden.device
+        out = torch.empty((B, K), dtype=torch.int32, device=dev)
+        lg = torch.empty((B, K, self.vocab), dtype=torch.float32, device=dev)
+        L.mtp_draft_sample(self.handle, hidden.data_ptr(), last_tokens.data_ptr(), cache.kv, B, K,
+                           float(temperature), seeds.data_ptr(), int(offset), out.data_ptr(),
+                           lg.data_ptr(), _stream(stream))
+        return out, lg
+
+    def verify_sample(self, target_logits: torch.Tensor, draft_logits: torch.Tensor | None,
+                      draft_tokens: torch.Tensor | None, temperature: float, seeds: torch.Tensor,
+                      offset: int, accepted: torch.Tensor | None = None,
+                      next_token: torch.Tensor | None = None, stream=None):
+        """Speculative-sampling verification against target logits [B, K+1, V]."""
+        B, K1, V = target_logits.shape
+        dev = target_logits.device
+        if accepted is None:
+            accepted = torch.empty(B, dtype=torch.int32, device=dev)
+        if next_token is None:
+            next_token = torch.empty(B, dtype=torch.int32, device=dev)
+        L.mtp_verify_sample(self.handle, target_logits.data_ptr(), _ptr(draft_logits),
+                            _ptr(draft_tokens), B, K1 - 1, float(temperature), seeds.data_ptr(),
+                            int(offset), accepted.data_ptr(), next_token.data_ptr(),
+                            _stream(stream))
+        return accepted, next_token
+
     def verify(self, target_logits: torch.Tensor, draft_tokens: torch.Tensor | None,
                accepted: torch.Tensor | None = None, next_token: torch.Tensor | None = None,
                stream=None):

@@ -24,6 +24,9 @@ chunk), so the values depend neither on the thread count nor on the machine.
     stream 13 target hidden states for verification from hidden states, N(0, 1)
               (sub = iteration)
     stream 14 the target's final-norm gain, N(1, 0.02)
+    stream 15 logits for sampling verification (sub 2*it: target rows, N(0, scale^2);
+              sub 2*it+1: draft-row perturbation, N(0, noise^2))
+    stream 16 per-sequence random-stream seeds, uniform 63-bit integers
 
 bf16 configurations draw in fp32 and round to bf16 (round to nearest even);
 bf16 arrays are carried as their uint16 bit patterns.
@@ -206,6 +209,22 @@ def plant_target_logits(cfg: Config, draft_tokens: np.ndarray, it: int = 0,
         bb, jj = np.nonzero(hit)
         t[bb, jj, d[bb, jj]] += np.float32(bump)
     return t
+
+
+def sampling_logits(cfg: Config, K: int, it: int = 0, scale: float = 3.0,
+                    noise: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+    """Target logits [B, K+1, V] ~ N(0, scale^2) and draft logits [B, K, V] equal to the
+    first K target rows plus N(0, noise^2), float32. With the defaults about 60% of
+    sampled drafts are accepted at temperature 1 over a large vocabulary."""
+    B, V = cfg.batch, cfg.vocab
+    t = normal(cfg.cid, 15, 2 * it, B * (K + 1) * V, 0.0, scale, "f32").reshape(B, K + 1, V)
+    e = normal(cfg.cid, 15, 2 * it + 1, B * K * V, 0.0, noise, "f32").reshape(B, K, V)
+    return t, (t[:, :K] + e).astype(np.float32)
+
+
+def sample_seeds(cfg: Config, sub: int = 0) -> np.ndarray:
+    """One random-stream seed per sequence, [B] uint64."""
+    return _rng(cfg.cid, 16, sub).integers(0, 2 ** 63, size=cfg.batch, dtype=np.uint64)
 
 
 TARGET_PROJ = ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")

@@ -90,6 +90,10 @@ def test_null_arguments_rejected_before_any_device_call():
     assert L.LIB.mtp_verify_hidden(None, None, None, None, 1, 1, None, None, None) == 1
     assert L.LIB.mtp_kv_rollback(None, ctypes.byref(kv), None, 1, 1, None) == 1
     assert L.LIB.mtp_kv_catchup(None, ctypes.byref(kv), None, None, None, 1, 1, None) == 1
+    assert L.LIB.mtp_draft_sample(None, None, None, ctypes.byref(kv), 1, 1, 1.0, None, 0, None,
+                                  None, None) == 1
+    assert L.LIB.mtp_verify_sample(None, None, None, None, 1, 1, 1.0, None, 0, None, None,
+                                   None) == 1
     assert L.LIB.mtp_get_error(None, None, None) == 1
     L.LIB.mtp_destroy(None)
 
