@@ -145,6 +145,81 @@ def cpu_baseline(cfg, inp, K: int, reps: int = 3) -> dict:
                       f"float32 NumPy, {cores} BLAS threads"}
 
 
+def sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up) -> dict:
+    """Temperature sampling at T = 1, timed like the greedy pass: the draft samples each
+    token in the lm_head kernel (draft logits written); the target's rows are the draft's
+    logits plus N(0, 1) noise (row K: N(0, 1.3^2)), which gives about 60% acceptance per
+    draft; speculative-sampling verification decides and the cache is rolled back. The
+    iteration index is the random-stream offset, so the replay reproduces the recording."""
+    import numpy as np
+    import torch
+
+    import mtp_synth as S
+    from mtp_self_speculative_amd._lib import KERNEL_CLASSES
+    dev = hidden.device
+    B, K, V = cfg.batch, cfg.K, cfg.vocab
+    iters = args.warmup + args.steps
+    T = 1.0
+    seeds = torch.from_numpy(S.sample_seeds(cfg).view(np.int64)).to(dev)
+    toks = torch.empty((iters, B, K), dtype=torch.int32, device=dev)
+    dlog = torch.empty((iters, B, K, V), dtype=torch.float32, device=dev)
+    tlog = torch.empty((iters, B, K + 1, V), dtype=torch.float32, device=dev)
+    acc = torch.empty((iters, B), dtype=torch.int32, device=dev)
+    nxt = torch.empty((iters, B), dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.cid * 1000 + 17)
+
+    def run(it, last, plant=False):
+        head.draft_sample(hidden[it], last, cache, K, T, seeds, it, out=toks[it], logits=dlog[it])
+        if plant:
+            tlog[it, :, :K] = dlog[it] + torch.randn((B, K, V), generator=gen, device=dev)
+            tlog[it, :, K] = 1.3 * torch.randn((B, V), generator=gen, device=dev)
+        head.verify_sample(tlog[it], dlog[it], toks[it], T, seeds, it, acc[it], nxt[it])
+        head.rollback(cache, acc[it], K)
+        return nxt[it]
+
+    def replay(mask, plant=False):
+        cache.len.copy_(len0)
+        cache.pos.copy_(pos0)
+        last = last0
+        head.set_profiling(0)
+        for it in range(args.warmup):
+            last = run(it, last, plant)
+        torch.cuda.synchronize()
+        head.set_profiling(mask)
+        t0 = time.perf_counter()
+        for it in range(args.warmup, iters):
+            last = run(it, last, plant)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        head.set_profiling(0)
+        return t1 - t0, head.get_profile()
+
+    replay(0, plant=True)
+    rec_t, rec_a = toks.clone(), acc.clone()
+    assert head.get_error() == 0
+    elapsed, _ = replay(0)
+    if not (torch.equal(toks, rec_t) and torch.equal(acc, rec_a)):
+        raise RuntimeError("timed sampling replay diverged from the recording pass")
+    mask = (1 << KERNEL_CLASSES.index("lm_head_argmax")) | (1 << KERNEL_CLASSES.index("verify"))
+    _, prof = replay(mask)
+    a = acc[args.warmup:].cpu().numpy().astype(np.int64)
+    lm_ms, lm_n = prof["lm_head_argmax"]
+    v_ms, v_n = prof["verify"]
+    log(f"sampling pass: {args.steps} iterations in {elapsed * 1e3:.2f} ms, "
+        f"acceptance {a.mean() / K:.3f}")
+    out = {"temperature": T, "draft_steps_per_s": round(K * args.steps / elapsed, 3),
+           "verified_tok_per_s": round(float((a + 1).sum()) / elapsed, 2),
+           "acceptance_per_draft": round(float(a.mean()) / K, 4),
+           "lm_head_sample_us": round(lm_ms * 1e3 / lm_n, 2),
+           "verify_sample_us": round(v_ms * 1e3 / v_n, 2)}
+    cache.len.copy_(len0)
+    cache.pos.copy_(pos0)
+    del dlog, tlog
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +365,8 @@ def main() -> int:
     assert head.get_error() == 0
     log(f"exact cache catch-up: {cu_us:.2f} us per call")
 
+    samp = sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up)
+
     acc_np = acc[args.warmup:].cpu().numpy().astype(np.int64)
     tokens = int((acc_np + 1).sum())
     rows = int((acc_np + 1).sum())
@@ -327,6 +404,7 @@ def main() -> int:
                                  "algorithmic_bytes": int(vh_bytes),
                                  "hbm_frac": round(vh_bytes / (vh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     out["kv_catchup"] = {"us_per_call": round(cu_us, 2), "candidate_rows": B * K}
+    out["sampling"] = samp
     if kernel_us:
         out["kernel_us_per_launch"] = kernel_us
     head.close()

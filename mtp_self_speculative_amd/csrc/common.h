@@ -260,9 +260,16 @@ __device__ __forceinline__ uint64_t philox_word(const Philox4& b, int i) {
 __device__ __forceinline__ float rng_uniform(uint64_t w) {
   return (float)((uint32_t)(w >> 40) | 1u) * 0x1p-24f;
 }
-// Standard Gumbel variate: adding one to each log-weight and taking the argmax samples
-// the categorical distribution of the weights.
-__device__ __forceinline__ float gumbel_of(uint64_t w) { return -logf(-logf(rng_uniform(w))); }
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32, about 1 ulp).
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+// Standard Gumbel variate -ln(-ln U), in base 2: -ln2 * log2(-ln2 * log2 U). Adding one to
+// each log-weight and taking the argmax samples the categorical distribution of the weights.
+__device__ __forceinline__ float gumbel_of(uint64_t w) {
+  return -kLn2 * hw_log2(-kLn2 * hw_log2(rng_uniform(w)));
+}
 
 // ---------------------------------------------------------------- argmax keys
 // A logit and its index packed so that a larger key means a larger value and,

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
           for (int i = 0; i < 4; ++i) {
             if (r0 + i < N) {
               float val = acc[m][nb][i];
-              if constexpr (EPI == EPI_SAMPLE) val = val / p.smp.temp + noise[i];
+              if constexpr (EPI == EPI_SAMPLE) val = val * p.smp.inv_temp + noise[i];
               const unsigned long long ki = pack_key(val, (uint32_t)(r0 + i));
               k = ki > k ? ki : k;
               if (p.logits && b < p.B) p.logits[(long)b * p.logits_ld + r0 + i] = acc[m][nb][i];
@@ -296,7 +296,7 @@ static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
 
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   if (epi != EPI_STORE && !epi_is_argmax(epi)) return hipErrorInvalidValue;
-  if (epi == EPI_SAMPLE && (!(p.smp.temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
+  if (epi == EPI_SAMPLE && (!(p.smp.inv_temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
   if (p.B < 1 || p.B > 16 * kMmMaxNB || p.nrows < 1 || p.ncols < 8 || p.ncols % 8 != 0 ||
       p.ldx < p.ncols || p.ldx % 8 != 0 || !p.x || !p.x_lo || p.nsplit < 1 ||
       mm_chunks(p.ncols) % p.nsplit != 0 || grid < 1)

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
               if constexpr (EPI == EPI_SAMPLE) {
                 const Philox4 rb = rng_block(p.smp.seeds[b], p.smp.offset, RNG_DRAFT,
                                              (uint64_t)p.smp.row, (uint64_t)(lrow[r] >> 2));
-                val = y / p.smp.temp + gumbel_of(philox_word(rb, lrow[r] & 3));
+                val = y * p.smp.inv_temp + gumbel_of(philox_word(rb, lrow[r] & 3));
               }
               const unsigned long long k = pack_key(val, (uint32_t)lrow[r]);
               best[i] = k > best[i] ? k : best[i];
@@ -314,7 +314,7 @@ hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int ma
   const int step = 64 * (wdtype == 0 ? F32::kVec : BF16::kVec);
   if (p.col_block < step || p.col_block % step != 0 || p.ncols < 1 || p.nrows < 1)
     return hipErrorInvalidValue;
-  if (epi == EPI_SAMPLE && (!(p.smp.temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
+  if (epi == EPI_SAMPLE && (!(p.smp.inv_temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
   return wdtype == 0 ? launch_dt<F32>(pro, epi, p, max_grid, s)
                      : launch_dt<BF16>(pro, epi, p, max_grid, s);
 }

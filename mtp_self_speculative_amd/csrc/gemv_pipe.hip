@@ -282,7 +282,7 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
             if (p.dbg) p.dbg[(long)i * p.dbg_ld + r] = y;
           } else {
             float val = acc[0][i];
-            if constexpr (EPI == EPI_SAMPLE) val = val / p.smp.temp + nz[i];
+            if constexpr (EPI == EPI_SAMPLE) val = val * p.smp.inv_temp + nz[i];
             const unsigned long long k = pack_key(val, (uint32_t)r);
             best[i] = k > best[i] ? k : best[i];
             if (p.logits) p.logits[(long)i * p.logits_ld + r] = acc[0][i];
@@ -383,7 +383,7 @@ hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, i
   if (!gemv_pipe_fits(p.ncols, p.B, wdtype) || p.ncols % 8 != 0 || p.nrows < 1 || grid < 1)
     return hipErrorInvalidValue;
   if (pro == PRO_EH && !p.h_is_f32) return hipErrorInvalidValue;
-  if (epi == EPI_SAMPLE && (!(p.smp.temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
+  if (epi == EPI_SAMPLE && (!(p.smp.inv_temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
   static_assert(kPipeCH * kWave * 16 <= kDummyBytes, "dummy region too small");
   if (!p.dummy) return hipErrorInvalidValue;
   return wdtype == 0 ? pipe_dt<F32>(pro, epi, p, grid, s) : pipe_dt<BF16>(pro, epi, p, grid, s);

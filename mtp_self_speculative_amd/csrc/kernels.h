@@ -21,10 +21,11 @@ enum Epi : int {
 };
 constexpr bool epi_is_argmax(int e) { return e == EPI_ARGMAX || e == EPI_SAMPLE; }
 
-// EPI_SAMPLE: the noise of vocabulary row r for batch row b comes from the stream
+// EPI_SAMPLE: the key of vocabulary row r is y * inv_temp + G; the Gumbel noise G of
+// batch row b comes from the stream
 // (seed seeds[b], offset, purpose draft, row `row`).
 struct SampleParams {
-  float temp;              // > 0
+  float inv_temp;          // 1 / temperature (> 0)
   const uint64_t* seeds;   // [B] device
   uint64_t offset;
   int row;                 // draft step (0-based)
@@ -211,8 +212,8 @@ struct VSampleParams {
   const float* tlog;  // [B, K+1, V] target logits
   const float* dlog;  // [B, K, V] draft logits (row j produced draft j)
   const int* draft;   // [B, K]
-  int K, V, nchunk;   // nchunk = vs_chunks(V)
-  float temp;
+  int K, V, nchunk;   // nchunk = vs_chunks(V): partial slots per row (the most any launch uses)
+  float inv_temp;     // 1 / temperature
   const uint64_t* seeds;     // [B]
   uint64_t offset;
   unsigned long long* part;  // [B, 2K+1, nchunk] (max, sum) pairs, left zero

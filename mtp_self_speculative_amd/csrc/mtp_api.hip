@@ -701,9 +701,10 @@ mtp_status mtp_draft_sample(mtp_handle* h, const void* hidden, const int32_t* la
                             const uint64_t* seeds, uint64_t offset, int32_t* draft_tokens,
                             float* draft_logits, void* stream) {
   if (!h) return MTP_ERR_INVALID_ARG;
-  if (!(temperature > 0.f) || !std::isfinite(temperature)) return MTP_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(1.0f / temperature)) return MTP_ERR_INVALID_ARG;
+  if (!std::isfinite(temperature)) return MTP_ERR_INVALID_ARG;
   if (K > 0 && (!seeds || !draft_logits || !aligned(draft_logits, 4))) return MTP_ERR_INVALID_ARG;
-  SampleParams smp{temperature, seeds, offset, 0};
+  SampleParams smp{1.0f / temperature, seeds, offset, 0};
   const int V = h->cfg.vocab;
   return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, nullptr, nullptr,
                     LmOut{draft_logits, (size_t)V, K * V, &smp}, stream);
@@ -746,7 +747,8 @@ mtp_status mtp_verify_sample(mtp_handle* h, const float* target_logits, const fl
                              const uint64_t* seeds, uint64_t offset, int32_t* accepted_len,
                              int32_t* next_token, void* stream) {
   if (!h || !target_logits || !seeds || !accepted_len || !next_token) return MTP_ERR_INVALID_ARG;
-  if (!(temperature > 0.f) || !std::isfinite(temperature)) return MTP_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.0f / temperature))
+    return MTP_ERR_INVALID_ARG;
   if (K < 0 || B < 1) return MTP_ERR_SHAPE;
   if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
   if (K > 0 && (!draft_tokens || !draft_logits)) return MTP_ERR_INVALID_ARG;
@@ -757,7 +759,7 @@ mtp_status mtp_verify_sample(mtp_handle* h, const float* target_logits, const fl
   p.K = K;
   p.V = h->cfg.vocab;
   p.nchunk = vs_chunks(p.V);
-  p.temp = temperature;
+  p.inv_temp = 1.0f / temperature;
   p.seeds = seeds;
   p.offset = offset;
   p.part = h->at<unsigned long long>(h->L.vs_part);

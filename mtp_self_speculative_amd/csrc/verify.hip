@@ -131,94 +131,131 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_vec_kernel(VerifyParams
 // ---------------------------------------------------------------- sampling verification
 // Speculative sampling at temperature T, in two launches.
 // (1) grid (chunk, row, sequence) over the K+1 target rows and the K draft rows: each
-//     workgroup reduces its chunk of x / T to the pair (max m, sum of exp(x/T - m)) and
-//     publishes it with a returning atomic exchange. The last workgroup of a sequence
-//     merges every row's pairs in chunk order into a log-sum-exp, then runs the
-//     acceptance tests in order: draft d_{j+1} is accepted iff
-//     log U_j < (t_j[d]/T - lse_t[j]) - (z_j[d]/T - lse_z[j]), i.e. U < p/q; it writes the
-//     accepted length a and the two log-sum-exps of row a.
+//     workgroup reduces its chunk to the pair (max m, sum of 2^(y - m)) of y = x log2(e) / T
+//     (base 2, so that each entry costs one hardware exp2) and publishes it with a
+//     returning atomic exchange. The last workgroup of a sequence
+//     merges each row's pairs (one wave per row, lanes over chunks, then a fixed butterfly
+//     over the wave) into a log-sum-exp. Wave 0 then evaluates the acceptance tests of up
+//     to 64 drafts at once, draft d_{j+1} passing iff
+//     log U_j < (t_j[d]/T - lse_t[j]) - (z_j[d]/T - lse_z[j]), i.e. U < p/q; the first
+//     failing lane (a ballot) gives the accepted length a. It writes a and the two
+//     log-sum-exps of row a.
 // (2) grid (chunk, sequence): Gumbel-max draws over row a, one of log(p_a - q_a) where
 //     positive (a < K: the residual distribution) and one of t_a / T (the target's own
 //     distribution: the bonus token when a = K, the fallback when rounding left no
-//     positive residual). Each lane takes four consecutive entries and one random block.
+//     positive residual). Each lane takes groups of four consecutive entries, one random
+//     block per group.
+// Rows whose length is a multiple of 4 (16-byte aligned) are read with 16-byte loads.
 constexpr int kVsThreads = 256;
-constexpr int kVsPer = 8;
-constexpr int kVsChunk = kVsThreads * kVsPer;  // logits per workgroup and row
+constexpr int kVsPer = 8;                                  // loads in flight per lane
+constexpr int kVsChunkScalar = kVsThreads * kVsPer;        // logits per statistics workgroup
+constexpr int kVsChunkVec = kVsThreads * kVsPer * 4;
+constexpr int kVsResChunk = kVsThreads * 8;                // logits per resampling workgroup
 
-int vs_chunks(int V) { return (V + kVsChunk - 1) / kVsChunk; }
+int vs_chunks(int V) { return (V + kVsChunkScalar - 1) / kVsChunkScalar; }
 
 __device__ __forceinline__ unsigned long long pack_pair(float m, float sum) {
   return ((unsigned long long)__float_as_uint(m) << 32) | (unsigned long long)__float_as_uint(sum);
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kVsThreads) void vs_stats_kernel(VSampleParams p) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
   __shared__ float red[kVsThreads / kWave];
   __shared__ float lse_s[2 * kVsMaxK + 1];
   __shared__ int flag;
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = p.K, V = p.V, R = 2 * K + 1;
   const float* row = r <= K ? p.tlog + ((long)b * (K + 1) + r) * V
                             : p.dlog + ((long)b * K + (r - K - 1)) * V;
-  const int lo = c * kVsChunk;
-  float x[kVsPer];
+  constexpr int N = VEC ? 4 * kVsPer : kVsPer;
+  const float sc2 = kLog2e * p.inv_temp;
+  float x[N];
+  if constexpr (VEC) {
+    const f32x4v* row4 = reinterpret_cast<const f32x4v*>(row);
+    const int lo = c * (kVsChunkVec / 4);
+#pragma unroll
+    for (int k = 0; k < kVsPer; ++k) {
+      const int i4 = lo + (int)threadIdx.x + k * kVsThreads;
+      f32x4v v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (i4 < V / 4) v = __builtin_nontemporal_load(row4 + i4) * sc2;
+      x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+    }
+  } else {
+    const int lo = c * kVsChunkScalar;
+#pragma unroll
+    for (int k = 0; k < kVsPer; ++k) {
+      const int idx = lo + (int)threadIdx.x + k * kVsThreads;
+      x[k] = idx < V ? __builtin_nontemporal_load(row + idx) * sc2 : -INFINITY;
+    }
+  }
   float m = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kVsPer; ++k) {
-    const int idx = lo + (int)threadIdx.x + k * kVsThreads;
-    x[k] = idx < V ? __builtin_nontemporal_load(row + idx) / p.temp : -INFINITY;
-    m = fmaxf(m, x[k]);
-  }
+  for (int k = 0; k < N; ++k) m = fmaxf(m, x[k]);
   m = block_max(m, red);  // finite: every chunk holds at least one entry
   float sum = 0.f;
 #pragma unroll
-  for (int k = 0; k < kVsPer; ++k) sum += expf(x[k] - m);
+  for (int k = 0; k < N; ++k) sum += hw_exp2(x[k] - m);
   sum = block_sum(sum, red);
   if (threadIdx.x == 0)
     keep_alive(__hip_atomic_exchange(p.part + ((long)b * R + r) * p.nchunk + c, pack_pair(m, sum),
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   if (!last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) return;
-  // Merge each row's pairs in chunk order (running max, rescaled sum).
-  for (int q = threadIdx.x; q < R; q += kVsThreads) {
+  // Merge each row's pairs: lane-local running (max, rescaled sum), then the wave.
+  for (int q = wave; q < R; q += kVsThreads / kWave) {
     unsigned long long* pp = p.part + ((long)b * R + q) * p.nchunk;
     float M = -INFINITY, S = 0.f;
-    for (int cc = 0; cc < p.nchunk; ++cc) {
+    for (int cc = lane; cc < p.nchunk; cc += kWave) {
       const unsigned long long v = take_key(pp + cc);
       const float mc = __uint_as_float((uint32_t)(v >> 32));
       const float sc = __uint_as_float((uint32_t)v);
       if (mc > M) {
-        S = S * expf(M - mc) + sc;
+        S = S * hw_exp2(M - mc) + sc;
         M = mc;
       } else {
-        S += sc * expf(mc - M);
+        S += sc * hw_exp2(mc - M);
       }
     }
-    lse_s[q] = M + logf(S);
+    const float Mw = wave_max(M);
+    const float Sw = wave_sum(S * hw_exp2(M - Mw));
+    // sum_v e^(x_v / T) = 2^Mw * Sw, so its natural log is Mw ln 2 + ln Sw
+    if (lane == 0) lse_s[q] = Mw * kLn2 + logf(Sw);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int a = 0;
-    for (int j = 0; j < K; ++j) {
+  if (wave != 0) return;
+  int a = K;
+  for (int base = 0; base < K; base += kWave) {
+    const int j = base + lane;
+    bool rej = false;
+    if (j < K) {
       const int d = p.draft[(long)b * K + j];
       if (d < 0 || d >= V) {  // an invalid draft token is rejected
         set_error(p.err, 1u);
-        break;
-      }
-      const float lp = p.tlog[((long)b * (K + 1) + j) * V + d] / p.temp - lse_s[j];
-      const float lq = p.dlog[((long)b * K + j) * V + d] / p.temp - lse_s[K + 1 + j];
-      const Philox4 rb = rng_block(p.seeds[b], p.offset, RNG_ACCEPT, (uint64_t)j, 0ull);
-      if (logf(rng_uniform(rb.w[0])) < lp - lq) {
-        ++a;
+        rej = true;
       } else {
-        break;
+        const float lp = p.tlog[((long)b * (K + 1) + j) * V + d] * p.inv_temp - lse_s[j];
+        const float lq = p.dlog[((long)b * K + j) * V + d] * p.inv_temp - lse_s[K + 1 + j];
+        const Philox4 rb = rng_block(p.seeds[b], p.offset, RNG_ACCEPT, (uint64_t)j, 0ull);
+        rej = !(logf(rng_uniform(rb.w[0])) < lp - lq);
       }
     }
+    const unsigned long long m = __ballot(rej);
+    if (m) {
+      a = base + __ffsll(m) - 1;
+      break;
+    }
+  }
+  if (lane == 0) {
     p.accepted[b] = a;
     p.lse[2 * b] = lse_s[a];
     p.lse[2 * b + 1] = a < K ? lse_s[K + 1 + a] : 0.f;
   }
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
   __shared__ unsigned long long kred[2][kVsThreads / kWave];
   __shared__ int flag;
   const int c = blockIdx.x, b = blockIdx.y;
@@ -233,22 +270,38 @@ __global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p
   const uint64_t seed = p.seeds[b];
   unsigned long long kr = 0ull, kp = 0ull;
 #pragma unroll
-  for (int g = 0; g < kVsPer / 4; ++g) {
-    const int v0 = c * kVsChunk + (g * kVsThreads + (int)threadIdx.x) * 4;
+  for (int g = 0; g < kVsResChunk / (4 * kVsThreads); ++g) {
+    const int v0 = c * kVsResChunk + (g * kVsThreads + (int)threadIdx.x) * 4;
     if (v0 >= V) continue;
+    float tv[4], zv[4];
+    if constexpr (VEC) {  // V % 4 == 0: the whole group is in range
+      const f32x4v t4 = *reinterpret_cast<const f32x4v*>(trow + v0);
+      tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
+      if (resid) {
+        const f32x4v z4 = *reinterpret_cast<const f32x4v*>(drow + v0);
+        zv[0] = z4.x; zv[1] = z4.y; zv[2] = z4.z; zv[3] = z4.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = v0 + e < V ? v0 + e : V - 1;
+        tv[e] = trow[v];
+        if (resid) zv[e] = drow[v];
+      }
+    }
     const Philox4 rb = rng_block(seed, p.offset, RNG_RESAMPLE, (uint64_t)a, (uint64_t)(v0 >> 2));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = v0 + e;
       if (v >= V) break;
-      const float tv = trow[v] / p.temp;
+      const float t = tv[e] * p.inv_temp;
       const float gv = gumbel_of(rb.w[e]);
-      const unsigned long long k1 = pack_key(tv + gv, (uint32_t)v);
+      const unsigned long long k1 = pack_key(t + gv, (uint32_t)v);
       kp = k1 > kp ? k1 : kp;
       if (resid) {
-        const float rv = expf(tv - lt) - expf(drow[v] / p.temp - lz);
+        const float rv = hw_exp2((t - lt) * kLog2e) - hw_exp2((zv[e] * p.inv_temp - lz) * kLog2e);
         if (rv > 0.f) {
-          const unsigned long long k2 = pack_key(logf(rv) + gv, (uint32_t)v);
+          const unsigned long long k2 = pack_key(hw_log2(rv) * kLn2 + gv, (uint32_t)v);
           kr = k2 > kr ? k2 : kr;
         }
       }
@@ -277,13 +330,27 @@ __global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p
 
 hipError_t launch_verify_sample(const VSampleParams& p, int B, hipStream_t s) {
   if (p.V < 1 || p.K < 0 || p.K > kVsMaxK || B < 1 || p.nchunk != vs_chunks(p.V) ||
-      !(p.temp > 0.f) || !p.seeds || !p.tlog || (p.K > 0 && (!p.dlog || !p.draft)) || !p.part ||
+      !(p.inv_temp > 0.f) || !p.seeds || !p.tlog || (p.K > 0 && (!p.dlog || !p.draft)) || !p.part ||
       !p.lse || !p.keys || !p.counters || !p.accepted || !p.next || !p.err)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(vs_stats_kernel, dim3(p.nchunk, 2 * p.K + 1, B), dim3(kVsThreads), 0, s, p);
+  const bool vec = p.V % 4 == 0 && ((uintptr_t)p.tlog & 15) == 0 &&
+                   (p.K == 0 || ((uintptr_t)p.dlog & 15) == 0);
+  VSampleParams q = p;
+  const int nres = (p.V + kVsResChunk - 1) / kVsResChunk;
+  if (vec) {
+    q.nchunk = (p.V + kVsChunkVec - 1) / kVsChunkVec;
+    hipLaunchKernelGGL(vs_stats_kernel<true>, dim3(q.nchunk, 2 * p.K + 1, B), dim3(kVsThreads), 0,
+                       s, q);
+  } else {
+    hipLaunchKernelGGL(vs_stats_kernel<false>, dim3(q.nchunk, 2 * p.K + 1, B), dim3(kVsThreads),
+                       0, s, q);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_resample_kernel, dim3(p.nchunk, B), dim3(kVsThreads), 0, s, p);
+  if (vec)
+    hipLaunchKernelGGL(vs_resample_kernel<true>, dim3(nres, B), dim3(kVsThreads), 0, s, q);
+  else
+    hipLaunchKernelGGL(vs_resample_kernel<false>, dim3(nres, B), dim3(kVsThreads), 0, s, q);
   return hipGetLastError();
 }
 

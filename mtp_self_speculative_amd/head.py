@@ -100,13 +100,18 @@ class MtpHead:
         return out, hid, mx, lg
 
     def draft_sample(self, hidden: torch.Tensor, last_tokens: torch.Tensor, cache: MtpCache,
-                     K: int, temperature: float, seeds: torch.Tensor, offset: int, stream=None):
+                     K: int, temperature: float, seeds: torch.Tensor, offset: int,
+                     out: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                     stream=None):
         """K draft steps sampling at `temperature`; seeds [B] int64 on the device.
         Returns (draft tokens [B, K] int32, draft logits [B, K, V] fp32)."""
         B = hidden.shape[0]
         dev = hidden.device
-        out = torch.empty((B, K), dtype=torch.int32, device=dev)
-        lg = torch.empty((B, K, self.vocab), dtype=torch.float32, device=dev)
+        if out is None:
+            out = torch.empty((B, K), dtype=torch.int32, device=dev)
+        lg = logits
+        if lg is None:
+            lg = torch.empty((B, K, self.vocab), dtype=torch.float32, device=dev)
         L.mtp_draft_sample(self.handle, hidden.data_ptr(), last_tokens.data_ptr(), cache.kv, B, K,
                            float(temperature), seeds.data_ptr(), int(offset), out.data_ptr(),
                            lg.data_ptr(), _stream(stream))
