@@ -73,12 +73,15 @@ int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
   return (int)(g < 1 ? 1 : g);
 }
 
-template <int NB, int EPI>
-__global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
+// OCC: waves per SIMD the register allocation must allow (the sampling epilogue at one or
+// two tiles is held to two, the occupancy its grid of two workgroups per CU needs).
+template <int NB, int EPI, int OCC>
+__global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   constexpr int BP = 16 * NB;
   constexpr int XPASS = BP / 8;  // 16-byte input loads per thread, plane and stage
   extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][kMmLdsRow]
   __shared__ unsigned long long kred[kMmWaves][BP];
+  __shared__ uint64_t seed_s[EPI == EPI_SAMPLE ? BP : 1];  // random-stream seeds, read once
   __shared__ int flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -209,10 +212,12 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
           // of one random block as their Gumbel noise.
           float noise[4] = {0.f, 0.f, 0.f, 0.f};
           if constexpr (EPI == EPI_SAMPLE) {
-            const Philox4 rb = rng_block(b < p.B ? p.smp.seeds[b] : 0ull, p.smp.offset,
-                                         RNG_DRAFT, (uint64_t)p.smp.row, (uint64_t)(r0 >> 2));
+            const Philox4 rb = rng_block(seed_s[b], p.smp.offset, RNG_DRAFT, (uint64_t)p.smp.row,
+                                         (uint64_t)(r0 >> 2));
 #pragma unroll
             for (int i = 0; i < 4; ++i) noise[i] = gumbel_of(rb.w[i]);
+            // one random block at a time: interleaving them would exceed the register budget
+            __builtin_amdgcn_sched_barrier(0);
           }
           unsigned long long k = 0ull;
 #pragma unroll
@@ -245,6 +250,9 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(MmParams p) {
     __syncthreads();
   };
 
+  if constexpr (EPI == EPI_SAMPLE) {
+    if (tid < BP) seed_s[tid] = tid < p.B ? p.smp.seeds[tid] : 0ull;  // visible after the first barrier
+  }
   xload(0);
   wload(A, 0);
   wload(Bf, 1);
@@ -286,11 +294,12 @@ template <int NB>
 static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   const size_t lds = mm_lds_bytes(NB);
   if (epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX>), dim3(grid), dim3(kMmThreads), lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1>), dim3(grid), dim3(kMmThreads), lds, s, p);
   else if (epi == EPI_SAMPLE)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE>), dim3(grid), dim3(kMmThreads), lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1>), dim3(grid), dim3(kMmThreads),
+                       lds, s, p);
   else
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE>), dim3(grid), dim3(kMmThreads), lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1>), dim3(grid), dim3(kMmThreads), lds, s, p);
   return hipGetLastError();
 }
 

@@ -211,10 +211,12 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
     for (int i = 0; i < NB; ++i) acc[q][i] = 0.f;
   unsigned long long best[NB];
   float gum[NB];
+  uint64_t seed[NB];  // EPI_SAMPLE: the sequences' random-stream seeds, read once
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     best[i] = 0ull;
     gum[i] = 0.f;
+    seed[i] = (EPI == EPI_SAMPLE && i < B) ? p.smp.seeds[i] : 0ull;
   }
 
   auto consume = [&](u32x4 (&buf)[P][CH], int it) {
@@ -257,8 +259,8 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
           const int rl = gw + (j + lane) * nw;  // rows past the end are drawn, never used
 #pragma unroll
           for (int i = 0; i < NB; ++i) {
-            const Philox4 rb = rng_block(i < B ? p.smp.seeds[i] : 0ull, p.smp.offset, RNG_DRAFT,
-                                         (uint64_t)p.smp.row, (uint64_t)(rl >> 2));
+            const Philox4 rb = rng_block(seed[i], p.smp.offset, RNG_DRAFT, (uint64_t)p.smp.row,
+                                         (uint64_t)(rl >> 2));
             gum[i] = gumbel_of(philox_word(rb, rl & 3));
           }
         }

@@ -196,12 +196,19 @@ struct RedParams {
 int red_max_cols();  // largest n the norm modes accept
 hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s);
 
+// Per-sequence completion counters and keys of the verification kernels start on their
+// own 256-byte line, so that the atomics of different sequences do not queue on one line.
+constexpr int kSeqLineU32 = 64;  // counter of sequence b at counters[b * kSeqLineU32]
+constexpr int kSeqLineU64 = 32;  // key stride unit (u64)
+
 struct VerifyParams {
   const float* logits;  // [B, K+1, V]
   const int* draft;     // [B, K]
-  int K, V, chunk, nchunk;
-  unsigned long long* keys;  // [B * (K+1)] zero on entry/exit
-  unsigned* counters;        // [B]
+  int K, V;
+  int seg;                   // set by launch_verify: load units per workgroup
+  unsigned long long* keys;  // row j of sequence b at keys[b * kstride + j], zero on entry/exit
+  int kstride;               // >= K + 1, a multiple of kSeqLineU64
+  unsigned* counters;        // [B * kSeqLineU32] zero on entry/exit
   int* accepted;
   int* next;
 };
@@ -213,13 +220,14 @@ struct VSampleParams {
   const float* dlog;  // [B, K, V] draft logits (row j produced draft j)
   const int* draft;   // [B, K]
   int K, V, nchunk;   // nchunk = vs_chunks(V): partial slots per row (the most any launch uses)
+  int seg;            // set by launch_verify_sample
   float inv_temp;     // 1 / temperature
   const uint64_t* seeds;     // [B]
   uint64_t offset;
   unsigned long long* part;  // [B, 2K+1, nchunk] (max, sum) pairs, left zero
   float* lse;                // [B, 2] log-sum-exps of the target / draft row a
-  unsigned long long* keys;  // [B, 2] zero on entry/exit
-  unsigned* counters;        // [B] zero on entry/exit
+  unsigned long long* keys;  // [B * kSeqLineU64], two used per sequence, zero on entry/exit
+  unsigned* counters;        // [B * kSeqLineU32] zero on entry/exit
   int* accepted;
   int* next;
   unsigned* err;

@@ -22,7 +22,6 @@ constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
 constexpr int kMaxK = 100;
 static_assert(kMaxK <= kVsMaxK, "sampling verification holds 2K+1 log-sum-exps in LDS");
 constexpr int kMaxGroupHeads = 8;
-constexpr int kVerifyChunk = 2048;
 constexpr size_t kGemvLdsBudget = 32 * 1024;
 constexpr int kGemvMaxGrid = 2048;
 
@@ -40,6 +39,7 @@ struct Layout {
   int cu_rows, cu_ld;
   // sampling verification: (max, sum) pairs per (sequence, row, chunk), row a's lse, keys
   size_t vs_part, vs_lse, vs_keys;
+  int v_kstride;  // keys per sequence in v_keys
   size_t total;
 };
 
@@ -88,8 +88,9 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   L.part_ml = take(B * nq * kMaxSplits * 2 * 4);
   L.lm_keys = take(B * 8);
   L.lm_cnt = take(4);
-  L.v_keys = take(B * (size_t)(max_k + 1) * 8);
-  L.v_cnt = take(B * 4);
+  L.v_kstride = (max_k + 1 + kSeqLineU64 - 1) / kSeqLineU64 * kSeqLineU64;
+  L.v_keys = take(B * (size_t)L.v_kstride * 8);
+  L.v_cnt = take(B * kSeqLineU32 * 4);
   L.err = take(4);
   L.dummy = take(kDummyBytes);
   L.ldq = 0;
@@ -153,7 +154,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   }
   L.vs_part = take((size_t)max_batch * (2 * max_k + 1) * vs_chunks(c.vocab) * 8);
   L.vs_lse = take((size_t)max_batch * 2 * 4);
-  L.vs_keys = take((size_t)max_batch * 2 * 8);
+  L.vs_keys = take((size_t)max_batch * kSeqLineU64 * 8);
   L.total = off;
   return L;
 }
@@ -731,9 +732,8 @@ mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* 
   p.draft = draft_tokens;
   p.K = K;
   p.V = h->cfg.vocab;
-  p.chunk = kVerifyChunk;
-  p.nchunk = (p.V + kVerifyChunk - 1) / kVerifyChunk;
   p.keys = h->at<unsigned long long>(h->L.v_keys);
+  p.kstride = h->L.v_kstride;
   p.counters = h->at<unsigned>(h->L.v_cnt);
   p.accepted = accepted_len;
   p.next = next_token;

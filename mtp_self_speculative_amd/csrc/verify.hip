@@ -1,12 +1,15 @@
-// Greedy verification and MTP-cache rollback.
+// Greedy verification, sampling verification and MTP-cache rollback.
 //
-// Verify: grid (vocabulary chunk, row j = 0..K, sequence b). Each workgroup reduces its
-// chunk of target-logit row (b, j) to a packed (value, index) key — larger value wins,
-// lowest index on ties — and folds it into a per-row key with an atomic max, which is
-// order independent and hence deterministic. The last workgroup of sequence b turns the
-// K+1 keys into the target's tokens, scans the longest prefix of drafts that match them
-// and writes accepted_len and the bonus token.
-// Rows of a length divisible by 4 take a variant with 16-byte loads and larger chunks.
+// Greedy verify: grid (segment, row j = 0..K, sequence b). Each workgroup walks its
+// segment of target-logit row (b, j) in stages of 8 loads per lane and reduces it to a
+// packed (value, index) key — larger value wins, lowest index on ties — which it folds
+// into the row's key with an atomic max (order independent, hence deterministic). The
+// last workgroup of sequence b turns the K+1 keys into the target's tokens, scans the
+// longest prefix of drafts that match them and writes accepted_len and the bonus token.
+// The segment count is chosen per launch so that the grid holds about four workgroups per
+// CU: enough loads in flight to stream HBM, and few enough completion atomics per
+// sequence. Each sequence's counter and keys sit on their own 256-byte line.
+// Rows whose length is a multiple of 4 (16-byte aligned) are read with 16-byte loads.
 // Sampling verification (temperature > 0) is described above its kernels below.
 // Rollback: one lane per sequence moves len/pos to the committed prefix.
 #include "common.h"
@@ -14,42 +17,85 @@
 
 namespace mtp {
 
-constexpr int kVerifyThreads = 256;
-constexpr int kVerifyPer = 8;  // logits per lane; a workgroup covers kVerifyThreads * kVerifyPer
+constexpr int kVThreads = 256;
+constexpr int kVPer = 8;                      // loads in flight per lane and stage
+constexpr int kVStage = kVThreads * kVPer;    // load units (floats or float4s) per stage
+constexpr int kTargetGroups = 1024;           // about four workgroups per CU
 
-__global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) {
-  __shared__ unsigned long long kred[kVerifyThreads / kWave];
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Segments of `units` load units for `rows` rows: about kTargetGroups workgroups in all,
+// at most one per stage of the row.
+static void segments(long rows, int units, int* nseg, int* seg) {
+  const int max_seg = (units + kVStage - 1) / kVStage;
+  long s = (kTargetGroups + rows - 1) / rows;
+  if (s > max_seg) s = max_seg;
+  if (s < 1) s = 1;
+  *seg = (int)((units + s - 1) / s);
+  *nseg = (units + *seg - 1) / *seg;
+}
+
+// Loads kVPer units of `row` starting at unit i0 + threadIdx.x with stride kVThreads,
+// indexes clamped to hi - 1 (a repeated unit only repeats a key or is masked by the
+// caller); VEC units are float4 groups.
+template <bool VEC>
+__device__ __forceinline__ void load_stage(const float* row, int i0, int hi, int* idx,
+                                           f32x4v* v) {
+#pragma unroll
+  for (int k = 0; k < kVPer; ++k) {
+    idx[k] = min(i0 + (int)threadIdx.x + k * kVThreads, hi - 1);
+    if constexpr (VEC) {
+      v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(row) + idx[k]);
+    } else {
+      const float x = __builtin_nontemporal_load(row + idx[k]);
+      v[k] = f32x4v{x, x, x, x};
+    }
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
+  __shared__ unsigned long long kred[kVThreads / kWave];
   __shared__ int flag;
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* row = p.logits + ((long)b * (p.K + 1) + j) * p.V;
-  const int lo = c * p.chunk, hi = min(lo + p.chunk, p.V);
-  // All loads are issued before any is used; indexes past the row end are clamped to its
-  // last element, whose key then only repeats.
-  int idx[kVerifyPer];
-  float v[kVerifyPer];
-#pragma unroll
-  for (int k = 0; k < kVerifyPer; ++k) {
-    idx[k] = min(lo + (int)threadIdx.x + k * kVerifyThreads, hi - 1);
-    v[k] = __builtin_nontemporal_load(row + idx[k]);
-  }
+  const int units = VEC ? p.V / 4 : p.V;
+  const int lo = c * p.seg, hi = min(lo + p.seg, units);
   unsigned long long best = 0ull;
+  for (int i0 = lo; i0 < hi; i0 += kVStage) {
+    int idx[kVPer];
+    f32x4v v[kVPer];
+    load_stage<VEC>(row, i0, hi, idx, v);
 #pragma unroll
-  for (int k = 0; k < kVerifyPer; ++k) {
-    const unsigned long long key = pack_key(v[k], (uint32_t)idx[k]);
-    best = key > best ? key : best;
+    for (int k = 0; k < kVPer; ++k) {
+      unsigned long long key;
+      if constexpr (VEC) {
+        const uint32_t e0 = (uint32_t)idx[k] * 4;
+        key = pack_key(v[k].x, e0);
+        unsigned long long t = pack_key(v[k].y, e0 + 1);
+        key = t > key ? t : key;
+        t = pack_key(v[k].z, e0 + 2);
+        key = t > key ? t : key;
+        t = pack_key(v[k].w, e0 + 3);
+        key = t > key ? t : key;
+      } else {
+        key = pack_key(v[k].x, (uint32_t)idx[k]);
+      }
+      best = key > best ? key : best;
+    }
   }
   best = wave_max_u64(best);
   if (lane == 0) kred[wave] = best;
   __syncthreads();
+  unsigned long long* kb = p.keys + (long)b * p.kstride;
   if (threadIdx.x == 0) {
-    for (int w = 1; w < kVerifyThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
-    if (best) keep_alive(atomic_max_key(p.keys + (long)b * (p.K + 1) + j, best));
+    for (int w = 1; w < kVThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
+    if (best) keep_alive(atomic_max_key(kb + j, best));
   }
-  if (last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) {
+  if (last_to_arrive(p.counters + (long)b * kSeqLineU32, gridDim.x * gridDim.y, &flag)) {
     // Take (and reset) the K+1 row keys and scan for the first mismatch.
     if (threadIdx.x == 0) {
-      unsigned long long* kb = p.keys + (long)b * (p.K + 1);
       int a = 0, next = -1;
       for (int q = 0; q <= p.K; ++q) {
         const int t = (int)key_index(take_key(kb + q));
@@ -67,101 +113,48 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(VerifyParams p) 
   }
 }
 
-// Same reduction for rows whose length is a multiple of 4 (16-byte aligned rows): each
-// lane keeps kVerifyVecPer float4 loads in flight, a workgroup covers kVerifyVecChunk
-// logits, so far fewer workgroups (and same-address atomics) are needed per row.
-constexpr int kVerifyVecPer = 8;
-constexpr int kVerifyVecChunk = kVerifyThreads * kVerifyVecPer * 4;
-
-__global__ __launch_bounds__(kVerifyThreads) void verify_vec_kernel(VerifyParams p) {
-  __shared__ unsigned long long kred[kVerifyThreads / kWave];
-  __shared__ int flag;
-  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  typedef float f32x4v __attribute__((ext_vector_type(4)));
-  const f32x4v* row = reinterpret_cast<const f32x4v*>(p.logits + ((long)b * (p.K + 1) + j) * p.V);
-  const int lo = c * (kVerifyVecChunk / 4), hi = min(lo + kVerifyVecChunk / 4, p.V / 4);
-  int idx[kVerifyVecPer];
-  f32x4v v[kVerifyVecPer];
-#pragma unroll
-  for (int k = 0; k < kVerifyVecPer; ++k) {
-    idx[k] = min(lo + (int)threadIdx.x + k * kVerifyThreads, hi - 1);
-    v[k] = __builtin_nontemporal_load(row + idx[k]);
-  }
-  unsigned long long best = 0ull;
-#pragma unroll
-  for (int k = 0; k < kVerifyVecPer; ++k) {
-    const uint32_t i0 = (uint32_t)idx[k] * 4;
-    unsigned long long key = pack_key(v[k].x, i0);
-    unsigned long long t = pack_key(v[k].y, i0 + 1);
-    key = t > key ? t : key;
-    t = pack_key(v[k].z, i0 + 2);
-    key = t > key ? t : key;
-    t = pack_key(v[k].w, i0 + 3);
-    key = t > key ? t : key;
-    best = key > best ? key : best;
-  }
-  best = wave_max_u64(best);
-  if (lane == 0) kred[wave] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kVerifyThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
-    if (best) keep_alive(atomic_max_key(p.keys + (long)b * (p.K + 1) + j, best));
-  }
-  if (last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) {
-    if (threadIdx.x == 0) {
-      unsigned long long* kb = p.keys + (long)b * (p.K + 1);
-      int a = 0, next = -1;
-      for (int q = 0; q <= p.K; ++q) {
-        const int t = (int)key_index(take_key(kb + q));
-        if (next < 0) {
-          if (q < p.K && p.draft[(long)b * p.K + q] == t) {
-            ++a;
-          } else {
-            next = t;
-          }
-        }
-      }
-      p.accepted[b] = a;
-      p.next[b] = next;
-    }
-  }
+hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s) {
+  if (p.V < 1 || p.K < 0 || B < 1 || !p.logits || !p.keys || !p.counters || !p.accepted ||
+      !p.next || (p.K > 0 && !p.draft) || p.kstride < p.K + 1)
+    return hipErrorInvalidValue;
+  const bool vec = p.V % 4 == 0 && ((uintptr_t)p.logits & 15) == 0;
+  VerifyParams q = p;
+  int nseg;
+  segments((long)B * (p.K + 1), vec ? p.V / 4 : p.V, &nseg, &q.seg);
+  if (vec)
+    hipLaunchKernelGGL(verify_kernel<true>, dim3(nseg, p.K + 1, B), dim3(kVThreads), 0, s, q);
+  else
+    hipLaunchKernelGGL(verify_kernel<false>, dim3(nseg, p.K + 1, B), dim3(kVThreads), 0, s, q);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- sampling verification
 // Speculative sampling at temperature T, in two launches.
-// (1) grid (chunk, row, sequence) over the K+1 target rows and the K draft rows: each
-//     workgroup reduces its chunk to the pair (max m, sum of 2^(y - m)) of y = x log2(e) / T
-//     (base 2, so that each entry costs one hardware exp2) and publishes it with a
-//     returning atomic exchange. The last workgroup of a sequence
-//     merges each row's pairs (one wave per row, lanes over chunks, then a fixed butterfly
-//     over the wave) into a log-sum-exp. Wave 0 then evaluates the acceptance tests of up
-//     to 64 drafts at once, draft d_{j+1} passing iff
-//     log U_j < (t_j[d]/T - lse_t[j]) - (z_j[d]/T - lse_z[j]), i.e. U < p/q; the first
-//     failing lane (a ballot) gives the accepted length a. It writes a and the two
+// (1) grid (segment, row, sequence) over the K+1 target rows and the K draft rows: each
+//     workgroup reduces its segment to the pair (max m, sum of 2^(y - m)) of
+//     y = x log2(e) / T (base 2, so that each entry costs one hardware exp2), keeping a
+//     running pair per lane across stages, and publishes it with a returning atomic
+//     exchange. The last workgroup of a sequence merges each row's pairs (one wave per
+//     row, lanes over segments, then a fixed butterfly over the wave) into a log-sum-exp.
+//     Wave 0 then evaluates the acceptance tests of up to 64 drafts at once, draft d_{j+1}
+//     passing iff log U_j < (t_j[d]/T - lse_t[j]) - (z_j[d]/T - lse_z[j]), i.e. U < p/q; the
+//     first failing lane (a ballot) gives the accepted length a. It writes a and the two
 //     log-sum-exps of row a.
-// (2) grid (chunk, sequence): Gumbel-max draws over row a, one of log(p_a - q_a) where
+// (2) grid (segment, sequence): Gumbel-max draws over row a, one of log(p_a - q_a) where
 //     positive (a < K: the residual distribution) and one of t_a / T (the target's own
 //     distribution: the bonus token when a = K, the fallback when rounding left no
 //     positive residual). Each lane takes groups of four consecutive entries, one random
 //     block per group.
-// Rows whose length is a multiple of 4 (16-byte aligned) are read with 16-byte loads.
-constexpr int kVsThreads = 256;
-constexpr int kVsPer = 8;                                  // loads in flight per lane
-constexpr int kVsChunkScalar = kVsThreads * kVsPer;        // logits per statistics workgroup
-constexpr int kVsChunkVec = kVsThreads * kVsPer * 4;
-constexpr int kVsResChunk = kVsThreads * 8;                // logits per resampling workgroup
 
-int vs_chunks(int V) { return (V + kVsChunkScalar - 1) / kVsChunkScalar; }
+int vs_chunks(int V) { return (V + kVStage - 1) / kVStage; }
 
 __device__ __forceinline__ unsigned long long pack_pair(float m, float sum) {
   return ((unsigned long long)__float_as_uint(m) << 32) | (unsigned long long)__float_as_uint(sum);
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kVsThreads) void vs_stats_kernel(VSampleParams p) {
-  typedef float f32x4v __attribute__((ext_vector_type(4)));
-  __shared__ float red[kVsThreads / kWave];
+__global__ __launch_bounds__(kVThreads) void vs_stats_kernel(VSampleParams p) {
+  __shared__ float red[kVThreads / kWave];
   __shared__ float lse_s[2 * kVsMaxK + 1];
   __shared__ int flag;
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
@@ -169,56 +162,61 @@ __global__ __launch_bounds__(kVsThreads) void vs_stats_kernel(VSampleParams p) {
   const int K = p.K, V = p.V, R = 2 * K + 1;
   const float* row = r <= K ? p.tlog + ((long)b * (K + 1) + r) * V
                             : p.dlog + ((long)b * K + (r - K - 1)) * V;
-  constexpr int N = VEC ? 4 * kVsPer : kVsPer;
+  const int units = VEC ? V / 4 : V;
+  const int lo = c * p.seg, hi = min(lo + p.seg, units);
   const float sc2 = kLog2e * p.inv_temp;
-  float x[N];
-  if constexpr (VEC) {
-    const f32x4v* row4 = reinterpret_cast<const f32x4v*>(row);
-    const int lo = c * (kVsChunkVec / 4);
+  // Running (max, sum of 2^(y - max)) of this lane; units repeated by the index clamp
+  // are masked out.
+  float m = -INFINITY, sum = 0.f;
+  for (int i0 = lo; i0 < hi; i0 += kVStage) {
+    int idx[kVPer];
+    f32x4v v[kVPer];
+    load_stage<VEC>(row, i0, hi, idx, v);
+    float y[kVPer][4];
+    float sm = m;
 #pragma unroll
-    for (int k = 0; k < kVsPer; ++k) {
-      const int i4 = lo + (int)threadIdx.x + k * kVsThreads;
-      f32x4v v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (i4 < V / 4) v = __builtin_nontemporal_load(row4 + i4) * sc2;
-      x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+    for (int k = 0; k < kVPer; ++k) {
+      const bool live = i0 + (int)threadIdx.x + k * kVThreads < hi;
+      y[k][0] = live ? v[k].x * sc2 : -INFINITY;
+      y[k][1] = live && VEC ? v[k].y * sc2 : -INFINITY;
+      y[k][2] = live && VEC ? v[k].z * sc2 : -INFINITY;
+      y[k][3] = live && VEC ? v[k].w * sc2 : -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm = fmaxf(sm, y[k][e]);
     }
-  } else {
-    const int lo = c * kVsChunkScalar;
+    if (sm > -INFINITY) {
+      sum = m > -INFINITY ? sum * hw_exp2(m - sm) : 0.f;
+      m = sm;
 #pragma unroll
-    for (int k = 0; k < kVsPer; ++k) {
-      const int idx = lo + (int)threadIdx.x + k * kVsThreads;
-      x[k] = idx < V ? __builtin_nontemporal_load(row + idx) * sc2 : -INFINITY;
+      for (int k = 0; k < kVPer; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += hw_exp2(y[k][e] - m);
     }
   }
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < N; ++k) m = fmaxf(m, x[k]);
-  m = block_max(m, red);  // finite: every chunk holds at least one entry
-  float sum = 0.f;
-#pragma unroll
-  for (int k = 0; k < N; ++k) sum += hw_exp2(x[k] - m);
-  sum = block_sum(sum, red);
+  const float M = block_max(m, red);  // finite: every segment holds at least one entry
+  const float S = block_sum(m > -INFINITY ? sum * hw_exp2(m - M) : 0.f, red);
   if (threadIdx.x == 0)
-    keep_alive(__hip_atomic_exchange(p.part + ((long)b * R + r) * p.nchunk + c, pack_pair(m, sum),
+    keep_alive(__hip_atomic_exchange(p.part + ((long)b * R + r) * p.nchunk + c, pack_pair(M, S),
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  if (!last_to_arrive(p.counters + b, gridDim.x * gridDim.y, &flag)) return;
+  if (!last_to_arrive(p.counters + (long)b * kSeqLineU32, gridDim.x * gridDim.y, &flag)) return;
   // Merge each row's pairs: lane-local running (max, rescaled sum), then the wave.
-  for (int q = wave; q < R; q += kVsThreads / kWave) {
+  const int nseg = gridDim.x;
+  for (int q = wave; q < R; q += kVThreads / kWave) {
     unsigned long long* pp = p.part + ((long)b * R + q) * p.nchunk;
-    float M = -INFINITY, S = 0.f;
-    for (int cc = lane; cc < p.nchunk; cc += kWave) {
-      const unsigned long long v = take_key(pp + cc);
-      const float mc = __uint_as_float((uint32_t)(v >> 32));
-      const float sc = __uint_as_float((uint32_t)v);
-      if (mc > M) {
-        S = S * hw_exp2(M - mc) + sc;
-        M = mc;
+    float Mq = -INFINITY, Sq = 0.f;
+    for (int cc = lane; cc < nseg; cc += kWave) {
+      const unsigned long long pv = take_key(pp + cc);
+      const float mc = __uint_as_float((uint32_t)(pv >> 32));
+      const float sc = __uint_as_float((uint32_t)pv);
+      if (mc > Mq) {
+        Sq = Sq * hw_exp2(Mq - mc) + sc;
+        Mq = mc;
       } else {
-        S += sc * hw_exp2(mc - M);
+        Sq += sc * hw_exp2(mc - Mq);
       }
     }
-    const float Mw = wave_max(M);
-    const float Sw = wave_sum(S * hw_exp2(M - Mw));
+    const float Mw = wave_max(Mq);
+    const float Sw = wave_sum(Mq > -INFINITY ? Sq * hw_exp2(Mq - Mw) : 0.f);
     // sum_v e^(x_v / T) = 2^Mw * Sw, so its natural log is Mw ln 2 + ln Sw
     if (lane == 0) lse_s[q] = Mw * kLn2 + logf(Sw);
   }
@@ -240,9 +238,9 @@ __global__ __launch_bounds__(kVsThreads) void vs_stats_kernel(VSampleParams p) {
         rej = !(logf(rng_uniform(rb.w[0])) < lp - lq);
       }
     }
-    const unsigned long long m = __ballot(rej);
-    if (m) {
-      a = base + __ffsll(m) - 1;
+    const unsigned long long msk = __ballot(rej);
+    if (msk) {
+      a = base + __ffsll(msk) - 1;
       break;
     }
   }
@@ -254,9 +252,8 @@ __global__ __launch_bounds__(kVsThreads) void vs_stats_kernel(VSampleParams p) {
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p) {
-  typedef float f32x4v __attribute__((ext_vector_type(4)));
-  __shared__ unsigned long long kred[2][kVsThreads / kWave];
+__global__ __launch_bounds__(kVThreads) void vs_resample_kernel(VSampleParams p) {
+  __shared__ unsigned long long kred[2][kVThreads / kWave];
   __shared__ int flag;
   const int c = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -268,11 +265,11 @@ __global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p
   const float* drow = resid ? p.dlog + ((long)b * K + a) * V : trow;
   const float lt = p.lse[2 * b], lz = p.lse[2 * b + 1];
   const uint64_t seed = p.seeds[b];
+  const int ngroups = (V + 3) / 4;
+  const int lo = c * p.seg, hi = min(lo + p.seg, ngroups);
   unsigned long long kr = 0ull, kp = 0ull;
-#pragma unroll
-  for (int g = 0; g < kVsResChunk / (4 * kVsThreads); ++g) {
-    const int v0 = c * kVsResChunk + (g * kVsThreads + (int)threadIdx.x) * 4;
-    if (v0 >= V) continue;
+  for (int g = lo + (int)threadIdx.x; g < hi; g += kVThreads) {
+    const int v0 = 4 * g;
     float tv[4], zv[4];
     if constexpr (VEC) {  // V % 4 == 0: the whole group is in range
       const f32x4v t4 = *reinterpret_cast<const f32x4v*>(trow + v0);
@@ -289,7 +286,7 @@ __global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p
         if (resid) zv[e] = drow[v];
       }
     }
-    const Philox4 rb = rng_block(seed, p.offset, RNG_RESAMPLE, (uint64_t)a, (uint64_t)(v0 >> 2));
+    const Philox4 rb = rng_block(seed, p.offset, RNG_RESAMPLE, (uint64_t)a, (uint64_t)g);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = v0 + e;
@@ -314,16 +311,17 @@ __global__ __launch_bounds__(kVsThreads) void vs_resample_kernel(VSampleParams p
     kred[1][wave] = kp;
   }
   __syncthreads();
+  unsigned long long* kb = p.keys + (long)b * kSeqLineU64;
   if (threadIdx.x < 2) {
     unsigned long long k = 0ull;
-    for (int w = 0; w < kVsThreads / kWave; ++w) k = kred[threadIdx.x][w] > k ? kred[threadIdx.x][w] : k;
-    if (k) keep_alive(atomic_max_key(p.keys + 2 * b + threadIdx.x, k));
+    for (int w = 0; w < kVThreads / kWave; ++w) k = kred[threadIdx.x][w] > k ? kred[threadIdx.x][w] : k;
+    if (k) keep_alive(atomic_max_key(kb + threadIdx.x, k));
   }
-  if (last_to_arrive(p.counters + b, gridDim.x, &flag)) {
+  if (last_to_arrive(p.counters + (long)b * kSeqLineU32, gridDim.x, &flag)) {
     if (threadIdx.x == 0) {
-      const unsigned long long r = take_key(p.keys + 2 * b);
-      const unsigned long long q = take_key(p.keys + 2 * b + 1);
-      p.next[b] = (int)key_index(r ? r : q);
+      const unsigned long long rk = take_key(kb);
+      const unsigned long long qk = take_key(kb + 1);
+      p.next[b] = (int)key_index(rk ? rk : qk);
     }
   }
 }
@@ -336,21 +334,26 @@ hipError_t launch_verify_sample(const VSampleParams& p, int B, hipStream_t s) {
   const bool vec = p.V % 4 == 0 && ((uintptr_t)p.tlog & 15) == 0 &&
                    (p.K == 0 || ((uintptr_t)p.dlog & 15) == 0);
   VSampleParams q = p;
-  const int nres = (p.V + kVsResChunk - 1) / kVsResChunk;
-  if (vec) {
-    q.nchunk = (p.V + kVsChunkVec - 1) / kVsChunkVec;
-    hipLaunchKernelGGL(vs_stats_kernel<true>, dim3(q.nchunk, 2 * p.K + 1, B), dim3(kVsThreads), 0,
-                       s, q);
-  } else {
-    hipLaunchKernelGGL(vs_stats_kernel<false>, dim3(q.nchunk, 2 * p.K + 1, B), dim3(kVsThreads),
-                       0, s, q);
-  }
+  int nseg;
+  segments((long)B * (2 * p.K + 1), vec ? p.V / 4 : p.V, &nseg, &q.seg);
+  if (vec)
+    hipLaunchKernelGGL(vs_stats_kernel<true>, dim3(nseg, 2 * p.K + 1, B), dim3(kVThreads), 0, s, q);
+  else
+    hipLaunchKernelGGL(vs_stats_kernel<false>, dim3(nseg, 2 * p.K + 1, B), dim3(kVThreads), 0, s, q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // Resampling: groups of four entries; about kTargetGroups workgroups, at least one
+  // group per lane.
+  const int ngroups = (p.V + 3) / 4;
+  long sr = (kTargetGroups + B - 1) / B;
+  const long max_sr = (ngroups + kVThreads - 1) / kVThreads;
+  if (sr > max_sr) sr = max_sr;
+  q.seg = (int)((ngroups + sr - 1) / sr);
+  const int nres = (ngroups + q.seg - 1) / q.seg;
   if (vec)
-    hipLaunchKernelGGL(vs_resample_kernel<true>, dim3(nres, B), dim3(kVsThreads), 0, s, q);
+    hipLaunchKernelGGL(vs_resample_kernel<true>, dim3(nres, B), dim3(kVThreads), 0, s, q);
   else
-    hipLaunchKernelGGL(vs_resample_kernel<false>, dim3(nres, B), dim3(kVsThreads), 0, s, q);
+    hipLaunchKernelGGL(vs_resample_kernel<false>, dim3(nres, B), dim3(kVThreads), 0, s, q);
   return hipGetLastError();
 }
 
@@ -366,20 +369,6 @@ __global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, 
   const int keep = (a + 1 < K) ? a + 1 : K;
   len[b] += keep - K;
   pos[b] += a + 1 - K;
-}
-
-hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s) {
-  if (p.V < 1 || p.K < 0 || B < 1) return hipErrorInvalidValue;
-  if (p.V % 4 == 0 && ((uintptr_t)p.logits & 15) == 0) {
-    const int nchunk = (p.V + kVerifyVecChunk - 1) / kVerifyVecChunk;
-    hipLaunchKernelGGL(verify_vec_kernel, dim3(nchunk, p.K + 1, B), dim3(kVerifyThreads), 0, s, p);
-    return hipGetLastError();
-  }
-  if (p.chunk != kVerifyThreads * kVerifyPer || (long)p.nchunk * p.chunk < p.V ||
-      (long)(p.nchunk - 1) * p.chunk >= p.V)
-    return hipErrorInvalidValue;
-  hipLaunchKernelGGL(verify_kernel, dim3(p.nchunk, p.K + 1, B), dim3(kVerifyThreads), 0, s, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
