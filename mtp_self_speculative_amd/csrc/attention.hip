@@ -1,7 +1,7 @@
 // Decode attention of the MTP layer over its own single-layer cache, with RoPE and the
 // cache append fused in, split over the context, then merged by a second kernel.
 //
-// Grid (split, kv head, sequence). A workgroup owns one KV head and all G query heads
+// Grid: one workgroup per (split, kv head, sequence). A workgroup owns one KV head and all G query heads
 // that share it (GQA), and one chunk of cache positions, so every K/V byte is read from
 // HBM once per step. Its K and V rows are requested with 16-byte loads before anything
 // else (the new slot excepted), so the HBM round trip overlaps the set-up: q and the new
@@ -52,7 +52,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   constexpr int KS = D / 32;                // MFMA k-steps per 16-slot score tile
   extern __shared__ __align__(16) float sm[];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // One-dimensional grid, (kv head, sequence) varying fastest: workgroups are dealt to the
+  // XCDs round-robin, so each XCD takes whole heads of every sequence and the ragged split
+  // work of different sequences spreads evenly (split-major order would give XCD i all of
+  // split i, the late splits of short sequences being empty).
+  const int ngb = p.n_kv * p.batch;
+  const int s = (int)blockIdx.x / ngb;
+  const int g = (int)blockIdx.x % p.n_kv, b = ((int)blockIdx.x % ngb) / p.n_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPR, dl = (lane % LPR) * VEC;
   const int G = p.n_q / p.n_kv;
@@ -435,8 +441,10 @@ hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int 
 
 template <class CT, int D, int GP>
 static hipError_t launch_attn_g(const AttnParams& p, int B, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<CT, D, GP>), dim3(p.nsplit, p.n_kv, B), dim3(kAttnThreads),
-                     attn_lds_bytes(D, p.chunk), s, p);
+  AttnParams q = p;
+  q.batch = B;
+  hipLaunchKernelGGL((attn_kernel<CT, D, GP>), dim3(p.nsplit * p.n_kv * B), dim3(kAttnThreads),
+                     attn_lds_bytes(D, p.chunk), s, q);
   return hipGetLastError();
 }
 

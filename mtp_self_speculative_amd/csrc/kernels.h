@@ -105,6 +105,7 @@ struct AttnParams {
   const int* len;  // start-of-call values
   const int* pos;
   int step;   // 0-based step index: slot len+step, position pos+step
+  int batch;  // sequences (set by launch_attention)
   int chunk;  // positions per workgroup (multiple of 64)
   int nsplit;
   const float* rope;  // [B, d]: cos then sin of the step's position
