@@ -1,4 +1,5 @@
-// Row-wise steps of the batched draft path, one workgroup per sequence.
+// Row-wise steps of the batched draft path: one workgroup per sequence where a norm needs
+// the whole row, column blocks otherwise.
 //
 // The MFMA contraction writes fp32 partial sums per K split. Each kernel here adds the
 // splits in a fixed order (deterministic), applies the step's epilogue (residual add,
@@ -43,7 +44,10 @@ __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y +
 template <int MODE>
 __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
   __shared__ float red[kRedThreads / kWave];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  // Column modes (QKV, SwiGLU): grid (column block, sequence), one float4 group per thread.
+  // Norm modes: one workgroup per sequence.
+  constexpr bool kCols = MODE == RED_QKV || MODE == RED_SWIGLU;
+  const int b = kCols ? (int)blockIdx.y : (int)blockIdx.x, tid = threadIdx.x;
   const int n = p.n;
   // All split partials of a column group are requested at once (indexes past nsplit
   // repeat the last split and are not added), then added in split order.
@@ -62,10 +66,11 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
   };
 
   if constexpr (MODE == RED_QKV) {
-    for (int c = 4 * tid; c < n; c += 4 * kRedThreads)
-      *reinterpret_cast<float4*>(p.out + (long)b * n + c) = sum_part(c);
+    const int c = 4 * ((int)blockIdx.x * kRedThreads + tid);
+    if (c < n) *reinterpret_cast<float4*>(p.out + (long)b * n + c) = sum_part(c);
   } else if constexpr (MODE == RED_SWIGLU) {
-    for (int c = 4 * tid; c < n; c += 4 * kRedThreads) {
+    const int c = 4 * ((int)blockIdx.x * kRedThreads + tid);
+    if (c < n) {
       const float4 g = sum_part(c), u = sum_part(n + c);
       const long o = (long)b * p.ldq + c;
       store4_split(p.xq + o, p.xq_lo + o, g.x / (1.0f + expf(-g.x)) * u.x,
@@ -142,11 +147,12 @@ hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s) {
       (!p.part || p.nsplit < 1 || p.nsplit > kRedMaxSplit || p.bp < B || p.n_part % 4 != 0))
     return hipErrorInvalidValue;
   const dim3 g(B), t(kRedThreads);
+  const dim3 gc((p.n / 4 + kRedThreads - 1) / kRedThreads, B);  // column modes
   switch (mode) {
     case RED_EH: hipLaunchKernelGGL(red_kernel<RED_EH>, g, t, 0, s, p); break;
-    case RED_QKV: hipLaunchKernelGGL(red_kernel<RED_QKV>, g, t, 0, s, p); break;
+    case RED_QKV: hipLaunchKernelGGL(red_kernel<RED_QKV>, gc, t, 0, s, p); break;
     case RED_RESID: hipLaunchKernelGGL(red_kernel<RED_RESID>, g, t, 0, s, p); break;
-    case RED_SWIGLU: hipLaunchKernelGGL(red_kernel<RED_SWIGLU>, g, t, 0, s, p); break;
+    case RED_SWIGLU: hipLaunchKernelGGL(red_kernel<RED_SWIGLU>, gc, t, 0, s, p); break;
     case PREP_EH: hipLaunchKernelGGL(red_kernel<PREP_EH>, g, t, 0, s, p); break;
     case PREP_NORM: hipLaunchKernelGGL(red_kernel<PREP_NORM>, g, t, 0, s, p); break;
     default: return hipErrorInvalidValue;

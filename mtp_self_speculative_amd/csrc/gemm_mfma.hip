@@ -44,37 +44,53 @@ constexpr int kMmMaxSplit = 16;  // the row-wise reductions add at most this man
 __host__ __device__ int mm_chunks(int ncols) { return (ncols + kMmChunk - 1) / kMmChunk; }
 int mm_batch_pad(int B) { return (B + 15) / 16 * 16; }
 
-// K splits: enough items to occupy the chip (about 512), at most 16, while the partial
-// sums stay below an eighth of the weight bytes (nsplit * 16NB * 4 B per row <= ncols * 2 B / 8).
+// Workgroups a launch is sized for: one per CU of MI355X. Measured over every projection
+// shape of the batched workloads (B = 8, 32, 64), one resident workgroup per CU streams
+// better than two, and the split that minimises the rounds of items per workgroup times
+// the chunks per item is the fastest or within a few percent of it.
+constexpr int kMmTargetGroups = 256;
+
+// K splits: the divisor s of the chunk count (s <= 16, and partial sums below an eighth of
+// the weight bytes: s * 16NB * 4 B per row <= ncols * 2 B / 8) that minimises
+// ceil(items / groups) * (chunks / s), items = tiles * s; ties go to fewer splits (less
+// partial traffic).
 int mm_split(int nrows, int ncols, int B) {
-  const int ntiles = (nrows + kMmTileRows - 1) / kMmTileRows;
+  const long ntiles = (nrows + kMmTileRows - 1) / kMmTileRows;
   const int nch = mm_chunks(ncols);
-  int want = 512 / ntiles;
-  if (want > kMmMaxSplit) want = kMmMaxSplit;
-  const int cap = ncols / (16 * mm_batch_pad(B));
-  if (want > cap) want = cap;
-  if (want > nch) want = nch;
+  int cap = ncols / (16 * mm_batch_pad(B));
+  if (cap > kMmMaxSplit) cap = kMmMaxSplit;
+  if (cap > nch) cap = nch;
   int best = 1;
-  for (int s = 1; s <= want; ++s)
-    if (nch % s == 0) best = s;
+  long best_cost = -1;
+  for (int s = 1; s <= cap; ++s) {
+    if (nch % s != 0) continue;
+    const long items = ntiles * s;
+    const long groups = items < kMmTargetGroups ? items : kMmTargetGroups;
+    const long cost = (items + groups - 1) / groups * (nch / s);
+    if (best_cost < 0 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
   return best;
 }
 
 // LDS: [2 buffers][2 planes][16 NB rows][kMmLdsRow] bf16
 static size_t mm_lds_bytes(int nb) { return (size_t)4 * 16 * nb * kMmLdsRow * sizeof(uint16_t); }
 
+// Persistent grid: one workgroup per CU, or one per item when there are fewer items.
 int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
   const long items = (long)((nrows + kMmTileRows - 1) / kMmTileRows) * nsplit;
-  const int nb = mm_batch_pad(B) / 16;
-  const int per_cu = nb >= 3 ? 1 : 2;  // resident workgroups (LDS, registers)
-  long g = (long)per_cu * num_cu;
+  long g = num_cu;
   if (g > items) g = items;
   (void)ncols;
+  (void)B;
   return (int)(g < 1 ? 1 : g);
 }
 
 // OCC: waves per SIMD the register allocation must allow (the sampling epilogue at one or
-// two tiles is held to two, the occupancy its grid of two workgroups per CU needs).
+// two tiles is held to two, which keeps it free of the extra registers its random blocks
+// would otherwise take).
 template <int NB, int EPI, int OCC>
 __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   constexpr int BP = 16 * NB;
