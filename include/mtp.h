@@ -103,13 +103,19 @@ typedef struct {
 typedef struct mtp_handle mtp_handle;
 
 /* Bytes of device workspace a handle needs for up to max_batch sequences, up to
- * max_k steps per call and caches of up to max_capacity slots. Host only. */
+ * max_k steps per call and caches of up to max_capacity slots. Host only. For bf16
+ * configurations with max_batch >= 3 this includes a copy of the eh_proj, attention,
+ * MLP and lm_head matrices laid out for the matrix-core kernels (about the size of those
+ * weights: 1.7 GB for a Qwen3-8B-shaped head). */
 mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
                               int32_t max_capacity, size_t* bytes);
 
 /* Create a handle. `workspace` is caller-owned device memory of at least
  * mtp_workspace_size() bytes, 256-byte aligned, used only by this handle; it is
- * zeroed here (synchronously). Supported shapes: head_dim 64 or 128,
+ * zeroed here (synchronously), and for bf16 configurations with max_batch >= 3 it receives
+ * the re-laid-out copy of the weights: the weights must hold their final values when the
+ * handle is created, and later changes to them are not seen by batches of 3 or more
+ * sequences (create a new handle instead). Supported shapes: head_dim 64 or 128,
  * n_q_heads / n_kv_heads <= 8, hidden and ffn multiples of 8, max_k <= 100,
  * max_capacity <= 262144 (256 attention splits of up to 1024 slots).
  * On success *out receives the handle; on failure *out is NULL. */

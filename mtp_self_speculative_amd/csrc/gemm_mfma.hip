@@ -18,6 +18,9 @@
 // are double-buffered in registers; all loads are unconditional (indexes past the end
 // are clamped), so the compiler can wait for exactly the buffer being consumed.
 //
+// With a packed copy of W (launch_pack) the weight loads are contiguous instead: 1 KB per
+// wave instruction, each 128 x 256 block one 64 KB region.
+//
 // Epilogues: EPI_STORE writes the fp32 partial sums of the item's K split (a row-wise
 // reduction kernel adds the splits in a fixed order, so results are deterministic);
 // EPI_ARGMAX (one split) folds each row's value into a packed (value, index) key per
@@ -42,6 +45,7 @@ constexpr int kMmMaxNB = 4;
 constexpr int kMmMaxSplit = 16;  // the row-wise reductions add at most this many splits
 
 __host__ __device__ int mm_chunks(int ncols) { return (ncols + kMmChunk - 1) / kMmChunk; }
+constexpr long kMmPackBlock = (long)kMmTileRows * kMmChunk;  // elements per packed block
 int mm_batch_pad(int B) { return (B + 15) / 16 * 16; }
 
 // Workgroups a launch is sized for: one per CU of MI355X. Measured over every projection
@@ -128,6 +132,20 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   // of 256 bf16) and never consumed.
   auto wload = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
     const bool live = it < stages;
+    if (p.packed) {  // contiguous 1 KB per wave instruction
+      const long blk = live ? (long)(item_of(it) / p.nsplit) * mm_chunks(Kd) + chunk_of(it) : 0;
+      const uint16_t* bp = live ? p.packed + blk * kMmPackBlock
+                                : static_cast<const uint16_t*>(p.dummy);
+#pragma unroll
+      for (int m = 0; m < kMmMT; ++m)
+#pragma unroll
+        for (int k = 0; k < kMmKSteps; ++k) {
+          const long off = live ? (((long)(wave * kMmMT + m) * kMmKSteps + k) * kWave + lane) * 8
+                                : (long)(lane & 15) * kMmChunk + (lane >> 4) * 8 + k * 32;
+          buf[m][k] = *reinterpret_cast<const u32x4*>(bp + off);
+        }
+      return;
+    }
     const int c0 = live ? chunk_of(it) * kMmChunk + (lane >> 4) * 8 : (lane >> 4) * 8;
 #pragma unroll
     for (int m = 0; m < kMmMT; ++m) {
@@ -304,6 +322,46 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
       }
     }
   }
+}
+
+size_t mm_packed_elems(int nrows, int ncols) {
+  return (size_t)((nrows + kMmTileRows - 1) / kMmTileRows) * mm_chunks(ncols) * kMmPackBlock;
+}
+
+// One thread per 16-byte vector of the packed copy: vector v of block (tile, chunk) is the
+// load of lane v % 64, k-step (v / 64) % 8, slice v / 512 (wave * 2 + slice).
+__global__ void pack_kernel(const uint16_t* w0, const uint16_t* w1, const uint16_t* w2, int seg1,
+                            int seg2, int nrows, int ncols, uint16_t* dst, long nvec) {
+  const int nch = mm_chunks(ncols);
+  for (long v = blockIdx.x * (long)blockDim.x + threadIdx.x; v < nvec;
+       v += (long)gridDim.x * blockDim.x) {
+    const long blk = v / (kMmPackBlock / 8);
+    const int q = (int)(v % (kMmPackBlock / 8));
+    const int lane = q % kWave, k = (q / kWave) % kMmKSteps, sm = q / (kWave * kMmKSteps);
+    const long row = (blk / nch) * kMmTileRows + sm * 16 + (lane & 15);
+    const int col = (int)(blk % nch) * kMmChunk + k * 32 + (lane >> 4) * 8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (row < nrows && col < ncols) {
+      const uint16_t* src = row < seg1   ? w0 + row * ncols
+                            : row < seg2 ? w1 + (row - seg1) * ncols
+                                         : w2 + (row - seg2) * ncols;
+      val = *reinterpret_cast<const u32x4*>(src + col);
+    }
+    *reinterpret_cast<u32x4*>(dst + v * 8) = val;
+  }
+}
+
+hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1, int seg2,
+                       int nrows, int ncols, uint16_t* dst, hipStream_t s) {
+  if (!w0 || !w1 || !w2 || !dst || nrows < 1 || ncols < 8 || ncols % 8 != 0 || seg1 > seg2)
+    return hipErrorInvalidValue;
+  const long nvec = (long)(mm_packed_elems(nrows, ncols) / 8);
+  long blocks = (nvec + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w0), static_cast<const uint16_t*>(w1),
+                     static_cast<const uint16_t*>(w2), seg1, seg2, nrows, ncols, dst, nvec);
+  return hipGetLastError();
 }
 
 template <int NB>

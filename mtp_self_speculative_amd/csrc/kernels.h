@@ -155,10 +155,21 @@ struct MmParams {
   int advance;
   const void* dummy;  // as GemvParams::dummy
   SampleParams smp;   // EPI_SAMPLE
+  // When set, W is read from this packed copy (see launch_pack) and w0/w1/w2/seg1/seg2
+  // are not used.
+  const uint16_t* packed;
 };
 __host__ __device__ int mm_chunks(int ncols);  // K chunks of the contraction
 int mm_batch_pad(int B);                           // 16 * NB for batch B
 int mm_split(int nrows, int ncols, int B);         // K splits used for these sizes
+// Packed copy of the logical matrix w0 | w1 | w2 (segments as in MmParams, [nrows, ncols]
+// bf16) for mm_kernel: blocks of 128 rows x 256 columns, block (tile, chunk) at element
+// (tile * chunks + chunk) * 32768, each block in the order the kernel's lanes load it, so
+// that every wave load instruction reads 1 KB of contiguous memory; rows and columns past
+// the matrix are zero.
+size_t mm_packed_elems(int nrows, int ncols);
+hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1, int seg2,
+                       int nrows, int ncols, uint16_t* dst, hipStream_t s);
 int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu);
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s);
 

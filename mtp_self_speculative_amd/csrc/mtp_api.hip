@@ -40,6 +40,8 @@ struct Layout {
   // sampling verification: (max, sum) pairs per (sequence, row, chunk), row a's lse, keys
   size_t vs_part, vs_lse, vs_keys;
   int v_kstride;  // keys per sequence in v_keys
+  // batched path: packed copies of the draft step's matrices (launch_pack), 0 when absent
+  size_t pk_eh, pk_qkv, pk_o, pk_gu, pk_down, pk_lm;
   size_t total;
 };
 
@@ -151,6 +153,17 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
       }
       L.cu_part = take(part * 4);
     }
+  }
+  // packed weights for the matrix-core draft path (made once by mtp_create)
+  L.pk_eh = L.pk_qkv = L.pk_o = L.pk_gu = L.pk_down = L.pk_lm = 0;
+  if (mm_eligible(c) && max_batch >= kMmMinBatch) {
+    const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    L.pk_eh = take(mm_packed_elems(H, 2 * H) * 2);
+    L.pk_qkv = take(mm_packed_elems(qd + 2 * kvd, H) * 2);
+    L.pk_o = take(mm_packed_elems(H, qd) * 2);
+    L.pk_gu = take(mm_packed_elems(2 * c.ffn, H) * 2);
+    L.pk_down = take(mm_packed_elems(H, c.ffn) * 2);
+    L.pk_lm = take(mm_packed_elems(c.vocab, H) * 2);
   }
   L.vs_part = take((size_t)max_batch * (2 * max_k + 1) * vs_chunks(c.vocab) * 8);
   L.vs_lse = take((size_t)max_batch * 2 * 4);
@@ -327,6 +340,24 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
   const Layout L = make_layout(*cfg, max_batch, max_k);
   if (workspace_bytes < L.total) return MTP_ERR_CAPACITY;
   if (hipMemset(workspace, 0, L.total) != hipSuccess) return MTP_ERR_HIP;
+  if (L.pk_lm) {
+    // Packed copies of the batched path's matrices (contiguous matrix-core loads).
+    char* ws = static_cast<char*>(workspace);
+    auto pk = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+    const mtp_config& c = *cfg;
+    const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    const int F = c.ffn;
+    hipError_t e = launch_pack(w->w_eh, w->w_eh, w->w_eh, H, H, H, 2 * H, pk(L.pk_eh), 0);
+    if (e == hipSuccess)
+      e = launch_pack(w->w_q, w->w_k, w->w_v, qd, qd + kvd, qd + 2 * kvd, H, pk(L.pk_qkv), 0);
+    if (e == hipSuccess) e = launch_pack(w->w_o, w->w_o, w->w_o, H, H, H, qd, pk(L.pk_o), 0);
+    if (e == hipSuccess)
+      e = launch_pack(w->w_gate, w->w_up, w->w_up, F, 2 * F, 2 * F, H, pk(L.pk_gu), 0);
+    if (e == hipSuccess) e = launch_pack(w->w_down, w->w_down, w->w_down, H, H, H, F, pk(L.pk_down), 0);
+    if (e == hipSuccess)
+      e = launch_pack(w->lm_head, w->lm_head, w->lm_head, c.vocab, c.vocab, c.vocab, H, pk(L.pk_lm), 0);
+    if (e != hipSuccess) return MTP_ERR_HIP;
+  }
   if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;
   mtp_handle* h = new (std::nothrow) mtp_handle();
   if (!h) return MTP_ERR_CAPACITY;
@@ -446,10 +477,14 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
   auto g16 = [&](const void* p) { return static_cast<const uint16_t*>(p); };
 
   // One contraction (rows r of w0|w1|w2 against xq) into partials; returns the splits.
+  auto pkp = [&](size_t off) -> const uint16_t* {
+    return off ? reinterpret_cast<const uint16_t*>(h->ws + off) : nullptr;
+  };
   auto mm = [&](const void* w0, const void* w1, const void* w2, int seg1, int seg2, int N,
-                int Kd, int* ns) -> hipError_t {
+                int Kd, size_t pk_off, int* ns) -> hipError_t {
     MmParams m{};
     m.w0 = w0; m.w1 = w1; m.w2 = w2; m.seg1 = seg1; m.seg2 = seg2;
+    m.packed = pkp(pk_off);
     m.nrows = N; m.ncols = Kd; m.x = xq; m.x_lo = xq_lo; m.ldx = L.ldq; m.B = B;
     m.nsplit = mm_split(N, Kd, B);
     m.part = part;
@@ -481,14 +516,14 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       r.tok_stride = k == 0 ? 1 : K;
       r.vocab = V; r.err = err;
       hipError_t e2 = launch_red(PREP_EH, r, B, s);
-      if (e2 == hipSuccess) e2 = mm(w.w_eh, w.w_eh, w.w_eh, H, H, H, 2 * H, &ns);
+      if (e2 == hipSuccess) e2 = mm(w.w_eh, w.w_eh, w.w_eh, H, H, H, 2 * H, L.pk_eh, &ns);
       if (e2 == hipSuccess) e2 = red(RED_EH, ns, H, H, nullptr, x, nullptr, w.g_attn);
       return e2;
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
     // 2. QKV (the attention norm was applied by the previous row kernel)
     e = timed(h, KC_QKV, s, [&] {
-      hipError_t e2 = mm(w.w_q, w.w_k, w.w_v, nq * d, (nq + nkv) * d, qkvd, H, &ns);
+      hipError_t e2 = mm(w.w_q, w.w_k, w.w_v, nq * d, (nq + nkv) * d, qkvd, H, L.pk_qkv, &ns);
       if (e2 == hipSuccess) e2 = red(RED_QKV, ns, qkvd, qkvd, nullptr, h->at<float>(L.qkv), nullptr, nullptr);
       return e2;
     });
@@ -502,21 +537,21 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       return MTP_ERR_HIP;
     // 4. O projection + residual; writes RMSNorm(x1) * g_mlp
     e = timed(h, KC_OPROJ, s, [&] {
-      hipError_t e2 = mm(w.w_o, w.w_o, w.w_o, H, H, H, nq * d, &ns);
+      hipError_t e2 = mm(w.w_o, w.w_o, w.w_o, H, H, H, nq * d, L.pk_o, &ns);
       if (e2 == hipSuccess) e2 = red(RED_RESID, ns, H, H, x, x1, nullptr, w.g_mlp);
       return e2;
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
     // 5. gate / up + SwiGLU
     e = timed(h, KC_GATEUP, s, [&] {
-      hipError_t e2 = mm(w.w_gate, w.w_up, w.w_up, F, 2 * F, 2 * F, H, &ns);
+      hipError_t e2 = mm(w.w_gate, w.w_up, w.w_up, F, 2 * F, 2 * F, H, L.pk_gu, &ns);
       if (e2 == hipSuccess) e2 = red(RED_SWIGLU, ns, 2 * F, F, nullptr, nullptr, nullptr, nullptr);
       return e2;
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
     // 6. down + residual -> h^(k); writes RMSNorm(h^(k)) * g_final
     e = timed(h, KC_DOWN, s, [&] {
-      hipError_t e2 = mm(w.w_down, w.w_down, w.w_down, H, H, H, F, &ns);
+      hipError_t e2 = mm(w.w_down, w.w_down, w.w_down, H, H, H, F, L.pk_down, &ns);
       if (e2 == hipSuccess)
         e2 = red(RED_RESID, ns, H, H, x1, hb, hidden_out ? hidden_out + (size_t)k * B * H : nullptr,
                  w.g_final);
@@ -528,6 +563,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       MmParams m{};
       m.w0 = m.w1 = m.w2 = w.lm_head;
       m.seg1 = m.seg2 = V;
+      m.packed = pkp(L.pk_lm);
       m.nrows = V; m.ncols = H; m.x = xq; m.x_lo = xq_lo; m.ldx = L.ldq; m.B = B; m.nsplit = 1;
       m.keys = h->at<unsigned long long>(L.lm_keys);
       m.counter = h->at<unsigned>(L.lm_cnt);
@@ -807,6 +843,7 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
         if (e != hipSuccess) break;
         MmParams m{};
         m.w0 = m.w1 = m.w2 = h->w.lm_head;
+        m.packed = L.pk_lm ? reinterpret_cast<const uint16_t*>(h->ws + L.pk_lm) : nullptr;
         m.seg1 = m.seg2 = V;
         m.nrows = V; m.ncols = H;
         m.x = h->at<uint16_t>(L.vh_q); m.x_lo = h->at<uint16_t>(L.vh_q_lo); m.ldx = L.vh_ld;
