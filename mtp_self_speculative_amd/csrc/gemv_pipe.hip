@@ -339,12 +339,21 @@ bool gemv_pipe_fits(int ncols, int B, int wdtype) {
   return B >= 1 && B <= 2 && ncols >= 8 && ldl * B * sizeof(float) <= kPipeMaxLds;
 }
 
+// 16-byte chunks per lane and stage. Measured at batch 1 on MI355X (q8b shapes, caches
+// flushed): the lm_head and gate/up streams run best with 2 KB per wave stage (the lm_head
+// at 6.97 TB/s against 6.67 with 4 KB), the shorter matrices with 4 KB.
+template <int EPI>
+constexpr int pipe_ch() {
+  return (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE || EPI == EPI_SWIGLU) ? 2 : kPipeCH;
+}
+
 template <class WT, int NB, int P, int PRO, int EPI>
 static hipError_t pipe_one(const GemvParams& p, int grid, hipStream_t s) {
-  const int sw = kPipeCH * kWave * WT::kVec;
+  constexpr int CH = pipe_ch<EPI>();
+  const int sw = CH * kWave * WT::kVec;
   const size_t ldl = (size_t)(p.ncols + sw - 1) / sw * sw;
   const size_t lds = (size_t)NB * ldl * sizeof(float);
-  hipLaunchKernelGGL((gemv_pipe_kernel<WT, NB, P, kPipeCH, kPipeWPB, PRO, EPI>), dim3(grid),
+  hipLaunchKernelGGL((gemv_pipe_kernel<WT, NB, P, CH, kPipeWPB, PRO, EPI>), dim3(grid),
                      dim3(kPipeWPB * 64), lds, s, p);
   return hipGetLastError();
 }
