@@ -106,7 +106,7 @@ struct AttnParams {
   const int* pos;
   int step;   // 0-based step index: slot len+step, position pos+step
   int batch;  // sequences (set by launch_attention)
-  int chunk;  // positions per workgroup (multiple of 64)
+  int chunk;  // positions per workgroup (multiple of attn_chunk_quantum())
   int nsplit;
   const float* rope;  // [B, d]: cos then sin of the step's position
   float scale;
@@ -117,10 +117,17 @@ struct AttnParams {
   uint16_t* o_bf16_lo;  // [b * ld_o_bf16 + ...]) instead of fp32
   int ld_o_bf16;
   unsigned* err;
+  const int* perm;  // launch order of the items (attn_plan_kernel), or null: natural order
 };
 // Attention (partials per split) followed by the split merge into o. p.chunk must be a
-// positive multiple of attn_chunk_quantum().
+// positive multiple of attn_chunk_quantum() and at most attn_max_chunk(cdtype).
 int attn_chunk_quantum();
+int attn_max_chunk(int cdtype);
+// Longest-first item order for one draft call, written to perm[nsplit * n_kv * B]; wanted
+// when the items outnumber what the chip runs at once.
+bool attn_plan_wanted(int B, int nkv, int nsplit, int num_cu);
+hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, int nsplit, int* perm,
+                            hipStream_t s);
 hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
 
 // ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions

@@ -16,9 +16,8 @@ namespace {
 using namespace mtp;
 
 constexpr int kMaxSplits = 256;
-constexpr int kMinChunk = 64;
-constexpr int kMaxChunk = 1024;
-constexpr int kMaxCapacity = kMaxSplits * kMaxChunk;
+// Cache capacity limit: kMaxSplits chunks of the fp32 kernel's longest chunk (1024).
+constexpr int kMaxCapacity = kMaxSplits * 1024;
 constexpr int kMaxK = 100;
 static_assert(kMaxK <= kVsMaxK, "sampling verification holds 2K+1 log-sum-exps in LDS");
 constexpr int kMaxGroupHeads = 8;
@@ -26,8 +25,8 @@ constexpr size_t kGemvLdsBudget = 32 * 1024;
 constexpr int kGemvMaxGrid = 2048;
 
 struct Layout {
-  size_t x, x1, h, qkv, o, act, rope, part_o, part_ml, lm_keys, lm_cnt, v_keys, v_cnt,
-      err;
+  size_t x, x1, h, qkv, o, act, rope, part_o, part_ml, attn_perm, lm_keys, lm_cnt, v_keys,
+      v_cnt, err;
   size_t dummy;        // zeroed target of never-consumed tail prefetches
   size_t xq, xq_lo, mm_part;  // batched path: bf16 operand planes, K-split partial sums
   int ldq;
@@ -88,6 +87,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   L.rope = take((size_t)(max_k > 0 ? max_k : 1) * B * d * 4);
   L.part_o = take(B * nq * kMaxSplits * d * 4);
   L.part_ml = take(B * nq * kMaxSplits * 2 * 4);
+  L.attn_perm = take(B * nkv * kMaxSplits * 4);
   L.lm_keys = take(B * 8);
   L.lm_cnt = take(4);
   L.v_kstride = (max_k + 1 + kSeqLineU64 - 1) / kSeqLineU64 * kSeqLineU64;
@@ -427,7 +427,7 @@ static mtp_status check_kv(const mtp_handle* h, const mtp_kv* kv, int B) {
 
 // Attention parameters of step k (shared by both paths).
 static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int chunk,
-                              int nsplit) {
+                              int nsplit, const int* perm) {
   const mtp_config& c = h->cfg;
   const Layout& L = h->L;
   AttnParams a{};
@@ -443,6 +443,7 @@ static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int
   a.part_ml = h->at<float>(L.part_ml);
   a.o = h->at<float>(L.o);
   a.err = h->at<unsigned>(L.err);
+  a.perm = perm;
   return a;
 }
 
@@ -460,7 +461,7 @@ struct LmOut {
 static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_kv* kv,
                                  int32_t B, int32_t K, int32_t* draft_tokens, float* hidden_out,
                                  float* max_logit_out, const LmOut& lo, int chunk, int nsplit,
-                                 hipStream_t s) {
+                                 const int* perm, hipStream_t s) {
   const mtp_config& c = h->cfg;
   const mtp_weights& w = h->w;
   const Layout& L = h->L;
@@ -529,7 +530,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
     // 3. RoPE + cache append + attention; the merge writes o as the next bf16 operand
-    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit);
+    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit, perm);
     a.o_bf16 = xq;
     a.o_bf16_lo = xq_lo;
     a.ld_o_bf16 = L.ldq;
@@ -614,14 +615,15 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   unsigned* err = h->at<unsigned>(L.err);
 
   // Attention splits: aim for about one workgroup per CU over (split, kv head, sequence),
-  // with chunks of q..1024 cache positions (q = the kernel's quantum) and <= kMaxSplits.
-  // (Fewer, longer splits also make the merge cheaper; measured on MI355X at batch 1,
-  // 256-position chunks beat 128.)
+  // with chunks of q .. attn_max_chunk cache positions (q = the kernels' quantum) and
+  // <= kMaxSplits. (Fewer, longer splits also make the merge cheaper; measured on MI355X
+  // at batch 1, 256-position chunks beat 128, and for the bf16 cache at 32K contexts 2048
+  // beat 1024.)
   const int q = attn_chunk_quantum();
   long want = ((long)kv->capacity * B * nkv + h->num_cu - 1) / h->num_cu;
   int chunk = (int)((want + q - 1) / q * q);
   if (chunk < q) chunk = q;
-  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  if (chunk > attn_max_chunk(c.dtype)) chunk = attn_max_chunk(c.dtype);
   const int min_chunk = (kv->capacity + kMaxSplits - 1) / kMaxSplits;
   if (chunk < min_chunk) chunk = (min_chunk + q - 1) / q * q;
   const int nsplit = (kv->capacity + chunk - 1) / chunk;
@@ -629,9 +631,17 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   if (launch_draft_setup(c.dtype, h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, hidden,
                          hb, H, s) != hipSuccess)
     return MTP_ERR_HIP;
+  // With more attention items than run at once, order them longest first (per call).
+  const int* perm = nullptr;
+  if (attn_plan_wanted(B, nkv, nsplit, h->num_cu)) {
+    if (launch_attn_plan(kv->len, B, nkv, chunk, nsplit, h->at<int>(L.attn_perm), s) !=
+        hipSuccess)
+      return MTP_ERR_HIP;
+    perm = h->at<int>(L.attn_perm);
+  }
   if (use_mm(c, B))
     return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out, lo,
-                          chunk, nsplit, s);
+                          chunk, nsplit, perm, s);
   for (int k = 0; k < K; ++k) {
     hipError_t e;
     // 1. embedding gather + separate RMSNorms + concat + eh_proj
@@ -667,7 +677,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
       return MTP_ERR_HIP;
 
     // 3. RoPE + cache append + split decode attention + merge
-    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit);
+    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit, perm);
     if ((e = timed(h, KC_ATTN, s, [&] { return launch_attention(c.dtype, a, B, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
