@@ -573,10 +573,12 @@ __global__ __launch_bounds__(kFlashThreads) void attn_flash_kernel(AttnParams p)
 }
 
 // Merge the splits of one (query head, sequence): o = sum_q w_q o_q with
-// w_q = exp(m_q - M) / sum_q' l_q' exp(m_q' - M). One thread per dimension; the
-// split partials are read with all loads of a batch in flight.
+// w_q = exp(m_q - M) / sum_q' l_q' exp(m_q' - M). One thread per dimension. The first
+// UB split partials of o are requested together with the (max, sum) pairs, so up to UB
+// splits cost one memory round trip; later batches have all their loads in flight.
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
+  constexpr int UB = 32;
   __shared__ float w[256];
   __shared__ float red[D / kWave];
   const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
@@ -586,6 +588,10 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
   const int nvalid = (T_valid + p.chunk - 1) / p.chunk;
   const long hb = (long)b * p.n_q + hq;
   const float* ml = p.part_ml + hb * p.nsplit * 2;
+  const float* po = p.part_o + hb * p.nsplit * D + t;
+  float v[UB];
+#pragma unroll
+  for (int j = 0; j < UB; ++j) v[j] = j < nvalid ? po[(long)j * D] : 0.f;
   float m = -INFINITY;
   for (int q = t; q < nvalid; q += D) m = fmaxf(m, ml[2 * q]);
   m = wave_max(m);
@@ -605,13 +611,12 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
   __syncthreads();
   float L = 0.f;
   for (int i = 0; i < D / kWave; ++i) L += red[i];
-  const float* po = p.part_o + hb * p.nsplit * D + t;
-  constexpr int UB = 32;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < nvalid; q0 += UB) {
-    float v[UB];
+    if (q0 > 0) {
 #pragma unroll
-    for (int j = 0; j < UB; ++j) v[j] = (q0 + j < nvalid) ? po[(long)(q0 + j) * D] : 0.f;
+      for (int j = 0; j < UB; ++j) v[j] = (q0 + j < nvalid) ? po[(long)(q0 + j) * D] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < UB; ++j)
       if (q0 + j < nvalid) acc[j & 3] = fmaf(v[j], w[q0 + j], acc[j & 3]);

@@ -76,6 +76,10 @@ CASES = {
                     vocab=5000, batch=33, K=2, ctx_lo=30, ctx_hi=300),
     "mm-b64": small(name="mm64", cid=107, hidden=768, n_q=6, n_kv=2, head_dim=128, ffn=2304,
                     vocab=8192, batch=64, K=2, ctx_lo=1, ctx_hi=120),
+    # bf16, B = 40 ragged caches (len 1..4000) over 8 KV heads (G = 2): 640 attention
+    # items, more than the chip runs at once, so they run in the longest-first order
+    "mm-b40-ragged-order": small(name="order", cid=108, hidden=256, n_q=16, n_kv=8, head_dim=64,
+                                 ffn=512, vocab=2048, batch=40, K=2, ctx_lo=1, ctx_hi=4000),
     # bf16, B = 2, a cache long enough for several attention splits (len 3000..3100)
     "small-bf16-long": small(name="long", cid=103, hidden=256, n_q=4, n_kv=4, head_dim=128,
                              ffn=512, vocab=2048, batch=2, K=3, ctx_lo=3000, ctx_hi=3100),
