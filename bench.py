@@ -223,8 +223,8 @@ def sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up) -> dict
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="q8b", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
@@ -323,6 +323,37 @@ def main() -> int:
     el_ev, prof = replay(LMHEAD_BIT)
     log(f"lm_head-event pass: {args.steps} iterations in {el_ev * 1e3:.2f} ms")
 
+    # Per-call latency: HIP events (torch's current stream, which the library runs on)
+    # bracket each ABI call of the same replay; median and 10th / 90th percentiles.
+    cache.len.copy_(len0)
+    cache.pos.copy_(pos0)
+    last = last0
+    for it in range(args.warmup):
+        last = run(it, last)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for j, it in enumerate(range(args.warmup, iters)):
+        e = ev[j]
+        e[0].record()
+        head.draft(hidden[it], last, cache, K, out=drafts[it])
+        e[1].record()
+        head.verify(logits[it], drafts[it], acc[it], nxt[it])
+        e[2].record()
+        head.rollback(cache, acc[it], K)
+        e[3].record()
+        last = nxt[it]
+    torch.cuda.synchronize()
+
+    def pct(vals):
+        q = np.percentile(np.asarray(vals) * 1e3, [10, 50, 90])
+        return {"p10": round(float(q[0]), 2), "p50": round(float(q[1]), 2), "p90": round(float(q[2]), 2)}
+
+    latency = {"samples": args.steps,
+               "draft": pct([e[0].elapsed_time(e[1]) for e in ev]),
+               "verify": pct([e[1].elapsed_time(e[2]) for e in ev]),
+               "rollback": pct([e[2].elapsed_time(e[3]) for e in ev]),
+               "iteration": pct([e[0].elapsed_time(e[3]) for e in ev])}
+    log(f"per-call latency (us): {latency}")
+
     kernel_us = None
     if args.breakdown:
         _, bprof = replay((1 << 9) - 1)
@@ -404,6 +435,7 @@ def main() -> int:
                                  "algorithmic_bytes": int(vh_bytes),
                                  "hbm_frac": round(vh_bytes / (vh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     out["kv_catchup"] = {"us_per_call": round(cu_us, 2), "candidate_rows": B * K}
+    out["latency_us"] = latency
     out["sampling"] = samp
     if kernel_us:
         out["kernel_us_per_launch"] = kernel_us
