@@ -142,7 +142,8 @@ def cpu_baseline(cfg, inp, K: int, reps: int = 3) -> dict:
     return {"value": round(K / t, 4), "unit": "draft-steps/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} timed iterations (after 1 warm-up) of {K} draft steps + verify "
                       f"+ rollback for the same workload, median {t:.3f} s per iteration; "
-                      f"float32 NumPy, {cores} BLAS threads"}
+                      f"float64 NumPy (tokens decided on float32-rounded logits), "
+                      f"{cores} BLAS threads"}
 
 
 def sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up) -> dict:

@@ -5,8 +5,11 @@ the pages. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
 leg of ``bench.py`` may import it; the product library never does, and it
 shares no code with the HIP path (inputs come from ``mtp_synth`` only).
 
-Arithmetic is NumPy in float32 by default (``dt=np.float64`` re-runs the same
-steps in double precision). Matrices are row-major ``[out, in]``, ``y = W @ x``.
+Arithmetic is NumPy in float64 by default (``dt=np.float32`` re-runs the same
+steps in single precision). Where a floating-point value decides an integer (the
+argmax that picks a draft or target token), the decision is taken on the logits
+rounded to float32, the precision the kernels decide in; ties go to the lowest index
+on both sides. Matrices are row-major ``[out, in]``, ``y = W @ x``.
 
 Sources (page title, then section):
   [SPEC]  speculators user guide, "MTP (Multi-Token Prediction)",
@@ -151,7 +154,7 @@ class OracleWeights:
     The embedding table stays in storage dtype; only gathered rows are widened.
     """
 
-    def __init__(self, cfg, weights: dict, dt=np.float32):
+    def __init__(self, cfg, weights: dict, dt=np.float64):
         self.cfg, self.dt = cfg, dt
         self.storage = cfg.dtype
         self.embed_store = weights["embed"]
@@ -229,8 +232,9 @@ def draft(cfg, W: OracleWeights, hidden: np.ndarray, last_tokens: np.ndarray,
         x2 = x1 + act @ w["w_down"].T
         # Final norm + shared lm_head + argmax.
         lg = rmsnorm(x2, w["g_final"], eps) @ w["lm_head"].T
-        dk = argmax_lowest(lg)
-        srt = np.partition(lg, V - 2, axis=1)[:, V - 2:]
+        lg32 = lg.astype(np.float32)  # the token is decided in the kernels' precision
+        dk = argmax_lowest(lg32)
+        srt = np.partition(lg32, V - 2, axis=1)[:, V - 2:]
         top1[k] = srt[:, 1]
         margin[k] = srt[:, 1] - srt[:, 0]
         if sample is not None:
@@ -278,7 +282,7 @@ def verify(target_logits: np.ndarray, draft_tokens: np.ndarray):
 
 
 def verify_from_hidden(cfg, target_hidden: np.ndarray, target_norm: np.ndarray,
-                       lm_head: np.ndarray, draft_tokens: np.ndarray, dt=np.float32):
+                       lm_head: np.ndarray, draft_tokens: np.ndarray, dt=np.float64):
     """Greedy verification from the target's hidden states.  [OVSD] Overview;
     [SPEC] Architecture (the LM head is shared with the verifier).
 
@@ -293,7 +297,8 @@ def verify_from_hidden(cfg, target_hidden: np.ndarray, target_norm: np.ndarray,
     th = as_float(target_hidden, st, dt)
     g = as_float(target_norm, st, dt)
     w = as_float(lm_head, st, dt)
-    logits = rmsnorm(th, g, cfg.rms_eps) @ w.T
+    # tokens are decided on the logits rounded to float32, the kernels' precision
+    logits = (rmsnorm(th, g, cfg.rms_eps) @ w.T).astype(np.float32)
     V = logits.shape[-1]
     srt = np.partition(logits, V - 2, axis=-1)[..., V - 2:]
     acc, nxt = verify(logits, draft_tokens)

@@ -285,10 +285,12 @@ def test_identity_projection_pins():
 
 
 def test_recursion_consumes_previous_token_and_hidden():
-    """Step k+1 equals a fresh 1-step draft started from (h^(k), d_k) at pos+k, len+k."""
+    """Step k+1 equals a fresh 1-step draft started from (h^(k), d_k) at pos+k, len+k.
+    The restart hands h^(k) over in the storage dtype (fp32 here), which is lossless
+    when the oracle itself runs in fp32."""
     cfg = small_cfg()
     inp = _inputs(cfg, 20)
-    W = O.OracleWeights(cfg, inp.weights)
+    W = O.OracleWeights(cfg, inp.weights, np.float32)
     kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
     r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, 3)
     kc2, vc2 = inp.k_cache.copy(), inp.v_cache.copy()
