@@ -95,7 +95,9 @@ int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
 // OCC: waves per SIMD the register allocation must allow (the sampling epilogue at one or
 // two tiles is held to two, which keeps it free of the extra registers its random blocks
 // would otherwise take).
-template <int NB, int EPI, int OCC>
+// PK: W is read from the packed copy (p.packed). Each instantiation has one straight load
+// path: a branch per load (packed or not, live or not) made the compiler serialise loads.
+template <int NB, int EPI, int OCC, bool PK>
 __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   constexpr int BP = 16 * NB;
   constexpr int XPASS = BP / 8;  // 16-byte input loads per thread, plane and stage
@@ -128,22 +130,20 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   };
 
   u32x4 A[kMmMT][kMmKSteps], Bf[kMmMT][kMmKSteps];
-  // Stages past the workgroup's last one are prefetched from the dummy region (16 rows
-  // of 256 bf16) and never consumed.
+  // Stages past the workgroup's last one are prefetched from the dummy region and never
+  // consumed (packed: the same offsets in a 64 KB dummy block; else 16 rows of 256 bf16).
   auto wload = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
     const bool live = it < stages;
-    if (p.packed) {  // contiguous 1 KB per wave instruction
-      const long blk = live ? (long)(item_of(it) / p.nsplit) * mm_chunks(Kd) + chunk_of(it) : 0;
-      const uint16_t* bp = live ? p.packed + blk * kMmPackBlock
-                                : static_cast<const uint16_t*>(p.dummy);
+    if constexpr (PK) {  // contiguous 1 KB per wave instruction, one base per wave
+      const long blk = (long)(item_of(it) / p.nsplit) * mm_chunks(Kd) + chunk_of(it);
+      const uint16_t* bp = (live ? p.packed + blk * kMmPackBlock
+                                 : static_cast<const uint16_t*>(p.dummy)) +
+                           (long)wave * (kMmMT * kMmKSteps * kWave * 8) + lane * 8;
 #pragma unroll
       for (int m = 0; m < kMmMT; ++m)
 #pragma unroll
-        for (int k = 0; k < kMmKSteps; ++k) {
-          const long off = live ? (((long)(wave * kMmMT + m) * kMmKSteps + k) * kWave + lane) * 8
-                                : (long)(lane & 15) * kMmChunk + (lane >> 4) * 8 + k * 32;
-          buf[m][k] = *reinterpret_cast<const u32x4*>(bp + off);
-        }
+        for (int k = 0; k < kMmKSteps; ++k)
+          buf[m][k] = *reinterpret_cast<const u32x4*>(bp + (m * kMmKSteps + k) * kWave * 8);
       return;
     }
     const int c0 = live ? chunk_of(it) * kMmChunk + (lane >> 4) * 8 : (lane >> 4) * 8;
@@ -364,17 +364,21 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
   return hipGetLastError();
 }
 
-template <int NB>
-static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
+template <int NB, bool PK>
+static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   const size_t lds = mm_lds_bytes(NB);
   if (epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1>), dim3(grid), dim3(kMmThreads), lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK>), dim3(grid), dim3(kMmThreads), lds, s, p);
   else if (epi == EPI_SAMPLE)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1>), dim3(grid), dim3(kMmThreads),
-                       lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK>), dim3(grid),
+                       dim3(kMmThreads), lds, s, p);
   else
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1>), dim3(grid), dim3(kMmThreads), lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK>), dim3(grid), dim3(kMmThreads), lds, s, p);
   return hipGetLastError();
+}
+template <int NB>
+static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
+  return p.packed ? mm_nbp<NB, true>(epi, p, grid, s) : mm_nbp<NB, false>(epi, p, grid, s);
 }
 
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
@@ -387,7 +391,8 @@ hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   if (epi_is_argmax(epi) && (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
     return hipErrorInvalidValue;
   if (epi == EPI_STORE && !p.part) return hipErrorInvalidValue;
-  static_assert(16 * kMmChunk * 2 <= kDummyBytes, "dummy region too small");
+  static_assert(16 * kMmChunk * 2 <= kDummyBytes && kMmPackBlock * 2 <= kDummyBytes,
+                "dummy region too small");
   if (!p.dummy) return hipErrorInvalidValue;
   switch (mm_batch_pad(p.B) / 16) {
     case 1: return mm_nb<1>(epi, p, grid, s);

@@ -73,12 +73,12 @@ struct GemvParams {
   int* len;  // when advance > 0 the last workgroup adds it to len[b] and pos[b]
   int* pos;
   int advance;
-  // >= kDummyBytes of readable device memory: the target of the pipelined kernel's
-  // prefetches past a wave's last stage, which are issued but never consumed
+  // >= kDummyBytes of readable device memory: the target of the weight-streaming
+  // kernels' prefetches past a wave's last stage, which are issued but never consumed
   const void* dummy;
   SampleParams smp;  // EPI_SAMPLE
 };
-constexpr int kDummyBytes = 16 * 1024;
+constexpr int kDummyBytes = 64 * 1024;
 
 // Column-blocked GEMV for any batch (batch rows in blockIdx.y tiles of up to 8).
 hipError_t launch_gemv(int wdtype, Pro pro, Epi epi, const GemvParams& p, int max_grid,
