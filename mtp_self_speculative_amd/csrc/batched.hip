@@ -15,11 +15,13 @@
 
 namespace mtp {
 
-constexpr int kRedThreads = 512;
-constexpr int kRedVPT = 4;  // float4 groups per thread in the norm modes
+constexpr int kRedThreads = 512;       // column modes: one float4 group per thread
+constexpr int kRedNormThreads = 1024;  // norm modes: one workgroup per sequence
+constexpr int kRedNormVPT = 2;         // float4 groups per thread in the norm modes
 constexpr int kRedMaxSplit = 16;
+constexpr int kRedBatch = 8;  // split partials of a group requested together
 
-int red_max_cols() { return 4 * kRedVPT * kRedThreads; }
+int red_max_cols() { return 4 * kRedNormVPT * kRedNormThreads; }
 
 // Four values as bf16 hi / lo planes (see split_bf16).
 __device__ __forceinline__ void store4_split(uint16_t* hi, uint16_t* lo, float a, float b, float c,
@@ -41,37 +43,57 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 }
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 
+// Sum over the splits of the partial sums of NG float4 column groups c[0..NG), added in
+// split order (deterministic). The loads of all groups for a batch of kRedBatch splits are
+// issued together (indexes past nsplit repeat the last split and are not added), so a row
+// costs one memory round trip per batch.
+template <int NG>
+__device__ __forceinline__ void sum_splits(const RedParams& p, int b, const int (&c)[NG],
+                                           float4 (&v)[NG]) {
+  for (int s0 = 0; s0 < p.nsplit; s0 += kRedBatch) {
+    float4 t[NG][kRedBatch];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int s = 0; s < kRedBatch; ++s) {
+        const int sc = s0 + s < p.nsplit ? s0 + s : p.nsplit - 1;
+        t[g][s] = *reinterpret_cast<const float4*>(p.part + ((long)sc * p.bp + b) * p.n_part + c[g]);
+      }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int s = 0; s < kRedBatch; ++s) {
+        if (s0 + s == 0) v[g] = t[g][s];
+        else if (s0 + s < p.nsplit) v[g] = add4(v[g], t[g][s]);
+      }
+  }
+}
+
 template <int MODE>
-__global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
-  __shared__ float red[kRedThreads / kWave];
+__global__ __launch_bounds__(MODE == RED_QKV || MODE == RED_SWIGLU ? kRedThreads : kRedNormThreads)
+void red_kernel(RedParams p) {
   // Column modes (QKV, SwiGLU): grid (column block, sequence), one float4 group per thread.
-  // Norm modes: one workgroup per sequence.
+  // Norm modes: one workgroup per sequence, kRedNormVPT groups per thread.
   constexpr bool kCols = MODE == RED_QKV || MODE == RED_SWIGLU;
+  constexpr int NT = kCols ? kRedThreads : kRedNormThreads;
+  __shared__ float red[NT / kWave];
   const int b = kCols ? (int)blockIdx.y : (int)blockIdx.x, tid = threadIdx.x;
   const int n = p.n;
-  // All split partials of a column group are requested at once (indexes past nsplit
-  // repeat the last split and are not added), then added in split order.
-  auto sum_part = [&](int c) -> float4 {
-    float4 t[kRedMaxSplit];
-#pragma unroll
-    for (int s = 0; s < kRedMaxSplit; ++s) {
-      const int sc = s < p.nsplit ? s : p.nsplit - 1;
-      t[s] = *reinterpret_cast<const float4*>(p.part + ((long)sc * p.bp + b) * p.n_part + c);
-    }
-    float4 v = t[0];
-#pragma unroll
-    for (int s = 1; s < kRedMaxSplit; ++s)
-      if (s < p.nsplit) v = add4(v, t[s]);
-    return v;
-  };
 
   if constexpr (MODE == RED_QKV) {
     const int c = 4 * ((int)blockIdx.x * kRedThreads + tid);
-    if (c < n) *reinterpret_cast<float4*>(p.out + (long)b * n + c) = sum_part(c);
+    const int cc[1] = {c < n ? c : n - 4};
+    float4 v[1];
+    sum_splits<1>(p, b, cc, v);
+    if (c < n) *reinterpret_cast<float4*>(p.out + (long)b * n + c) = v[0];
   } else if constexpr (MODE == RED_SWIGLU) {
     const int c = 4 * ((int)blockIdx.x * kRedThreads + tid);
+    const int cl = c < n ? c : n - 4;
+    const int cc[2] = {cl, n + cl};
+    float4 v[2];
+    sum_splits<2>(p, b, cc, v);
     if (c < n) {
-      const float4 g = sum_part(c), u = sum_part(n + c);
+      const float4 g = v[0], u = v[1];
       const long o = (long)b * p.ldq + c;
       store4_split(p.xq + o, p.xq_lo + o, g.x / (1.0f + expf(-g.x)) * u.x,
                   g.y / (1.0f + expf(-g.y)) * u.y, g.z / (1.0f + expf(-g.z)) * u.z,
@@ -90,12 +112,20 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
     }
 #pragma unroll
     for (int q = 0; q < NPART; ++q) {
-      float4 v[kRedVPT];
+      float4 v[kRedNormVPT];
       float ss = 0.f;
+      if constexpr (MODE == RED_EH || MODE == RED_RESID) {
+        int cc[kRedNormVPT];
 #pragma unroll
-      for (int j = 0; j < kRedVPT; ++j) {
-        const int c = 4 * (tid + j * kRedThreads);
-        v[j] = float4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kRedNormVPT; ++j) {
+          const int c = 4 * (tid + j * kRedNormThreads);
+          cc[j] = c < n ? c : n - 4;
+        }
+        sum_splits<kRedNormVPT>(p, b, cc, v);
+      }
+#pragma unroll
+      for (int j = 0; j < kRedNormVPT; ++j) {
+        const int c = 4 * (tid + j * kRedNormThreads);
         if (c < n) {
           if constexpr (MODE == PREP_NORM) {
             v[j] = p.h16 ? load4_bf16(p.h16 + (long)b * n + c)
@@ -104,7 +134,6 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
             v[j] = q == 0 ? *reinterpret_cast<const float4*>(p.h + (long)b * n + c)
                           : load4_bf16(p.embed + (long)t * n + c);
           } else {
-            v[j] = sum_part(c);
             if constexpr (MODE == RED_RESID)
               v[j] = add4(*reinterpret_cast<const float4*>(p.res + (long)b * n + c), v[j]);
             *reinterpret_cast<float4*>(p.out + (long)b * n + c) = v[j];
@@ -112,14 +141,16 @@ __global__ __launch_bounds__(kRedThreads) void red_kernel(RedParams p) {
               *reinterpret_cast<float4*>(p.dbg + (long)b * p.dbg_ld + c) = v[j];
           }
           ss += dot4(v[j]);
+        } else {
+          v[j] = float4{0.f, 0.f, 0.f, 0.f};
         }
       }
       const float tot = block_sum(ss, red);
       const float r = 1.0f / sqrtf(tot / (float)n + p.eps);
       const uint16_t* g = q == 0 ? p.gain : p.gain2;
 #pragma unroll
-      for (int j = 0; j < kRedVPT; ++j) {
-        const int c = 4 * (tid + j * kRedThreads);
+      for (int j = 0; j < kRedNormVPT; ++j) {
+        const int c = 4 * (tid + j * kRedNormThreads);
         if (c < n) {
           const float4 gv = load4_bf16(g + c);
           const long o = (long)b * p.ldq + q * n + c;
@@ -146,13 +177,13 @@ hipError_t launch_red(RedMode mode, const RedParams& p, int B, hipStream_t s) {
   if (mode != PREP_EH && mode != PREP_NORM &&
       (!p.part || p.nsplit < 1 || p.nsplit > kRedMaxSplit || p.bp < B || p.n_part % 4 != 0))
     return hipErrorInvalidValue;
-  const dim3 g(B), t(kRedThreads);
-  const dim3 gc((p.n / 4 + kRedThreads - 1) / kRedThreads, B);  // column modes
+  const dim3 g(B), t(kRedNormThreads);
+  const dim3 gc((p.n / 4 + kRedThreads - 1) / kRedThreads, B), tc(kRedThreads);  // column modes
   switch (mode) {
     case RED_EH: hipLaunchKernelGGL(red_kernel<RED_EH>, g, t, 0, s, p); break;
-    case RED_QKV: hipLaunchKernelGGL(red_kernel<RED_QKV>, gc, t, 0, s, p); break;
+    case RED_QKV: hipLaunchKernelGGL(red_kernel<RED_QKV>, gc, tc, 0, s, p); break;
     case RED_RESID: hipLaunchKernelGGL(red_kernel<RED_RESID>, g, t, 0, s, p); break;
-    case RED_SWIGLU: hipLaunchKernelGGL(red_kernel<RED_SWIGLU>, gc, t, 0, s, p); break;
+    case RED_SWIGLU: hipLaunchKernelGGL(red_kernel<RED_SWIGLU>, gc, tc, 0, s, p); break;
     case PREP_EH: hipLaunchKernelGGL(red_kernel<PREP_EH>, g, t, 0, s, p); break;
     case PREP_NORM: hipLaunchKernelGGL(red_kernel<PREP_NORM>, g, t, 0, s, p); break;
     default: return hipErrorInvalidValue;
