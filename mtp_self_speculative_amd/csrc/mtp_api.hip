@@ -924,24 +924,36 @@ mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
         r.embed = static_cast<const uint16_t*>(w.embed);
         r.tok = draft_tokens + r0; r.tok_stride = 1; r.vocab = c.vocab; r.err = err;
         if ((e = launch_red(PREP_EH, r, rows, s)) != hipSuccess) break;
-        auto mm = [&](const void* w0, const void* w1, int seg1, int N, int Kd, int* ns) {
+        // packed: the matrix's rows in the handle's packed copy (or null: read w0/w1)
+        auto mm = [&](const void* w0, const void* w1, int seg1, int N, int Kd,
+                      const uint16_t* packed, int* ns) {
           MmParams m{};
           m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
           m.nrows = N; m.ncols = Kd; m.x = q; m.x_lo = qlo; m.ldx = L.cu_ld; m.B = rows;
           m.nsplit = mm_split(N, Kd, rows);
           m.part = part;
           m.dummy = h->ws + L.dummy;
+          m.packed = packed;
           *ns = m.nsplit;
           return launch_mm(EPI_STORE, m, mm_grid(N, Kd, rows, m.nsplit, h->num_cu), s);
         };
+        // The K/V rows of the packed [W_q; W_k; W_v] copy start at a whole 128-row tile
+        // when n_q * d is a multiple of 128; the packed copy is tile-major.
+        const int qd = c.n_q_heads * c.head_dim;
+        const uint16_t* pk_kv =
+            L.pk_qkv && qd % 128 == 0
+                ? h->at<uint16_t>(L.pk_qkv) + (size_t)(qd / 128) * mm_packed_elems(128, H)
+                : nullptr;
         int ns = 1;
-        if ((e = mm(w.w_eh, w.w_eh, H, H, 2 * H, &ns)) != hipSuccess) break;
+        if ((e = mm(w.w_eh, w.w_eh, H, H, 2 * H, L.pk_eh ? h->at<uint16_t>(L.pk_eh) : nullptr,
+                    &ns)) != hipSuccess)
+          break;
         r = RedParams{};
         r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = H; r.n = H;
         r.out = xrows; r.gain = static_cast<const uint16_t*>(w.g_attn); r.eps = c.rms_eps;
         r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld;
         if ((e = launch_red(RED_EH, r, rows, s)) != hipSuccess) break;
-        if ((e = mm(w.w_k, w.w_v, kvd, 2 * kvd, H, &ns)) != hipSuccess) break;
+        if ((e = mm(w.w_k, w.w_v, kvd, 2 * kvd, H, pk_kv, &ns)) != hipSuccess) break;
         r = RedParams{};
         r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = 2 * kvd; r.n = 2 * kvd;
         r.out = kvrows; r.ldq = L.cu_ld;
