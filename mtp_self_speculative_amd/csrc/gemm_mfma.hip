@@ -123,11 +123,6 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
     return (item_of(it) / p.nsplit) * kMmTileRows + (wave * kMmMT + m) * 16;
   };
 
-  auto row_ptr = [&](int r) -> const uint16_t* {
-    if (r < p.seg1) return static_cast<const uint16_t*>(p.w0) + (long)r * Kd;
-    if (r < p.seg2) return static_cast<const uint16_t*>(p.w1) + (long)(r - p.seg1) * Kd;
-    return static_cast<const uint16_t*>(p.w2) + (long)(r - p.seg2) * Kd;
-  };
 
   u32x4 A[kMmMT][kMmKSteps], Bf[kMmMT][kMmKSteps];
   // Stages past the workgroup's last one are prefetched from the dummy region and never
@@ -146,19 +141,20 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
           buf[m][k] = *reinterpret_cast<const u32x4*>(bp + (m * kMmKSteps + k) * kWave * 8);
       return;
     }
+    // Row pointers and column clamps as selects (no branch per load): columns past the row
+    // end (a ragged last chunk) re-read the row's last 8 elements.
     const int c0 = live ? chunk_of(it) * kMmChunk + (lane >> 4) * 8 : (lane >> 4) * 8;
+    const int cmax = live ? Kd - 8 : kMmChunk - 8;
 #pragma unroll
     for (int m = 0; m < kMmMT; ++m) {
-      int r = slice_row(it, m) + (lane & 15);
-      r = r < N ? r : N - 1;
-      const uint16_t* rp = live ? row_ptr(r)
-                                : static_cast<const uint16_t*>(p.dummy) + (lane & 15) * kMmChunk;
+      const int r = min(slice_row(it, m) + (lane & 15), N - 1);
+      const uint16_t* rp = r < p.seg1 ? static_cast<const uint16_t*>(p.w0) + (long)r * Kd
+                         : r < p.seg2 ? static_cast<const uint16_t*>(p.w1) + (long)(r - p.seg1) * Kd
+                                      : static_cast<const uint16_t*>(p.w2) + (long)(r - p.seg2) * Kd;
+      rp = live ? rp : static_cast<const uint16_t*>(p.dummy) + (lane & 15) * kMmChunk;
 #pragma unroll
-      for (int k = 0; k < kMmKSteps; ++k) {
-        int col = c0 + k * 32;
-        col = (col < Kd || !live) ? col : Kd - 8;
-        buf[m][k] = *reinterpret_cast<const u32x4*>(rp + col);
-      }
+      for (int k = 0; k < kMmKSteps; ++k)
+        buf[m][k] = *reinterpret_cast<const u32x4*>(rp + min(c0 + k * 32, cmax));
     }
   };
 
