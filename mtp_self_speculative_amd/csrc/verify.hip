@@ -63,10 +63,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
   const int units = VEC ? p.V / 4 : p.V;
   const int lo = c * p.seg, hi = min(lo + p.seg, units);
   unsigned long long best = 0ull;
-  for (int i0 = lo; i0 < hi; i0 += kVStage) {
-    int idx[kVPer];
-    f32x4v v[kVPer];
-    load_stage<VEC>(row, i0, hi, idx, v);
+  auto process = [&](const int (&idx)[kVPer], const f32x4v (&v)[kVPer]) {
 #pragma unroll
     for (int k = 0; k < kVPer; ++k) {
       unsigned long long key;
@@ -84,6 +81,18 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
       }
       best = key > best ? key : best;
     }
+  };
+  // Two stages in flight: the next stage's loads go out before this stage's keys are
+  // formed (indexes past the segment are clamped, so the extra stage is harmless).
+  int ia[kVPer], ib[kVPer];
+  f32x4v va[kVPer], vb[kVPer];
+  load_stage<VEC>(row, lo, hi, ia, va);
+  for (int i0 = lo; i0 < hi; i0 += 2 * kVStage) {
+    load_stage<VEC>(row, i0 + kVStage, hi, ib, vb);
+    process(ia, va);
+    if (i0 + kVStage >= hi) break;
+    load_stage<VEC>(row, i0 + 2 * kVStage, hi, ia, va);
+    process(ib, vb);
   }
   best = wave_max_u64(best);
   if (lane == 0) kred[wave] = best;
@@ -168,10 +177,7 @@ __global__ __launch_bounds__(kVThreads) void vs_stats_kernel(VSampleParams p) {
   // Running (max, sum of 2^(y - max)) of this lane; units repeated by the index clamp
   // are masked out.
   float m = -INFINITY, sum = 0.f;
-  for (int i0 = lo; i0 < hi; i0 += kVStage) {
-    int idx[kVPer];
-    f32x4v v[kVPer];
-    load_stage<VEC>(row, i0, hi, idx, v);
+  auto process = [&](const f32x4v (&v)[kVPer], int i0) {
     float y[kVPer][4];
     float sm = m;
 #pragma unroll
@@ -192,6 +198,17 @@ __global__ __launch_bounds__(kVThreads) void vs_stats_kernel(VSampleParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum += hw_exp2(y[k][e] - m);
     }
+  };
+  // Two stages in flight, as in verify_kernel.
+  int ia[kVPer], ib[kVPer];
+  f32x4v va[kVPer], vb[kVPer];
+  load_stage<VEC>(row, lo, hi, ia, va);
+  for (int i0 = lo; i0 < hi; i0 += 2 * kVStage) {
+    load_stage<VEC>(row, i0 + kVStage, hi, ib, vb);
+    process(va, i0);
+    if (i0 + kVStage >= hi) break;
+    load_stage<VEC>(row, i0 + 2 * kVStage, hi, ia, va);
+    process(vb, i0 + kVStage);
   }
   const float M = block_max(m, red);  // finite: every segment holds at least one entry
   const float S = block_sum(m > -INFINITY ? sum * hw_exp2(m - M) : 0.f, red);
