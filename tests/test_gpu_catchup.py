@@ -23,6 +23,10 @@ CASES = {
     # bf16, 20 x 4 = 80 rows: two groups
     "bf16-groups": small(name="cu4", cid=163, batch=20, K=4, hidden=512, n_q=8, n_kv=2,
                          ctx_lo=0, ctx_hi=120),
+    # bf16, 4 x 3 rows on the matrix cores with n_q * d = 320, not a whole 128-row tile:
+    # eh_proj from the packed copy, the K/V rows from the row-major weights
+    "bf16-mm-kv-rowmajor": small(name="cu5", cid=164, batch=4, K=3, hidden=320, n_q=5, n_kv=1,
+                                 head_dim=64, ffn=640, vocab=2053, ctx_lo=3, ctx_hi=90),
     # the Qwen3-8B-shaped head at full size, B=1 K=5 and B=32 K=3
     "q8b": S.get_config("q8b"),
     "q8b-b32": S.get_config("q8b-b32"),
