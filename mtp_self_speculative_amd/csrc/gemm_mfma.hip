@@ -34,10 +34,9 @@ namespace mtp {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMmWaves = 4;
-constexpr int kMmThreads = kMmWaves * kWave;
+constexpr int kMmWaves = 4;                       // waves of a 128-row item
 constexpr int kMmMT = 2;                          // 16-row slices per wave
-constexpr int kMmTileRows = 16 * kMmMT * kMmWaves;  // 128
+constexpr int kMmTileRows = 16 * kMmMT * kMmWaves;  // 128: rows of a packed block
 constexpr int kMmChunk = 256;                     // columns per stage
 constexpr int kMmKSteps = kMmChunk / 32;          // MFMA k-steps per stage
 constexpr int kMmLdsRow = kMmChunk + 8;           // bf16 per LDS row: 16-byte pad against bank conflicts
@@ -58,8 +57,8 @@ constexpr int kMmTargetGroups = 256;
 // the weight bytes: s * 16NB * 4 B per row <= ncols * 2 B / 8) that minimises
 // ceil(items / groups) * (chunks / s), items = tiles * s; ties go to fewer splits (less
 // partial traffic).
-int mm_split(int nrows, int ncols, int B) {
-  const long ntiles = (nrows + kMmTileRows - 1) / kMmTileRows;
+int mm_split(int nrows, int ncols, int B, int tile_rows) {
+  const long ntiles = (nrows + tile_rows - 1) / tile_rows;
   const int nch = mm_chunks(ncols);
   int cap = ncols / (16 * mm_batch_pad(B));
   if (cap > kMmMaxSplit) cap = kMmMaxSplit;
@@ -79,16 +78,39 @@ int mm_split(int nrows, int ncols, int B) {
   return best;
 }
 
+// Rows per work item. A workgroup stages each chunk of the inputs (16NB rows, hi and lo
+// planes: 1 KB per row) in LDS once for all its rows, so at 16NB = 64 the staging equals
+// the 64 KB of weights a 128-row item reads per chunk. Items of 256 rows (eight waves, two
+// packed blocks) halve that ratio: on packed weights at B = 64 they cut the projections
+// and the lm_head by 11-17% when their items still cover most of the grid, while at
+// B <= 32 they lose 1-30%, and with a quarter or an eighth of the grid in items (the
+// small catch-up contractions) twice the rows per workgroup cost about twice the time.
+// So: 256-row items for packed weights at 16NB >= 48 when their split gives at least
+// three quarters of num_cu items. The sampling epilogue keeps 128 rows (its random
+// blocks would spill at eight waves).
+MmPlan mm_plan(Epi epi, int nrows, int ncols, int B, bool packed, int num_cu) {
+  const bool split = epi == EPI_STORE;
+  MmPlan q{kMmTileRows, split ? mm_split(nrows, ncols, B, kMmTileRows) : 1, 0};
+  if (packed && epi != EPI_SAMPLE && mm_batch_pad(B) / 16 >= 3) {
+    const int tr = 2 * kMmTileRows;
+    const int s8 = split ? mm_split(nrows, ncols, B, tr) : 1;
+    if (4L * ((nrows + tr - 1) / tr) * s8 >= 3L * num_cu) {
+      q.tile_rows = tr;
+      q.nsplit = s8;
+    }
+  }
+  q.grid = mm_grid(nrows, q.tile_rows, q.nsplit, num_cu);
+  return q;
+}
+
 // LDS: [2 buffers][2 planes][16 NB rows][kMmLdsRow] bf16
 static size_t mm_lds_bytes(int nb) { return (size_t)4 * 16 * nb * kMmLdsRow * sizeof(uint16_t); }
 
 // Persistent grid: one workgroup per CU, or one per item when there are fewer items.
-int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
-  const long items = (long)((nrows + kMmTileRows - 1) / kMmTileRows) * nsplit;
+int mm_grid(int nrows, int tile_rows, int nsplit, int num_cu) {
+  const long items = (long)((nrows + tile_rows - 1) / tile_rows) * nsplit;
   long g = num_cu;
   if (g > items) g = items;
-  (void)ncols;
-  (void)B;
   return (int)(g < 1 ? 1 : g);
 }
 
@@ -97,19 +119,26 @@ int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu) {
 // would otherwise take).
 // PK: W is read from the packed copy (p.packed). Each instantiation has one straight load
 // path: a branch per load (packed or not, live or not) made the compiler serialise loads.
-template <int NB, int EPI, int OCC, bool PK>
-__global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
+// WV: waves per workgroup, 32 rows each (4: 128-row items; 8: 256-row items, packed only,
+// wave w reading the (w % 4)-th quarter of packed block 2 * item + w / 4).
+template <int NB, int EPI, int OCC, bool PK, int WV>
+__global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
+  static_assert(WV == kMmWaves || (WV == 2 * kMmWaves && PK), "eight waves read packed blocks");
   constexpr int BP = 16 * NB;
-  constexpr int XPASS = BP / 8;  // 16-byte input loads per thread, plane and stage
+  constexpr int NT = WV * kWave;
+  constexpr int TR = 16 * kMmMT * WV;   // rows per item
+  constexpr int XPASS = BP * 32 / NT;  // 16-byte input loads per thread, plane and stage
+  static_assert(XPASS * NT == BP * 32, "input staging must divide over the threads");
   extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][kMmLdsRow]
-  __shared__ unsigned long long kred[kMmWaves][BP];
+  __shared__ unsigned long long kred[WV][BP];
   __shared__ uint64_t seed_s[EPI == EPI_SAMPLE ? BP : 1];  // random-stream seeds, read once
   __shared__ int flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = p.nrows, Kd = p.ncols;
   const int C = mm_chunks(Kd) / p.nsplit;  // chunks per item
-  const int ntiles = (N + kMmTileRows - 1) / kMmTileRows;
+  const int ntiles = (N + TR - 1) / TR;
+  const int nblk_rows = (N + kMmTileRows - 1) / kMmTileRows;  // packed block rows
   const int nitems = ntiles * p.nsplit;
   const int G = gridDim.x;
   const int my_items = (int)blockIdx.x < nitems ? (nitems - 1 - (int)blockIdx.x) / G + 1 : 0;
@@ -120,7 +149,7 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   auto chunk_of = [&](int it) { return (item_of(it) % p.nsplit) * C + it % C; };
   // first row of slice m of this wave in the tile of stage it
   auto slice_row = [&](int it, int m) {
-    return (item_of(it) / p.nsplit) * kMmTileRows + (wave * kMmMT + m) * 16;
+    return (item_of(it) / p.nsplit) * TR + (wave * kMmMT + m) * 16;
   };
 
 
@@ -130,10 +159,13 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
   auto wload = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
     const bool live = it < stages;
     if constexpr (PK) {  // contiguous 1 KB per wave instruction, one base per wave
-      const long blk = (long)(item_of(it) / p.nsplit) * mm_chunks(Kd) + chunk_of(it);
-      const uint16_t* bp = (live ? p.packed + blk * kMmPackBlock
-                                 : static_cast<const uint16_t*>(p.dummy)) +
-                           (long)wave * (kMmMT * kMmKSteps * kWave * 8) + lane * 8;
+      // the second block of a 256-row item past the last block row reads the dummy
+      const int brow = (item_of(it) / p.nsplit) * (WV / kMmWaves) + wave / kMmWaves;
+      const bool lw = live && brow < nblk_rows;
+      const long blk = (long)brow * mm_chunks(Kd) + chunk_of(it);
+      const uint16_t* bp = (lw ? p.packed + blk * kMmPackBlock
+                               : static_cast<const uint16_t*>(p.dummy)) +
+                           (long)(wave % kMmWaves) * (kMmMT * kMmKSteps * kWave * 8) + lane * 8;
 #pragma unroll
       for (int m = 0; m < kMmMT; ++m)
 #pragma unroll
@@ -163,7 +195,7 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
     const int c0 = chunk_of(clampit(it)) * kMmChunk;
 #pragma unroll
     for (int j = 0; j < XPASS; ++j) {
-      const int q = tid + j * kMmThreads;
+      const int q = tid + j * NT;
       const int row = q >> 5, col = c0 + (q & 31) * 8;
       const int rr = row < p.B ? row : p.B - 1;
       const int cc = col < Kd ? col : Kd - 8;
@@ -176,7 +208,7 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
     const int c0 = chunk_of(clampit(it)) * kMmChunk;
 #pragma unroll
     for (int j = 0; j < XPASS; ++j) {
-      const int q = tid + j * kMmThreads;
+      const int q = tid + j * NT;
       const int row = q >> 5, cp = q & 31;
       const bool live = row < p.B && c0 + cp * 8 < Kd;
       const u32x4 z = {0u, 0u, 0u, 0u};
@@ -303,11 +335,11 @@ __global__ __launch_bounds__(kMmThreads, OCC) void mm_kernel(MmParams p) {
     if (tid < BP && tid < p.B) {
       unsigned long long k = 0ull;
 #pragma unroll
-      for (int w = 0; w < kMmWaves; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
+      for (int w = 0; w < WV; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
       if (k) keep_alive(atomic_max_key(p.keys + tid, k));
     }
     if (last_to_arrive(p.counter, gridDim.x, &flag)) {
-      for (int b = tid; b < p.B; b += kMmThreads) {
+      for (int b = tid; b < p.B; b += NT) {
         const unsigned long long k = take_key(p.keys + b);
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
         if (p.maxlogit) p.maxlogit[b] = key_value(k);
@@ -360,21 +392,28 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
   return hipGetLastError();
 }
 
-template <int NB, bool PK>
+template <int NB, bool PK, int WV>
 static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   const size_t lds = mm_lds_bytes(NB);
+  const dim3 block(WV * kWave);
   if (epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK>), dim3(grid), dim3(kMmThreads), lds, s, p);
-  else if (epi == EPI_SAMPLE)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK>), dim3(grid),
-                       dim3(kMmThreads), lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV>), dim3(grid), block, lds, s, p);
+  else if (epi == EPI_STORE)
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK, WV>), dim3(grid), block, lds, s, p);
+  else if constexpr (WV == kMmWaves)
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK, WV>), dim3(grid), block,
+                       lds, s, p);
   else
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK>), dim3(grid), dim3(kMmThreads), lds, s, p);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 template <int NB>
 static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
-  return p.packed ? mm_nbp<NB, true>(epi, p, grid, s) : mm_nbp<NB, false>(epi, p, grid, s);
+  if (!p.packed) return mm_nbp<NB, false, kMmWaves>(epi, p, grid, s);
+  if constexpr (NB >= 3) {
+    if (p.tile_rows == 2 * kMmTileRows) return mm_nbp<NB, true, 2 * kMmWaves>(epi, p, grid, s);
+  }
+  return mm_nbp<NB, true, kMmWaves>(epi, p, grid, s);
 }
 
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
@@ -387,6 +426,9 @@ hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   if (epi_is_argmax(epi) && (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
     return hipErrorInvalidValue;
   if (epi == EPI_STORE && !p.part) return hipErrorInvalidValue;
+  if (p.tile_rows != 0 && p.tile_rows != kMmTileRows &&
+      !(p.tile_rows == 2 * kMmTileRows && p.packed && epi != EPI_SAMPLE && p.B > 32))
+    return hipErrorInvalidValue;
   static_assert(16 * kMmChunk * 2 <= kDummyBytes && kMmPackBlock * 2 <= kDummyBytes,
                 "dummy region too small");
   if (!p.dummy) return hipErrorInvalidValue;

@@ -149,6 +149,9 @@ struct MmParams {
   int ldx;
   int B;
   int nsplit;   // divides mm_chunks(ncols)
+  // Rows per work item: 0 or 128 (four waves); 256 (eight waves) needs packed weights,
+  // 33..64 sequences and the store or greedy epilogue.
+  int tile_rows;
   float* part;  // EPI_STORE: [nsplit][16*NB][nrows]
   unsigned long long* keys;  // EPI_ARGMAX, as GemvParams
   unsigned* counter;
@@ -168,7 +171,7 @@ struct MmParams {
 };
 __host__ __device__ int mm_chunks(int ncols);  // K chunks of the contraction
 int mm_batch_pad(int B);                           // 16 * NB for batch B
-int mm_split(int nrows, int ncols, int B);         // K splits used for these sizes
+int mm_split(int nrows, int ncols, int B, int tile_rows);  // K splits used for these sizes
 // Packed copy of the logical matrix w0 | w1 | w2 (segments as in MmParams, [nrows, ncols]
 // bf16) for mm_kernel: blocks of 128 rows x 256 columns, block (tile, chunk) at element
 // (tile * chunks + chunk) * 32768, each block in the order the kernel's lanes load it, so
@@ -177,7 +180,12 @@ int mm_split(int nrows, int ncols, int B);         // K splits used for these si
 size_t mm_packed_elems(int nrows, int ncols);
 hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1, int seg2,
                        int nrows, int ncols, uint16_t* dst, hipStream_t s);
-int mm_grid(int nrows, int ncols, int B, int nsplit, int num_cu);
+int mm_grid(int nrows, int tile_rows, int nsplit, int num_cu);
+// Item rows, K splits (1 outside EPI_STORE) and grid of one contraction.
+struct MmPlan {
+  int tile_rows, nsplit, grid;
+};
+MmPlan mm_plan(Epi epi, int nrows, int ncols, int B, bool packed, int num_cu);
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s);
 
 // Row-wise steps between contractions, one workgroup per sequence b:

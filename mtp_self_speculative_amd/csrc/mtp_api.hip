@@ -66,6 +66,14 @@ void mm_shapes(const mtp_config& c, int shapes[5][2]) {
   }
 }
 
+// Most K splits a contraction of these sizes takes with 128- or 256-row items (sizes the
+// partials).
+int mm_split_max(int nrows, int ncols, int B) {
+  const int s1 = mm_split(nrows, ncols, B, 128);
+  const int s2 = mm_split(nrows, ncols, B, 256);
+  return s1 > s2 ? s1 : s2;
+}
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
@@ -110,7 +118,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
     size_t part = 0;
     for (int b = kMmMinBatch; b <= bmax; ++b)
       for (auto& sh : shapes) {
-        const size_t e = (size_t)mm_split(sh[0], sh[1], b) * mm_batch_pad(b) * sh[0];
+        const size_t e = (size_t)mm_split_max(sh[0], sh[1], b) * mm_batch_pad(b) * sh[0];
         if (e > part) part = e;
       }
     L.mm_part = take(part * 4);
@@ -146,8 +154,9 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
       L.cu_q_lo = take((size_t)mm_batch_pad(L.cu_rows) * L.cu_ld * 2);
       size_t part = 0;
       for (int b = kMmMinBatch; b <= L.cu_rows; ++b) {
-        const size_t e1 = (size_t)mm_split(c.hidden, 2 * c.hidden, b) * mm_batch_pad(b) * c.hidden;
-        const size_t e2 = (size_t)mm_split(kvd2, c.hidden, b) * mm_batch_pad(b) * kvd2;
+        const size_t e1 =
+            (size_t)mm_split_max(c.hidden, 2 * c.hidden, b) * mm_batch_pad(b) * c.hidden;
+        const size_t e2 = (size_t)mm_split_max(kvd2, c.hidden, b) * mm_batch_pad(b) * kvd2;
         part = e1 > part ? e1 : part;
         part = e2 > part ? e2 : part;
       }
@@ -487,11 +496,13 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
     m.w0 = w0; m.w1 = w1; m.w2 = w2; m.seg1 = seg1; m.seg2 = seg2;
     m.packed = pkp(pk_off);
     m.nrows = N; m.ncols = Kd; m.x = xq; m.x_lo = xq_lo; m.ldx = L.ldq; m.B = B;
-    m.nsplit = mm_split(N, Kd, B);
+    const MmPlan q = mm_plan(EPI_STORE, N, Kd, B, m.packed != nullptr, h->num_cu);
+    m.tile_rows = q.tile_rows;
+    m.nsplit = q.nsplit;
     m.part = part;
     m.dummy = h->ws + L.dummy;
     *ns = m.nsplit;
-    return launch_mm(EPI_STORE, m, mm_grid(N, Kd, B, m.nsplit, h->num_cu), s);
+    return launch_mm(EPI_STORE, m, q.grid, s);
   };
   auto red = [&](RedMode mode, int ns, int n_part, int n, const float* res, float* out,
                  float* dbg, const void* gain) -> hipError_t {
@@ -580,7 +591,10 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
         m.smp = *lo.smp;
         m.smp.row = k;
       }
-      return launch_mm(lo.smp ? EPI_SAMPLE : EPI_ARGMAX, m, mm_grid(V, H, B, 1, h->num_cu), s);
+      const Epi epi = lo.smp ? EPI_SAMPLE : EPI_ARGMAX;
+      const MmPlan q = mm_plan(epi, V, H, B, m.packed != nullptr, h->num_cu);
+      m.tile_rows = q.tile_rows;
+      return launch_mm(epi, m, q.grid, s);
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -862,7 +876,9 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
         m.counter = h->at<unsigned>(L.vh_cnt);
         m.tok_out = tok + r0; m.tok_out_stride = 1;
         m.dummy = h->ws + L.dummy;
-        e = launch_mm(EPI_ARGMAX, m, mm_grid(V, H, rows, 1, h->num_cu), s);
+        const MmPlan q = mm_plan(EPI_ARGMAX, V, H, rows, m.packed != nullptr, h->num_cu);
+        m.tile_rows = q.tile_rows;
+        e = launch_mm(EPI_ARGMAX, m, q.grid, s);
       } else {
         const float* x = reinterpret_cast<const float*>(src);
         if (c.dtype == MTP_BF16) {
@@ -930,12 +946,14 @@ mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
           MmParams m{};
           m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
           m.nrows = N; m.ncols = Kd; m.x = q; m.x_lo = qlo; m.ldx = L.cu_ld; m.B = rows;
-          m.nsplit = mm_split(N, Kd, rows);
+          const MmPlan pl = mm_plan(EPI_STORE, N, Kd, rows, packed != nullptr, h->num_cu);
+          m.tile_rows = pl.tile_rows;
+          m.nsplit = pl.nsplit;
           m.part = part;
           m.dummy = h->ws + L.dummy;
           m.packed = packed;
           *ns = m.nsplit;
-          return launch_mm(EPI_STORE, m, mm_grid(N, Kd, rows, m.nsplit, h->num_cu), s);
+          return launch_mm(EPI_STORE, m, pl.grid, s);
         };
         // The K/V rows of the packed [W_q; W_k; W_v] copy start at a whole 128-row tile
         // when n_q * d is a multiple of 128; the packed copy is tile-major.
