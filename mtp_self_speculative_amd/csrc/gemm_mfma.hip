@@ -119,14 +119,16 @@ int mm_grid(int nrows, int tile_rows, int nsplit, int num_cu) {
 // would otherwise take).
 // PK: W is read from the packed copy (p.packed). Each instantiation has one straight load
 // path: a branch per load (packed or not, live or not) made the compiler serialise loads.
-// WV: waves per workgroup, 32 rows each (4: 128-row items; 8: 256-row items, packed only,
-// wave w reading the (w % 4)-th quarter of packed block 2 * item + w / 4).
-template <int NB, int EPI, int OCC, bool PK, int WV>
+// WV, MT: waves per workgroup and 16-row slices per wave (4 x 2: 128-row items; other
+// shapes read packed blocks only, wave w taking slices w*MT .. w*MT+MT-1 of the item, each
+// 16-row slice of a packed block being contiguous).
+template <int NB, int EPI, int OCC, bool PK, int WV, int MT>
 __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
-  static_assert(WV == kMmWaves || (WV == 2 * kMmWaves && PK), "eight waves read packed blocks");
+  static_assert((WV == kMmWaves && MT == kMmMT) || (PK && WV * MT % 8 == 0),
+                "other item shapes read whole packed blocks");
   constexpr int BP = 16 * NB;
   constexpr int NT = WV * kWave;
-  constexpr int TR = 16 * kMmMT * WV;   // rows per item
+  constexpr int TR = 16 * MT * WV;   // rows per item
   constexpr int XPASS = BP * 32 / NT;  // 16-byte input loads per thread, plane and stage
   static_assert(XPASS * NT == BP * 32, "input staging must divide over the threads");
   extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][kMmLdsRow]
@@ -149,25 +151,26 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   auto chunk_of = [&](int it) { return (item_of(it) % p.nsplit) * C + it % C; };
   // first row of slice m of this wave in the tile of stage it
   auto slice_row = [&](int it, int m) {
-    return (item_of(it) / p.nsplit) * TR + (wave * kMmMT + m) * 16;
+    return (item_of(it) / p.nsplit) * TR + (wave * MT + m) * 16;
   };
 
 
-  u32x4 A[kMmMT][kMmKSteps], Bf[kMmMT][kMmKSteps];
+  u32x4 A[MT][kMmKSteps], Bf[MT][kMmKSteps];
   // Stages past the workgroup's last one are prefetched from the dummy region and never
   // consumed (packed: the same offsets in a 64 KB dummy block; else 16 rows of 256 bf16).
-  auto wload = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
+  auto wload = [&](u32x4 (&buf)[MT][kMmKSteps], int it) {
     const bool live = it < stages;
     if constexpr (PK) {  // contiguous 1 KB per wave instruction, one base per wave
       // the second block of a 256-row item past the last block row reads the dummy
-      const int brow = (item_of(it) / p.nsplit) * (WV / kMmWaves) + wave / kMmWaves;
+      const int sl0 = wave * MT;  // the wave's first 16-row slice in the item (8 per block)
+      const int brow = (item_of(it) / p.nsplit) * (TR / kMmTileRows) + sl0 / 8;
       const bool lw = live && brow < nblk_rows;
       const long blk = (long)brow * mm_chunks(Kd) + chunk_of(it);
       const uint16_t* bp = (lw ? p.packed + blk * kMmPackBlock
                                : static_cast<const uint16_t*>(p.dummy)) +
-                           (long)(wave % kMmWaves) * (kMmMT * kMmKSteps * kWave * 8) + lane * 8;
+                           (long)(sl0 % 8) * (kMmKSteps * kWave * 8) + lane * 8;
 #pragma unroll
-      for (int m = 0; m < kMmMT; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int k = 0; k < kMmKSteps; ++k)
           buf[m][k] = *reinterpret_cast<const u32x4*>(bp + (m * kMmKSteps + k) * kWave * 8);
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     const int c0 = live ? chunk_of(it) * kMmChunk + (lane >> 4) * 8 : (lane >> 4) * 8;
     const int cmax = live ? Kd - 8 : kMmChunk - 8;
 #pragma unroll
-    for (int m = 0; m < kMmMT; ++m) {
+    for (int m = 0; m < MT; ++m) {
       const int r = min(slice_row(it, m) + (lane & 15), N - 1);
       const uint16_t* rp = r < p.seg1 ? static_cast<const uint16_t*>(p.w0) + (long)r * Kd
                          : r < p.seg2 ? static_cast<const uint16_t*>(p.w1) + (long)(r - p.seg1) * Kd
@@ -219,9 +222,9 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     }
   };
 
-  f32x4 acc[kMmMT][NB];
+  f32x4 acc[MT][NB];
 #pragma unroll
-  for (int m = 0; m < kMmMT; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   unsigned long long best[NB];
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   for (int nb = 0; nb < NB; ++nb) best[nb] = 0ull;
 
   // Each input fragment read from LDS serves both 16-row slices of the wave.
-  auto consume = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
+  auto consume = [&](u32x4 (&buf)[MT][kMmKSteps], int it) {
     const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * kMmLdsRow + (lane & 15) * kMmLdsRow +
                          (lane >> 4) * 8;
 #pragma unroll
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
         const bf16x8 bl = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * kMmLdsRow + k * 32));
 #pragma unroll
-        for (int m = 0; m < kMmMT; ++m) {
+        for (int m = 0; m < MT; ++m) {
           const bf16x8 w = __builtin_bit_cast(bf16x8, buf[m][k]);
           acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bh, acc[m][nb], 0, 0, 0);
           acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bl, acc[m][nb], 0, 0, 0);
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   auto finish_item = [&](int it) {
     const int split = item_of(it) % p.nsplit;
 #pragma unroll
-    for (int m = 0; m < kMmMT; ++m) {
+    for (int m = 0; m < MT; ++m) {
       const int r0 = slice_row(it, m) + (lane >> 4) * 4;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     }
   };
 
-  auto stage = [&](u32x4 (&buf)[kMmMT][kMmKSteps], int it) {
+  auto stage = [&](u32x4 (&buf)[MT][kMmKSteps], int it) {
     xload(it + 1);
     consume(buf, it);
     wload(buf, it + 2);
@@ -392,16 +395,16 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
   return hipGetLastError();
 }
 
-template <int NB, bool PK, int WV>
+template <int NB, bool PK, int WV, int MT>
 static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   const size_t lds = mm_lds_bytes(NB);
   const dim3 block(WV * kWave);
   if (epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV>), dim3(grid), block, lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV, MT>), dim3(grid), block, lds, s, p);
   else if (epi == EPI_STORE)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK, WV>), dim3(grid), block, lds, s, p);
-  else if constexpr (WV == kMmWaves)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK, WV>), dim3(grid), block,
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK, WV, MT>), dim3(grid), block, lds, s, p);
+  else if constexpr (WV == kMmWaves && MT == kMmMT)
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK, WV, MT>), dim3(grid), block,
                        lds, s, p);
   else
     return hipErrorInvalidValue;
@@ -409,11 +412,11 @@ static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
 }
 template <int NB>
 static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
-  if (!p.packed) return mm_nbp<NB, false, kMmWaves>(epi, p, grid, s);
+  if (!p.packed) return mm_nbp<NB, false, kMmWaves, kMmMT>(epi, p, grid, s);
   if constexpr (NB >= 3) {
-    if (p.tile_rows == 2 * kMmTileRows) return mm_nbp<NB, true, 2 * kMmWaves>(epi, p, grid, s);
+    if (p.tile_rows == 2 * kMmTileRows) return mm_nbp<NB, true, 2 * kMmWaves, kMmMT>(epi, p, grid, s);
   }
-  return mm_nbp<NB, true, kMmWaves>(epi, p, grid, s);
+  return mm_nbp<NB, true, kMmWaves, kMmMT>(epi, p, grid, s);
 }
 
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
