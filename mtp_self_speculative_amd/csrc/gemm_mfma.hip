@@ -155,6 +155,10 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   };
 
 
+  // Streaming (non-temporal) weight loads keep the input operand's lines in L2. Measured on
+  // packed weights: the lm_head 4-10% faster at B = 8..64 and the B = 8 projections 2-9%;
+  // the K-split projections at B = 32..64 1-7% slower, so they load normally.
+  constexpr bool kStream = EPI != EPI_STORE || NB == 1;
   u32x4 A[MT][kMmKSteps], Bf[MT][kMmKSteps];
   // Stages past the workgroup's last one are prefetched from the dummy region and never
   // consumed (packed: the same offsets in a 64 KB dummy block; else 16 rows of 256 bf16).
@@ -172,8 +176,10 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int k = 0; k < kMmKSteps; ++k)
-          buf[m][k] = *reinterpret_cast<const u32x4*>(bp + (m * kMmKSteps + k) * kWave * 8);
+        for (int k = 0; k < kMmKSteps; ++k) {
+          const u32x4* a = reinterpret_cast<const u32x4*>(bp + (m * kMmKSteps + k) * kWave * 8);
+          buf[m][k] = kStream ? __builtin_nontemporal_load(a) : *a;
+        }
       return;
     }
     // Row pointers and column clamps as selects (no branch per load): columns past the row
