@@ -13,13 +13,15 @@
 // items in turn (a persistent grid); wave w owns two 16-row slices of the tile, which
 // share every input fragment it reads from LDS. Each item is walked in chunks of 256
 // columns: per chunk a wave streams 32 rows x 512 bytes of W (sixteen 16-byte loads per
-// lane, so every row piece is a full 64-byte segment) and runs 32 x NB MFMAs. The input rows (both planes) of the chunk are staged
-// once per workgroup in LDS (double-buffered) and read from there by all four waves. W stages
-// are double-buffered in registers; all loads are unconditional (indexes past the end
-// are clamped), so the compiler can wait for exactly the buffer being consumed.
+// lane, so every row piece is a full 64-byte segment) and runs 32 x NB MFMAs. The input
+// rows (both planes) of the chunk are staged once per workgroup in LDS (double-buffered)
+// and read from there by all waves. W stages are double-buffered in registers; all loads
+// are unconditional (indexes past the end are clamped), so the compiler can wait for
+// exactly the buffer being consumed.
 //
 // With a packed copy of W (launch_pack) the weight loads are contiguous instead: 1 KB per
-// wave instruction, each 128 x 256 block one 64 KB region.
+// wave instruction, each 128 x 256 block one 64 KB region. On packed weights at 33..64
+// sequences, items may also be 256 rows (eight waves over two blocks; see mm_plan).
 //
 // Epilogues: EPI_STORE writes the fp32 partial sums of the item's K split (a row-wise
 // reduction kernel adds the splits in a fixed order, so results are deterministic);

@@ -133,9 +133,9 @@ hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t 
 // ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions
 
 // y[b, r] = sum_c W[r, c] * x[b, c] for r < nrows, with W bf16 rows (segments as in
-// GemvParams) and x a bf16 operand [16*NB, ldx]. Work items are (64-row tile, K split);
-// EPI_STORE writes fp32 partial sums per split, EPI_ARGMAX (nsplit == 1) finishes an
-// argmax over r per batch row as the GEMV does.
+// GemvParams) and x a bf16 operand [16*NB, ldx]. Work items are (128- or 256-row item,
+// K split); EPI_STORE writes fp32 partial sums per split, EPI_ARGMAX (nsplit == 1)
+// finishes an argmax over r per batch row as the GEMV does.
 struct MmParams {
   const void* w0;
   const void* w1;
