@@ -70,11 +70,18 @@ def algorithmic_bytes(cfg, lens0, K: int, acc_sum_rows: int) -> dict:
 
 
 def lmhead_source_hash() -> str:
+    """Hash of the lm_head kernel's sources with comments and blank lines removed, so that
+    only a change of code (not of its comments) retires the recorded counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in LMHEAD_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        lines = [ln.rstrip() for ln in src.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
