@@ -222,6 +222,18 @@ __device__ __forceinline__ void rope_cs(int position, int i, int d, float theta,
 struct Philox4 {
   uint64_t w[4];
 };
+// 64 x 64 -> 128-bit product from four 32 x 32 + 64 -> 64-bit multiply-adds: with a, c split
+// into 32-bit halves, p1 = ah*cl + hi(al*cl) and p2 = al*ch + lo(p1) stay below 2^64, and
+// a*c = (ah*ch + hi(p1) + hi(p2)) * 2^64 + lo(p2) * 2^32 + lo(al*cl).
+__host__ __device__ __forceinline__ void mul64_wide(uint64_t a, uint64_t c, uint64_t& hi,
+                                                    uint64_t& lo) {
+  const uint64_t al = (uint32_t)a, ah = a >> 32, cl = (uint32_t)c, ch = c >> 32;
+  const uint64_t p0 = al * cl;
+  const uint64_t p1 = ah * cl + (p0 >> 32);
+  const uint64_t p2 = al * ch + (uint32_t)p1;
+  hi = ah * ch + (p1 >> 32) + (p2 >> 32);
+  lo = (p2 << 32) | (uint32_t)p0;
+}
 __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
                                                  uint64_t c3, uint64_t k0, uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
@@ -232,8 +244,9 @@ __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint6
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mul64_wide(M0, c0, hi0, lo0);
+    mul64_wide(M1, c2, hi1, lo1);
     c0 = hi1 ^ c1 ^ k0;
     c1 = lo1;
     c2 = hi0 ^ c3 ^ k1;
