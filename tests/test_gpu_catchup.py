@@ -27,9 +27,9 @@ CASES = {
     # eh_proj from the packed copy, the K/V rows from the row-major weights
     "bf16-mm-kv-rowmajor": small(name="cu5", cid=164, batch=4, K=3, hidden=320, n_q=5, n_kv=1,
                                  head_dim=64, ffn=640, vocab=2053, ctx_lo=3, ctx_hi=90),
-    # bf16, 12 x 4 = 48 rows on 256-row items: eh_proj's 384 rows end half-way through the
-    # second item, and the K/V rows start at the packed copy's third (odd) 128-row block
-    "bf16-mm-wide-items": small(name="cu6", cid=165, batch=12, K=4, hidden=384, n_q=3, n_kv=1,
+    # bf16, 12 x 4 = 48 rows (three 16-row tiles): eh_proj's 384 rows are three 128-row
+    # blocks, and the K/V rows start at the packed copy's third (odd) 128-row block
+    "bf16-mm-odd-kv-block": small(name="cu6", cid=165, batch=12, K=4, hidden=384, n_q=3, n_kv=1,
                                 head_dim=128, ffn=768, vocab=3001, ctx_lo=2, ctx_hi=150),
     # the Qwen3-8B-shaped head at full size, B=1 K=5 and B=32 K=3
     "q8b": S.get_config("q8b"),
