@@ -382,7 +382,9 @@ def main() -> int:
         head.verify_hidden(th, tn, drafts[args.warmup + it], vacc, vnxt)
     torch.cuda.synchronize()
     vh_us = (time.perf_counter() - t0v) / args.steps * 1e6
-    vh_passes = -(-(B * (K + 1)) // 64)
+    # rows per lm_head pass: 128 on the packed copy (bf16 heads made for 3+ sequences), else 64
+    vh_group = 128 if (cfg.dtype == "bf16" and B >= 3) else 64
+    vh_passes = -(-(B * (K + 1)) // vh_group)
     vh_bytes = vh_passes * cfg.vocab * cfg.hidden * (2 if cfg.dtype == "bf16" else 4) + \
         B * (K + 1) * cfg.hidden * (2 if cfg.dtype == "bf16" else 4)
     log(f"verify from hidden states: {vh_us:.2f} us per call")

@@ -41,8 +41,8 @@ constexpr int kMmMT = 2;                          // 16-row slices per wave
 constexpr int kMmTileRows = 16 * kMmMT * kMmWaves;  // 128: rows of a packed block
 constexpr int kMmChunk = 256;                     // columns per stage
 constexpr int kMmKSteps = kMmChunk / 32;          // MFMA k-steps per stage
-constexpr int kMmLdsRow = kMmChunk + 8;           // bf16 per LDS row: 16-byte pad against bank conflicts
-constexpr int kMmMaxNB = 4;
+constexpr int kMmMaxNB = 4;       // 16-sequence tiles of the general kernel
+constexpr int kMmMaxNBArgmax = 8;  // of the greedy lm_head on packed weights (half-chunk stages)
 constexpr int kMmMaxSplit = 16;  // the row-wise reductions add at most this many splits
 
 __host__ __device__ int mm_chunks(int ncols) { return (ncols + kMmChunk - 1) / kMmChunk; }
@@ -105,8 +105,8 @@ MmPlan mm_plan(Epi epi, int nrows, int ncols, int B, bool packed, int num_cu) {
   return q;
 }
 
-// LDS: [2 buffers][2 planes][16 NB rows][kMmLdsRow] bf16
-static size_t mm_lds_bytes(int nb) { return (size_t)4 * 16 * nb * kMmLdsRow * sizeof(uint16_t); }
+// LDS: [2 buffers][2 planes][16 NB rows][ck + 8] bf16
+static size_t mm_lds_bytes(int nb, int ck) { return (size_t)4 * 16 * nb * (ck + 8) * sizeof(uint16_t); }
 
 // Persistent grid: one workgroup per CU, or one per item when there are fewer items.
 int mm_grid(int nrows, int tile_rows, int nsplit, int num_cu) {
@@ -124,23 +124,30 @@ int mm_grid(int nrows, int tile_rows, int nsplit, int num_cu) {
 // WV, MT: waves per workgroup and 16-row slices per wave (4 x 2: 128-row items; other
 // shapes read packed blocks only, wave w taking slices w*MT .. w*MT+MT-1 of the item, each
 // 16-row slice of a packed block being contiguous).
-template <int NB, int EPI, int OCC, bool PK, int WV, int MT>
+// CK: columns per stage, 256 or (packed only, so that 128 input rows fit the LDS twice)
+// 128, each stage then reading one half of every packed block's columns.
+template <int NB, int EPI, int OCC, bool PK, int WV, int MT, int CK>
 __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   static_assert((WV == kMmWaves && MT == kMmMT) || (PK && WV * MT % 8 == 0),
                 "other item shapes read whole packed blocks");
+  static_assert(CK == kMmChunk || (PK && CK == kMmChunk / 2), "half chunks read packed blocks");
   constexpr int BP = 16 * NB;
   constexpr int NT = WV * kWave;
   constexpr int TR = 16 * MT * WV;   // rows per item
-  constexpr int XPASS = BP * 32 / NT;  // 16-byte input loads per thread, plane and stage
-  static_assert(XPASS * NT == BP * 32, "input staging must divide over the threads");
-  extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][kMmLdsRow]
+  constexpr int KS = CK / 32;        // MFMA k-steps per stage
+  constexpr int LROW = CK + 8;       // bf16 per LDS row: 16-byte pad against bank conflicts
+  constexpr int CPR = CK / 8;        // 16-byte column groups per input row and stage
+  constexpr int HALVES = kMmChunk / CK;
+  constexpr int XPASS = BP * CPR / NT;  // 16-byte input loads per thread, plane and stage
+  static_assert(XPASS * NT == BP * CPR, "input staging must divide over the threads");
+  extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][LROW]
   __shared__ unsigned long long kred[WV][BP];
   __shared__ uint64_t seed_s[EPI == EPI_SAMPLE ? BP : 1];  // random-stream seeds, read once
   __shared__ int flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = p.nrows, Kd = p.ncols;
-  const int C = mm_chunks(Kd) / p.nsplit;  // chunks per item
+  const int C = mm_chunks(Kd) * HALVES / p.nsplit;  // stages per item
   const int ntiles = (N + TR - 1) / TR;
   const int nblk_rows = (N + kMmTileRows - 1) / kMmTileRows;  // packed block rows
   const int nitems = ntiles * p.nsplit;
@@ -161,24 +168,25 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   // packed weights: the lm_head 4-10% faster at B = 8..64 and the B = 8 projections 2-9%;
   // the K-split projections at B = 32..64 1-7% slower, so they load normally.
   constexpr bool kStream = EPI != EPI_STORE || NB == 1;
-  u32x4 A[MT][kMmKSteps], Bf[MT][kMmKSteps];
+  u32x4 A[MT][KS], Bf[MT][KS];
   // Stages past the workgroup's last one are prefetched from the dummy region and never
   // consumed (packed: the same offsets in a 64 KB dummy block; else 16 rows of 256 bf16).
-  auto wload = [&](u32x4 (&buf)[MT][kMmKSteps], int it) {
+  auto wload = [&](u32x4 (&buf)[MT][KS], int it) {
     const bool live = it < stages;
     if constexpr (PK) {  // contiguous 1 KB per wave instruction, one base per wave
       // the second block of a 256-row item past the last block row reads the dummy
       const int sl0 = wave * MT;  // the wave's first 16-row slice in the item (8 per block)
       const int brow = (item_of(it) / p.nsplit) * (TR / kMmTileRows) + sl0 / 8;
       const bool lw = live && brow < nblk_rows;
-      const long blk = (long)brow * mm_chunks(Kd) + chunk_of(it);
+      const long blk = (long)brow * mm_chunks(Kd) + chunk_of(it) / HALVES;
       const uint16_t* bp = (lw ? p.packed + blk * kMmPackBlock
                                : static_cast<const uint16_t*>(p.dummy)) +
-                           (long)(sl0 % 8) * (kMmKSteps * kWave * 8) + lane * 8;
+                           (long)(sl0 % 8) * (kMmKSteps * kWave * 8) +
+                           (chunk_of(it) % HALVES) * (KS * kWave * 8) + lane * 8;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int k = 0; k < kMmKSteps; ++k) {
+        for (int k = 0; k < KS; ++k) {
           const u32x4* a = reinterpret_cast<const u32x4*>(bp + (m * kMmKSteps + k) * kWave * 8);
           buf[m][k] = kStream ? __builtin_nontemporal_load(a) : *a;
         }
@@ -196,18 +204,18 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
                                       : static_cast<const uint16_t*>(p.w2) + (long)(r - p.seg2) * Kd;
       rp = live ? rp : static_cast<const uint16_t*>(p.dummy) + (lane & 15) * kMmChunk;
 #pragma unroll
-      for (int k = 0; k < kMmKSteps; ++k)
+      for (int k = 0; k < KS; ++k)
         buf[m][k] = *reinterpret_cast<const u32x4*>(rp + min(c0 + k * 32, cmax));
     }
   };
 
   u32x4 xr[2][XPASS];
   auto xload = [&](int it) {
-    const int c0 = chunk_of(clampit(it)) * kMmChunk;
+    const int c0 = chunk_of(clampit(it)) * CK;
 #pragma unroll
     for (int j = 0; j < XPASS; ++j) {
       const int q = tid + j * NT;
-      const int row = q >> 5, col = c0 + (q & 31) * 8;
+      const int row = q / CPR, col = c0 + (q % CPR) * 8;
       const int rr = row < p.B ? row : p.B - 1;
       const int cc = col < Kd ? col : Kd - 8;
       const long o = (long)rr * p.ldx + cc;
@@ -216,16 +224,16 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     }
   };
   auto xstore = [&](int it, int bufi) {
-    const int c0 = chunk_of(clampit(it)) * kMmChunk;
+    const int c0 = chunk_of(clampit(it)) * CK;
 #pragma unroll
     for (int j = 0; j < XPASS; ++j) {
       const int q = tid + j * NT;
-      const int row = q >> 5, cp = q & 31;
+      const int row = q / CPR, cp = q % CPR;
       const bool live = row < p.B && c0 + cp * 8 < Kd;
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int pl = 0; pl < 2; ++pl)
-        *reinterpret_cast<u32x4*>(xl + ((long)(2 * bufi + pl) * BP + row) * kMmLdsRow + cp * 8) =
+        *reinterpret_cast<u32x4*>(xl + ((long)(2 * bufi + pl) * BP + row) * LROW + cp * 8) =
             live ? xr[pl][j] : z;
     }
   };
@@ -240,17 +248,17 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   for (int nb = 0; nb < NB; ++nb) best[nb] = 0ull;
 
   // Each input fragment read from LDS serves both 16-row slices of the wave.
-  auto consume = [&](u32x4 (&buf)[MT][kMmKSteps], int it) {
-    const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * kMmLdsRow + (lane & 15) * kMmLdsRow +
+  auto consume = [&](u32x4 (&buf)[MT][KS], int it) {
+    const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * LROW + (lane & 15) * LROW +
                          (lane >> 4) * 8;
 #pragma unroll
-    for (int k = 0; k < kMmKSteps; ++k) {
+    for (int k = 0; k < KS; ++k) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const bf16x8 bh = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(xb + nb * 16 * kMmLdsRow + k * 32));
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + nb * 16 * LROW + k * 32));
         const bf16x8 bl = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * kMmLdsRow + k * 32));
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * LROW + k * 32));
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const bf16x8 w = __builtin_bit_cast(bf16x8, buf[m][k]);
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     }
   };
 
-  auto stage = [&](u32x4 (&buf)[MT][kMmKSteps], int it) {
+  auto stage = [&](u32x4 (&buf)[MT][KS], int it) {
     xload(it + 1);
     consume(buf, it);
     wload(buf, it + 2);
@@ -419,15 +427,17 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
 
 template <int NB, bool PK, int WV, int MT>
 static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
-  const size_t lds = mm_lds_bytes(NB);
+  constexpr int CK = kMmChunk;
+  const size_t lds = mm_lds_bytes(NB, CK);
   const dim3 block(WV * kWave);
   if (epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV, MT>), dim3(grid), block, lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV, MT, CK>), dim3(grid), block, lds, s,
+                       p);
   else if (epi == EPI_STORE)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK, WV, MT>), dim3(grid), block, lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK, WV, MT, CK>), dim3(grid), block, lds, s, p);
   else if constexpr (WV == kMmWaves && MT == kMmMT)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK, WV, MT>), dim3(grid), block,
-                       lds, s, p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK, WV, MT, CK>), dim3(grid),
+                       block, lds, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -441,10 +451,30 @@ static hipError_t mm_nb(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   return mm_nbp<NB, true, kMmWaves, kMmMT>(epi, p, grid, s);
 }
 
+// 65..128 sequences (the greedy lm_head of verification from hidden states): eight
+// 16-sequence tiles, so that one pass over the lm_head serves them all. Two input planes of
+// 128 rows fit the LDS twice only at 128 columns per stage (136 KB), so each packed block
+// is read in two stages. With 256-row items (eight waves, two per SIMD, so that one wave's
+// MFMAs overlap another's LDS reads) the 128-row lm_head pass at q8b shapes takes 438 µs,
+// against 518 µs with four waves and 2 x 266 µs for two 64-row passes.
+static hipError_t mm_argmax_nb8(const MmParams& p, int grid, hipStream_t s) {
+  constexpr int CK = kMmChunk / 2;
+  if (p.tile_rows == 2 * kMmTileRows)
+    hipLaunchKernelGGL((mm_kernel<kMmMaxNBArgmax, EPI_ARGMAX, 1, true, 2 * kMmWaves, kMmMT, CK>),
+                       dim3(grid), dim3(2 * kMmWaves * kWave), mm_lds_bytes(kMmMaxNBArgmax, CK),
+                       s, p);
+  else
+    hipLaunchKernelGGL((mm_kernel<kMmMaxNBArgmax, EPI_ARGMAX, 1, true, kMmWaves, kMmMT, CK>),
+                       dim3(grid), dim3(kMmWaves * kWave), mm_lds_bytes(kMmMaxNBArgmax, CK), s,
+                       p);
+  return hipGetLastError();
+}
+
 hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   if (epi != EPI_STORE && !epi_is_argmax(epi)) return hipErrorInvalidValue;
   if (epi == EPI_SAMPLE && (!(p.smp.inv_temp > 0.f) || !p.smp.seeds)) return hipErrorInvalidValue;
-  if (p.B < 1 || p.B > 16 * kMmMaxNB || p.nrows < 1 || p.ncols < 8 || p.ncols % 8 != 0 ||
+  const int max_b = (epi == EPI_ARGMAX && p.packed ? kMmMaxNBArgmax : kMmMaxNB) * 16;
+  if (p.B < 1 || p.B > max_b || p.nrows < 1 || p.ncols < 8 || p.ncols % 8 != 0 ||
       p.ldx < p.ncols || p.ldx % 8 != 0 || !p.x || !p.x_lo || p.nsplit < 1 ||
       mm_chunks(p.ncols) % p.nsplit != 0 || grid < 1)
     return hipErrorInvalidValue;
@@ -452,7 +482,8 @@ hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
     return hipErrorInvalidValue;
   if (epi == EPI_STORE && !p.part) return hipErrorInvalidValue;
   if (p.tile_rows != 0 && p.tile_rows != kMmTileRows &&
-      !(p.tile_rows == 2 * kMmTileRows && p.packed && epi != EPI_SAMPLE && p.B > 32))
+      !(p.tile_rows == 2 * kMmTileRows && p.packed && epi != EPI_SAMPLE && p.B > 32 &&
+        (p.B <= 16 * kMmMaxNB || epi == EPI_ARGMAX)))
     return hipErrorInvalidValue;
   static_assert(16 * kMmChunk * 2 <= kDummyBytes && kMmPackBlock * 2 <= kDummyBytes,
                 "dummy region too small");
@@ -461,7 +492,8 @@ hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
     case 1: return mm_nb<1>(epi, p, grid, s);
     case 2: return mm_nb<2>(epi, p, grid, s);
     case 3: return mm_nb<3>(epi, p, grid, s);
-    default: return mm_nb<4>(epi, p, grid, s);
+    case 4: return mm_nb<4>(epi, p, grid, s);
+    default: return mm_argmax_nb8(p, grid, s);
   }
 }
 

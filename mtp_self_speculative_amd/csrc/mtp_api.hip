@@ -47,7 +47,8 @@ struct Layout {
 // Batched (MFMA) path: bf16 weights, 3..64 sequences, rows short enough for the
 // row-wise norm kernels.
 constexpr int kMmMinBatch = 3;
-constexpr int kVhGroup = 64;  // rows of target hidden states per lm_head pass
+constexpr int kVhGroup = 64;      // rows per pass of the general lm_head / contraction
+constexpr int kVhGroupPk = 128;   // rows per greedy lm_head pass on the packed copy
 constexpr int kMmMaxBatch = 64;
 bool mm_eligible(const mtp_config& c) {
   return c.dtype == MTP_BF16 && c.hidden <= red_max_cols();
@@ -126,7 +127,9 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   // verification from the target's hidden states
   {
     const long rows_all = (long)max_batch * (max_k + 1);
-    L.vh_rows = (int)(rows_all < kVhGroup ? rows_all : kVhGroup);
+    // the packed lm_head copy exists under the same condition as below
+    const int grp = mm_eligible(c) && max_batch >= kMmMinBatch ? kVhGroupPk : kVhGroup;
+    L.vh_rows = (int)(rows_all < grp ? rows_all : grp);
     L.vh_ld = (c.hidden + 7) / 8 * 8;
     L.vh_x = take((size_t)L.vh_rows * c.hidden * 4);
     L.vh_q = L.vh_q_lo = off;
