@@ -20,8 +20,11 @@ CASES = {
     "bf16-gemv": small(name="vh2", cid=151, batch=1, K=1, hidden=512, vocab=4099),
     # fp32, 2 x 4 rows: column-blocked GEMV
     "f32": small(name="vh3", cid=152, batch=2, K=3, hidden=256, vocab=3001, dtype="f32"),
-    # bf16, 20 x 4 = 80 rows: two groups (64 + 16) of lm_head passes
+    # bf16, 20 x 4 = 80 rows: one lm_head pass of eight 16-sequence tiles, three of them
+    # partly or wholly past the rows
     "bf16-groups": small(name="vh4", cid=153, batch=20, K=3, hidden=512, vocab=4099),
+    # bf16, 30 x 5 = 150 rows: two groups (128 + 22) of lm_head passes
+    "bf16-two-groups": small(name="vh6", cid=155, batch=30, K=4, hidden=384, vocab=5003),
     # K = 0: the target's token of row 0 only
     "bf16-k0": small(name="vh5", cid=154, batch=5, K=0),
     # full Qwen3-8B-shaped head (H=4096, V=151936), one sequence, K=5
