@@ -30,7 +30,8 @@ struct Layout {
   size_t dummy;        // zeroed target of never-consumed tail prefetches
   size_t xq, xq_lo, mm_part;  // batched path: bf16 operand planes, K-split partial sums
   int ldq;
-  // verification from hidden states: one group of up to kVhGroup rows at a time
+  // verification from hidden states: one group of up to kVhGroupPk rows at a time (with
+  // the packed lm_head copy; else kVhGroup)
   size_t vh_x, vh_q, vh_q_lo, vh_keys, vh_cnt, vh_tok;
   int vh_rows, vh_ld;
   // exact cache catch-up: one group of up to kVhGroup candidate rows at a time
