@@ -181,7 +181,8 @@ mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_le
  *                 outputs before its final norm at inputs [last_token, d_1 .. d_K]
  *   target_norm   [hidden] config dtype, 16-byte aligned: the target's final-norm gain
  *   draft_tokens, accepted_len, next_token: as mtp_verify.
- * Rows are processed in groups of up to 128 for bf16 heads created for 3 or more sequences,
+ * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192) created for 3 or
+ * more sequences,
  * else of up to 64 (each group streams the lm_head once).
  * Errors: as mtp_verify.
  */
