@@ -182,8 +182,7 @@ mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_le
  *   target_norm   [hidden] config dtype, 16-byte aligned: the target's final-norm gain
  *   draft_tokens, accepted_len, next_token: as mtp_verify.
  * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192) created for 3 or
- * more sequences,
- * else of up to 64 (each group streams the lm_head once).
+ * more sequences, else of up to 64 (each group streams the lm_head once).
  * Errors: as mtp_verify.
  */
 mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,
