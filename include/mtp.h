@@ -162,9 +162,15 @@ mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* 
                       void* stream);
 
 /*
- * Cut the MTP cache back to the committed prefix after a K-step draft:
+ * Cut the MTP cache back to the committed prefix after a K-step draft (devnotes, "How
+ * OpenVINO MTP Speculative Decoding Works Internally", "Stateful execution": the MTP
+ * layer's cache follows the committed sequence; OpenVINO GenAI "Speculative Decoding",
+ * "How Tree Drafting Works": after verification the caches are advanced to the accepted
+ * prefix only):
  *   len[b] += min(a+1, K) - K,  pos[b] += a + 1 - K,  a = accepted_len[b] (device).
  * Slot k was computed from the token committed iff k <= a+1; no KV data moves.
+ * K = 0 advances pos by 1 (the bonus token) and leaves len. Errors: host checks as
+ * mtp_draft; an accepted length outside [0, K] sets MTP_DEVERR_ACCEPT and is clamped.
  */
 mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,
                            int32_t K, void* stream);
@@ -257,9 +263,21 @@ mtp_status mtp_verify_sample(mtp_handle* h, const float* target_logits, const fl
                              const uint64_t* seeds, uint64_t offset, int32_t* accepted_len,
                              int32_t* next_token, void* stream);
 
-/* Synchronise `stream`, read and clear the device error word. *bits receives the
- * MTP_DEVERR_* bits (may be NULL). Returns MTP_ERR_DEVICE when any bit was set. */
+/* Synchronise `stream` (only that stream), read and clear the device error word. *bits
+ * receives the MTP_DEVERR_* bits (may be NULL). Returns MTP_ERR_DEVICE when any bit was
+ * set. Not for use under stream capture. */
 mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits);
+
+/* What a handle holds and how it groups rows (host only, no device call). */
+typedef struct {
+  size_t workspace_bytes;       /* device workspace the handle uses (mtp_workspace_size)      */
+  size_t packed_weight_bytes;   /* of which: the re-laid-out weight copy (0 when none)        */
+  int32_t verify_hidden_group_rows; /* rows per lm_head pass of mtp_verify_hidden             */
+  int32_t catchup_group_rows;   /* candidate rows per pass of mtp_kv_catchup                  */
+  int32_t matrix_core_min_batch; /* draft batches in [min, max] run the matrix-core path;     */
+  int32_t matrix_core_max_batch; /* both 0 when the configuration has no such path (fp32)    */
+} mtp_info;
+mtp_status mtp_get_info(const mtp_handle* h, mtp_info* out);
 
 /*
  * Kernel timing with HIP events, for measurement only. Bit i of `mask` brackets every

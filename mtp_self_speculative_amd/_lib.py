@@ -54,6 +54,14 @@ class mtp_kv(ctypes.Structure):
                 ("capacity", ctypes.c_int32)]
 
 
+class mtp_info(ctypes.Structure):
+    _fields_ = [("workspace_bytes", ctypes.c_size_t), ("packed_weight_bytes", ctypes.c_size_t),
+                ("verify_hidden_group_rows", ctypes.c_int32),
+                ("catchup_group_rows", ctypes.c_int32),
+                ("matrix_core_min_batch", ctypes.c_int32),
+                ("matrix_core_max_batch", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SIGS = {
@@ -72,6 +80,7 @@ _SIGS = {
     "mtp_kv_catchup": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _P, _P, _I, _I, _P]),
     "mtp_kv_rollback": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P]),
     "mtp_get_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
+    "mtp_get_info": (_I, [_P, ctypes.POINTER(mtp_info)]),
     "mtp_set_profiling": (_I, [_P, ctypes.c_uint32]),
     "mtp_get_profile": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I), _I]),
     "mtp_destroy": (None, [_P]),
@@ -211,6 +220,13 @@ def mtp_get_error(handle: int, stream: int | None) -> int:
     if st not in (MTP_OK, 7):
         _check(st, "mtp_get_error")
     return int(bits.value)
+
+
+def mtp_get_info(handle: int) -> dict:
+    """Workspace bytes, packed-copy bytes and row grouping of a handle (host only)."""
+    info = mtp_info()
+    _check(LIB.mtp_get_info(handle, ctypes.byref(info)), "mtp_get_info")
+    return {n: int(getattr(info, n)) for n, _ in mtp_info._fields_}
 
 
 KERNEL_CLASSES = ("eh_proj", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head_argmax",

@@ -1030,14 +1030,39 @@ mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_le
 mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits) {
   if (!h) return MTP_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipStreamSynchronize(s) != hipSuccess) return MTP_ERR_HIP;
+  // Only the caller's stream is waited for: the error word is written by work on it.
   unsigned v = 0;
   unsigned* dev = h->at<unsigned>(h->L.err);
-  if (hipMemcpy(&v, dev, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MTP_ERR_HIP;
-  if (v && hipMemset(dev, 0, sizeof(v)) != hipSuccess) return MTP_ERR_HIP;
-  if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;
+  if (hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MTP_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MTP_ERR_HIP;
+  if (v) {
+    if (hipMemsetAsync(dev, 0, sizeof(v), s) != hipSuccess) return MTP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MTP_ERR_HIP;
+  }
   if (bits) *bits = v;
   return v ? MTP_ERR_DEVICE : MTP_OK;
+}
+
+mtp_status mtp_get_info(const mtp_handle* h, mtp_info* out) {
+  if (!h || !out) return MTP_ERR_INVALID_ARG;
+  const Layout& L = h->L;
+  mtp_info i{};
+  i.workspace_bytes = L.total;
+  if (L.pk_lm) {
+    const mtp_config& c = h->cfg;
+    const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    i.packed_weight_bytes =
+        2 * (mm_packed_elems(H, 2 * H) + mm_packed_elems(qd + 2 * kvd, H) +
+             mm_packed_elems(H, qd) + mm_packed_elems(2 * c.ffn, H) +
+             mm_packed_elems(H, c.ffn) + mm_packed_elems(c.vocab, H));
+  }
+  i.verify_hidden_group_rows = L.vh_rows;
+  i.catchup_group_rows = L.cu_rows;
+  i.matrix_core_min_batch = mm_eligible(h->cfg) ? kMmMinBatch : 0;
+  i.matrix_core_max_batch = mm_eligible(h->cfg) ? kMmMaxBatch : 0;
+  *out = i;
+  return MTP_OK;
 }
 
 }  // extern "C"

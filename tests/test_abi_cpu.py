@@ -140,3 +140,96 @@ def test_adapt_k_entry_point():
     assert L.LIB.mtp_adapt_k(arr, 2, 5, 4, 3, ctypes.byref(out)) == 2
     assert L.LIB.mtp_adapt_k(arr, 2, 5, 1, 101, ctypes.byref(out)) == 2
     assert out.value == -7
+
+
+def _cpu_head(B=3, K=4, H=64, V=100, n_q=2, n_kv=1, d=64, F=128, dtype=None):
+    """An MtpHead whose checks accept CPU tensors and whose handle is null: a call that
+    passes the host-side checks reaches the library, which rejects the null handle."""
+    import torch
+    from mtp_self_speculative_amd.head import MtpHead
+    h = object.__new__(MtpHead)
+    h._device_type = "cpu"
+    h.dtype = dtype or torch.bfloat16
+    h.cfg = L.make_config(H, n_q, n_kv, d, F, V, 1e6, 1e-6, L.MTP_BF16)
+    h.max_batch, h.max_k, h.max_capacity = B, K, 64
+    h.handle = None
+    return h
+
+
+class _Stream:
+    cuda_stream = 0
+
+
+def test_head_rejects_mismatched_tensors_before_the_library():
+    """Wrong shape, dtype, device or layout raises ValueError on the host (the kernels
+    would otherwise read or write past the buffers); well-formed arguments reach the
+    library, which returns MTP_ERR_INVALID_ARG for the null handle."""
+    import torch
+    from mtp_self_speculative_amd.head import MtpCache
+    B, K, H, V = 3, 4, 64, 100
+    h = _cpu_head(B, K, H, V)
+    s = _Stream()
+    i32 = torch.int32
+    cache = MtpCache(torch.zeros((B, 1, 16, 64), dtype=torch.bfloat16),
+                     torch.zeros((B, 1, 16, 64), dtype=torch.bfloat16),
+                     torch.zeros(B, dtype=i32), torch.zeros(B, dtype=i32))
+    hid = torch.zeros((B, H), dtype=torch.bfloat16)
+    lt = torch.zeros(B, dtype=i32)
+    logits = torch.zeros((B, K + 1, V), dtype=torch.float32)
+    d = torch.zeros((B, K), dtype=i32)
+    acc = torch.zeros(B, dtype=i32)
+    th = torch.zeros((B, K + 1, H), dtype=torch.bfloat16)
+    tn = torch.zeros(H, dtype=torch.bfloat16)
+    bad = [
+        lambda: h.verify(torch.zeros((B, K + 1, V - 1)), d, stream=s),        # short rows
+        lambda: h.verify(logits.double(), d, stream=s),                        # dtype
+        lambda: h.verify(logits, d.long(), stream=s),                          # int64 drafts
+        lambda: h.verify(logits, d[:, :K - 1].contiguous(), stream=s),         # drafts short
+        lambda: h.verify(logits, d, acc[:B - 1], stream=s),                    # accepted short
+        lambda: h.verify(logits, None, stream=s),                              # drafts missing
+        lambda: h.verify(torch.zeros((B, K + 2, V)), None, stream=s),          # K > max_k
+        lambda: h.verify(logits.transpose(0, 1).contiguous().transpose(0, 1), d, stream=s),
+        lambda: h.draft(hid.float(), lt, cache, K, stream=s),                  # hidden dtype
+        lambda: h.draft(hid[:, :H - 8].contiguous(), lt, cache, K, stream=s),  # hidden width
+        lambda: h.draft(hid, lt.long(), cache, K, stream=s),                   # token dtype
+        lambda: h.draft(hid, lt[:2].contiguous(), cache, K, stream=s),         # tokens short
+        lambda: h.draft(hid, lt, cache, K + 1, stream=s),                      # K > max_k
+        lambda: h.verify_hidden(th.float(), tn, d, stream=s),
+        lambda: h.verify_hidden(th, tn[:H // 2].contiguous(), d, stream=s),
+        lambda: h.verify_hidden(th[:, :, :H - 8].contiguous(), tn, d, stream=s),
+        lambda: h.catchup(cache, th, d, acc.long(), stream=s),
+        lambda: h.catchup(cache, th[:, :1].contiguous(), d[:, :0].contiguous(), acc, stream=s),
+        lambda: h.rollback(cache, acc.long(), K, stream=s),
+        lambda: h.rollback(cache, torch.zeros(B + 1, dtype=i32), K, stream=s),
+        lambda: h.draft_sample(hid, lt, cache, K, 1.0, torch.zeros(B, dtype=i32), 0, stream=s),
+        lambda: h.verify_sample(logits, torch.zeros((B, K, V - 1)), d, 1.0,
+                                torch.zeros(B, dtype=torch.int64), 0, stream=s),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(ValueError):
+            f()
+    bad_cache = MtpCache(torch.zeros((B, 2, 16, 64), dtype=torch.bfloat16),
+                         torch.zeros((B, 2, 16, 64), dtype=torch.bfloat16),
+                         torch.zeros(B, dtype=i32), torch.zeros(B, dtype=i32))
+    with pytest.raises(ValueError):                                            # n_kv mismatch
+        h.draft(hid, lt, bad_cache, K, stream=s)
+    with pytest.raises(ValueError):
+        MtpCache(torch.zeros((B, 1, 16, 64)), torch.zeros((B, 1, 16, 64)),
+                 torch.zeros(B, dtype=torch.int64), torch.zeros(B, dtype=i32))
+    good = [
+        lambda: h.verify(logits, d, stream=s),
+        lambda: h.draft(hid, lt, cache, K, stream=s),
+        lambda: h.verify_hidden(th, tn, d, stream=s),
+        lambda: h.catchup(cache, th, d, acc, stream=s),
+        lambda: h.rollback(cache, acc, K, stream=s),
+    ]
+    for f in good:
+        with pytest.raises(L.MtpError) as e:
+            f()
+        assert e.value.status == 1
+
+
+def test_get_info_rejects_null():
+    info = L.mtp_info()
+    assert L.LIB.mtp_get_info(None, ctypes.byref(info)) == 1
+

@@ -32,7 +32,7 @@ CASES = {
     "bf16-mm-odd-kv-block": small(name="cu6", cid=165, batch=12, K=4, hidden=384, n_q=3, n_kv=1,
                                 head_dim=128, ffn=768, vocab=3001, ctx_lo=2, ctx_hi=150),
     # bf16, 33 x 4 = 132 rows: three groups (64, 64, then 4), all on the matrix cores
-    "bf16-two-groups": small(name="cu7", cid=166, batch=33, K=4, hidden=256, n_q=4, n_kv=2,
+    "bf16-three-groups": small(name="cu7", cid=166, batch=33, K=4, hidden=256, n_q=4, n_kv=2,
                              head_dim=64, ffn=512, vocab=3001, ctx_lo=2, ctx_hi=100),
     # the Qwen3-8B-shaped head at full size, B=1 K=5 and B=32 K=3
     "q8b": S.get_config("q8b"),

@@ -259,17 +259,35 @@ def test_device_error_paths_stay_in_bounds():
 
 
 def test_host_validation_errors():
+    """Out-of-range K and B are refused twice over: by the wrapper (ValueError, before the
+    library) and by the library itself (status returned before any launch)."""
+    import ctypes
+
     from mtp_self_speculative_amd import MtpError
+    from mtp_self_speculative_amd import _lib as L
     cfg = CASES["small-bf16"]
     inp = S.make_inputs(cfg, capacity=320)
     head, cache = make_head(cfg, inp)
     hid = to_dev(inp.hidden, cfg.dtype)
     lt = torch.from_numpy(inp.last_tokens).cuda()
-    with pytest.raises(MtpError):
+    out = torch.zeros((cfg.batch, cfg.K + 1), dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(ValueError):
         head.draft(hid, lt, cache, cfg.K + 1)          # K > max_k
+    with pytest.raises(MtpError) as e:
+        L.mtp_draft(head.handle, hid.data_ptr(), lt.data_ptr(), cache.kv, cfg.batch, cfg.K + 1,
+                    out.data_ptr(), s)
+    assert e.value.status == 4
     big = torch.zeros((cfg.batch + 1, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(MtpError):
-        head.draft(big, torch.zeros(cfg.batch + 1, dtype=torch.int32, device="cuda"), cache, 1)
+    lt1 = torch.zeros(cfg.batch + 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        head.draft(big, lt1, cache, 1)
+    with pytest.raises(MtpError) as e:
+        L.mtp_draft(head.handle, big.data_ptr(), lt1.data_ptr(), cache.kv, cfg.batch + 1, 1,
+                    out.data_ptr(), s)
+    assert e.value.status == 4
+    assert L.LIB.mtp_draft(head.handle, hid.data_ptr(), lt.data_ptr(), ctypes.byref(cache.kv),
+                           cfg.batch, -1, out.data_ptr(), s) == 2
     head.close()
 
 
