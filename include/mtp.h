@@ -268,6 +268,24 @@ mtp_status mtp_verify_sample(mtp_handle* h, const float* target_logits, const fl
  * set. Not for use under stream capture. */
 mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits);
 
+/*
+ * Greedy verification that allocates nothing and needs no handle, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments and results as mtp_verify, with the vocabulary size
+ * passed directly; the kernels' per-row keys and per-sequence completion counters live in a
+ * fixed 320 KiB device array of the library (one per GPU, held until the process ends)
+ * instead of a workspace, and each call clears the part it uses with a kernel before
+ * verifying. Limits: 1 <= B <= MTP_NOALLOC_MAX_BATCH, 0 <= K <= 100 (MTP_ERR_CAPACITY
+ * beyond), vocab >= 1. The stream must belong to the current device. Every call on one GPU
+ * uses that GPU's array: calls that overlap in time on one GPU (different streams or
+ * host threads without ordering) race and give undefined results; calls ordered on one
+ * stream are safe. Never calls hipMalloc or hipFree.
+ */
+#define MTP_NOALLOC_MAX_BATCH 256
+mtp_status mtp_verify_noalloc(const float* target_logits, const int32_t* draft_tokens,
+                              int32_t B, int32_t K, int32_t vocab, int32_t* accepted_len,
+                              int32_t* next_token, void* stream);
+
 /* What a handle holds and how it groups rows (host only, no device call). */
 typedef struct {
   size_t workspace_bytes;       /* device workspace the handle uses (mtp_workspace_size)      */

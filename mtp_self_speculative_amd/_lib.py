@@ -81,6 +81,7 @@ _SIGS = {
     "mtp_kv_rollback": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P]),
     "mtp_get_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "mtp_get_info": (_I, [_P, ctypes.POINTER(mtp_info)]),
+    "mtp_verify_noalloc": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "mtp_set_profiling": (_I, [_P, ctypes.c_uint32]),
     "mtp_get_profile": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I), _I]),
     "mtp_destroy": (None, [_P]),
@@ -175,6 +176,12 @@ def mtp_verify(handle: int, target_logits: int, draft_tokens: int | None, B: int
                accepted_len: int, next_token: int, stream: int | None) -> None:
     _check(LIB.mtp_verify(handle, target_logits, draft_tokens, B, K, accepted_len, next_token,
                           stream), "mtp_verify")
+
+
+def mtp_verify_noalloc(target_logits: int, draft_tokens: int | None, B: int, K: int, vocab: int,
+                       accepted_len: int, next_token: int, stream: int | None) -> None:
+    _check(LIB.mtp_verify_noalloc(target_logits, draft_tokens, B, K, vocab, accepted_len,
+                                  next_token, stream), "mtp_verify_noalloc")
 
 
 def mtp_draft_sample(handle: int, hidden: int, last_tokens: int, kv: mtp_kv, B: int, K: int,

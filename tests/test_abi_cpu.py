@@ -233,3 +233,14 @@ def test_get_info_rejects_null():
     info = L.mtp_info()
     assert L.LIB.mtp_get_info(None, ctypes.byref(info)) == 1
 
+
+def test_verify_noalloc_host_checks():
+    """Argument checks of the allocation-free verification happen before any device call."""
+    p = ctypes.c_void_p(16)
+    assert L.LIB.mtp_verify_noalloc(None, p, 1, 1, 8, p, p, None) == 1
+    assert L.LIB.mtp_verify_noalloc(p, None, 1, 1, 8, p, p, None) == 1
+    assert L.LIB.mtp_verify_noalloc(p, p, 0, 1, 8, p, p, None) == 2
+    assert L.LIB.mtp_verify_noalloc(p, p, 1, -1, 8, p, p, None) == 2
+    assert L.LIB.mtp_verify_noalloc(p, p, 1, 1, 0, p, p, None) == 2
+    assert L.LIB.mtp_verify_noalloc(p, p, 257, 1, 8, p, p, None) == 4
+    assert L.LIB.mtp_verify_noalloc(p, p, 1, 101, 8, p, p, None) == 4
