@@ -293,40 +293,32 @@ def test_host_validation_errors():
 
 def test_q8b_full_size_parity():
     """The Qwen3-8B-shaped head at its real sizes (bf16, H=4096, V=151936, L=4096, K=5)
-    in the launch configuration the benchmark times, against the full oracle."""
+    in the launch configuration the benchmark times, against the full oracle: tokens,
+    hidden states, the max logit and every logit of every step."""
     cfg = S.get_config("q8b")
     inp = S.make_inputs(cfg, capacity=4096 + 64)
-    g = run_draft(cfg, inp, cfg.K, want_logits=False)
+    g = run_draft(cfg, inp, cfg.K, want_logits=True)
     r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
-    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
     assert n >= 4
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
 
-@pytest.mark.parametrize("name,sample", [("q8b-b32", None), ("q32b", (0, 5)), ("wide", (0, 31, 63))])
-def test_batched_full_size_sampled_parity(name, sample):
+@pytest.mark.parametrize("name", ["q8b-b32", "q32b", "wide"])
+def test_batched_full_size_parity(name):
     """The batched workloads at their real sizes, in the launch configuration the
-    benchmark times: every sequence of the batch runs on the GPU, the oracle recomputes a
-    sample of them (sequences are independent: the shortest and longest caches of the
-    ragged batch, else the listed ones)."""
+    benchmark times, against one oracle run over the whole batch: every sequence's
+    tokens (bit-exact above the near-tie margin, teacher-forced), hidden states, max
+    logits and every logit of every step, and every sequence's new cache slots."""
     cfg = S.get_config(name)
     lens = S.cache_lengths(cfg)
     inp = S.make_inputs(cfg, capacity=int(lens.max()) + cfg.K + 8)
-    g = run_draft(cfg, inp, cfg.K, want_logits=False)
-    idx = np.array(sample if sample else (int(np.argmin(lens)), int(np.argmax(lens))))
-    W = O.OracleWeights(cfg, inp.weights)
-    kc, vc = inp.k_cache[idx].copy(), inp.v_cache[idx].copy()
-    r = O.draft(cfg, W, inp.hidden[idx], inp.last_tokens[idx], kc, vc, inp.lens[idx],
-                inp.pos[idx], cfg.K, force_tokens=g["tokens"][idx])
-    n = compare_draft(cfg, r, g["tokens"][idx], g["hidden"][:, idx], g["max"][:, idx])
-    assert n >= len(idx) * cfg.K // 2
-    assert np.array_equal(g["len"], inp.lens + cfg.K) and np.array_equal(g["pos"], inp.pos + cfg.K)
-    for j, b in enumerate(idx):
-        L0 = int(inp.lens[b])
-        for name_, oc in (("k", kc), ("v", vc)):
-            new_g = O.as_float(g[name_][b, :, L0:L0 + cfg.K], cfg.dtype)
-            new_o = O.as_float(oc[j, :, L0:L0 + cfg.K], cfg.dtype)
-            assert np.allclose(new_g, new_o, rtol=1e-2, atol=TOL[cfg.dtype])
+    print(f"full-size batched parity: {name} B={cfg.batch} K={cfg.K}", flush=True)
+    g = run_draft(cfg, inp, cfg.K, want_logits=True)
+    r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    assert n >= cfg.batch * cfg.K // 2, f"only {n} tokens above the near-tie margin"
+    check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
 
 def test_speculative_decoding_with_gpu_head_equals_greedy():
