@@ -27,6 +27,8 @@ chunk), so the values depend neither on the thread count nor on the machine.
     stream 15 logits for sampling verification (sub 2*it: target rows, N(0, scale^2);
               sub 2*it+1: draft-row perturbation, N(0, noise^2))
     stream 16 per-sequence random-stream seeds, uniform 63-bit integers
+    stream 17 target hidden states over a prompt (prefill), N(0, 1) (sub = call)
+    stream 18 the token after each prompt position (prefill), uniform over the vocabulary
 
 bf16 configurations draw in fp32 and round to bf16 (round to nearest even);
 bf16 arrays are carried as their uint16 bit patterns.
@@ -171,6 +173,17 @@ def target_hidden(cfg: Config, K: int, it: int = 0) -> np.ndarray:
 def target_norm(cfg: Config) -> np.ndarray:
     """The target's final-norm gain, [H]."""
     return normal(cfg.cid, 14, 0, cfg.hidden, 1.0, 0.02, cfg.dtype)
+
+
+def prefill_hidden(cfg: Config, n: int, sub: int = 0) -> np.ndarray:
+    """The target's pre-norm hidden states at n prompt positions, [B, n, H], N(0, 1)."""
+    return normal(cfg.cid, 17, sub, cfg.batch * n * cfg.hidden, 0.0, 1.0,
+                  cfg.dtype).reshape(cfg.batch, n, cfg.hidden)
+
+
+def prefill_tokens(cfg: Config, n: int, sub: int = 0) -> np.ndarray:
+    """The token after each of n prompt positions, [B, n] int32, uniform over the vocabulary."""
+    return _rng(cfg.cid, 18, sub).integers(0, cfg.vocab, size=(cfg.batch, n)).astype(np.int32)
 
 
 def last_tokens(cfg: Config) -> np.ndarray:

@@ -41,6 +41,9 @@ Readings where the pages are silent (each is the plainest one the rest supports)
     next_token is the target's argmax at the first mismatch (row K if all match).
   rollback: slot k (from the pair (h^(k-1), tok_{k-1})) is kept iff tok_{k-1}
     was committed, so len advances by min(a+1, K) and pos by a+1.
+  prefill: the slot of prompt position s holds the pair (verifier hidden state at s,
+    token s+1), the same pair a one-step draft at s would process; after a prompt of
+    P tokens the cache holds P-1 slots and the first draft takes (h_{P-1}, x_P).
 """
 from __future__ import annotations
 
@@ -366,6 +369,53 @@ def kv_catchup(cfg, W: OracleWeights, target_hidden: np.ndarray, draft_tokens: n
                 k_cache[b, :, slot, :] = kb.astype(np.float32)
                 v_cache[b, :, slot, :] = vn.astype(np.float32)
     return lens - K + acc + 1, pos - K + acc + 1
+
+
+def kv_prefill(cfg, W: OracleWeights, target_hidden: np.ndarray, tokens: np.ndarray,
+               k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray, pos: np.ndarray,
+               n_valid: np.ndarray | None = None):
+    """Fill the MTP cache over a prompt from the verifier's hidden states.  [OVMTP] KV cache
+    and Stateful execution (the MTP layer keeps its own one-layer cache, filled for every
+    position it has seen); [SPEC] Architecture (the layer's input at position s is the
+    projection of the normalised verifier hidden state at s and the normalised embedding of
+    the token that follows it).
+
+    target_hidden [B, n, H] (storage dtype): the target's last-layer outputs before its
+    final norm at n consecutive positions pos[b] .. pos[b]+n-1; tokens [B, n]: the token
+    after each of those positions (row s pairs h_s with x_{s+1}). For every sequence b and
+    s < n_valid[b] (default n), the pair runs through the layer's input side (embedding
+    gather, separate RMSNorms, concat, eh_proj, attention norm, K/V projections, RoPE at
+    position pos[b]+s) and is written to slot lens[b]+s in the cache dtype.
+    Returns lens + n_valid, pos + n_valid.
+    """
+    dt = W.dt
+    w = W.w
+    nkv, d = cfg.n_kv, cfg.head_dim
+    eps = cfg.rms_eps
+    th = as_float(target_hidden, cfg.dtype, dt)
+    B, n = th.shape[0], th.shape[1]
+    tok = np.asarray(tokens, np.int64).reshape(B, n)
+    nv = np.full(B, n, np.int64) if n_valid is None else np.asarray(n_valid, np.int64)
+    lens = np.asarray(lens, np.int64)
+    pos = np.asarray(pos, np.int64)
+    for b in range(B):
+        for s in range(int(nv[b])):
+            e = W.embed_rows(tok[b, s:s + 1])
+            x = np.concatenate([rmsnorm(th[b, s][None], w["g_h"], eps),
+                                rmsnorm(e, w["g_e"], eps)], axis=1) @ w["w_eh"].T
+            a = rmsnorm(x, w["g_attn"], eps)
+            kn = (a @ w["w_k"].T).reshape(nkv, d)
+            vn = (a @ w["w_v"].T).reshape(nkv, d)
+            cos, sin = rope_tables(int(pos[b]) + s, d, cfg.rope_theta, dt)
+            kb = rope(kn, cos, sin)
+            slot = int(lens[b]) + s
+            if cfg.dtype == "bf16":
+                k_cache[b, :, slot, :] = _store_bf16(kb)
+                v_cache[b, :, slot, :] = _store_bf16(vn)
+            else:
+                k_cache[b, :, slot, :] = kb.astype(np.float32)
+                v_cache[b, :, slot, :] = vn.astype(np.float32)
+    return lens + nv, pos + nv
 
 
 def adapt_k(accepted_len, K: int, k_min: int, k_max: int) -> int:

@@ -476,13 +476,17 @@ def test_speculative_with_adaptive_k_equals_greedy():
     assert len(set(st["ks"])) > 1
 
 
-def _catchup_run(cfg, inp, W, tgt, prompt, n_new, K0, next_k, bad_at):
+def _catchup_run(cfg, inp, W, tgt, prompt, n_new, K0, next_k, bad_at, init=None):
     """Greedy speculative decoding with exact catch-up. The head runs every draft step
     (writing its cache) teacher-forced on the target's own greedy continuation with one
     planted error at index bad_at(iteration, K) (none when that is K, so all K drafts are
-    accepted). Returns the emitted tokens, accepted lengths and the head's cache state."""
+    accepted). init: the head's starting cache state (default: empty, at the position of
+    the prompt's last token). Returns the emitted tokens, accepted lengths and the head's
+    cache state."""
     st = {"kc": np.zeros_like(inp.k_cache), "vc": np.zeros_like(inp.v_cache),
           "len": np.array([0]), "pos": np.array([len(prompt) - 1]), "it": 0}
+    if init is not None:
+        st.update(init)
 
     def draft_fn(h, last, K, seq):
         cont = tgt.greedy(seq, K)
@@ -579,3 +583,81 @@ def test_speculative_equals_greedy_with_scripted_drafts():
     out, acc = speculative_greedy(tgt, prompt, 30, draft_fn, verify_fn, lambda a: None, K)
     assert out == ref
     assert acc == [i % (K + 1) for i in range(len(acc))]
+
+
+# ----------------------------------------------------------------------------- prompt prefill
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_equals_one_step_drafts(dtype):
+    """Prefill writes, for each prompt position s, the slot a one-step draft at s would
+    write from the same pair (verifier hidden state h_s, token x_{s+1}): the layer's input
+    side only, at RoPE position pos+s, slot len+s. Ragged counts leave the rows past a
+    sequence's count unread (NaN there changes nothing) and its later slots untouched."""
+    cfg = small_cfg(cid=93, batch=3, ctx_lo=4, ctx_hi=9, dtype=dtype)
+    n = 7
+    inp = _inputs(cfg, 40)
+    W = O.OracleWeights(cfg, inp.weights)
+    th = S.prefill_hidden(cfg, n)
+    tok = S.prefill_tokens(cfg, n)
+    nv = np.array([n, n - 3, 0])
+    th_p = th.copy()
+    if dtype == "bf16":
+        th_p[1, n - 3:] = 0x7FC0
+    else:
+        th_p[1, n - 3:] = np.nan
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    pos0 = inp.pos + 11
+    ln, ps = O.kv_prefill(cfg, W, th_p, tok, kc, vc, inp.lens, pos0, nv)
+    assert np.array_equal(ln, inp.lens + nv) and np.array_equal(ps, pos0 + nv)
+    rk, rv = inp.k_cache.copy(), inp.v_cache.copy()
+    for b in range(cfg.batch):
+        for s_ in range(int(nv[b])):
+            O.draft(cfg, W, th[b:b + 1, s_], tok[b:b + 1, s_], rk[b:b + 1], rv[b:b + 1],
+                    inp.lens[b:b + 1] + s_, pos0[b:b + 1] + s_, 1)
+    for got, ref in ((kc, rk), (vc, rv)):
+        if dtype == "bf16":
+            # one-ulp rounding flips are allowed between the two evaluation orders
+            g, r = O.as_float(got, "bf16"), O.as_float(ref, "bf16")
+            assert np.allclose(g, r, rtol=2 ** -7, atol=1e-6)
+        else:
+            assert np.allclose(got, ref, rtol=0, atol=1e-6)
+        for b in range(cfg.batch):
+            L1 = int(inp.lens[b] + nv[b])
+            assert np.array_equal(got[b, :, L1:], getattr(inp, "k_cache" if got is kc else
+                                                          "v_cache")[b, :, L1:])
+
+
+def test_prefill_then_exact_decoding_equals_prefill_of_the_committed_sequence():
+    """From an empty cache, prefilling the prompt and then decoding speculatively with
+    exact catch-up emits plain greedy decoding, and leaves the same cache as prefilling the
+    whole committed sequence at once: slot s holds the pair (h_s, x_{s+1}) at position s
+    whichever way the slot was written."""
+    cfg = small_cfg(cid=94, batch=1, vocab=16, ctx_lo=0, K=4)
+    inp = _inputs(cfg, 256)
+    W = O.OracleWeights(cfg, inp.weights)
+    tw = S.target_weights(cfg, 2)
+    tgt = TinyTarget(cfg, tw, inp.weights["embed"], inp.weights["lm_head"])
+    tgt.g_final_store = tw["g_final"]
+    prompt = [int(x) for x in S.prompt_tokens(cfg, 9)]
+    P = len(prompt)
+    hid, _ = tgt.forward(prompt)
+    kc, vc = np.zeros_like(inp.k_cache), np.zeros_like(inp.v_cache)
+    ln, ps = O.kv_prefill(cfg, W, hid[None, :P - 1], np.array([prompt[1:]]), kc, vc,
+                          np.array([0]), np.array([0]))
+    assert int(ln[0]) == P - 1 and int(ps[0]) == P - 1
+    n_new = 30
+    ref = tgt.greedy(prompt, n_new)
+    out, acc, st = _catchup_run(cfg, inp, W, tgt, prompt, n_new, 3, None,
+                                lambda it, K: it % (K + 1),
+                                init={"kc": kc, "vc": vc, "len": ln, "pos": ps})
+    assert out == ref
+    assert 3 in acc and 0 in acc
+    n = int(st["len"][0])
+    assert n > P + 10 and int(st["pos"][0]) == n
+    seq = prompt + ref
+    hid_all, _ = tgt.forward(seq)
+    rk, rv = np.zeros_like(inp.k_cache), np.zeros_like(inp.v_cache)
+    O.kv_prefill(cfg, W, hid_all[None, :n], np.array([seq[1:n + 1]]), rk, rv, np.array([0]),
+                 np.array([0]))
+    assert np.allclose(st["kc"][:, :, :n], rk[:, :, :n], rtol=0, atol=1e-5)
+    assert np.allclose(st["vc"][:, :, :n], rv[:, :, :n], rtol=0, atol=1e-5)
