@@ -399,22 +399,26 @@ def kv_prefill(cfg, W: OracleWeights, target_hidden: np.ndarray, tokens: np.ndar
     lens = np.asarray(lens, np.int64)
     pos = np.asarray(pos, np.int64)
     for b in range(B):
-        for s in range(int(nv[b])):
-            e = W.embed_rows(tok[b, s:s + 1])
-            x = np.concatenate([rmsnorm(th[b, s][None], w["g_h"], eps),
-                                rmsnorm(e, w["g_e"], eps)], axis=1) @ w["w_eh"].T
-            a = rmsnorm(x, w["g_attn"], eps)
-            kn = (a @ w["w_k"].T).reshape(nkv, d)
-            vn = (a @ w["w_v"].T).reshape(nkv, d)
+        m = int(nv[b])
+        if m == 0:
+            continue
+        # every row of the sequence at once: row s of each product is that row's projection
+        e = W.embed_rows(tok[b, :m])
+        x = np.concatenate([rmsnorm(th[b, :m], w["g_h"], eps), rmsnorm(e, w["g_e"], eps)],
+                           axis=1) @ w["w_eh"].T
+        a = rmsnorm(x, w["g_attn"], eps)
+        kn = (a @ w["w_k"].T).reshape(m, nkv, d)
+        vn = (a @ w["w_v"].T).reshape(m, nkv, d)
+        for s in range(m):
             cos, sin = rope_tables(int(pos[b]) + s, d, cfg.rope_theta, dt)
-            kb = rope(kn, cos, sin)
+            kb = rope(kn[s], cos, sin)
             slot = int(lens[b]) + s
             if cfg.dtype == "bf16":
                 k_cache[b, :, slot, :] = _store_bf16(kb)
-                v_cache[b, :, slot, :] = _store_bf16(vn)
+                v_cache[b, :, slot, :] = _store_bf16(vn[s])
             else:
                 k_cache[b, :, slot, :] = kb.astype(np.float32)
-                v_cache[b, :, slot, :] = vn.astype(np.float32)
+                v_cache[b, :, slot, :] = vn[s].astype(np.float32)
     return lens + nv, pos + nv
 
 
