@@ -57,6 +57,7 @@ typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
 #define MTP_DEVERR_TOKEN 1u    /* a token id (last_tokens or a draft) was outside [0, vocab) */
 #define MTP_DEVERR_CAPACITY 2u /* len + K exceeded the cache capacity                   */
 #define MTP_DEVERR_ACCEPT 4u   /* an accepted_len entry was outside [0, K]              */
+#define MTP_DEVERR_COUNT 8u    /* a prefill row count was outside [0, n]                 */
 
 /* Shape of the MTP head. rope_theta: RoPE base; rms_eps: RMSNorm epsilon. */
 typedef struct {
@@ -216,6 +217,33 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
 mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
                           const int32_t* draft_tokens, const int32_t* accepted_len, int32_t B,
                           int32_t K, void* stream);
+
+/*
+ * Prompt prefill of the MTP cache (devnotes "How OpenVINO MTP Speculative Decoding Works
+ * Internally", "KV cache" and "Stateful execution": the MTP layer keeps its own one-layer
+ * cache, filled for every position it has processed; speculators "MTP (Multi-Token
+ * Prediction)", Architecture: the layer's input at position s pairs the verifier's hidden
+ * state at s with the embedding of the token after s). For every sequence b and prompt row
+ * s < n_valid[b] (all n rows when n_valid is NULL), the pair (target_hidden[b, s],
+ * tokens[b, s]) runs through the layer's input side (embedding gather, separate RMSNorms,
+ * eh_proj, attention RMSNorm, K/V projections, RoPE at position pos[b] + s) and is written
+ * to slot len[b] + s in the cache dtype; then len[b] and pos[b] advance by that count.
+ * After a prompt of P tokens (rows 0 .. P-2 paired with tokens 1 .. P-1, from an empty
+ * cache) the first mtp_draft takes the hidden state at position P-1 and the target's first
+ * generated token, and writes slot P-1.
+ *   target_hidden [B, n, hidden] config dtype, 16-byte aligned: the target's last-layer
+ *                 outputs before its final norm at positions pos[b] .. pos[b]+n-1
+ *   tokens        [B, n] device int32: the token after each of those positions
+ *   n_valid       [B] device int32 rows to take per sequence (0..n), or NULL for n
+ * 0 <= n <= kv->capacity (n = 0 enqueues nothing), 1 <= B <= min(max_batch, kv->batch).
+ * Rows run in groups of up to 64 (each group streams eh_proj and the K/V projections once).
+ * Device conditions: a slot outside the capacity sets MTP_DEVERR_CAPACITY (the row is
+ * skipped); a token outside [0, vocab) sets MTP_DEVERR_TOKEN (row 0 of the embedding is
+ * used); an n_valid entry outside [0, n] sets MTP_DEVERR_COUNT and is clamped.
+ */
+mtp_status mtp_kv_prefill(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
+                          const int32_t* tokens, const int32_t* n_valid, int32_t B, int32_t n,
+                          void* stream);
 
 /*
  * K recursive draft steps that SAMPLE each token at temperature T instead of taking the

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "mtp.h")
 
 MTP_OK = 0
 MTP_F32, MTP_BF16 = 0, 1
-DEVERR_TOKEN, DEVERR_CAPACITY, DEVERR_ACCEPT = 1, 2, 4
+DEVERR_TOKEN, DEVERR_CAPACITY, DEVERR_ACCEPT, DEVERR_COUNT = 1, 2, 4, 8
 
 STATUS_NAMES = {0: "MTP_OK", 1: "MTP_ERR_INVALID_ARG", 2: "MTP_ERR_SHAPE", 3: "MTP_ERR_DTYPE",
                 4: "MTP_ERR_CAPACITY", 5: "MTP_ERR_UNSUPPORTED", 6: "MTP_ERR_HIP",
@@ -79,6 +79,7 @@ _SIGS = {
                                _P, _P]),
     "mtp_kv_catchup": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _P, _P, _I, _I, _P]),
     "mtp_kv_rollback": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P]),
+    "mtp_kv_prefill": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _P, _P, _I, _I, _P]),
     "mtp_get_error": (_I, [_P, _P, ctypes.POINTER(ctypes.c_uint32)]),
     "mtp_get_info": (_I, [_P, ctypes.POINTER(mtp_info)]),
     "mtp_verify_noalloc": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
@@ -212,6 +213,12 @@ def mtp_kv_catchup(handle: int, kv: mtp_kv, target_hidden: int, draft_tokens: in
                    accepted_len: int, B: int, K: int, stream: int | None) -> None:
     _check(LIB.mtp_kv_catchup(handle, ctypes.byref(kv), target_hidden, draft_tokens,
                               accepted_len, B, K, stream), "mtp_kv_catchup")
+
+
+def mtp_kv_prefill(handle: int, kv: mtp_kv, target_hidden: int, tokens: int,
+                   n_valid: int | None, B: int, n: int, stream: int | None) -> None:
+    _check(LIB.mtp_kv_prefill(handle, ctypes.byref(kv), target_hidden, tokens, n_valid, B, n,
+                              stream), "mtp_kv_prefill")
 
 
 def mtp_kv_rollback(handle: int, kv: mtp_kv, accepted_len: int, B: int, K: int,

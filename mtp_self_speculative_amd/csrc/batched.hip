@@ -230,20 +230,22 @@ hipError_t launch_accept(const int* tokens, const int* draft, int B, int K, int*
 }
 
 __global__ void gather_rows_kernel(const uint16_t* src16, const float* src32, float* dst, int r0,
-                                   int rows, int K, int H) {
+                                   int rows, int per, int src_per, int H) {
   const int i = blockIdx.y;
   const int r = r0 + i;
-  const long srow = (long)(r / K) * (K + 1) + r % K;
+  const long srow = (long)(r / per) * src_per + r % per;
   for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < H; c += gridDim.x * blockDim.x)
     dst[(long)i * H + c] = src16 ? bf16_to_f32(src16[srow * H + c]) : src32[srow * H + c];
 }
 
-hipError_t launch_gather_rows(int dtype, const void* src, float* dst, int r0, int rows, int K,
-                              int H, hipStream_t s) {
-  if (!src || !dst || rows < 1 || K < 1 || H < 1 || r0 < 0) return hipErrorInvalidValue;
+hipError_t launch_gather_rows(int dtype, const void* src, float* dst, int r0, int rows, int per,
+                              int src_per, int H, hipStream_t s) {
+  if (!src || !dst || rows < 1 || per < 1 || src_per < per || H < 1 || r0 < 0)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((H + 255) / 256, rows), dim3(256), 0, s,
                      dtype == 1 ? static_cast<const uint16_t*>(src) : nullptr,
-                     dtype == 1 ? nullptr : static_cast<const float*>(src), dst, r0, rows, K, H);
+                     dtype == 1 ? nullptr : static_cast<const float*>(src), dst, r0, rows, per,
+                     src_per, H);
   return hipGetLastError();
 }
 
@@ -254,12 +256,12 @@ __global__ void catchup_write_kernel(CatchupParams p) {
   const int i = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
   const int half = p.d / 2;
   const int r = p.r0 + i;
-  const int b = r / p.K, j = r % p.K + 1;
-  int a = p.accepted[b];
-  a = a < 0 ? 0 : a > p.K ? p.K : a;
-  if (j > a || t >= half) return;
-  const int slot = p.len[b] - p.K + j;
-  const int position = p.pos[b] - p.K + j;
+  const int b = r / p.per, j = r % p.per;
+  int lim = p.limit ? p.limit[b] : p.per;
+  lim = lim < 0 ? 0 : lim > p.per ? p.per : lim;
+  if (j >= lim || t >= half) return;
+  const int slot = p.len[b] + p.off + j;
+  const int position = p.pos[b] + p.off + j;
   if (slot < 0 || slot >= p.capacity) {
     if (t == 0) set_error(p.err, 2u);
     return;
@@ -277,7 +279,7 @@ __global__ void catchup_write_kernel(CatchupParams p) {
 }
 
 hipError_t launch_catchup_write(int cdtype, const CatchupParams& p, hipStream_t s) {
-  if (!p.kvrows || !p.kc || !p.vc || !p.len || !p.pos || !p.accepted || p.K < 1 || p.rows < 1 ||
+  if (!p.kvrows || !p.kc || !p.vc || !p.len || !p.pos || p.per < 1 || p.rows < 1 ||
       p.d < 2 || p.d > 1024 || p.d % 2 != 0)
     return hipErrorInvalidValue;
   const dim3 grid(p.rows, p.n_kv), block((p.d / 2 + 63) / 64 * 64);
@@ -288,24 +290,24 @@ hipError_t launch_catchup_write(int cdtype, const CatchupParams& p, hipStream_t 
   return hipGetLastError();
 }
 
-__global__ void catchup_commit_kernel(int* len, int* pos, const int* accepted, int B, int K,
-                                      unsigned* err) {
+__global__ void catchup_commit_kernel(int* len, int* pos, const int* limit, int B, int per,
+                                      int add, unsigned err_bit, unsigned* err) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
-  int a = accepted[b];
-  if (a < 0 || a > K) {
-    set_error(err, 4u);
-    a = a < 0 ? 0 : K;
+  int lim = limit ? limit[b] : per;
+  if (lim < 0 || lim > per) {
+    set_error(err, err_bit);
+    lim = lim < 0 ? 0 : per;
   }
-  len[b] += a + 1 - K;
-  pos[b] += a + 1 - K;
+  len[b] += lim + add;
+  pos[b] += lim + add;
 }
 
-hipError_t launch_catchup_commit(int* len, int* pos, const int* accepted, int B, int K,
-                                 unsigned* err, hipStream_t s) {
-  if (!len || !pos || !accepted || B < 1 || K < 1) return hipErrorInvalidValue;
+hipError_t launch_catchup_commit(int* len, int* pos, const int* limit, int B, int per, int add,
+                                 unsigned err_bit, unsigned* err, hipStream_t s) {
+  if (!len || !pos || !err || B < 1 || per < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(catchup_commit_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, pos,
-                     accepted, B, K, err);
+                     limit, B, per, add, err_bit, err);
   return hipGetLastError();
 }
 

@@ -268,15 +268,20 @@ hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K
 
 // dst[i] = src[i] widened to fp32 (src in weight dtype), i < n.
 hipError_t launch_widen(int dtype, const void* src, float* dst, long n, hipStream_t s);
-// dst[i, :] = fp32(src[(r / K) * (K + 1) + r % K, :]) for r = r0 + i, i < rows: the
-// verified-input rows j - 1 = r % K of sequence r / K (src [B, K+1, H], weight dtype).
-hipError_t launch_gather_rows(int dtype, const void* src, float* dst, int r0, int rows, int K,
-                              int H, hipStream_t s);
+// dst[i, :] = fp32(src[(r / per) * src_per + r % per, :]) for r = r0 + i, i < rows: row
+// r % per of sequence r / per, where src holds src_per rows per sequence ([B, src_per, H],
+// weight dtype). Catch-up reads the verified-input rows j - 1 = r % K (per = K,
+// src_per = K + 1); prefill reads every prompt row (per = src_per = n).
+hipError_t launch_gather_rows(int dtype, const void* src, float* dst, int r0, int rows, int per,
+                              int src_per, int H, hipStream_t s);
 
-// Exact cache catch-up, write side. kv rows [rows, 2 * n_kv * d] fp32 hold k (before RoPE)
-// then v of candidate rows r = r0 + i, sequence b = r / K, committed pair j = r % K + 1.
-// Rows with j <= accepted[b] are rotated at position pos[b] - K + j and written to slot
-// len[b] - K + j in the cache dtype (len / pos: values after the K-step draft).
+// Write side of the input-side passes (exact catch-up and prompt prefill). kv rows
+// [rows, 2 * n_kv * d] fp32 hold k (before RoPE) then v of candidate rows r = r0 + i,
+// sequence b = r / per, index j = r % per. Rows with j < lim(b) are rotated at position
+// pos[b] + off + j and written to slot len[b] + off + j in the cache dtype, where
+// lim(b) = limit[b] clamped to [0, per] (per when limit is null).
+//   catch-up: per = K, off = 1 - K, limit = accepted lengths (len / pos: after the draft)
+//   prefill:  per = n, off = 0, limit = per-sequence row counts or null
 struct CatchupParams {
   const float* kvrows;
   int ld;  // floats per kv row
@@ -285,15 +290,16 @@ struct CatchupParams {
   int n_kv, d, capacity;
   const int* len;
   const int* pos;
-  const int* accepted;
-  int K, r0, rows;
+  const int* limit;
+  int per, off, r0, rows;
   float theta;
   unsigned* err;
 };
 hipError_t launch_catchup_write(int cdtype, const CatchupParams& p, hipStream_t s);
-// len[b] += a + 1 - K and pos[b] += a + 1 - K (a clamped to 0..K, error bit 4 if not).
-hipError_t launch_catchup_commit(int* len, int* pos, const int* accepted, int B, int K,
-                                 unsigned* err, hipStream_t s);
+// len[b] += lim + add and pos[b] += lim + add, lim = limit[b] clamped to [0, per] (per when
+// limit is null); an entry outside [0, per] sets `err_bit` in the error word.
+hipError_t launch_catchup_commit(int* len, int* pos, const int* limit, int B, int per, int add,
+                                 unsigned err_bit, unsigned* err, hipStream_t s);
 
 // Prefix scan of verification from per-row target tokens: tokens[b * (K+1) + j] is the
 // target's token after input j; accepted[b] / next[b] as launch_verify writes them.

@@ -144,8 +144,9 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   }
   // exact cache catch-up
   {
-    const long rows_all = (long)max_batch * max_k;
-    L.cu_rows = (int)(rows_all < kVhGroup ? rows_all : kVhGroup);
+    // up to kVhGroup rows per pass: catch-up has max_batch * max_k candidate rows, prefill
+    // up to max_batch * capacity
+    L.cu_rows = kVhGroup;
     L.cu_ld = (2 * c.hidden + 7) / 8 * 8;
     const int kvd2 = 2 * c.n_kv_heads * c.head_dim;
     const int rr = L.cu_rows > 0 ? L.cu_rows : 1;
@@ -907,6 +908,112 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
   return timed(h, KC_VERIFY, s, run) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
+}  // extern "C"
+
+// The layer's input side over R candidate rows (exact catch-up and prompt prefill): row r
+// of sequence b = r / per, index j = r % per, reads hidden row (b * src_per + j) of `src`
+// and token tokens[r]; eh_proj, attention norm and K/V projections run in groups of
+// L.cu_rows rows (matrix cores from 3 rows on for bf16, else the GEMV); rows with
+// j < limit[b] are rotated and written (catchup_write_kernel), then len / pos advance by
+// limit[b] + add.
+static hipError_t input_side_pass(mtp_handle* h, mtp_kv* kv, const void* src, int per,
+                                  int src_per, const int32_t* tokens, const int32_t* limit,
+                                  int B, int off, int add, unsigned limit_err, hipStream_t s) {
+  const mtp_config& c = h->cfg;
+  const mtp_weights& w = h->w;
+  const Layout& L = h->L;
+  const int H = c.hidden, kvd = c.n_kv_heads * c.head_dim;
+  const int R = B * per;
+  unsigned* err = h->at<unsigned>(L.err);
+  float* hrows = h->at<float>(L.cu_h);
+  float* xrows = h->at<float>(L.cu_x);
+  float* kvrows = h->at<float>(L.cu_kv);
+  hipError_t e = hipSuccess;
+  for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.cu_rows) {
+    const int rows = R - r0 < L.cu_rows ? R - r0 : L.cu_rows;
+    e = launch_gather_rows(c.dtype, src, hrows, r0, rows, per, src_per, H, s);
+    if (e != hipSuccess) break;
+    if (mm_eligible(c) && rows >= kMmMinBatch) {
+      uint16_t* q = h->at<uint16_t>(L.cu_q);
+      uint16_t* qlo = h->at<uint16_t>(L.cu_q_lo);
+      float* part = h->at<float>(L.cu_part);
+      const int bp = mm_batch_pad(rows);
+      RedParams r{};
+      r.n = H; r.gain = static_cast<const uint16_t*>(w.g_h);
+      r.gain2 = static_cast<const uint16_t*>(w.g_e); r.eps = c.rms_eps;
+      r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld; r.h = hrows;
+      r.embed = static_cast<const uint16_t*>(w.embed);
+      r.tok = tokens + r0; r.tok_stride = 1; r.vocab = c.vocab; r.err = err;
+      if ((e = launch_red(PREP_EH, r, rows, s)) != hipSuccess) break;
+      // packed: the matrix's rows in the handle's packed copy (or null: read w0/w1)
+      auto mm = [&](const void* w0, const void* w1, int seg1, int N, int Kd,
+                    const uint16_t* packed, int* ns) {
+        MmParams m{};
+        m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
+        m.nrows = N; m.ncols = Kd; m.x = q; m.x_lo = qlo; m.ldx = L.cu_ld; m.B = rows;
+        const MmPlan pl = mm_plan(EPI_STORE, N, Kd, rows, packed != nullptr, h->num_cu);
+        m.tile_rows = pl.tile_rows;
+        m.nsplit = pl.nsplit;
+        m.part = part;
+        m.dummy = h->ws + L.dummy;
+        m.packed = packed;
+        *ns = m.nsplit;
+        return launch_mm(EPI_STORE, m, pl.grid, s);
+      };
+      // The K/V rows of the packed [W_q; W_k; W_v] copy start at a whole 128-row tile
+      // when n_q * d is a multiple of 128; the packed copy is tile-major.
+      const int qd = c.n_q_heads * c.head_dim;
+      const uint16_t* pk_kv =
+          L.pk_qkv && qd % 128 == 0
+              ? h->at<uint16_t>(L.pk_qkv) + (size_t)(qd / 128) * mm_packed_elems(128, H)
+              : nullptr;
+      int ns = 1;
+      if ((e = mm(w.w_eh, w.w_eh, H, H, 2 * H, L.pk_eh ? h->at<uint16_t>(L.pk_eh) : nullptr,
+                  &ns)) != hipSuccess)
+        break;
+      r = RedParams{};
+      r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = H; r.n = H;
+      r.out = xrows; r.gain = static_cast<const uint16_t*>(w.g_attn); r.eps = c.rms_eps;
+      r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld;
+      if ((e = launch_red(RED_EH, r, rows, s)) != hipSuccess) break;
+      if ((e = mm(w.w_k, w.w_v, kvd, 2 * kvd, H, pk_kv, &ns)) != hipSuccess) break;
+      r = RedParams{};
+      r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = 2 * kvd; r.n = 2 * kvd;
+      r.out = kvrows; r.ldq = L.cu_ld;
+      if ((e = launch_red(RED_QKV, r, rows, s)) != hipSuccess) break;
+    } else {
+      GemvParams g{};
+      g.w0 = g.w1 = g.w2 = w.w_eh;
+      g.nrows = g.seg1 = g.seg2 = H;
+      g.ncols = 2 * H; g.B = rows;
+      g.gain = w.g_h; g.gain2 = w.g_e; g.eps = c.rms_eps;
+      g.h = hrows; g.h_is_f32 = 1; g.ldh = H;
+      g.embed = w.embed; g.tok = tokens + r0; g.tok_stride = 1; g.vocab = c.vocab;
+      g.err = err; g.out = xrows; g.ldo = H;
+      if ((e = run_gemv(h, PRO_EH, EPI_STORE, g, s)) != hipSuccess) break;
+      g = GemvParams{};
+      g.w0 = w.w_k; g.w1 = w.w_v; g.w2 = w.w_v;
+      g.seg1 = kvd; g.seg2 = 2 * kvd; g.nrows = 2 * kvd;
+      g.ncols = H; g.B = rows;
+      g.x = xrows; g.ldx = H; g.gain = w.g_attn; g.eps = c.rms_eps;
+      g.out = kvrows; g.ldo = 2 * kvd;
+      if ((e = run_gemv(h, PRO_RMS, EPI_STORE, g, s)) != hipSuccess) break;
+    }
+    CatchupParams cp{};
+    cp.kvrows = kvrows; cp.ld = 2 * kvd; cp.kc = kv->k; cp.vc = kv->v;
+    cp.n_kv = c.n_kv_heads; cp.d = c.head_dim; cp.capacity = kv->capacity;
+    cp.len = kv->len; cp.pos = kv->pos; cp.limit = limit;
+    cp.per = per; cp.off = off; cp.r0 = r0; cp.rows = rows; cp.theta = c.rope_theta;
+    cp.err = err;
+    e = launch_catchup_write(c.dtype, cp, s);
+  }
+  if (e == hipSuccess)
+    e = launch_catchup_commit(kv->len, kv->pos, limit, B, per, add, limit_err, err, s);
+  return e;
+}
+
+extern "C" {
+
 mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
                           const int32_t* draft_tokens, const int32_t* accepted_len, int32_t B,
                           int32_t K, void* stream) {
@@ -916,99 +1023,36 @@ mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
   if (K > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
   mtp_status st = check_kv(h, kv, B);
   if (st != MTP_OK) return st;
-  const mtp_config& c = h->cfg;
-  const mtp_weights& w = h->w;
-  const Layout& L = h->L;
-  const int H = c.hidden, kvd = c.n_kv_heads * c.head_dim;
-  const int R = B * K;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  unsigned* err = h->at<unsigned>(L.err);
-  float* hrows = h->at<float>(L.cu_h);
-  float* xrows = h->at<float>(L.cu_x);
-  float* kvrows = h->at<float>(L.cu_kv);
-  auto run = [&]() -> hipError_t {
-    hipError_t e = hipSuccess;
-    for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.cu_rows) {
-      const int rows = R - r0 < L.cu_rows ? R - r0 : L.cu_rows;
-      e = launch_gather_rows(c.dtype, target_hidden, hrows, r0, rows, K, H, s);
-      if (e != hipSuccess) break;
-      if (mm_eligible(c) && rows >= kMmMinBatch) {
-        uint16_t* q = h->at<uint16_t>(L.cu_q);
-        uint16_t* qlo = h->at<uint16_t>(L.cu_q_lo);
-        float* part = h->at<float>(L.cu_part);
-        const int bp = mm_batch_pad(rows);
-        RedParams r{};
-        r.n = H; r.gain = static_cast<const uint16_t*>(w.g_h);
-        r.gain2 = static_cast<const uint16_t*>(w.g_e); r.eps = c.rms_eps;
-        r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld; r.h = hrows;
-        r.embed = static_cast<const uint16_t*>(w.embed);
-        r.tok = draft_tokens + r0; r.tok_stride = 1; r.vocab = c.vocab; r.err = err;
-        if ((e = launch_red(PREP_EH, r, rows, s)) != hipSuccess) break;
-        // packed: the matrix's rows in the handle's packed copy (or null: read w0/w1)
-        auto mm = [&](const void* w0, const void* w1, int seg1, int N, int Kd,
-                      const uint16_t* packed, int* ns) {
-          MmParams m{};
-          m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
-          m.nrows = N; m.ncols = Kd; m.x = q; m.x_lo = qlo; m.ldx = L.cu_ld; m.B = rows;
-          const MmPlan pl = mm_plan(EPI_STORE, N, Kd, rows, packed != nullptr, h->num_cu);
-          m.tile_rows = pl.tile_rows;
-          m.nsplit = pl.nsplit;
-          m.part = part;
-          m.dummy = h->ws + L.dummy;
-          m.packed = packed;
-          *ns = m.nsplit;
-          return launch_mm(EPI_STORE, m, pl.grid, s);
-        };
-        // The K/V rows of the packed [W_q; W_k; W_v] copy start at a whole 128-row tile
-        // when n_q * d is a multiple of 128; the packed copy is tile-major.
-        const int qd = c.n_q_heads * c.head_dim;
-        const uint16_t* pk_kv =
-            L.pk_qkv && qd % 128 == 0
-                ? h->at<uint16_t>(L.pk_qkv) + (size_t)(qd / 128) * mm_packed_elems(128, H)
-                : nullptr;
-        int ns = 1;
-        if ((e = mm(w.w_eh, w.w_eh, H, H, 2 * H, L.pk_eh ? h->at<uint16_t>(L.pk_eh) : nullptr,
-                    &ns)) != hipSuccess)
-          break;
-        r = RedParams{};
-        r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = H; r.n = H;
-        r.out = xrows; r.gain = static_cast<const uint16_t*>(w.g_attn); r.eps = c.rms_eps;
-        r.xq = q; r.xq_lo = qlo; r.ldq = L.cu_ld;
-        if ((e = launch_red(RED_EH, r, rows, s)) != hipSuccess) break;
-        if ((e = mm(w.w_k, w.w_v, kvd, 2 * kvd, H, pk_kv, &ns)) != hipSuccess) break;
-        r = RedParams{};
-        r.part = part; r.nsplit = ns; r.bp = bp; r.n_part = 2 * kvd; r.n = 2 * kvd;
-        r.out = kvrows; r.ldq = L.cu_ld;
-        if ((e = launch_red(RED_QKV, r, rows, s)) != hipSuccess) break;
-      } else {
-        GemvParams g{};
-        g.w0 = g.w1 = g.w2 = w.w_eh;
-        g.nrows = g.seg1 = g.seg2 = H;
-        g.ncols = 2 * H; g.B = rows;
-        g.gain = w.g_h; g.gain2 = w.g_e; g.eps = c.rms_eps;
-        g.h = hrows; g.h_is_f32 = 1; g.ldh = H;
-        g.embed = w.embed; g.tok = draft_tokens + r0; g.tok_stride = 1; g.vocab = c.vocab;
-        g.err = err; g.out = xrows; g.ldo = H;
-        if ((e = run_gemv(h, PRO_EH, EPI_STORE, g, s)) != hipSuccess) break;
-        g = GemvParams{};
-        g.w0 = w.w_k; g.w1 = w.w_v; g.w2 = w.w_v;
-        g.seg1 = kvd; g.seg2 = 2 * kvd; g.nrows = 2 * kvd;
-        g.ncols = H; g.B = rows;
-        g.x = xrows; g.ldx = H; g.gain = w.g_attn; g.eps = c.rms_eps;
-        g.out = kvrows; g.ldo = 2 * kvd;
-        if ((e = run_gemv(h, PRO_RMS, EPI_STORE, g, s)) != hipSuccess) break;
-      }
-      CatchupParams cp{};
-      cp.kvrows = kvrows; cp.ld = 2 * kvd; cp.kc = kv->k; cp.vc = kv->v;
-      cp.n_kv = c.n_kv_heads; cp.d = c.head_dim; cp.capacity = kv->capacity;
-      cp.len = kv->len; cp.pos = kv->pos; cp.accepted = accepted_len;
-      cp.K = K; cp.r0 = r0; cp.rows = rows; cp.theta = c.rope_theta; cp.err = err;
-      e = launch_catchup_write(c.dtype, cp, s);
-    }
-    if (e == hipSuccess) e = launch_catchup_commit(kv->len, kv->pos, accepted_len, B, K, err, s);
-    return e;
-  };
-  return timed(h, KC_ROLLBACK, s, run) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
+  // committed pair j = r % K + 1 of sequence b: hidden row j - 1 of K + 1, token d_j, slot
+  // len - K + j; len / pos then move by a + 1 - K
+  return timed(h, KC_ROLLBACK, s, [&] {
+           return input_side_pass(h, kv, target_hidden, K, K + 1, draft_tokens, accepted_len, B,
+                                  1 - K, 1 - K, MTP_DEVERR_ACCEPT, s);
+         }) == hipSuccess
+             ? MTP_OK
+             : MTP_ERR_HIP;
+}
+
+mtp_status mtp_kv_prefill(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
+                          const int32_t* tokens, const int32_t* n_valid, int32_t B, int32_t n,
+                          void* stream) {
+  if (!h) return MTP_ERR_INVALID_ARG;
+  if (n < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (B > h->max_batch) return MTP_ERR_CAPACITY;
+  mtp_status st = check_kv(h, kv, B);
+  if (st != MTP_OK) return st;
+  if (n > kv->capacity) return MTP_ERR_CAPACITY;
+  if (n == 0) return MTP_OK;  // nothing to read: the row pointers may be null
+  if (!target_hidden || !tokens) return MTP_ERR_INVALID_ARG;
+  if (!aligned(target_hidden, 16)) return MTP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(h, KC_ROLLBACK, s, [&] {
+           return input_side_pass(h, kv, target_hidden, n, n, tokens, n_valid, B, 0, 0,
+                                  MTP_DEVERR_COUNT, s);
+         }) == hipSuccess
+             ? MTP_OK
+             : MTP_ERR_HIP;
 }
 
 mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,

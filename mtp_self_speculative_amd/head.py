@@ -287,6 +287,24 @@ class MtpHead:
         L.mtp_kv_catchup(self.handle, cache.kv, th.data_ptr(), draft_tokens.data_ptr(),
                          accepted.data_ptr(), B, K1 - 1, _stream(stream))
 
+    def prefill(self, cache: MtpCache, target_hidden: torch.Tensor, tokens: torch.Tensor,
+                n_valid: torch.Tensor | None = None, stream=None) -> None:
+        """Fill the cache over a prompt: row s of target_hidden [B, n, H] (the target's
+        pre-norm hidden state at position pos+s) with tokens [B, n] int32 (the token after
+        that position) goes to slot len+s; len / pos advance by n (or n_valid [B])."""
+        if not isinstance(target_hidden, torch.Tensor) or target_hidden.dim() != 3:
+            raise ValueError("target_hidden must be a [B, n, hidden] tensor")
+        B, n = target_hidden.shape[0], target_hidden.shape[1]
+        if not 1 <= B <= self.max_batch:
+            raise ValueError(f"batch {B} outside 1..{self.max_batch}")
+        self._t("target_hidden", target_hidden, self.dtype, (B, n, self.cfg.hidden))
+        self._t("tokens", tokens, torch.int32, (B, n))
+        if n_valid is not None:
+            self._t("n_valid", n_valid, torch.int32, (B,))
+        self._check_cache(cache, B)
+        L.mtp_kv_prefill(self.handle, cache.kv, target_hidden.data_ptr(), tokens.data_ptr(),
+                         _ptr(n_valid), B, n, _stream(stream))
+
     def rollback(self, cache: MtpCache, accepted: torch.Tensor, K: int, stream=None) -> None:
         if not isinstance(accepted, torch.Tensor) or accepted.dim() != 1:
             raise ValueError("accepted must be a [B] int32 tensor")

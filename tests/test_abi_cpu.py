@@ -244,3 +244,10 @@ def test_verify_noalloc_host_checks():
     assert L.LIB.mtp_verify_noalloc(p, p, 1, 1, 0, p, p, None) == 2
     assert L.LIB.mtp_verify_noalloc(p, p, 257, 1, 8, p, p, None) == 4
     assert L.LIB.mtp_verify_noalloc(p, p, 1, 101, 8, p, p, None) == 4
+
+
+def test_prefill_host_checks():
+    """mtp_kv_prefill refuses a null handle and bad shapes before any device call."""
+    kv = L.mtp_kv()
+    p = ctypes.c_void_p(16)
+    assert L.LIB.mtp_kv_prefill(None, ctypes.byref(kv), p, p, None, 1, 4, None) == 1
