@@ -435,6 +435,79 @@ def adapt_k(accepted_len, K: int, k_min: int, k_max: int) -> int:
     return int(min(max(int(want.max()), k_min), k_max))
 
 
+def adapt_k_seq(accepted_hist, k_hist, k_min: int, k_max: int) -> np.ndarray:
+    """Per-sequence speculative lengths for the next iteration from a window of recent
+    iterations.  [OVSD] Backend Differences (the length follows recent acceptance and backs
+    off when it is low); [FI] 7.3 (depth adapted to the live acceptance rate, per request).
+
+    accepted_hist, k_hist [W, B]: the accepted length a and the length k each sequence used
+    in each of its last W iterations (any order). Reading: iteration i of sequence b asks
+    for k+1 when it accepted all k drafts and for a+1 otherwise (the batch-wide rule, per
+    sequence); the sequence takes the mean of its W requests rounded up, clipped to
+    [k_min, k_max]. With W = 1 this is the per-iteration rule applied to each sequence.
+    Returns k_next [B].
+    """
+    a = np.asarray(accepted_hist, np.int64)
+    k = np.asarray(k_hist, np.int64)
+    a = a.reshape(-1, a.shape[-1]) if a.ndim > 1 else a.reshape(1, -1)
+    k = k.reshape(a.shape)
+    want = np.where(a >= k, k + 1, a + 1)
+    W = want.shape[0]
+    mean_up = -(-want.sum(axis=0) // W)
+    return np.clip(mean_up, k_min, k_max)
+
+
+def draft_seqk(cfg, W: OracleWeights, hidden, last_tokens, k_cache, v_cache, lens, pos,
+               k_seq, K_max: int) -> dict:
+    """Draft with a speculative length per sequence: sequence b runs k_seq[b] (0..K_max)
+    recursive steps, exactly as ``draft`` with K = k_seq[b] on that sequence alone
+    ([SPEC] Architecture; [OVSD] Backend Differences). Returns draft_tokens [B, K_max]
+    (entries past k_seq[b] are -1, not drafted), lens / pos advanced by k_seq."""
+    B = hidden.shape[0]
+    ks = np.asarray(k_seq, np.int64)
+    drafts = np.full((B, K_max), -1, np.int64)
+    lens = np.asarray(lens, np.int64).copy()
+    pos = np.asarray(pos, np.int64).copy()
+    margin = np.full((K_max, B), np.inf)
+    for b in range(B):
+        kb = int(ks[b])
+        if kb == 0:
+            continue
+        r = draft(cfg, W, hidden[b:b + 1], np.asarray(last_tokens)[b:b + 1], k_cache[b:b + 1],
+                  v_cache[b:b + 1], lens[b:b + 1], pos[b:b + 1], kb)
+        drafts[b, :kb] = r["draft_tokens"][0]
+        margin[:kb, b] = r["margin"][:, 0]
+        lens[b], pos[b] = r["lens"][0], r["pos"][0]
+    return {"draft_tokens": drafts, "lens": lens, "pos": pos, "margin": margin}
+
+
+def verify_seqk(target_logits, draft_tokens, k_seq):
+    """Greedy verification with a length per sequence: sequence b checks its first
+    k_seq[b] drafts against target rows 0..k_seq[b] ([OVSD] Overview), rows past that are
+    not read. Returns accepted_len [B] (0..k_seq[b]) and next_token [B]."""
+    t = np.asarray(target_logits)
+    d = np.asarray(draft_tokens, np.int64)
+    ks = np.asarray(k_seq, np.int64)
+    B = t.shape[0]
+    acc = np.zeros(B, np.int64)
+    nxt = np.zeros(B, np.int64)
+    for b in range(B):
+        kb = int(ks[b])
+        a, n = verify(t[b:b + 1, :kb + 1], d[b:b + 1, :kb])
+        acc[b], nxt[b] = a[0], n[0]
+    return acc, nxt
+
+
+def kv_rollback_seqk(lens, pos, accepted_len, k_seq):
+    """Rollback after a draft with a length per sequence: ``kv_rollback`` with K = k_seq[b]
+    for each sequence ([OVMTP] Stateful execution)."""
+    ks = np.asarray(k_seq, np.int64)
+    a = np.asarray(accepted_len, np.int64)
+    lens = np.asarray(lens, np.int64) - ks + np.minimum(a + 1, ks)
+    pos = np.asarray(pos, np.int64) - ks + a + 1
+    return lens, pos
+
+
 def step_weights(beta: float, K: int) -> np.ndarray:
     """Normalised exponential-decay step weights alpha_k = beta^(k-1) / sum_j beta^(j-1).
     [SPEC] Step Weight Formula."""

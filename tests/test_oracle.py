@@ -661,3 +661,142 @@ def test_prefill_then_exact_decoding_equals_prefill_of_the_committed_sequence():
                  np.array([0]))
     assert np.allclose(st["kc"][:, :, :n], rk[:, :, :n], rtol=0, atol=1e-5)
     assert np.allclose(st["vc"][:, :, :n], rv[:, :, :n], rtol=0, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------- per-sequence K
+
+def test_adapt_k_seq_golden_cases():
+    """The per-sequence window rule against hand-worked cases (cited in the fixture)."""
+    gold = json.load(open(os.path.join(GOLDEN, "adapt_k_seq_cases.json")))
+    for c in gold["cases"]:
+        got = O.adapt_k_seq(c["accepted"], c["k"], c["k_min"], c["k_max"])
+        assert got.tolist() == c["k_next"], c
+
+
+def test_verify_seqk_reads_only_the_sequence_rows():
+    """Target rows past k_b and drafts past k_b do not matter (poisoned with NaN and
+    out-of-range ids); k_b = K for every sequence is the uniform verification; brute force
+    over every draft in [0,4)^k_b for each k_b <= 3 against the definition."""
+    rng = np.random.default_rng(7)
+    B, K, V = 6, 3, 4
+    t = rng.normal(size=(B, K + 1, V)).astype(np.float32)
+    d = rng.integers(0, V, size=(B, K))
+    ks = np.array([0, 1, 2, 3, 3, 1])
+    tp, dp = t.copy(), d.copy()
+    for b in range(B):
+        tp[b, ks[b] + 1:] = np.nan
+        dp[b, ks[b]:] = -1
+    a1, n1 = O.verify_seqk(t, d, ks)
+    a2, n2 = O.verify_seqk(tp, dp, ks)
+    assert np.array_equal(a1, a2) and np.array_equal(n1, n2)
+    assert np.all(a1 <= ks) and np.all(a1 >= 0)
+    a3, n3 = O.verify_seqk(t, d, np.full(B, K))
+    a4, n4 = O.verify(t, d)
+    assert np.array_equal(a3, a4) and np.array_equal(n3, n4)
+    for kb in range(K + 1):
+        for dd in itertools.product(range(V), repeat=kb):
+            dr = np.full((1, K), -1)
+            dr[0, :kb] = dd
+            a, n = O.verify_seqk(t[:1], dr, np.array([kb]))
+            g = [int(np.argmax(t[0, j])) for j in range(K + 1)]
+            ref = 0
+            while ref < kb and dd[ref] == g[ref]:
+                ref += 1
+            assert a[0] == ref and n[0] == g[ref]
+
+
+def test_seqk_draft_and_rollback_is_per_sequence_truncation():
+    """Drafting k_b steps per sequence then rolling back to a_b leaves, for every sequence,
+    the cache a fresh min(a_b+1, k_b)-step draft of that sequence alone would leave, and
+    sequences with k_b = 0 are untouched except pos += 1 after rollback."""
+    cfg = small_cfg(K=4, batch=4)
+    inp = _inputs(cfg, 30)
+    W = O.OracleWeights(cfg, inp.weights)
+    ks = np.array([4, 0, 2, 1])
+    kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
+    r = O.draft_seqk(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, ks, 4)
+    assert np.array_equal(r["lens"], inp.lens + ks) and np.array_equal(r["pos"], inp.pos + ks)
+    assert np.all(r["draft_tokens"][1] == -1) and np.all(r["draft_tokens"][3, 1:] == -1)
+    a = np.array([2, 0, 2, 0])
+    ln, ps = O.kv_rollback_seqk(r["lens"], r["pos"], a, ks)
+    assert np.array_equal(ln - inp.lens, np.minimum(a + 1, ks))
+    assert np.array_equal(ps - inp.pos, a + 1)
+    for b in range(cfg.batch):
+        kt, vt = inp.k_cache[b:b + 1].copy(), inp.v_cache[b:b + 1].copy()
+        m = int(min(a[b] + 1, ks[b]))
+        if m:
+            rt = O.draft(cfg, W, inp.hidden[b:b + 1], inp.last_tokens[b:b + 1], kt, vt,
+                         inp.lens[b:b + 1], inp.pos[b:b + 1], m)
+            assert np.array_equal(rt["draft_tokens"][0], r["draft_tokens"][b, :m])
+        assert np.array_equal(kc[b, :, :ln[b]], kt[0, :, :ln[b]])
+        assert np.array_equal(vc[b, :, :ln[b]], vt[0, :, :ln[b]])
+        # slots past the sequence's own draft are untouched
+        assert np.array_equal(kc[b, :, inp.lens[b] + ks[b]:],
+                              inp.k_cache[b, :, inp.lens[b] + ks[b]:])
+
+
+def lockstep_seqk(cfg, inp, W, tgt, prompts, n_new, k0, window, k_min, k_max, draft, verify,
+                  rollback):
+    """B sequences decoded speculatively in lock step, each with its own length: draft(h
+    [B, H], last [B], k [B], K_max) -> drafts [B, K_max]; verify(rows [B, K_max+1, V],
+    drafts, k) -> (a, next); rollback(a, k). The next lengths come from adapt_k_seq over the
+    last `window` iterations. Returns the emitted tokens per sequence and the k history."""
+    B = len(prompts)
+    seqs = [list(map(int, p)) for p in prompts]
+    hid = []
+    for b in range(B):
+        h, lg = tgt.forward(seqs[b])
+        seqs[b].append(int(np.argmax(lg[-1])))
+        hid.append(h[-1])
+    k = np.full(B, k0)
+    a_hist, k_hist = [], []
+    while min(len(s) - len(p) for s, p in zip(seqs, prompts)) < n_new:
+        d = np.asarray(draft(np.stack(hid), np.array([s[-1] for s in seqs]), k, k_max))
+        rows = np.zeros((B, k_max + 1, cfg.vocab), np.float32)
+        hrows = []
+        for b in range(B):
+            hb = []
+            for j in range(int(k[b]) + 1):
+                hj, lj = tgt.forward(seqs[b] + [int(x) for x in d[b, :j]])
+                rows[b, j] = lj[-1]
+                hb.append(hj[-1])
+            hrows.append(hb)
+        a, nxt = verify(rows, d, k)
+        rollback(a, k)
+        for b in range(B):
+            seqs[b] += [int(x) for x in d[b, :a[b]]] + [int(nxt[b])]
+            hid[b] = hrows[b][int(a[b])]
+        a_hist.append(np.asarray(a))
+        k_hist.append(k.copy())
+        k = O.adapt_k_seq(a_hist[-window:], k_hist[-window:], k_min, k_max)
+    return [s[len(p):len(p) + n_new] for s, p in zip(seqs, prompts)], np.array(k_hist)
+
+
+def test_speculative_with_per_sequence_k_equals_greedy():
+    """Each sequence of a batch drafts, verifies and rolls back with its own length, which
+    the window rule moves every iteration; every sequence still emits exactly its plain
+    greedy decoding, and the lengths differ across sequences and iterations."""
+    cfg = small_cfg(cid=95, batch=3, vocab=2, ctx_lo=4, K=3)
+    inp = _inputs(cfg, 512)
+    W = O.OracleWeights(cfg, inp.weights)
+    tgt = TinyTarget(cfg, S.target_weights(cfg, 2), inp.weights["embed"], inp.weights["lm_head"])
+    prompts = [S.prompt_tokens(cfg, 5 + b, sub=b) for b in range(cfg.batch)]
+    st = {"kc": inp.k_cache.copy(), "vc": inp.v_cache.copy(), "len": inp.lens.copy(),
+          "pos": np.array([len(p) - 1 for p in prompts])}
+
+    def draft(h, last, k, k_max):
+        r = O.draft_seqk(cfg, W, h, last, st["kc"], st["vc"], st["len"], st["pos"], k, k_max)
+        st["len"], st["pos"] = r["lens"], r["pos"]
+        return r["draft_tokens"]
+
+    def verify(rows, d, k):
+        return O.verify_seqk(rows, d, k)
+
+    def rollback(a, k):
+        st["len"], st["pos"] = O.kv_rollback_seqk(st["len"], st["pos"], a, k)
+
+    out, kh = lockstep_seqk(cfg, inp, W, tgt, prompts, 40, 2, 3, 0, 5, draft, verify, rollback)
+    for b in range(cfg.batch):
+        assert out[b] == tgt.greedy(prompts[b], 40), b
+    assert len(set(kh.reshape(-1).tolist())) > 2
+    assert any(len(set(row.tolist())) > 1 for row in kh)   # lengths differ within a batch
