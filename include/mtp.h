@@ -57,7 +57,7 @@ typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
 #define MTP_DEVERR_TOKEN 1u    /* a token id (last_tokens or a draft) was outside [0, vocab) */
 #define MTP_DEVERR_CAPACITY 2u /* len + K exceeded the cache capacity                   */
 #define MTP_DEVERR_ACCEPT 4u   /* an accepted_len entry was outside [0, K]              */
-#define MTP_DEVERR_COUNT 8u    /* a prefill row count was outside [0, n]                 */
+#define MTP_DEVERR_COUNT 8u    /* a prefill row count or per-sequence draft length was out of range */
 
 /* Shape of the MTP head. rope_theta: RoPE base; rms_eps: RMSNorm epsilon. */
 typedef struct {
@@ -175,6 +175,32 @@ mtp_status mtp_verify(mtp_handle* h, const float* target_logits, const int32_t* 
  */
 mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len, int32_t B,
                            int32_t K, void* stream);
+
+/*
+ * Speculative length per sequence (OpenVINO GenAI "Speculative Decoding", Backend
+ * Differences: the draft length follows each request's recent acceptance; forceinjection
+ * "MTP 深度解析", 7.3: depth adapted to the live acceptance rate). These are mtp_draft,
+ * mtp_verify and mtp_kv_rollback with sequence b running k_seq[b] (0 <= k_seq[b] <= K_max)
+ * steps instead of K; the batch still runs K_max steps in lock step and the steps of a
+ * sequence past its own length are masked: they read and write no cache slot, need no
+ * capacity, and leave unspecified (valid) token ids in draft_tokens[b, k_seq[b]..K_max-1].
+ *   k_seq [B] device int32, the same array for the draft, its verification and its rollback
+ *   mtp_draft_seqk:   len[b], pos[b] advance by k_seq[b]; slots len..len+k_seq[b]-1 written
+ *   mtp_verify_seqk:  target_logits [B, K_max+1, V]; only rows 0..k_seq[b] of sequence b are
+ *                     read; accepted_len[b] in [0, k_seq[b]], next_token[b] = argmax of row
+ *                     accepted_len[b]
+ *   mtp_kv_rollback_seqk: as mtp_kv_rollback with K = k_seq[b] per sequence
+ * Errors: as the uniform calls (K_max takes K's limits); a k_seq entry outside [0, K_max]
+ * sets MTP_DEVERR_COUNT in the draft and is clamped everywhere.
+ */
+mtp_status mtp_draft_seqk(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                          mtp_kv* kv, const int32_t* k_seq, int32_t B, int32_t K_max,
+                          int32_t* draft_tokens, void* stream);
+mtp_status mtp_verify_seqk(mtp_handle* h, const float* target_logits, const int32_t* draft_tokens,
+                           const int32_t* k_seq, int32_t B, int32_t K_max, int32_t* accepted_len,
+                           int32_t* next_token, void* stream);
+mtp_status mtp_kv_rollback_seqk(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len,
+                                const int32_t* k_seq, int32_t B, int32_t K_max, void* stream);
 
 /*
  * Greedy verification from the target's hidden states instead of its logits
@@ -358,6 +384,20 @@ const char* mtp_status_string(mtp_status s);
  */
 mtp_status mtp_adapt_k(const int32_t* accepted_len, int32_t B, int32_t K, int32_t k_min,
                        int32_t k_max, int32_t* k_next);
+
+/*
+ * Per-sequence speculative lengths from a window of recent iterations (OpenVINO GenAI
+ * "Speculative Decoding", Backend Differences; forceinjection "MTP 深度解析", 7.3). Host
+ * function; accepted_hist and k_hist are host [W, B] arrays (row i: one iteration's accepted
+ * lengths and the lengths it used, any order of rows). Iteration i of sequence b asks for
+ * k+1 when it accepted all k drafts and for a+1 otherwise; k_next[b] (host, [B]) is the mean
+ * of its W requests rounded up, clipped to [k_min, k_max]. W = 1 is the per-iteration rule
+ * of mtp_adapt_k applied to each sequence on its own. Errors: MTP_ERR_INVALID_ARG for NULL
+ * pointers or an entry with k outside 0..100 or a outside 0..k; MTP_ERR_SHAPE for W < 1,
+ * B < 1, k_min < 0, k_max < k_min or k_max > 100. Nothing is written on error.
+ */
+mtp_status mtp_adapt_k_seq(const int32_t* accepted_hist, const int32_t* k_hist, int32_t W,
+                           int32_t B, int32_t k_min, int32_t k_max, int32_t* k_next);
 
 /*
  * Training-loss weights of the K MTP steps, speculators user guide "MTP (Multi-Token

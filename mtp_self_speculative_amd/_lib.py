@@ -89,6 +89,11 @@ _SIGS = {
     "mtp_status_string": (ctypes.c_char_p, [_I]),
     "mtp_step_weights": (_I, [ctypes.c_float, _I, ctypes.POINTER(ctypes.c_float)]),
     "mtp_adapt_k": (_I, [ctypes.POINTER(_I), _I, _I, _I, _I, ctypes.POINTER(_I)]),
+    "mtp_adapt_k_seq": (_I, [ctypes.POINTER(_I), ctypes.POINTER(_I), _I, _I, _I, _I,
+                             ctypes.POINTER(_I)]),
+    "mtp_draft_seqk": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _P, _I, _I, _P, _P]),
+    "mtp_verify_seqk": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "mtp_kv_rollback_seqk": (_I, [_P, ctypes.POINTER(mtp_kv), _P, _P, _I, _I, _P]),
 }
 
 
@@ -284,3 +289,34 @@ def mtp_step_weights(beta: float, K: int) -> list:
     out = (ctypes.c_float * max(int(K), 1))()
     _check(LIB.mtp_step_weights(float(beta), int(K), out), "mtp_step_weights")
     return [float(out[i]) for i in range(int(K))]
+
+
+def mtp_draft_seqk(handle: int, hidden: int, last_tokens: int, kv: mtp_kv, k_seq: int, B: int,
+                   K_max: int, draft_tokens: int, stream: int | None) -> None:
+    _check(LIB.mtp_draft_seqk(handle, hidden, last_tokens, ctypes.byref(kv), k_seq, B, K_max,
+                              draft_tokens, stream), "mtp_draft_seqk")
+
+
+def mtp_verify_seqk(handle: int, target_logits: int, draft_tokens: int | None, k_seq: int, B: int,
+                    K_max: int, accepted_len: int, next_token: int, stream: int | None) -> None:
+    _check(LIB.mtp_verify_seqk(handle, target_logits, draft_tokens, k_seq, B, K_max,
+                               accepted_len, next_token, stream), "mtp_verify_seqk")
+
+
+def mtp_kv_rollback_seqk(handle: int, kv: mtp_kv, accepted_len: int, k_seq: int, B: int,
+                         K_max: int, stream: int | None) -> None:
+    _check(LIB.mtp_kv_rollback_seqk(handle, ctypes.byref(kv), accepted_len, k_seq, B, K_max,
+                                    stream), "mtp_kv_rollback_seqk")
+
+
+def mtp_adapt_k_seq(accepted_hist, k_hist, k_min: int, k_max: int) -> list:
+    """Per-sequence lengths from the last W iterations' accepted lengths and lengths
+    (host nested sequences [W][B])."""
+    a = [[int(x) for x in row] for row in accepted_hist]
+    k = [[int(x) for x in row] for row in k_hist]
+    W, B = len(a), len(a[0]) if a else 0
+    fa = (_I * max(W * B, 1))(*[x for row in a for x in row])
+    fk = (_I * max(W * B, 1))(*[x for row in k for x in row])
+    out = (_I * max(B, 1))()
+    _check(LIB.mtp_adapt_k_seq(fa, fk, W, B, int(k_min), int(k_max), out), "mtp_adapt_k_seq")
+    return [int(out[i]) for i in range(B)]

@@ -84,8 +84,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   float* sc = vn + D;                    // [kMaxGroup][chunk]
   float* ored = sc + kMaxGroup * chunk;  // [kAttnWaves][kMaxGroup][D]
 
-  const int slot = p.len[b] + p.step;
-  const bool overflow = slot >= p.capacity;
+  // A masked sequence (past its own step count) attends to its new key alone: slot 0 of an
+  // empty cache, which only split 0 holds and which comes from LDS, never from memory.
+  const bool masked = p.kseq && p.step >= seq_steps(p.kseq, b, p.step + 1);
+  const int slot = masked ? 0 : p.len[b] + p.step;
+  const bool overflow = !masked && slot >= p.capacity;
   if (overflow && s == 0 && g == 0 && tid == 0) set_error(p.err, 2u);
   const int T_valid = overflow ? p.capacity : slot + 1;
   const int t0 = s * chunk;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     }
   }
   // ---- the workgroup whose chunk holds the new slot appends it to the cache
-  if (has_new && tid < D) {
+  if (has_new && !masked && tid < D) {
     const long o = (kv_base + slot) * D + tid;
     CT::put(kc, o, kn[tid]);
     CT::put(vc, o, vn[tid]);
@@ -348,8 +351,11 @@ __global__ __launch_bounds__(kFlashThreads) void attn_flash_kernel(AttnParams p)
   float* wml = snew + kMaxGroup;                  // [kFlashWaves][kMaxGroup][2]
   float* wo = wml + kFlashWaves * kMaxGroup * 2;  // [kFlashWaves][kMaxGroup][D]
 
-  const int slot = p.len[b] + p.step;
-  const bool overflow = slot >= p.capacity;
+  // A masked sequence (past its own step count) attends to its new key alone: slot 0 of an
+  // empty cache, which only split 0 holds and which comes from LDS, never from memory.
+  const bool masked = p.kseq && p.step >= seq_steps(p.kseq, b, p.step + 1);
+  const int slot = masked ? 0 : p.len[b] + p.step;
+  const bool overflow = !masked && slot >= p.capacity;
   if (overflow && s == 0 && g == 0 && tid == 0) set_error(p.err, 2u);
   const int T_valid = overflow ? p.capacity : slot + 1;
   const int t0 = s * p.chunk;
@@ -565,7 +571,7 @@ __global__ __launch_bounds__(kFlashThreads) void attn_flash_kernel(AttnParams p)
     }
   }
   // ---- the workgroup whose chunk holds the new slot appends it to the cache
-  if (has_new && tid < D) {
+  if (has_new && !masked && tid < D) {
     const long o = (kv_base + slot) * D + tid;
     static_cast<uint16_t*>(p.kc)[o] = f32_to_bf16(kn[tid]);
     static_cast<uint16_t*>(p.vc)[o] = f32_to_bf16(vn[tid]);
@@ -583,7 +589,8 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
   __shared__ float red[D / kWave];
   const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
-  const int slot = p.len[b] + p.step;
+  const bool masked = p.kseq && p.step >= seq_steps(p.kseq, b, p.step + 1);
+  const int slot = masked ? 0 : p.len[b] + p.step;
   const int T_valid = slot >= p.capacity ? p.capacity : slot + 1;
   const int nvalid = (T_valid + p.chunk - 1) / p.chunk;
   const long hb = (long)b * p.n_q + hq;
@@ -733,7 +740,8 @@ hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, int nspli
 // hidden state widened to fp32 (the first step's input).
 template <class CT>
 __global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int d, float theta,
-                                   const void* hidden, float* hf, int H) {
+                                   const void* hidden, float* hf, int H, const int* kseq,
+                                   unsigned err_bit, unsigned* err) {
   const int half = d / 2;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e < K * B * half) {
@@ -741,18 +749,22 @@ __global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int
     rope_cs(pos[b] + k, i, d, theta, tab[(long)kb * d + i], tab[(long)kb * d + half + i]);
   }
   if (e < B * H) hf[e] = CT::get(static_cast<const typename CT::T*>(hidden), e);
+  if (kseq && e < B && (kseq[e] < 0 || kseq[e] > K)) set_error(err, err_bit);
 }
 
 hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
-                              float theta, const void* hidden, float* hf, int H, hipStream_t s) {
+                              float theta, const void* hidden, float* hf, int H, const int* kseq,
+                              unsigned err_bit, unsigned* err, hipStream_t s) {
+  if (kseq && !err) return hipErrorInvalidValue;
   const int n1 = K * B * (d / 2), n2 = B * H;
-  const int n = n1 > n2 ? n1 : n2;
+  int n = n1 > n2 ? n1 : n2;
+  n = n > B ? n : B;
   if (dtype == 0)
     hipLaunchKernelGGL(draft_setup_kernel<F32>, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos,
-                       B, K, d, theta, hidden, hf, H);
+                       B, K, d, theta, hidden, hf, H, kseq, err_bit, err);
   else
     hipLaunchKernelGGL(draft_setup_kernel<BF16>, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos,
-                       B, K, d, theta, hidden, hf, H);
+                       B, K, d, theta, hidden, hf, H, kseq, err_bit, err);
   return hipGetLastError();
 }
 

@@ -342,6 +342,14 @@ __device__ __forceinline__ unsigned long long take_key(unsigned long long* p) {
   return __hip_atomic_exchange(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Steps of sequence b in a call of K steps: its own length kseq[b] clamped to [0, K], or K
+// when the call has no per-sequence lengths.
+__device__ __forceinline__ int seq_steps(const int* kseq, int b, int K) {
+  if (!kseq) return K;
+  const int k = kseq[b];
+  return k < 0 ? 0 : k > K ? K : k;
+}
+
 __device__ __forceinline__ void set_error(unsigned int* err, unsigned int bit) {
   __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

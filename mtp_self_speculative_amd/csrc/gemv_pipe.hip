@@ -323,8 +323,9 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
         if (p.maxlogit) p.maxlogit[b] = key_value(k);
         if (p.advance > 0) {
-          p.len[b] += p.advance;
-          p.pos[b] += p.advance;
+          const int adv = seq_steps(p.kseq, b, p.advance);  // the sequence's own steps
+          p.len[b] += adv;
+          p.pos[b] += adv;
         }
       }
     }

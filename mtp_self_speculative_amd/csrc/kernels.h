@@ -73,6 +73,7 @@ struct GemvParams {
   int* len;  // when advance > 0 the last workgroup adds it to len[b] and pos[b]
   int* pos;
   int advance;
+  const int* kseq;  // per-sequence step counts of the call (advance by kseq[b]), or null
   // >= kDummyBytes of readable device memory: the target of the weight-streaming
   // kernels' prefetches past a wave's last stage, which are issued but never consumed
   const void* dummy;
@@ -92,8 +93,10 @@ hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, i
 // Per-call set-up: RoPE tables of K consecutive steps (tab[k][b][0..d/2) = cos,
 // tab[k][b][d/2..d) = sin of (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded
 // to fp32) and hidden [B, H] (weight dtype) widened to fp32 into hf.
+// With kseq (per-sequence step counts) it also sets `err_bit` for a count outside [0, K].
 hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
-                              float theta, const void* hidden, float* hf, int H, hipStream_t s);
+                              float theta, const void* hidden, float* hf, int H, const int* kseq,
+                              unsigned err_bit, unsigned* err, hipStream_t s);
 
 struct AttnParams {
   const float* qkv;  // [B, ldqkv] fp32: q (n_q*d) | k (n_kv*d) | v (n_kv*d), before RoPE
@@ -118,6 +121,10 @@ struct AttnParams {
   int ld_o_bf16;
   unsigned* err;
   const int* perm;  // launch order of the items (attn_plan_kernel), or null: natural order
+  // Per-sequence step counts, or null. A sequence past its count at this step is masked:
+  // it attends only to the step's own key (no cache read, no cache write, no capacity
+  // check), so its output is finite and is discarded by the caller.
+  const int* kseq;
 };
 // Attention (partials per split) followed by the split merge into o. p.chunk must be a
 // positive multiple of attn_chunk_quantum() and at most attn_max_chunk(cdtype).
@@ -163,6 +170,7 @@ struct MmParams {
   int* len;
   int* pos;
   int advance;
+  const int* kseq;  // as GemvParams::kseq
   const void* dummy;  // as GemvParams::dummy
   SampleParams smp;   // EPI_SAMPLE
   // When set, W is read from this packed copy (see launch_pack) and w0/w1/w2/seg1/seg2
@@ -238,6 +246,7 @@ struct VerifyParams {
   unsigned* counters;        // [B * kSeqLineU32] zero on entry/exit
   int* accepted;
   int* next;
+  const int* kseq;  // per-sequence draft counts (rows past kseq[b] are not read), or null
 };
 hipError_t launch_verify(const VerifyParams& p, int B, hipStream_t s);
 
@@ -263,8 +272,9 @@ constexpr int kVsMaxK = 100;
 int vs_chunks(int V);
 hipError_t launch_verify_sample(const VSampleParams& p, int B, hipStream_t s);
 
-hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
-                           hipStream_t s);
+// kseq: per-sequence draft counts of the call being rolled back (K for all when null).
+hipError_t launch_rollback(int* len, int* pos, const int* accepted, const int* kseq, int B, int K,
+                           unsigned* err, hipStream_t s);
 
 // dst[i] = src[i] widened to fp32 (src in weight dtype), i < n.
 hipError_t launch_widen(int dtype, const void* src, float* dst, long n, hipStream_t s);

@@ -441,7 +441,7 @@ static mtp_status check_kv(const mtp_handle* h, const mtp_kv* kv, int B) {
 
 // Attention parameters of step k (shared by both paths).
 static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int chunk,
-                              int nsplit, const int* perm) {
+                              int nsplit, const int* perm, const int* kseq) {
   const mtp_config& c = h->cfg;
   const Layout& L = h->L;
   AttnParams a{};
@@ -458,6 +458,7 @@ static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int
   a.o = h->at<float>(L.o);
   a.err = h->at<unsigned>(L.err);
   a.perm = perm;
+  a.kseq = kseq;
   return a;
 }
 
@@ -475,7 +476,7 @@ struct LmOut {
 static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_kv* kv,
                                  int32_t B, int32_t K, int32_t* draft_tokens, float* hidden_out,
                                  float* max_logit_out, const LmOut& lo, int chunk, int nsplit,
-                                 const int* perm, hipStream_t s) {
+                                 const int* perm, const int* kseq, hipStream_t s) {
   const mtp_config& c = h->cfg;
   const mtp_weights& w = h->w;
   const Layout& L = h->L;
@@ -546,7 +547,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
     // 3. RoPE + cache append + attention; the merge writes o as the next bf16 operand
-    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit, perm);
+    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit, perm, kseq);
     a.o_bf16 = xq;
     a.o_bf16_lo = xq_lo;
     a.ld_o_bf16 = L.ldq;
@@ -591,6 +592,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       m.logits_ld = lo.ld;
       m.len = kv->len; m.pos = kv->pos;
       m.advance = (k == K - 1) ? K : 0;
+      m.kseq = kseq;
       m.dummy = h->ws + L.dummy;
       if (lo.smp) {
         m.smp = *lo.smp;
@@ -609,7 +611,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
 static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                              mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
                              float* hidden_out, float* max_logit_out, const LmOut& lo,
-                             void* stream) {
+                             void* stream, const int32_t* kseq = nullptr) {
   if (!h || !hidden || !last_tokens) return MTP_ERR_INVALID_ARG;
   if (!aligned(hidden, 16)) return MTP_ERR_INVALID_ARG;
   if (K < 0 || B < 1) return MTP_ERR_SHAPE;
@@ -648,7 +650,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   const int nsplit = (kv->capacity + chunk - 1) / chunk;
 
   if (launch_draft_setup(c.dtype, h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, hidden,
-                         hb, H, s) != hipSuccess)
+                         hb, H, kseq, MTP_DEVERR_COUNT, err, s) != hipSuccess)
     return MTP_ERR_HIP;
   // With more attention items than run at once, order them longest first (per call).
   const int* perm = nullptr;
@@ -660,7 +662,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   }
   if (use_mm(c, B))
     return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out, lo,
-                          chunk, nsplit, perm, s);
+                          chunk, nsplit, perm, kseq, s);
   for (int k = 0; k < K; ++k) {
     hipError_t e;
     // 1. embedding gather + separate RMSNorms + concat + eh_proj
@@ -696,7 +698,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
       return MTP_ERR_HIP;
 
     // 3. RoPE + cache append + split decode attention + merge
-    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit, perm);
+    AttnParams a = attn_params(h, kv, k, B, chunk, nsplit, perm, kseq);
     if ((e = timed(h, KC_ATTN, s, [&] { return launch_attention(c.dtype, a, B, s); })) != hipSuccess)
       return MTP_ERR_HIP;
 
@@ -747,6 +749,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.logits_ld = lo.ld;
     g.len = kv->len; g.pos = kv->pos;
     g.advance = (k == K - 1) ? K : 0;
+    g.kseq = kseq;
     if (lo.smp) {
       g.smp = *lo.smp;
       g.smp.row = k;
@@ -1064,11 +1067,78 @@ mtp_status mtp_kv_rollback(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_le
   if (st != MTP_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed(h, KC_ROLLBACK, s, [&] {
-           return launch_rollback(kv->len, kv->pos, accepted_len, B, K,
+           return launch_rollback(kv->len, kv->pos, accepted_len, nullptr, B, K,
                                   h->at<unsigned>(h->L.err), s);
          }) == hipSuccess
              ? MTP_OK
              : MTP_ERR_HIP;
+}
+
+mtp_status mtp_draft_seqk(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
+                          mtp_kv* kv, const int32_t* k_seq, int32_t B, int32_t K_max,
+                          int32_t* draft_tokens, void* stream) {
+  if (!h || (K_max > 0 && !k_seq)) return MTP_ERR_INVALID_ARG;
+  return draft_impl(h, hidden, last_tokens, kv, B, K_max, draft_tokens, nullptr, nullptr,
+                    LmOut{nullptr, 0, 0, nullptr}, stream, k_seq);
+}
+
+mtp_status mtp_verify_seqk(mtp_handle* h, const float* target_logits, const int32_t* draft_tokens,
+                           const int32_t* k_seq, int32_t B, int32_t K_max, int32_t* accepted_len,
+                           int32_t* next_token, void* stream) {
+  if (!h || !target_logits || !k_seq || !accepted_len || !next_token) return MTP_ERR_INVALID_ARG;
+  if (K_max < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K_max > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  if (K_max > 0 && !draft_tokens) return MTP_ERR_INVALID_ARG;
+  VerifyParams p{};
+  p.logits = target_logits;
+  p.draft = draft_tokens;
+  p.K = K_max;
+  p.V = h->cfg.vocab;
+  p.keys = h->at<unsigned long long>(h->L.v_keys);
+  p.kstride = h->L.v_kstride;
+  p.counters = h->at<unsigned>(h->L.v_cnt);
+  p.accepted = accepted_len;
+  p.next = next_token;
+  p.kseq = k_seq;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(h, KC_VERIFY, s, [&] { return launch_verify(p, B, s); }) == hipSuccess ? MTP_OK
+                                                                                      : MTP_ERR_HIP;
+}
+
+mtp_status mtp_kv_rollback_seqk(mtp_handle* h, mtp_kv* kv, const int32_t* accepted_len,
+                                const int32_t* k_seq, int32_t B, int32_t K_max, void* stream) {
+  if (!h || !accepted_len || !k_seq) return MTP_ERR_INVALID_ARG;
+  if (K_max < 0 || B < 1) return MTP_ERR_SHAPE;
+  if (K_max > h->max_k || B > h->max_batch) return MTP_ERR_CAPACITY;
+  mtp_status st = check_kv(h, kv, B);
+  if (st != MTP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(h, KC_ROLLBACK, s, [&] {
+           return launch_rollback(kv->len, kv->pos, accepted_len, k_seq, B, K_max,
+                                  h->at<unsigned>(h->L.err), s);
+         }) == hipSuccess
+             ? MTP_OK
+             : MTP_ERR_HIP;
+}
+
+mtp_status mtp_adapt_k_seq(const int32_t* accepted_hist, const int32_t* k_hist, int32_t W,
+                           int32_t B, int32_t k_min, int32_t k_max, int32_t* k_next) {
+  if (!accepted_hist || !k_hist || !k_next) return MTP_ERR_INVALID_ARG;
+  if (W < 1 || B < 1 || k_min < 0 || k_max < k_min || k_max > kMaxK) return MTP_ERR_SHAPE;
+  for (long i = 0; i < (long)W * B; ++i)
+    if (k_hist[i] < 0 || k_hist[i] > kMaxK || accepted_hist[i] < 0 ||
+        accepted_hist[i] > k_hist[i])
+      return MTP_ERR_INVALID_ARG;
+  for (int b = 0; b < B; ++b) {
+    long sum = 0;
+    for (int i = 0; i < W; ++i) {
+      const int a = accepted_hist[(long)i * B + b], k = k_hist[(long)i * B + b];
+      sum += a >= k ? k + 1 : a + 1;
+    }
+    const long want = (sum + W - 1) / W;  // mean of the requests, rounded up
+    k_next[b] = (int32_t)(want < k_min ? k_min : want > k_max ? k_max : want);
+  }
+  return MTP_OK;
 }
 
 mtp_status mtp_get_error(mtp_handle* h, void* stream, uint32_t* bits) {

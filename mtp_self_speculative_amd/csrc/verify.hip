@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* row = p.logits + ((long)b * (p.K + 1) + j) * p.V;
   const int units = VEC ? p.V / 4 : p.V;
-  const int lo = c * p.seg, hi = min(lo + p.seg, units);
+  const int ks = seq_steps(p.kseq, b, p.K);  // the sequence's own draft count
+  const int lo = c * p.seg, hi = j <= ks ? min(lo + p.seg, units) : lo;  // rows past ks: skipped
   unsigned long long best = 0ull;
   auto process = [&](const int (&idx)[kVPer], const f32x4v (&v)[kVPer]) {
 #pragma unroll
@@ -86,13 +87,15 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
   // formed (indexes past the segment are clamped, so the extra stage is harmless).
   int ia[kVPer], ib[kVPer];
   f32x4v va[kVPer], vb[kVPer];
-  load_stage<VEC>(row, lo, hi, ia, va);
-  for (int i0 = lo; i0 < hi; i0 += 2 * kVStage) {
-    load_stage<VEC>(row, i0 + kVStage, hi, ib, vb);
-    process(ia, va);
-    if (i0 + kVStage >= hi) break;
-    load_stage<VEC>(row, i0 + 2 * kVStage, hi, ia, va);
-    process(ib, vb);
+  if (lo < hi) {
+    load_stage<VEC>(row, lo, hi, ia, va);
+    for (int i0 = lo; i0 < hi; i0 += 2 * kVStage) {
+      load_stage<VEC>(row, i0 + kVStage, hi, ib, vb);
+      process(ia, va);
+      if (i0 + kVStage >= hi) break;
+      load_stage<VEC>(row, i0 + 2 * kVStage, hi, ia, va);
+      process(ib, vb);
+    }
   }
   best = wave_max_u64(best);
   if (lane == 0) kred[wave] = best;
@@ -106,10 +109,10 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
     // Take (and reset) the K+1 row keys and scan for the first mismatch.
     if (threadIdx.x == 0) {
       int a = 0, next = -1;
-      for (int q = 0; q <= p.K; ++q) {
+      for (int q = 0; q <= p.K; ++q) {  // every key is reset; rows past kseq decide nothing
         const int t = (int)key_index(take_key(kb + q));
-        if (next < 0) {
-          if (q < p.K && p.draft[(long)b * p.K + q] == t) {
+        if (next < 0 && q <= ks) {
+          if (q < ks && p.draft[(long)b * p.K + q] == t) {
             ++a;
           } else {
             next = t;
@@ -374,24 +377,25 @@ hipError_t launch_verify_sample(const VSampleParams& p, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void rollback_kernel(int* len, int* pos, const int* accepted, int B, int K,
-                                unsigned* err) {
+__global__ void rollback_kernel(int* len, int* pos, const int* accepted, const int* kseq, int B,
+                                int K, unsigned* err) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
+  const int k = seq_steps(kseq, b, K);  // the draft's steps for this sequence
   int a = accepted[b];
-  if (a < 0 || a > K) {
+  if (a < 0 || a > k) {
     set_error(err, 4u);
-    a = a < 0 ? 0 : K;
+    a = a < 0 ? 0 : k;
   }
-  const int keep = (a + 1 < K) ? a + 1 : K;
-  len[b] += keep - K;
-  pos[b] += a + 1 - K;
+  const int keep = (a + 1 < k) ? a + 1 : k;
+  len[b] += keep - k;
+  pos[b] += a + 1 - k;
 }
 
-hipError_t launch_rollback(int* len, int* pos, const int* accepted, int B, int K, unsigned* err,
-                           hipStream_t s) {
+hipError_t launch_rollback(int* len, int* pos, const int* accepted, const int* kseq, int B, int K,
+                           unsigned* err, hipStream_t s) {
   hipLaunchKernelGGL(rollback_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, pos, accepted,
-                     B, K, err);
+                     kseq, B, K, err);
   return hipGetLastError();
 }
 

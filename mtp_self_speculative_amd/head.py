@@ -287,6 +287,51 @@ class MtpHead:
         L.mtp_kv_catchup(self.handle, cache.kv, th.data_ptr(), draft_tokens.data_ptr(),
                          accepted.data_ptr(), B, K1 - 1, _stream(stream))
 
+    def draft_seqk(self, hidden: torch.Tensor, last_tokens: torch.Tensor, cache: MtpCache,
+                   k_seq: torch.Tensor, K_max: int, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+        """Draft with k_seq[b] (int32 [B] on the device, 0..K_max) steps for sequence b;
+        returns [B, K_max] int32 (entries past k_seq[b] are unspecified)."""
+        B = self._check_draft_in(hidden, last_tokens, cache, K_max)
+        self._t("k_seq", k_seq, torch.int32, (B,))
+        if out is None:
+            out = torch.empty((B, K_max), dtype=torch.int32, device=hidden.device)
+        self._t("out", out, torch.int32, (B, K_max))
+        L.mtp_draft_seqk(self.handle, hidden.data_ptr(), last_tokens.data_ptr(), cache.kv,
+                         k_seq.data_ptr(), B, K_max, out.data_ptr(), _stream(stream))
+        return out
+
+    def verify_seqk(self, target_logits: torch.Tensor, draft_tokens: torch.Tensor | None,
+                    k_seq: torch.Tensor, accepted: torch.Tensor | None = None,
+                    next_token: torch.Tensor | None = None, stream=None):
+        """Greedy verification of k_seq[b] drafts per sequence against target_logits
+        [B, K_max+1, V] (rows past k_seq[b] are not read)."""
+        B, K = self._check_logits(target_logits)
+        self._check_drafts(draft_tokens, B, K, required=True)
+        self._t("k_seq", k_seq, torch.int32, (B,))
+        self._check_outs(B, accepted, next_token)
+        dev = target_logits.device
+        if accepted is None:
+            accepted = torch.empty(B, dtype=torch.int32, device=dev)
+        if next_token is None:
+            next_token = torch.empty(B, dtype=torch.int32, device=dev)
+        L.mtp_verify_seqk(self.handle, target_logits.data_ptr(), _ptr(draft_tokens),
+                          k_seq.data_ptr(), B, K, accepted.data_ptr(), next_token.data_ptr(),
+                          _stream(stream))
+        return accepted, next_token
+
+    def rollback_seqk(self, cache: MtpCache, accepted: torch.Tensor, k_seq: torch.Tensor,
+                      K_max: int, stream=None) -> None:
+        if not isinstance(accepted, torch.Tensor) or accepted.dim() != 1:
+            raise ValueError("accepted must be a [B] int32 tensor")
+        B = accepted.shape[0]
+        self._check_batch(B, K_max)
+        self._t("accepted", accepted, torch.int32, (B,))
+        self._t("k_seq", k_seq, torch.int32, (B,))
+        self._check_cache(cache, B)
+        L.mtp_kv_rollback_seqk(self.handle, cache.kv, accepted.data_ptr(), k_seq.data_ptr(), B,
+                               K_max, _stream(stream))
+
     def prefill(self, cache: MtpCache, target_hidden: torch.Tensor, tokens: torch.Tensor,
                 n_valid: torch.Tensor | None = None, stream=None) -> None:
         """Fill the cache over a prompt: row s of target_hidden [B, n, H] (the target's

@@ -110,6 +110,52 @@ def speculative_greedy(target: TinyTarget, prompt, n_new: int, draft_fn, verify_
     return seq[len(prompt):len(prompt) + n_new], accepted
 
 
+def lockstep_seqk(target: TinyTarget, prompts, n_new: int, k0: int, window: int, k_min: int,
+                  k_max: int, draft_fn, verify_fn, rollback_fn, adapt_fn):
+    """Greedy speculative decoding of several sequences in lock step, each with its own
+    speculative length (OpenVINO GenAI "Speculative Decoding", Backend Differences).
+
+    draft_fn(hidden [B, H], last [B], k [B], k_max) -> drafts [B, k_max] (entries past k[b]
+    unused); verify_fn(target rows [B, k_max+1, V], drafts, k) -> (accepted [B], next [B]);
+    rollback_fn(accepted, k). adapt_fn(accepted history [W, B], length history [W, B],
+    k_min, k_max) -> next lengths [B], over the last `window` iterations. Target rows of
+    sequence b are full forwards over its committed prefix extended by j drafts (rows past
+    k[b] are zero). Returns the first n_new emitted tokens per sequence and the length
+    history [iterations, B].
+    """
+    B = len(prompts)
+    seqs = [[int(x) for x in p] for p in prompts]
+    hid = []
+    for b in range(B):
+        h, lg = target.forward(seqs[b])
+        seqs[b].append(int(argmax_lowest(lg[-1])))
+        hid.append(h[-1])
+    k = np.full(B, k0, np.int64)
+    a_hist, k_hist = [], []
+    while min(len(s) - len(p) for s, p in zip(seqs, prompts)) < n_new:
+        d = np.asarray(draft_fn(np.stack(hid), np.array([s[-1] for s in seqs]), k, k_max))
+        rows = np.zeros((B, k_max + 1, target.cfg.vocab), np.float32)
+        hrows = []
+        for b in range(B):
+            hb = []
+            for j in range(int(k[b]) + 1):
+                hj, lj = target.forward(seqs[b] + [int(x) for x in d[b, :j]])
+                rows[b, j] = lj[-1]
+                hb.append(hj[-1])
+            hrows.append(hb)
+        a, nxt = verify_fn(rows, d, k)
+        a, nxt = np.asarray(a, np.int64), np.asarray(nxt, np.int64)
+        rollback_fn(a, k)
+        for b in range(B):
+            seqs[b] += [int(x) for x in d[b, :a[b]]] + [int(nxt[b])]
+            hid[b] = hrows[b][int(a[b])]
+        a_hist.append(a)
+        k_hist.append(k.copy())
+        k = np.asarray(adapt_fn(np.array(a_hist[-window:]), np.array(k_hist[-window:]), k_min,
+                                k_max), np.int64)
+    return [s[len(p):len(p) + n_new] for s, p in zip(seqs, prompts)], np.array(k_hist)
+
+
 def softmax_rows(logits: np.ndarray, T: float) -> np.ndarray:
     x = np.asarray(logits, np.float64) / T
     x = np.exp(x - x.max(axis=-1, keepdims=True))

@@ -251,3 +251,40 @@ def test_prefill_host_checks():
     kv = L.mtp_kv()
     p = ctypes.c_void_p(16)
     assert L.LIB.mtp_kv_prefill(None, ctypes.byref(kv), p, p, None, 1, 4, None) == 1
+
+
+def test_adapt_k_seq_entry_point():
+    """The library's per-sequence window rule against the hand-worked cases and the oracle."""
+    import json
+    import os
+    from oracle import mtp_oracle as O
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "adapt_k_seq_cases.json")))
+    for c in gold["cases"]:
+        assert L.mtp_adapt_k_seq(c["accepted"], c["k"], c["k_min"], c["k_max"]) == c["k_next"], c
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        W, B = int(rng.integers(1, 6)), int(rng.integers(1, 9))
+        k = rng.integers(0, 9, size=(W, B))
+        a = (rng.random((W, B)) * (k + 1)).astype(int)
+        kmin = int(rng.integers(0, 3))
+        kmax = int(rng.integers(kmin, 12))
+        assert L.mtp_adapt_k_seq(a.tolist(), k.tolist(), kmin, kmax) == \
+            O.adapt_k_seq(a, k, kmin, kmax).tolist()
+    out = (ctypes.c_int32 * 2)(-7, -7)
+    a = (ctypes.c_int32 * 2)(1, 3)
+    k = (ctypes.c_int32 * 2)(2, 2)                      # accepted 3 > k 2
+    assert L.LIB.mtp_adapt_k_seq(a, k, 1, 2, 1, 5, out) == 1
+    assert L.LIB.mtp_adapt_k_seq(None, k, 1, 2, 1, 5, out) == 1
+    assert L.LIB.mtp_adapt_k_seq(a, k, 0, 2, 1, 5, out) == 2
+    assert L.LIB.mtp_adapt_k_seq(a, k, 1, 2, 3, 2, out) == 2
+    assert L.LIB.mtp_adapt_k_seq(a, k, 1, 2, 1, 101, out) == 2
+    assert list(out) == [-7, -7]
+
+
+def test_seqk_entry_points_reject_null_arguments():
+    kv = L.mtp_kv()
+    p = ctypes.c_void_p(16)
+    assert L.LIB.mtp_draft_seqk(None, p, p, ctypes.byref(kv), p, 1, 1, p, None) == 1
+    assert L.LIB.mtp_verify_seqk(None, p, p, p, 1, 1, p, p, None) == 1
+    assert L.LIB.mtp_kv_rollback_seqk(None, ctypes.byref(kv), p, p, 1, 1, None) == 1

@@ -11,7 +11,7 @@ import pytest
 
 import mtp_synth as S
 from oracle import mtp_oracle as O
-from oracle.tiny_target import TinyTarget, speculative_greedy
+from oracle.tiny_target import TinyTarget, lockstep_seqk, speculative_greedy
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -735,43 +735,6 @@ def test_seqk_draft_and_rollback_is_per_sequence_truncation():
                               inp.k_cache[b, :, inp.lens[b] + ks[b]:])
 
 
-def lockstep_seqk(cfg, inp, W, tgt, prompts, n_new, k0, window, k_min, k_max, draft, verify,
-                  rollback):
-    """B sequences decoded speculatively in lock step, each with its own length: draft(h
-    [B, H], last [B], k [B], K_max) -> drafts [B, K_max]; verify(rows [B, K_max+1, V],
-    drafts, k) -> (a, next); rollback(a, k). The next lengths come from adapt_k_seq over the
-    last `window` iterations. Returns the emitted tokens per sequence and the k history."""
-    B = len(prompts)
-    seqs = [list(map(int, p)) for p in prompts]
-    hid = []
-    for b in range(B):
-        h, lg = tgt.forward(seqs[b])
-        seqs[b].append(int(np.argmax(lg[-1])))
-        hid.append(h[-1])
-    k = np.full(B, k0)
-    a_hist, k_hist = [], []
-    while min(len(s) - len(p) for s, p in zip(seqs, prompts)) < n_new:
-        d = np.asarray(draft(np.stack(hid), np.array([s[-1] for s in seqs]), k, k_max))
-        rows = np.zeros((B, k_max + 1, cfg.vocab), np.float32)
-        hrows = []
-        for b in range(B):
-            hb = []
-            for j in range(int(k[b]) + 1):
-                hj, lj = tgt.forward(seqs[b] + [int(x) for x in d[b, :j]])
-                rows[b, j] = lj[-1]
-                hb.append(hj[-1])
-            hrows.append(hb)
-        a, nxt = verify(rows, d, k)
-        rollback(a, k)
-        for b in range(B):
-            seqs[b] += [int(x) for x in d[b, :a[b]]] + [int(nxt[b])]
-            hid[b] = hrows[b][int(a[b])]
-        a_hist.append(np.asarray(a))
-        k_hist.append(k.copy())
-        k = O.adapt_k_seq(a_hist[-window:], k_hist[-window:], k_min, k_max)
-    return [s[len(p):len(p) + n_new] for s, p in zip(seqs, prompts)], np.array(k_hist)
-
-
 def test_speculative_with_per_sequence_k_equals_greedy():
     """Each sequence of a batch drafts, verifies and rolls back with its own length, which
     the window rule moves every iteration; every sequence still emits exactly its plain
@@ -795,7 +758,8 @@ def test_speculative_with_per_sequence_k_equals_greedy():
     def rollback(a, k):
         st["len"], st["pos"] = O.kv_rollback_seqk(st["len"], st["pos"], a, k)
 
-    out, kh = lockstep_seqk(cfg, inp, W, tgt, prompts, 40, 2, 3, 0, 5, draft, verify, rollback)
+    out, kh = lockstep_seqk(tgt, prompts, 40, 2, 3, 0, 5, draft, verify, rollback,
+                            O.adapt_k_seq)
     for b in range(cfg.batch):
         assert out[b] == tgt.greedy(prompts[b], 40), b
     assert len(set(kh.reshape(-1).tolist())) > 2
