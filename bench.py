@@ -10,7 +10,11 @@ pass and are resident in HBM before the timed pass replays the identical chain
 
 Prints one JSON line: draft-steps/s (value), verified tokens/s, the HBM roofline
 fraction of the whole iteration and of the lm_head kernel (HIP events on the
-library's stream), and the oracle timed on the host's cores.
+library's stream), and the oracle timed on the host's cores. The headline workload
+is the Qwen3-8B-shaped head at batch 1; the same run also times the other workloads
+(B=32 ragged, the Qwen3-32B shape at 32K context, the wide B=64 head and the tiny
+fp32 head) under "workloads", each with its own throughput, HBM fraction, lm_head
+fraction and device memory.
 """
 from __future__ import annotations
 
@@ -118,11 +122,13 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(cfg, inp, K: int, iter_bytes: int, reps32: int = 10, reps64: int = 5) -> dict:
+def cpu_baseline(cfg, inp, K: int, iter_bytes: int, budget32: float = 8.0,
+                 budget64: float = 4.0) -> dict:
     """The oracle (plain NumPy, untuned) on the host cores: one speculative iteration of the
-    same workload (K draft steps + verify + rollback), 1 warm-up then the median of the
-    timed runs; the stated value is the float32 oracle, the float64 one is reported beside
-    it. Input generation and the widening of the weights are not timed."""
+    same workload (K draft steps + verify + rollback), 1 warm-up then the median of as many
+    timed iterations as fit the time budget (at least 3); the stated value is the float32
+    oracle, the float64 one is reported beside it. Input generation and the widening of the
+    weights are not timed."""
     import numpy as np
 
     import mtp_synth as S
@@ -142,10 +148,12 @@ def cpu_baseline(cfg, inp, K: int, iter_bytes: int, reps32: int = 10, reps64: in
     except (AttributeError, OSError):  # pragma: no cover
         affinity = os.cpu_count() or 1
 
-    def timed(dt, reps):
+    def timed(dt, budget):
         W = O.OracleWeights(cfg, inp.weights, dt=dt)
         times = []
-        for rep in range(reps + 1):
+        rep = -1
+        while rep < 3 or (sum(times) < budget and rep < 200):
+            rep += 1
             kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
             t0 = time.perf_counter()
             r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, K)
@@ -158,11 +166,11 @@ def cpu_baseline(cfg, inp, K: int, iter_bytes: int, reps32: int = 10, reps64: in
             if rep:
                 times.append((t1 - t0) + (t3 - t2))
         log(f"cpu oracle ({np.dtype(dt).name}): median {statistics.median(times):.3f} s "
-            f"per iteration over {reps}")
-        return statistics.median(times)
+            f"per iteration over {len(times)}")
+        return statistics.median(times), len(times)
 
-    t32 = timed(np.float32, reps32)
-    t64 = timed(np.float64, reps64)
+    t32, reps32 = timed(np.float32, budget32)
+    t64, reps64 = timed(np.float64, budget64)
     return {"value": round(K / t32, 4), "unit": "draft-steps/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{reps32} timed iterations (after 1 warm-up) of {K} draft steps + verify "
@@ -251,26 +259,13 @@ def sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up) -> dict
     return out
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="q8b", choices=sorted(DESCR))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true",
-                    help="extra untimed pass with HIP events around every kernel class")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain device copy of 1 GiB (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration()
-        return 0
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
-                                   "(the path shards by sequence with no exchange step)"}))
-        return 2
+def run_workload(name: str, args, full: bool) -> dict:
+    """Record, then replay and time `args.steps` speculative iterations of one workload.
 
+    full (the headline workload): also the lm_head's own HIP-event roofline, per-call
+    latency percentiles, the optional per-kernel breakdown, verification from hidden states,
+    exact catch-up, prompt prefill and the sampling pass. Otherwise: throughput, HBM
+    fraction, the lm_head fraction, verification from hidden states and catch-up."""
     import numpy as np
     import torch
 
@@ -278,15 +273,16 @@ def main() -> int:
     from mtp_self_speculative_amd import MtpCache, MtpHead
 
     dev = torch.device("cuda:0")
-    cfg = S.get_config(args.config)
+    cfg = S.get_config(name)
     B, K = cfg.batch, cfg.K
     iters = args.warmup + args.steps
     lens0 = S.cache_lengths(cfg)
     cap = int(lens0.max()) + (iters + 2) * K + 8
     t0 = time.time()
     inp = S.make_inputs(cfg, capacity=cap)
-    log(f"generated {args.config} inputs in {time.time() - t0:.1f} s")
+    log(f"generated {name} inputs in {time.time() - t0:.1f} s")
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    esz = 2 if cfg.dtype == "bf16" else 4
 
     def up(a):
         if cfg.dtype == "bf16":
@@ -306,7 +302,14 @@ def main() -> int:
     drafts = torch.empty((iters, B, K), dtype=torch.int32, device=dev)
     acc = torch.empty((iters, B), dtype=torch.int32, device=dev)
     nxt = torch.empty((iters, B), dtype=torch.int32, device=dev)
-    log("inputs resident on the device")
+    info = head.info()
+    shared = int(w["embed"].numel() + w["lm_head"].numel()) * esz
+    memory = {"weights_bytes": int(sum(t.numel() for t in w.values())) * esz,
+              "of_which_shared_embed_lm_head_bytes": shared,
+              "workspace_bytes": info["workspace_bytes"],
+              "of_which_packed_copy_bytes": info["packed_weight_bytes"],
+              "kv_cache_bytes": int(cache.k.numel() + cache.v.numel()) * esz}
+    log(f"{name}: inputs resident on the device; memory {memory}")
 
     # Recording pass: plant each iteration's target logits from the drafts it produced.
     logits = []
@@ -321,7 +324,7 @@ def main() -> int:
     torch.cuda.synchronize()
     rec_drafts, rec_acc = drafts.clone(), acc.clone()
     assert head.get_error() == 0
-    log("recording pass done")
+    log(f"{name}: recording pass done")
 
     def run(it, last):
         head.draft(hidden[it], last, cache, K, out=drafts[it])
@@ -349,134 +352,222 @@ def main() -> int:
     elapsed, _ = replay(0)
     if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
         raise RuntimeError("timed replay diverged from the recording pass")
-    log(f"timed pass: {args.steps} iterations in {elapsed * 1e3:.2f} ms")
+    log(f"{name}: timed pass: {args.steps} iterations in {elapsed * 1e3:.2f} ms")
     # Same replay with HIP events around every lm_head launch (on the library's stream).
     el_ev, prof = replay(LMHEAD_BIT)
-    log(f"lm_head-event pass: {args.steps} iterations in {el_ev * 1e3:.2f} ms")
-
-    # Per-call latency: HIP events (torch's current stream, which the library runs on)
-    # bracket each ABI call of the same replay; median and 10th / 90th percentiles.
-    cache.len.copy_(len0)
-    cache.pos.copy_(pos0)
-    last = last0
-    for it in range(args.warmup):
-        last = run(it, last)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for j, it in enumerate(range(args.warmup, iters)):
-        e = ev[j]
-        e[0].record()
-        head.draft(hidden[it], last, cache, K, out=drafts[it])
-        e[1].record()
-        head.verify(logits[it], drafts[it], acc[it], nxt[it])
-        e[2].record()
-        head.rollback(cache, acc[it], K)
-        e[3].record()
-        last = nxt[it]
-    torch.cuda.synchronize()
-
-    def pct(vals):
-        q = np.percentile(np.asarray(vals) * 1e3, [10, 50, 90])
-        return {"p10": round(float(q[0]), 2), "p50": round(float(q[1]), 2), "p90": round(float(q[2]), 2)}
-
-    latency = {"samples": args.steps,
-               "draft": pct([e[0].elapsed_time(e[1]) for e in ev]),
-               "verify": pct([e[1].elapsed_time(e[2]) for e in ev]),
-               "rollback": pct([e[2].elapsed_time(e[3]) for e in ev]),
-               "iteration": pct([e[0].elapsed_time(e[3]) for e in ev])}
-    log(f"per-call latency (us): {latency}")
-
-    kernel_us = None
-    if args.breakdown:
-        _, bprof = replay((1 << 9) - 1)
-        kernel_us = {k: round(ms * 1e3 / n, 2) for k, (ms, n) in bprof.items() if n}
-        log(f"per-kernel us/launch: {kernel_us}")
-
-    # Verification from the target's hidden states (the alternative to mtp_verify that
-    # never materialises target logits): one call per recorded iteration's drafts.
-    th = up(S.target_hidden(cfg, K))
-    tn = up(S.target_norm(cfg))
-    vacc = torch.empty(B, dtype=torch.int32, device=dev)
-    vnxt = torch.empty(B, dtype=torch.int32, device=dev)
-    for it in range(3):
-        head.verify_hidden(th, tn, drafts[it], vacc, vnxt)
-    torch.cuda.synchronize()
-    t0v = time.perf_counter()
-    for it in range(args.steps):
-        head.verify_hidden(th, tn, drafts[args.warmup + it], vacc, vnxt)
-    torch.cuda.synchronize()
-    vh_us = (time.perf_counter() - t0v) / args.steps * 1e6
-    # rows per lm_head pass: 128 on the packed copy (bf16 heads made for 3+ sequences), else 64
-    vh_group = 128 if (cfg.dtype == "bf16" and B >= 3) else 64
-    vh_passes = -(-(B * (K + 1)) // vh_group)
-    vh_bytes = vh_passes * cfg.vocab * cfg.hidden * (2 if cfg.dtype == "bf16" else 4) + \
-        B * (K + 1) * cfg.hidden * (2 if cfg.dtype == "bf16" else 4)
-    log(f"verify from hidden states: {vh_us:.2f} us per call")
-    # Exact cache catch-up (the alternative to rollback), on the recorded drafts and
-    # accepted lengths, from the state right after a K-step draft.
-    len_k, pos_k = len0 + K, pos0 + K
-    cu_ms = []
-    for it in range(args.steps + 2):
-        cache.len.copy_(len_k)
-        cache.pos.copy_(pos_k)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        head.catchup(cache, th, drafts[args.warmup + it % args.steps], acc[args.warmup + it % args.steps])
-        e1.record()
-        e1.synchronize()
-        if it >= 2:
-            cu_ms.append(e0.elapsed_time(e1))
-    cu_us = float(np.median(cu_ms)) * 1e3
-    assert head.get_error() == 0
-    log(f"exact cache catch-up: {cu_us:.2f} us per call")
-
-    samp = sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up)
+    log(f"{name}: lm_head-event pass: {args.steps} iterations in {el_ev * 1e3:.2f} ms")
 
     acc_np = acc[args.warmup:].cpu().numpy().astype(np.int64)
     tokens = int((acc_np + 1).sum())
-    rows = int((acc_np + 1).sum())
-    ab = algorithmic_bytes(cfg, lens0, K, rows // max(1, args.steps))
+    ab = algorithmic_bytes(cfg, lens0, K, tokens // max(1, args.steps))
     it_s = elapsed / args.steps
     lm_ms, lm_n = prof["lm_head_argmax"]
     lm_avg_s = lm_ms / 1e3 / lm_n
     lm_gbs = ab["lm_head"] / lm_avg_s / 1e9
+    res = {"workload": DESCR[name], "dtype": cfg.dtype, "batch": B, "K": K,
+           "steps": args.steps, "warmup": args.warmup,
+           "draft_steps_per_s": round(K * args.steps / elapsed, 3),
+           "ms_per_iteration": round(it_s * 1e3, 4),
+           "us_per_draft_step": round(it_s * 1e6 / K, 2),
+           "verified_tok_per_s": round(tokens / elapsed, 2),
+           "tokens_per_iteration": round(tokens / (args.steps * B), 4),
+           "hbm_roofline_frac": round(ab["iteration"] / it_s / 1e9 / HBM_PEAK_GBS, 4),
+           "algorithmic_bytes_per_iteration": int(ab["iteration"]),
+           "lm_head": {"avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n,
+                       "achieved_gb_per_s": round(lm_gbs, 1),
+                       "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                       "algorithmic_bytes_per_launch": int(ab["lm_head"])},
+           "device_memory": memory}
+
+    if full:
+        # Per-call latency: HIP events (torch's current stream, which the library runs on)
+        # bracket each ABI call of the same replay; median and 10th / 90th percentiles.
+        cache.len.copy_(len0)
+        cache.pos.copy_(pos0)
+        last = last0
+        for it in range(args.warmup):
+            last = run(it, last)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for j, it in enumerate(range(args.warmup, iters)):
+            e = ev[j]
+            e[0].record()
+            head.draft(hidden[it], last, cache, K, out=drafts[it])
+            e[1].record()
+            head.verify(logits[it], drafts[it], acc[it], nxt[it])
+            e[2].record()
+            head.rollback(cache, acc[it], K)
+            e[3].record()
+            last = nxt[it]
+        torch.cuda.synchronize()
+
+        def pct(vals):
+            q = np.percentile(np.asarray(vals) * 1e3, [10, 50, 90])
+            return {"p10": round(float(q[0]), 2), "p50": round(float(q[1]), 2),
+                    "p90": round(float(q[2]), 2)}
+
+        res["latency_us"] = {"samples": args.steps,
+                             "draft": pct([e[0].elapsed_time(e[1]) for e in ev]),
+                             "verify": pct([e[1].elapsed_time(e[2]) for e in ev]),
+                             "rollback": pct([e[2].elapsed_time(e[3]) for e in ev]),
+                             "iteration": pct([e[0].elapsed_time(e[3]) for e in ev])}
+        log(f"{name}: per-call latency (us): {res['latency_us']}")
+        if args.breakdown:
+            _, bprof = replay((1 << 9) - 1)
+            res["kernel_us_per_launch"] = {k: round(ms * 1e3 / n, 2)
+                                           for k, (ms, n) in bprof.items() if n}
+            log(f"{name}: per-kernel us/launch: {res['kernel_us_per_launch']}")
+        res["_lm_head_prof"] = (lm_avg_s, lm_n, int(ab["lm_head"]), lm_gbs)
+
+    if cfg.dtype == "bf16":
+        # Verification from the target's hidden states (the alternative to mtp_verify that
+        # never materialises target logits): one call per recorded iteration's drafts.
+        th = up(S.target_hidden(cfg, K))
+        tn = up(S.target_norm(cfg))
+        vacc = torch.empty(B, dtype=torch.int32, device=dev)
+        vnxt = torch.empty(B, dtype=torch.int32, device=dev)
+        for it in range(3):
+            head.verify_hidden(th, tn, drafts[it], vacc, vnxt)
+        torch.cuda.synchronize()
+        t0v = time.perf_counter()
+        for it in range(args.steps):
+            head.verify_hidden(th, tn, drafts[args.warmup + it], vacc, vnxt)
+        torch.cuda.synchronize()
+        vh_us = (time.perf_counter() - t0v) / args.steps * 1e6
+        vh_group = info["verify_hidden_group_rows"]
+        vh_passes = -(-(B * (K + 1)) // vh_group)
+        vh_bytes = vh_passes * cfg.vocab * cfg.hidden * esz + B * (K + 1) * cfg.hidden * esz
+        res["verify_from_hidden"] = {
+            "us_per_call": round(vh_us, 2), "rows": B * (K + 1), "rows_per_pass": vh_group,
+            "algorithmic_bytes": int(vh_bytes),
+            "hbm_frac": round(vh_bytes / (vh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"{name}: verify from hidden states: {vh_us:.2f} us per call")
+        # Exact cache catch-up (the alternative to rollback), on the recorded drafts and
+        # accepted lengths, from the state right after a K-step draft.
+        len_k, pos_k = len0 + K, pos0 + K
+        cu_ms = []
+        for it in range(args.steps + 2):
+            cache.len.copy_(len_k)
+            cache.pos.copy_(pos_k)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            head.catchup(cache, th, drafts[args.warmup + it % args.steps],
+                         acc[args.warmup + it % args.steps])
+            e1.record()
+            e1.synchronize()
+            if it >= 2:
+                cu_ms.append(e0.elapsed_time(e1))
+        res["kv_catchup"] = {"us_per_call": round(float(np.median(cu_ms)) * 1e3, 2),
+                             "candidate_rows": B * K}
+        assert head.get_error() == 0
+        log(f"{name}: exact cache catch-up: {res['kv_catchup']['us_per_call']} us per call")
+
+    if full and cfg.dtype == "bf16":
+        # Prompt prefill: a 4096-token prompt per sequence into an emptied cache.
+        n = min(4096, cap)
+        ph = up(S.prefill_hidden(cfg.with_(batch=1), n)).expand(B, n, cfg.hidden).contiguous()
+        pt = torch.from_numpy(S.prefill_tokens(cfg.with_(batch=1), n)).to(dev).expand(B, n).contiguous()
+        pf_ms = []
+        for it in range(5):
+            cache.len.zero_()
+            cache.pos.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            head.prefill(cache, ph, pt)
+            e1.record()
+            e1.synchronize()
+            if it >= 1:
+                pf_ms.append(e0.elapsed_time(e1))
+        assert head.get_error() == 0
+        pf_us = float(np.median(pf_ms)) * 1e3
+        H, kvd = cfg.hidden, cfg.n_kv * cfg.head_dim
+        pf_bytes = (2 * H * H + 2 * kvd * H) * esz + B * n * (H * esz + 4 + H * esz + 2 * kvd * esz)
+        res["prefill"] = {"prompt_tokens": n, "sequences": B, "us_per_call": round(pf_us, 1),
+                          "prompt_tok_per_s": round(B * n / (pf_us * 1e-6), 1),
+                          "rows_per_pass": info["catchup_group_rows"],
+                          "algorithmic_bytes": int(pf_bytes),
+                          "hbm_frac": round(pf_bytes / (pf_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"{name}: prefill of {n} prompt tokens: {pf_us:.1f} us")
+        del ph, pt
+
+    if full:
+        res["sampling"] = sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up)
+        res["_inp"] = inp
+    head.close()
+    del w, cache, hidden, logits
+    torch.cuda.empty_cache()
+    return res
+
+
+EXTRA_WORKLOADS = ("q8b-b32", "q32b", "wide", "tiny")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="q8b", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the headline workload (not the other workloads)")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="extra untimed pass with HIP events around every kernel class")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+                                   "(the path shards by sequence with no exchange step)"}))
+        return 2
+
+    import mtp_synth as S
+
+    cfg = S.get_config(args.config)
+    head_res = run_workload(args.config, args, full=True)
+    inp = head_res.pop("_inp")
+    lm_avg_s, lm_n, lm_bytes, lm_gbs = head_res.pop("_lm_head_prof")
     out = {
         "metric": METRIC,
-        "value": round(K * args.steps / elapsed, 3),
+        "value": head_res["draft_steps_per_s"],
         "unit": "draft-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(it_s * 1e3, 4),
+        "ms_per_step": head_res["ms_per_iteration"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": DESCR[args.config], "name": args.config, "batch": B, "K": K},
-        "verified_tok_per_s": round(tokens / elapsed, 2),
-        "tokens_per_iteration": round(tokens / (args.steps * B), 4),
-        "hbm_roofline_frac": round(ab["iteration"] / it_s / 1e9 / HBM_PEAK_GBS, 4),
-        "algorithmic_bytes_per_iteration": int(ab["iteration"]),
+        "config": {"workload": DESCR[args.config], "name": args.config, "batch": cfg.batch,
+                   "K": cfg.K},
+        "verified_tok_per_s": head_res["verified_tok_per_s"],
+        "tokens_per_iteration": head_res["tokens_per_iteration"],
+        "hbm_roofline_frac": head_res["hbm_roofline_frac"],
+        "algorithmic_bytes_per_iteration": head_res["algorithmic_bytes_per_iteration"],
         "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
                      "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config),
                      "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n,
-                     "algorithmic_bytes_per_launch": int(ab["lm_head"])},
+                     "algorithmic_bytes_per_launch": lm_bytes},
     }
-    out["verify_from_hidden"] = {"us_per_call": round(vh_us, 2), "rows": B * (K + 1),
-                                 "algorithmic_bytes": int(vh_bytes),
-                                 "hbm_frac": round(vh_bytes / (vh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    out["kv_catchup"] = {"us_per_call": round(cu_us, 2), "candidate_rows": B * K}
-    out["latency_us"] = latency
-    out["sampling"] = samp
-    if kernel_us:
-        out["kernel_us_per_launch"] = kernel_us
-    head.close()
-    del w, cache, hidden, logits
-    torch.cuda.empty_cache()
+    for k in ("us_per_draft_step", "latency_us", "kernel_us_per_launch", "verify_from_hidden",
+              "kv_catchup", "prefill", "sampling", "device_memory"):
+        if k in head_res:
+            out[k] = head_res[k]
+    if not args.no_extra:
+        out["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            if name == args.config:
+                continue
+            r = run_workload(name, args, full=False)
+            out["workloads"][name] = r
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, K, int(ab["iteration"]))
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, cfg.K, out["algorithmic_bytes_per_iteration"])
     print(json.dumps(out), flush=True)
     return 0
 
