@@ -259,6 +259,52 @@ def sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up) -> dict
     return out
 
 
+def large_cache_probe(args, cfg, w, head, cache, hidden, last0, len0, pos0,
+                      capacity: int = 32768) -> dict:
+    """Attention + merge per launch (HIP events on the library's stream) with the bench's
+    cache and with a copy of it in a cache of `capacity` slots holding the same lengths:
+    the chunk is planned from the lengths, so the two should take about the same time."""
+    import torch
+
+    from mtp_self_speculative_amd import MtpCache, MtpHead
+    from mtp_self_speculative_amd._lib import KERNEL_CLASSES
+    bit = 1 << KERNEL_CLASSES.index("attention")
+    B, K = cfg.batch, cfg.K
+    cap0 = cache.capacity
+    k2 = torch.zeros((B, cfg.n_kv, capacity, cfg.head_dim), dtype=cache.k.dtype,
+                     device=cache.k.device)
+    v2 = torch.zeros_like(k2)
+    k2[:, :, :cap0] = cache.k
+    v2[:, :, :cap0] = cache.v
+    big = MtpCache(k2, v2, cache.len.clone(), cache.pos.clone())
+    head2 = MtpHead(hidden=cfg.hidden, n_q_heads=cfg.n_q, n_kv_heads=cfg.n_kv,
+                    head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, weights=w,
+                    max_batch=B, max_k=K, max_capacity=capacity, rope_theta=cfg.rope_theta,
+                    rms_eps=cfg.rms_eps, dtype=cache.k.dtype)
+    out = {"capacity": capacity, "len": int(len0.max())}
+    for key, hd, cc in (("us_cache_as_filled", head, cache), ("us_cache_32768", head2, big)):
+        hd.set_profiling(0)
+        for it in range(args.warmup + args.steps):
+            cc.len.copy_(len0)
+            cc.pos.copy_(pos0)
+            if it == args.warmup:
+                torch.cuda.synchronize()
+                hd.set_profiling(bit)
+            hd.draft(hidden[it], last0, cc, K)
+        torch.cuda.synchronize()
+        hd.set_profiling(0)
+        ms, n = hd.get_profile()["attention"]
+        out[key] = round(ms * 1e3 / max(n, 1), 2)
+    out["capacity_as_filled"] = cap0
+    head2.close()
+    cache.len.copy_(len0)
+    cache.pos.copy_(pos0)
+    del k2, v2, big
+    torch.cuda.empty_cache()
+    log(f"attention + merge with a {capacity}-slot cache: {out}")
+    return out
+
+
 def run_workload(name: str, args, full: bool) -> dict:
     """Record, then replay and time `args.steps` speculative iterations of one workload.
 
@@ -489,6 +535,9 @@ def run_workload(name: str, args, full: bool) -> dict:
         log(f"{name}: prefill of {n} prompt tokens: {pf_us:.1f} us")
         del ph, pt
 
+    if full and name == "q8b":
+        res["attention_large_cache"] = large_cache_probe(args, cfg, w, head, cache, hidden,
+                                                         last0, len0, pos0)
     if full:
         res["sampling"] = sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up)
         res["_inp"] = inp
@@ -556,7 +605,7 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": lm_bytes},
     }
     for k in ("us_per_draft_step", "latency_us", "kernel_us_per_launch", "verify_from_hidden",
-              "kv_catchup", "prefill", "sampling", "device_memory"):
+              "kv_catchup", "prefill", "attention_large_cache", "sampling", "device_memory"):
         if k in head_res:
             out[k] = head_res[k]
     if not args.no_extra:

@@ -53,6 +53,11 @@ size_t flash_lds_bytes(int d) {
                           (size_t)kFlashWaves * kMaxGroup * (d + 2));
 }
 
+// Positions per split of this call.
+__device__ __forceinline__ int attn_chunk(const AttnParams& p) {
+  return p.chunk_dev ? *p.chunk_dev : p.chunk;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPR, dl = (lane % LPR) * VEC;
   const int G = p.n_q / p.n_kv;
-  const int chunk = p.chunk;
+  const int chunk = attn_chunk(p);  // LDS is sized for p.chunk >= chunk
   float* q_l = sm;                       // [kMaxGroup][D]
   float* kn = q_l + kMaxGroup * D;       // [D]
   float* vn = kn + D;                    // [D]
@@ -358,8 +363,9 @@ __global__ __launch_bounds__(kFlashThreads) void attn_flash_kernel(AttnParams p)
   const bool overflow = !masked && slot >= p.capacity;
   if (overflow && s == 0 && g == 0 && tid == 0) set_error(p.err, 2u);
   const int T_valid = overflow ? p.capacity : slot + 1;
-  const int t0 = s * p.chunk;
-  const int t1 = min(t0 + p.chunk, T_valid);
+  const int chunk = attn_chunk(p);
+  const int t0 = s * chunk;
+  const int t1 = min(t0 + chunk, T_valid);
   if (t0 >= t1) return;  // nothing cached in this split (the merge skips it)
   // Cached rows [t0, te) are streamed; the new slot (when in this chunk) comes from LDS.
   const bool has_new = !overflow && slot >= t0 && slot < t1;
@@ -592,7 +598,8 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnParams p) {
   const bool masked = p.kseq && p.step >= seq_steps(p.kseq, b, p.step + 1);
   const int slot = masked ? 0 : p.len[b] + p.step;
   const int T_valid = slot >= p.capacity ? p.capacity : slot + 1;
-  const int nvalid = (T_valid + p.chunk - 1) / p.chunk;
+  const int chunk = attn_chunk(p);
+  const int nvalid = (T_valid + chunk - 1) / chunk;
   const long hb = (long)b * p.n_q + hq;
   const float* ml = p.part_ml + hb * p.nsplit * 2;
   const float* po = p.part_o + hb * p.nsplit * D + t;
@@ -673,8 +680,9 @@ __device__ int plan_scan(int v, int* wsum, int* total) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(const int* len, int B, int nkv,
-                                                                 int chunk, int nsplit,
-                                                                 int* perm) {
+                                                                 int chunk, const int* chunk_dev,
+                                                                 int nsplit, int* perm) {
+  if (chunk_dev) chunk = *chunk_dev;
   __shared__ int F[kPlanMaxBatch], R[kPlanMaxBatch], FP[kPlanMaxBatch], EP[kPlanMaxBatch];
   __shared__ int RK[kPlanMaxBatch];
   __shared__ int wsum[kPlanThreads / kWave];
@@ -727,11 +735,11 @@ bool attn_plan_wanted(int B, int nkv, int nsplit, int num_cu) {
   return B <= kPlanMaxBatch && (long)nsplit * nkv * B > 2L * num_cu;
 }
 
-hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, int nsplit, int* perm,
-                            hipStream_t s) {
+hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, const int* chunk_dev,
+                            int nsplit, int* perm, hipStream_t s) {
   if (B < 1 || B > kPlanMaxBatch || nsplit < 1 || chunk < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, len, B, nkv, chunk,
-                     nsplit, perm);
+                     chunk_dev, nsplit, perm);
   return hipGetLastError();
 }
 
@@ -741,9 +749,28 @@ hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, int nspli
 template <class CT>
 __global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int d, float theta,
                                    const void* hidden, float* hf, int H, const int* kseq,
-                                   unsigned err_bit, unsigned* err) {
+                                   unsigned err_bit, unsigned* err, ChunkPlan cp) {
   const int half = d / 2;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (cp.chunk_out && blockIdx.x == 0) {  // the call's attention chunk, from the lengths
+    __shared__ int wmax[256 / kWave];
+    int m = 0;
+    for (int b = threadIdx.x; b < B; b += blockDim.x) m = max(m, cp.len[b]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < (int)blockDim.x / kWave; ++w) m = max(m, wmax[w]);
+      long T = (long)m + K;
+      if (T > cp.capacity) T = cp.capacity;
+      const long per = (T + cp.nsplit - 1) / cp.nsplit;
+      long ch = (per + cp.q - 1) / cp.q * cp.q;
+      if (ch < cp.q) ch = cp.q;
+      if (ch > cp.max_chunk) ch = cp.max_chunk;
+      cp.chunk_out[0] = (int)ch;
+    }
+  }
   if (e < K * B * half) {
     const int i = e % half, kb = e / half, b = kb % B, k = kb / B;
     rope_cs(pos[b] + k, i, d, theta, tab[(long)kb * d + i], tab[(long)kb * d + half + i]);
@@ -754,17 +781,20 @@ __global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int
 
 hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
                               float theta, const void* hidden, float* hf, int H, const int* kseq,
-                              unsigned err_bit, unsigned* err, hipStream_t s) {
+                              unsigned err_bit, unsigned* err, const ChunkPlan& cp,
+                              hipStream_t s) {
   if (kseq && !err) return hipErrorInvalidValue;
+  if (cp.chunk_out && (!cp.len || cp.nsplit < 1 || cp.q < 1 || cp.max_chunk < cp.q))
+    return hipErrorInvalidValue;
   const int n1 = K * B * (d / 2), n2 = B * H;
   int n = n1 > n2 ? n1 : n2;
   n = n > B ? n : B;
   if (dtype == 0)
     hipLaunchKernelGGL(draft_setup_kernel<F32>, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos,
-                       B, K, d, theta, hidden, hf, H, kseq, err_bit, err);
+                       B, K, d, theta, hidden, hf, H, kseq, err_bit, err, cp);
   else
     hipLaunchKernelGGL(draft_setup_kernel<BF16>, dim3((n + 255) / 256), dim3(256), 0, s, tab, pos,
-                       B, K, d, theta, hidden, hf, H, kseq, err_bit, err);
+                       B, K, d, theta, hidden, hf, H, kseq, err_bit, err, cp);
   return hipGetLastError();
 }
 

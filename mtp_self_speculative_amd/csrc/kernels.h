@@ -94,9 +94,18 @@ hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, i
 // tab[k][b][d/2..d) = sin of (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded
 // to fp32) and hidden [B, H] (weight dtype) widened to fp32 into hf.
 // With kseq (per-sequence step counts) it also sets `err_bit` for a count outside [0, K].
+// With chunk_out it writes the call's attention chunk: the positions the longest sequence
+// attends at the call's last step, min(max_b len[b] + K, capacity), spread over nsplit
+// splits and rounded up to a multiple of q, at most max_chunk.
+struct ChunkPlan {
+  const int* len;
+  int capacity, nsplit, q, max_chunk;
+  int* chunk_out;
+};
 hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
                               float theta, const void* hidden, float* hf, int H, const int* kseq,
-                              unsigned err_bit, unsigned* err, hipStream_t s);
+                              unsigned err_bit, unsigned* err, const ChunkPlan& cp,
+                              hipStream_t s);
 
 struct AttnParams {
   const float* qkv;  // [B, ldqkv] fp32: q (n_q*d) | k (n_kv*d) | v (n_kv*d), before RoPE
@@ -111,6 +120,9 @@ struct AttnParams {
   int batch;  // sequences (set by launch_attention)
   int chunk;  // positions per workgroup (multiple of attn_chunk_quantum())
   int nsplit;
+  // When set, the call's chunk as the set-up kernel computed it from the lengths on the
+  // device (used instead of `chunk`; never larger).
+  const int* chunk_dev;
   const float* rope;  // [B, d]: cos then sin of the step's position
   float scale;
   float* part_o;   // [B, n_q, nsplit, d]
@@ -133,8 +145,8 @@ int attn_max_chunk(int cdtype);
 // Longest-first item order for one draft call, written to perm[nsplit * n_kv * B]; wanted
 // when the items outnumber what the chip runs at once.
 bool attn_plan_wanted(int B, int nkv, int nsplit, int num_cu);
-hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, int nsplit, int* perm,
-                            hipStream_t s);
+hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, const int* chunk_dev,
+                            int nsplit, int* perm, hipStream_t s);
 hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
 
 // ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions

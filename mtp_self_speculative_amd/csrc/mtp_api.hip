@@ -28,6 +28,7 @@ struct Layout {
   size_t x, x1, h, qkv, o, act, rope, part_o, part_ml, attn_perm, lm_keys, lm_cnt, v_keys,
       v_cnt, err;
   size_t dummy;        // zeroed target of never-consumed tail prefetches
+  size_t attn_chunk;   // the draft call's attention chunk (int), computed on the device
   size_t xq, xq_lo, mm_part;  // batched path: bf16 operand planes, K-split partial sums
   int ldq;
   // verification from hidden states: one group of up to kVhGroupPk rows at a time (with
@@ -105,6 +106,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   L.v_cnt = take(B * kSeqLineU32 * 4);
   L.err = take(4);
   L.dummy = take(kDummyBytes);
+  L.attn_chunk = take(4);
   L.ldq = 0;
   L.xq = L.xq_lo = L.mm_part = off;
   if (mm_eligible(c) && max_batch >= kMmMinBatch) {
@@ -459,6 +461,7 @@ static AttnParams attn_params(const mtp_handle* h, mtp_kv* kv, int k, int B, int
   a.err = h->at<unsigned>(L.err);
   a.perm = perm;
   a.kseq = kseq;
+  a.chunk_dev = h->at<int>(L.attn_chunk);
   return a;
 }
 
@@ -649,14 +652,18 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   if (chunk < min_chunk) chunk = (min_chunk + q - 1) / q * q;
   const int nsplit = (kv->capacity + chunk - 1) / chunk;
 
+  // The grid has nsplit splits per (kv head, sequence), sized for the capacity; the chunk
+  // itself is chosen on the device from the lengths, so a cache much larger than its
+  // contents still spreads the attended positions over every split.
+  const ChunkPlan cp{kv->len, kv->capacity, nsplit, q, chunk, h->at<int>(L.attn_chunk)};
   if (launch_draft_setup(c.dtype, h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, hidden,
-                         hb, H, kseq, MTP_DEVERR_COUNT, err, s) != hipSuccess)
+                         hb, H, kseq, MTP_DEVERR_COUNT, err, cp, s) != hipSuccess)
     return MTP_ERR_HIP;
   // With more attention items than run at once, order them longest first (per call).
   const int* perm = nullptr;
   if (attn_plan_wanted(B, nkv, nsplit, h->num_cu)) {
-    if (launch_attn_plan(kv->len, B, nkv, chunk, nsplit, h->at<int>(L.attn_perm), s) !=
-        hipSuccess)
+    if (launch_attn_plan(kv->len, B, nkv, chunk, h->at<int>(L.attn_chunk), nsplit,
+                         h->at<int>(L.attn_perm), s) != hipSuccess)
       return MTP_ERR_HIP;
     perm = h->at<int>(L.attn_perm);
   }

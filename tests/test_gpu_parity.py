@@ -304,6 +304,19 @@ def test_q8b_full_size_parity():
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
 
+def test_q8b_cache_much_larger_than_its_contents():
+    """The q8b head with a 32768-slot cache holding 4096 positions: the attention chunk is
+    planned on the device from the lengths (not from the capacity), and the result still
+    matches the oracle."""
+    cfg = S.get_config("q8b")
+    inp = S.make_inputs(cfg, capacity=32768)
+    g = run_draft(cfg, inp, cfg.K, want_logits=False)
+    r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"])
+    assert n >= 4
+    check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
+
+
 @pytest.mark.parametrize("name", ["q8b-b32", "q32b", "wide"])
 def test_batched_full_size_parity(name):
     """The batched workloads at their real sizes, in the launch configuration the
