@@ -27,6 +27,16 @@ CASES = {
     "bf16-two-groups": small(name="vh6", cid=155, batch=30, K=4, hidden=384, vocab=5003),
     # K = 0: the target's token of row 0 only
     "bf16-k0": small(name="vh5", cid=154, batch=5, K=0),
+    # 3..8 rows of a handle without the packed lm_head (1-2 sequences): the pipelined GEMV
+    # over all rows at once (3, 4, 7 and 8 rows, bf16 and fp32, ragged vocabulary)
+    "bf16-rows3": small(name="vr3", cid=156, batch=1, K=2, hidden=512, vocab=4099),
+    "bf16-rows4": small(name="vr4", cid=157, batch=2, K=1, hidden=640, vocab=5003),
+    "bf16-rows7": small(name="vr7", cid=173, batch=1, K=6, hidden=384, vocab=3001),
+    "bf16-rows8": small(name="vr8", cid=159, batch=2, K=3, hidden=512, vocab=4099),
+    "f32-rows5": small(name="vr5", cid=180, batch=1, K=4, hidden=256, vocab=3001, dtype="f32"),
+    # 2 x 4 rows too wide for the LDS of that GEMV (8 x 8192 floats): the matrix-core route
+    "bf16-rows8-wide": small(name="vr9", cid=171, batch=2, K=3, hidden=8192, n_q=8, n_kv=2,
+                             ffn=512, vocab=2053),
     # full Qwen3-8B-shaped head (H=4096, V=151936), one sequence, K=5
     "q8b": S.get_config("q8b"),
     # same head, 32 sequences, K=3: 128 rows
