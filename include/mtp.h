@@ -141,12 +141,19 @@ mtp_status mtp_draft(mtp_handle* h, const void* hidden, const int32_t* last_toke
 /*
  * Same kernels as mtp_draft, with diagnostic outputs (any may be NULL):
  *   hidden_out   [K, B, H] fp32: each step's layer output h^(k) (before the final norm)
- *   max_logit_out[K, B]    fp32: the largest logit of each step (the drafted token's)
+ *   top2_out     [K, B, 2] fp32: the largest logit of each step (the drafted token's) and
+ *                the largest among the other vocabulary rows, i.e. the margin by which the
+ *                greedy choice won (0 when two rows tie). The second value comes from a
+ *                second pass of the same fused lm_head argmax kernel with the drafted token
+ *                left out, so asking for it doubles the lm_head traffic of the call.
+ *                Near-ties matter because greedy drafts that differ only in rounding order
+ *                may pick different tokens where the top two logits are this close
+ *                (OpenVINO GenAI "Speculative Decoding", Overview).
  *   logits_out   [K, B, V] fp32: every logit of each step
  */
 mtp_status mtp_draft_debug(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                            mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
-                           float* hidden_out, float* max_logit_out, float* logits_out,
+                           float* hidden_out, float* top2_out, float* logits_out,
                            void* stream);
 
 /*

@@ -172,10 +172,10 @@ def mtp_draft(handle: int, hidden: int, last_tokens: int, kv: mtp_kv, B: int, K:
 
 
 def mtp_draft_debug(handle: int, hidden: int, last_tokens: int, kv: mtp_kv, B: int, K: int,
-                    draft_tokens: int, hidden_out: int | None, max_logit_out: int | None,
+                    draft_tokens: int, hidden_out: int | None, top2_out: int | None,
                     logits_out: int | None, stream: int | None) -> None:
     _check(LIB.mtp_draft_debug(handle, hidden, last_tokens, ctypes.byref(kv), B, K, draft_tokens,
-                               hidden_out, max_logit_out, logits_out, stream), "mtp_draft_debug")
+                               hidden_out, top2_out, logits_out, stream), "mtp_draft_debug")
 
 
 def mtp_verify(handle: int, target_logits: int, draft_tokens: int | None, B: int, K: int,

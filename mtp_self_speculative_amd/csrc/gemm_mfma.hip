@@ -143,6 +143,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][LROW]
   __shared__ unsigned long long kred[WV][BP];
   __shared__ uint64_t seed_s[EPI == EPI_SAMPLE ? BP : 1];  // random-stream seeds, read once
+  __shared__ int excl_s[EPI == EPI_ARGMAX ? BP : 1];        // row that never wins, or -1
   __shared__ int flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -308,7 +309,8 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
             if (r0 + i < N) {
               float val = acc[m][nb][i];
               if constexpr (EPI == EPI_SAMPLE) val = val * p.smp.inv_temp + noise[i];
-              const unsigned long long ki = pack_key(val, (uint32_t)(r0 + i));
+              unsigned long long ki = pack_key(val, (uint32_t)(r0 + i));
+              if constexpr (EPI == EPI_ARGMAX) ki = r0 + i == excl_s[b] ? 0ull : ki;
               k = ki > k ? ki : k;
             }
           }
@@ -348,6 +350,9 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   if constexpr (EPI == EPI_SAMPLE) {
     if (tid < BP) seed_s[tid] = tid < p.B ? p.smp.seeds[tid] : 0ull;  // visible after the first barrier
   }
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (tid < BP) excl_s[tid] = (p.excl && tid < p.B) ? p.excl[(long)tid * p.excl_stride] : -1;
+  }
   xload(0);
   wload(A, 0);
   wload(Bf, 1);
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
       for (int b = tid; b < p.B; b += NT) {
         const unsigned long long k = take_key(p.keys + b);
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
-        if (p.maxlogit) p.maxlogit[b] = key_value(k);
+        if (p.maxlogit) p.maxlogit[(long)b * (p.maxlogit_stride ? p.maxlogit_stride : 1)] = key_value(k);
         if (p.advance > 0) {
           const int adv = seq_steps(p.kseq, b, p.advance);  // the sequence's own steps
           p.len[b] += adv;

@@ -116,8 +116,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
   const int rows_per_group = kWavesPerBlock * ROWS;
   const int ngroups = (p.nrows + rows_per_group - 1) / rows_per_group;
   unsigned long long best[NB];
+  int exr[NB];  // row that never wins (second-best pass), or -1
 #pragma unroll
-  for (int i = 0; i < NB; ++i) best[i] = 0ull;
+  for (int i = 0; i < NB; ++i) {
+    best[i] = 0ull;
+    exr[i] = (epi_is_argmax(EPI) && p.excl && b0 + i < p.B)
+                 ? p.excl[(long)(b0 + i) * p.excl_stride] : -1;
+  }
 
   if (nblk == 1) {
     stage(0);
@@ -240,7 +245,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
                                              (uint64_t)p.smp.row, (uint64_t)(lrow[r] >> 2));
                 val = y * p.smp.inv_temp + gumbel_of(philox_word(rb, lrow[r] & 3));
               }
-              const unsigned long long k = pack_key(val, (uint32_t)lrow[r]);
+              const unsigned long long k =
+                  lrow[r] == exr[i] ? 0ull : pack_key(val, (uint32_t)lrow[r]);
               best[i] = k > best[i] ? k : best[i];
               if (p.logits) p.logits[(long)b * p.logits_ld + lrow[r]] = y;
             }
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
       for (int b = threadIdx.x; b < p.B; b += kThreads) {
         const unsigned long long k = take_key(p.keys + b);
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
-        if (p.maxlogit) p.maxlogit[b] = key_value(k);
+        if (p.maxlogit) p.maxlogit[(long)b * (p.maxlogit_stride ? p.maxlogit_stride : 1)] = key_value(k);
         if (p.advance > 0) {
           const int adv = seq_steps(p.kseq, b, p.advance);  // the sequence's own steps
           p.len[b] += adv;

@@ -212,8 +212,10 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
   unsigned long long best[NB];
   float gum[NB];
   uint64_t seed[NB];  // EPI_SAMPLE: the sequences' random-stream seeds, read once
+  int exr[NB];        // row that never wins (second-best pass), or -1
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
+    exr[i] = (epi_is_argmax(EPI) && p.excl && i < B) ? p.excl[(long)i * p.excl_stride] : -1;
     best[i] = 0ull;
     gum[i] = 0.f;
     seed[i] = (EPI == EPI_SAMPLE && i < B) ? p.smp.seeds[i] : 0ull;
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
           } else {
             float val = acc[0][i];
             if constexpr (EPI == EPI_SAMPLE) val = val * p.smp.inv_temp + nz[i];
-            const unsigned long long k = pack_key(val, (uint32_t)r);
+            const unsigned long long k = r == exr[i] ? 0ull : pack_key(val, (uint32_t)r);
             best[i] = k > best[i] ? k : best[i];
             if (p.logits) p.logits[(long)i * p.logits_ld + r] = acc[0][i];
           }
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
       for (int b = tid; b < B; b += NT) {
         const unsigned long long k = take_key(p.keys + b);
         p.tok_out[(long)b * p.tok_out_stride] = (int)key_index(k);
-        if (p.maxlogit) p.maxlogit[b] = key_value(k);
+        if (p.maxlogit) p.maxlogit[(long)b * (p.maxlogit_stride ? p.maxlogit_stride : 1)] = key_value(k);
         if (p.advance > 0) {
           const int adv = seq_steps(p.kseq, b, p.advance);  // the sequence's own steps
           p.len[b] += adv;

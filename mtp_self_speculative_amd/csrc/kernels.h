@@ -67,7 +67,12 @@ struct GemvParams {
   unsigned* counter;         // zero on entry, left zero on exit
   int* tok_out;              // token of b written to tok_out[b * tok_out_stride]
   int tok_out_stride;
-  float* maxlogit;  // [B] or null
+  float* maxlogit;  // value of b's winning key at maxlogit[b * maxlogit_stride], or null
+  int maxlogit_stride;  // 0 means 1
+  // Optional: row excl[b * excl_stride] never wins for batch row b (the second-best pass
+  // of the debug draft: the best value with the winner left out).
+  const int* excl;
+  int excl_stride;
   float* logits;    // [B, logits_ld] or null
   int logits_ld;
   int* len;  // when advance > 0 the last workgroup adds it to len[b] and pos[b]
@@ -177,6 +182,9 @@ struct MmParams {
   int* tok_out;
   int tok_out_stride;
   float* maxlogit;
+  int maxlogit_stride;  // as GemvParams
+  const int* excl;
+  int excl_stride;
   float* logits;
   int logits_ld;
   int* len;

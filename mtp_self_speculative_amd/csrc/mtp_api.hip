@@ -29,6 +29,7 @@ struct Layout {
       v_cnt, err;
   size_t dummy;        // zeroed target of never-consumed tail prefetches
   size_t attn_chunk;   // the draft call's attention chunk (int), computed on the device
+  size_t t2_tok;       // debug draft's second-best pass: its (discarded) winners [B]
   size_t xq, xq_lo, mm_part;  // batched path: bf16 operand planes, K-split partial sums
   int ldq;
   // verification from hidden states: one group of up to kVhGroupPk rows at a time (with
@@ -107,6 +108,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   L.err = take(4);
   L.dummy = take(kDummyBytes);
   L.attn_chunk = take(4);
+  L.t2_tok = take(B * 4);
   L.ldq = 0;
   L.xq = L.xq_lo = L.mm_part = off;
   if (mm_eligible(c) && max_batch >= kMmMinBatch) {
@@ -478,7 +480,7 @@ struct LmOut {
 
 static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_kv* kv,
                                  int32_t B, int32_t K, int32_t* draft_tokens, float* hidden_out,
-                                 float* max_logit_out, const LmOut& lo, int chunk, int nsplit,
+                                 float* top2_out, const LmOut& lo, int chunk, int nsplit,
                                  const int* perm, const int* kseq, hipStream_t s) {
   const mtp_config& c = h->cfg;
   const mtp_weights& w = h->w;
@@ -590,7 +592,8 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       m.counter = h->at<unsigned>(L.lm_cnt);
       m.tok_out = draft_tokens + k;
       m.tok_out_stride = K;
-      m.maxlogit = max_logit_out ? max_logit_out + (size_t)k * B : nullptr;
+      m.maxlogit = top2_out ? top2_out + (size_t)k * B * 2 : nullptr;
+      m.maxlogit_stride = 2;
       m.logits = lo.logits ? lo.logits + (size_t)k * lo.step_stride : nullptr;
       m.logits_ld = lo.ld;
       m.len = kv->len; m.pos = kv->pos;
@@ -604,7 +607,19 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
       const Epi epi = lo.smp ? EPI_SAMPLE : EPI_ARGMAX;
       const MmPlan q = mm_plan(epi, V, H, B, m.packed != nullptr, h->num_cu);
       m.tile_rows = q.tile_rows;
-      return launch_mm(epi, m, q.grid, s);
+      hipError_t e2 = launch_mm(epi, m, q.grid, s);
+      if (e2 == hipSuccess && top2_out) {
+        // second best: the same pass with each sequence's winner left out
+        m.tok_out = h->at<int>(L.t2_tok);
+        m.tok_out_stride = 1;
+        m.maxlogit = top2_out + (size_t)k * B * 2 + 1;
+        m.logits = nullptr;
+        m.advance = 0;
+        m.excl = draft_tokens + k;
+        m.excl_stride = K;
+        e2 = launch_mm(EPI_ARGMAX, m, q.grid, s);
+      }
+      return e2;
     });
     if (e != hipSuccess) return MTP_ERR_HIP;
   }
@@ -613,7 +628,7 @@ static mtp_status draft_steps_mm(mtp_handle* h, const int32_t* last_tokens, mtp_
 
 static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                              mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
-                             float* hidden_out, float* max_logit_out, const LmOut& lo,
+                             float* hidden_out, float* top2_out, const LmOut& lo,
                              void* stream, const int32_t* kseq = nullptr) {
   if (!h || !hidden || !last_tokens) return MTP_ERR_INVALID_ARG;
   if (!aligned(hidden, 16)) return MTP_ERR_INVALID_ARG;
@@ -668,7 +683,7 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     perm = h->at<int>(L.attn_perm);
   }
   if (use_mm(c, B))
-    return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out, lo,
+    return draft_steps_mm(h, last_tokens, kv, B, K, draft_tokens, hidden_out, top2_out, lo,
                           chunk, nsplit, perm, kseq, s);
   for (int k = 0; k < K; ++k) {
     hipError_t e;
@@ -751,7 +766,8 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     g.counter = h->at<unsigned>(L.lm_cnt);
     g.tok_out = draft_tokens + k;
     g.tok_out_stride = K;
-    g.maxlogit = max_logit_out ? max_logit_out + (size_t)k * B : nullptr;
+    g.maxlogit = top2_out ? top2_out + (size_t)k * B * 2 : nullptr;
+    g.maxlogit_stride = 2;
     g.logits = lo.logits ? lo.logits + (size_t)k * lo.step_stride : nullptr;
     g.logits_ld = lo.ld;
     g.len = kv->len; g.pos = kv->pos;
@@ -764,6 +780,17 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
     const Epi lm_epi = lo.smp ? EPI_SAMPLE : EPI_ARGMAX;
     if ((e = timed(h, KC_LMHEAD, s, [&] { return run_gemv(h, PRO_RMS, lm_epi, g, s); })) != hipSuccess)
       return MTP_ERR_HIP;
+    if (top2_out) {
+      // second best: the same pass with each sequence's winner left out
+      g.tok_out = h->at<int>(L.t2_tok);
+      g.tok_out_stride = 1;
+      g.maxlogit = top2_out + (size_t)k * B * 2 + 1;
+      g.logits = nullptr;
+      g.advance = 0;
+      g.excl = draft_tokens + k;
+      g.excl_stride = K;
+      if (run_gemv(h, PRO_RMS, EPI_ARGMAX, g, s) != hipSuccess) return MTP_ERR_HIP;
+    }
   }
   return MTP_OK;
 }
@@ -790,10 +817,10 @@ mtp_status mtp_draft_sample(mtp_handle* h, const void* hidden, const int32_t* la
 
 mtp_status mtp_draft_debug(mtp_handle* h, const void* hidden, const int32_t* last_tokens,
                            mtp_kv* kv, int32_t B, int32_t K, int32_t* draft_tokens,
-                           float* hidden_out, float* max_logit_out, float* logits_out,
+                           float* hidden_out, float* top2_out, float* logits_out,
                            void* stream) {
   if (!h) return MTP_ERR_INVALID_ARG;
-  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, hidden_out, max_logit_out,
+  return draft_impl(h, hidden, last_tokens, kv, B, K, draft_tokens, hidden_out, top2_out,
                     LmOut{logits_out, (size_t)B * h->cfg.vocab, h->cfg.vocab, nullptr}, stream);
 }
 

@@ -180,16 +180,19 @@ class MtpHead:
 
     def draft_debug(self, hidden, last_tokens, cache: MtpCache, K: int, want_logits=False,
                     stream=None):
+        """mtp_draft with diagnostics: (draft tokens [B, K], h^(k) [K, B, H], top-2 logits
+        [K, B, 2] (the drafted token's and the best other one), logits [K, B, V] or None)."""
         B = self._check_draft_in(hidden, last_tokens, cache, K)
         H = hidden.shape[1]
         dev = hidden.device
         out = torch.empty((B, K), dtype=torch.int32, device=dev)
         hid = torch.empty((K, B, H), dtype=torch.float32, device=dev)
-        mx = torch.empty((K, B), dtype=torch.float32, device=dev)
+        top2 = torch.empty((K, B, 2), dtype=torch.float32, device=dev)
         lg = torch.empty((K, B, self.vocab), dtype=torch.float32, device=dev) if want_logits else None
         L.mtp_draft_debug(self.handle, hidden.data_ptr(), last_tokens.data_ptr(), cache.kv, B, K,
-                          out.data_ptr(), hid.data_ptr(), mx.data_ptr(), _ptr(lg), _stream(stream))
-        return out, hid, mx, lg
+                          out.data_ptr(), hid.data_ptr(), top2.data_ptr(), _ptr(lg),
+                          _stream(stream))
+        return out, hid, top2, lg
 
     def draft_sample(self, hidden: torch.Tensor, last_tokens: torch.Tensor, cache: MtpCache,
                      K: int, temperature: float, seeds: torch.Tensor, offset: int,

@@ -49,21 +49,27 @@ def make_head(cfg, inp, max_batch=None, max_k=None):
     return head, cache
 
 
-def compare_draft(cfg, orc: dict, gpu_tokens, gpu_hidden, gpu_max, gpu_logits=None):
+def compare_draft(cfg, orc: dict, gpu_tokens, gpu_hidden, gpu_top2, gpu_logits=None):
     """Teacher-forced comparison: orc was run with force_tokens = gpu_tokens.
+    gpu_top2 [K, B, 2] holds the GPU's largest logit and the largest other one per step.
+    Tokens must agree wherever either side's own top-2 margin clears the near-tie margin.
     Returns the number of (b, k) tokens checked."""
     tol = TOL[cfg.dtype]
     K = gpu_tokens.shape[1]
+    gpu_margin = gpu_top2[..., 0] - gpu_top2[..., 1]
+    assert np.all(gpu_margin >= 0), "second-best logit above the drafted token's"
     checked = 0
     for k in range(K):
         for b in range(gpu_tokens.shape[0]):
-            if orc["margin"][k, b] > MARGIN:
+            if orc["margin"][k, b] > MARGIN or gpu_margin[k, b] > MARGIN + 2 * tol:
                 assert int(orc["draft_tokens"][b, k]) == int(gpu_tokens[b, k]), (k, b)
                 checked += 1
     dh = np.max(np.abs(gpu_hidden - orc["hidden_steps"]))
     assert dh < tol, f"hidden max-abs {dh}"
-    dm = np.max(np.abs(gpu_max - orc["top1"]))
+    dm = np.max(np.abs(gpu_top2[..., 0] - orc["top1"]))
     assert dm < tol, f"max-logit max-abs {dm}"
+    d2 = np.max(np.abs(gpu_top2[..., 1] - (orc["top1"] - orc["margin"])))
+    assert d2 < tol, f"second-logit max-abs {d2}"
     if gpu_logits is not None:
         dl = np.max(np.abs(gpu_logits - orc["logits"]))
         assert dl < tol, f"logits max-abs {dl}"

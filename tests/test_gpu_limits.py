@@ -35,9 +35,9 @@ def _draft(cfg, inp, K):
     head, cache = make_head(cfg, inp)
     hid = to_dev(inp.hidden, cfg.dtype)
     lt = torch.from_numpy(inp.last_tokens.astype(np.int32)).cuda()
-    tok, h, mx, lg = head.draft_debug(hid, lt, cache, K, want_logits=True)
+    tok, h, t2, lg = head.draft_debug(hid, lt, cache, K, want_logits=True)
     assert head.get_error() == 0
-    out = {"tokens": tok.cpu().numpy(), "hidden": h.cpu().numpy(), "max": mx.cpu().numpy(),
+    out = {"tokens": tok.cpu().numpy(), "hidden": h.cpu().numpy(), "top2": t2.cpu().numpy(),
            "logits": lg.cpu().numpy(), "k": cache_to_np(cache.k, cfg.dtype),
            "len": cache.len.cpu().numpy(), "pos": cache.pos.cpu().numpy()}
     return head, cache, out
@@ -54,7 +54,7 @@ def test_draft_parity_at_limits(case):
     kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
     r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, K,
                 force_tokens=g["tokens"])
-    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
     assert n >= 0.5 * K * cfg.batch
     assert np.array_equal(g["len"], inp.lens + K) and np.array_equal(g["pos"], inp.pos + K)
     tol = TOL[cfg.dtype]
@@ -149,7 +149,7 @@ def test_maximum_capacity_cache():
     kc, vc = inp.k_cache.copy(), inp.v_cache.copy()
     r = O.draft(cfg, W, inp.hidden, inp.last_tokens, kc, vc, inp.lens, inp.pos, cfg.K,
                 force_tokens=g["tokens"])
-    compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
     assert np.array_equal(g["len"], [cap])
     x = O.as_float(g["k"][0, :, cap - 2:], cfg.dtype)
     y = O.as_float(kc[0, :, cap - 2:], cfg.dtype)

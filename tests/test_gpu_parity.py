@@ -19,10 +19,10 @@ def run_draft(cfg, inp, K, want_logits=True, B=None):
     B = B or cfg.batch
     hid = to_dev(inp.hidden[:B], cfg.dtype)
     lt = torch.from_numpy(inp.last_tokens[:B].astype(np.int32)).cuda()
-    tok, h, mx, lg = head.draft_debug(hid, lt, cache, K, want_logits=want_logits)
+    tok, h, t2, lg = head.draft_debug(hid, lt, cache, K, want_logits=want_logits)
     assert head.get_error() == 0
     torch.cuda.synchronize()
-    out = {"tokens": tok.cpu().numpy(), "hidden": h.cpu().numpy(), "max": mx.cpu().numpy(),
+    out = {"tokens": tok.cpu().numpy(), "hidden": h.cpu().numpy(), "top2": t2.cpu().numpy(),
            "logits": None if lg is None else lg.cpu().numpy(),
            "k": cache_to_np(cache.k, cfg.dtype), "v": cache_to_np(cache.v, cfg.dtype),
            "len": cache.len.cpu().numpy(), "pos": cache.pos.cpu().numpy()}
@@ -96,7 +96,7 @@ def test_draft_parity(case):
     inp = S.make_inputs(cfg, capacity=int(S.cache_lengths(cfg).max()) + cfg.K + 7)
     g = run_draft(cfg, inp, cfg.K)
     r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
-    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
     assert n >= 0.5 * cfg.K * cfg.batch, f"only {n} tokens above the near-tie margin"
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
@@ -106,7 +106,7 @@ def test_draft_k1_and_k0():
     inp = S.make_inputs(cfg, capacity=320)
     g = run_draft(cfg, inp, 1)
     r = oracle_forced(cfg, inp, 1, g["tokens"])
-    compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
     head, cache = make_head(cfg, inp)
     hid = to_dev(inp.hidden, cfg.dtype)
     lt = torch.from_numpy(inp.last_tokens).cuda()
@@ -212,12 +212,12 @@ def test_chained_iterations():
     last = inp.last_tokens.copy()
     for it in range(iters):
         hid_np = S.hidden_states(cfg, it)
-        tok, hid, mx, _ = head.draft_debug(to_dev(hid_np, cfg.dtype),
+        tok, hid, t2, _ = head.draft_debug(to_dev(hid_np, cfg.dtype),
                                            torch.from_numpy(last.astype(np.int32)).cuda(), cache,
                                            cfg.K)
         g_tok = tok.cpu().numpy()
         r = O.draft(cfg, W, hid_np, last, kc, vc, lens, pos, cfg.K, force_tokens=g_tok)
-        compare_draft(cfg, r, g_tok, hid.cpu().numpy(), mx.cpu().numpy())
+        compare_draft(cfg, r, g_tok, hid.cpu().numpy(), t2.cpu().numpy())
         t = S.plant_target_logits(cfg, g_tok, it)
         acc, nxt = head.verify(torch.from_numpy(t).cuda(), tok)
         head.rollback(cache, acc, cfg.K)
@@ -299,7 +299,7 @@ def test_q8b_full_size_parity():
     inp = S.make_inputs(cfg, capacity=4096 + 64)
     g = run_draft(cfg, inp, cfg.K, want_logits=True)
     r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
-    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
     assert n >= 4
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
@@ -312,7 +312,7 @@ def test_q8b_cache_much_larger_than_its_contents():
     inp = S.make_inputs(cfg, capacity=32768)
     g = run_draft(cfg, inp, cfg.K, want_logits=False)
     r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
-    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"])
     assert n >= 4
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
@@ -329,7 +329,7 @@ def test_batched_full_size_parity(name):
     print(f"full-size batched parity: {name} B={cfg.batch} K={cfg.K}", flush=True)
     g = run_draft(cfg, inp, cfg.K, want_logits=True)
     r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
-    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["max"], g["logits"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
     assert n >= cfg.batch * cfg.K // 2, f"only {n} tokens above the near-tie margin"
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
