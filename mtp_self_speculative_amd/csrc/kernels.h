@@ -154,6 +154,30 @@ hipError_t launch_attn_plan(const int* len, int B, int nkv, int chunk, const int
                             int nsplit, int* perm, hipStream_t s);
 hipError_t launch_attention(int cdtype, const AttnParams& p, int B, hipStream_t s);
 
+// ---- verification from hidden states, up to 16 rows, row-major bf16 lm_head (lm_rows.hip)
+
+// One launch: final RMSNorm of the R rows, the argmax of every row over the lm_head and,
+// when `accepted` is set (R = B (K + 1)), the accepted-prefix scan of each sequence.
+struct LmRowsParams {
+  const uint16_t* h;     // [R][H] bf16 target hidden rows, before the final norm
+  const uint16_t* gain;  // [H] bf16 final-norm gain
+  float eps;
+  const uint16_t* W;     // [V][H] bf16 lm_head, row-major
+  int V, H, R;
+  unsigned long long* keys;  // [>= R], zero on entry, left zero
+  unsigned* counter;         // zero on entry, left zero
+  int* tok_out;              // [R] argmax of each row
+  const int* draft;          // [B][K] draft tokens (K > 0)
+  int B, K;
+  int* accepted;             // [B] accepted prefix lengths, or null (no scan)
+  int* next;                 // [B] the target's token after the accepted prefix
+};
+// Shapes the kernel takes: 1 <= R <= 16, H a multiple of 8 and at most 4096.
+bool lm_rows_fits(int H, int R);
+// Once per process and device before the first launch (raises the kernel's LDS limit).
+hipError_t lm_rows_prepare();
+hipError_t launch_lm_rows(const LmRowsParams& p, int grid, hipStream_t s);
+
 // ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions
 
 // y[b, r] = sum_c W[r, c] * x[b, c] for r < nrows, with W bf16 rows (segments as in

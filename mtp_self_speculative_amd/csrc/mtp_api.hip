@@ -238,6 +238,7 @@ struct mtp_handle {
   size_t ws_bytes;
   Layout L;
   int num_cu = 256;
+  bool lm_rows_ok = false;  // the single-launch small-row verification kernel is usable
   uint32_t prof_mask = 0;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
@@ -392,6 +393,7 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       ncu > 0)
     h->num_cu = ncu;
+  h->lm_rows_ok = cfg->dtype == MTP_BF16 && lm_rows_prepare() == hipSuccess;
   *out = h;
   return MTP_OK;
 }
@@ -895,6 +897,24 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
   const size_t esz = c.dtype == MTP_BF16 ? 2 : 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* tok = h->at<int>(L.vh_tok);
+  // Up to 16 rows without the packed lm_head copy: one launch (norm, row-major lm_head on
+  // the matrix cores, argmax, prefix scan).
+  if (h->lm_rows_ok && !L.pk_lm && lm_rows_fits(H, R)) {
+    LmRowsParams q{};
+    q.h = static_cast<const uint16_t*>(target_hidden);
+    q.gain = static_cast<const uint16_t*>(target_norm);
+    q.eps = c.rms_eps;
+    q.W = static_cast<const uint16_t*>(h->w.lm_head);
+    q.V = V; q.H = H; q.R = R;
+    q.keys = h->at<unsigned long long>(L.vh_keys);
+    q.counter = h->at<unsigned>(L.vh_cnt);
+    q.tok_out = tok;
+    q.draft = draft_tokens; q.B = B; q.K = K;
+    q.accepted = accepted_len; q.next = next_token;
+    return timed(h, KC_VERIFY, s, [&] { return launch_lm_rows(q, h->num_cu, s); }) == hipSuccess
+               ? MTP_OK
+               : MTP_ERR_HIP;
+  }
   auto run = [&]() -> hipError_t {
     hipError_t e = hipSuccess;
     for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.vh_rows) {
