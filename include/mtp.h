@@ -222,7 +222,9 @@ mtp_status mtp_kv_rollback_seqk(mtp_handle* h, mtp_kv* kv, const int32_t* accept
  *   target_norm   [hidden] config dtype, 16-byte aligned: the target's final-norm gain
  *   draft_tokens, accepted_len, next_token: as mtp_verify.
  * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192) created for 3 or
- * more sequences, else of up to 64 (each group streams the lm_head once).
+ * more sequences, else of up to 64 (each group streams the lm_head once); a bf16 head created
+ * for 1-2 sequences (no re-laid-out weight copy) with hidden <= 4096 and B (K+1) <= 16 does
+ * the whole call in one launch.
  * Errors: as mtp_verify.
  */
 mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,

@@ -42,6 +42,8 @@ constexpr size_t kLrLds = (size_t)kLrWaves * kLrTile * 2 + (size_t)kLrRing * kLr
 constexpr int kVm8 = 0x0F78;
 constexpr int kLgkm0 = 0xC07F;
 
+}  // namespace
+
 __global__ __launch_bounds__(kLrThreads, 1) void lm_rows_kernel(LmRowsParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* tiles = reinterpret_cast<uint16_t*>(smem);                            // [wave][tile]
@@ -236,8 +238,6 @@ __global__ __launch_bounds__(kLrThreads, 1) void lm_rows_kernel(LmRowsParams p) 
     }
   }
 }
-
-}  // namespace
 
 bool lm_rows_fits(int H, int R) { return R >= 1 && R <= 16 && H >= 8 && H % 8 == 0 && H <= kLrWaves * kLrCols; }
 
