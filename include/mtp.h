@@ -114,15 +114,50 @@ mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t 
 /* Create a handle. `workspace` is caller-owned device memory of at least
  * mtp_workspace_size() bytes, 256-byte aligned, used only by this handle; it is
  * zeroed here (synchronously), and for bf16 configurations with max_batch >= 3 it receives
- * the re-laid-out copy of the weights: the weights must hold their final values when the
- * handle is created, and later changes to them are not seen by batches of 3 or more
- * sequences (create a new handle instead). Supported shapes: head_dim 64 or 128,
+ * the re-laid-out copy of the weights: later changes to the weights are not seen by batches
+ * of 3 or more sequences until mtp_refresh_weights (or use mtp_create_ex with
+ * MTP_CREATE_NO_PACKED_COPY). Supported shapes: head_dim 64 or 128,
  * n_q_heads / n_kv_heads <= 8, hidden and ffn multiples of 8, max_k <= 100,
  * max_capacity <= 262144 (256 attention splits of up to 1024 slots).
  * On success *out receives the handle; on failure *out is NULL. */
 mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
                       int32_t max_k, int32_t max_capacity, void* workspace, size_t workspace_bytes,
                       mtp_handle** out);
+
+/*
+ * Flags of mtp_workspace_size_ex / mtp_create_ex (0 gives mtp_workspace_size / mtp_create).
+ *
+ * MTP_CREATE_NO_PACKED_COPY: keep no re-laid-out copy of the weights. The MTP head then
+ * reads the verifier's lm_head and embedding, and its own matrices, only where the caller
+ * keeps them (devnotes "How OpenVINO MTP Speculative Decoding Works Internally", "Shared
+ * embeddings reduce duplication"; speculators "MTP (Multi-Token Prediction)", How It Works >
+ * Training Process: embed_tokens and lm_head are shared with the verifier). The workspace
+ * shrinks by mtp_info.packed_weight_bytes of the default handle (1.7 GB for a
+ * Qwen3-8B-shaped head); batches of 3 or more sequences take the matrix-core kernels on the
+ * row-major weights instead, which are slower (the lm_head at 32 sequences by about 15%),
+ * and verification from hidden states runs 64 rows per lm_head pass instead of 128. Later
+ * changes to the weights are then seen by every call without mtp_refresh_weights.
+ * Unknown flag bits give MTP_ERR_INVALID_ARG.
+ */
+#define MTP_CREATE_NO_PACKED_COPY 1u
+
+mtp_status mtp_workspace_size_ex(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
+                                 int32_t max_capacity, uint32_t flags, size_t* bytes);
+mtp_status mtp_create_ex(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
+                         int32_t max_k, int32_t max_capacity, uint32_t flags, void* workspace,
+                         size_t workspace_bytes, mtp_handle** out);
+
+/*
+ * Rebuild the handle's re-laid-out weight copy from the weights given at creation, after
+ * the caller changed their values in place (devnotes "How OpenVINO MTP Speculative Decoding
+ * Works Internally", "Shared embeddings reduce duplication": the lm_head and embedding are
+ * the verifier's own tensors, so the verifier may update them). Enqueued on `stream` (null:
+ * the default stream); work on other streams that uses the handle must be ordered after it
+ * by the caller, and the weights must not change while it runs. A handle without the copy
+ * (mtp_info.packed_weight_bytes == 0) reads the weights directly: then this enqueues
+ * nothing and returns MTP_OK. Errors: MTP_ERR_INVALID_ARG (null handle), MTP_ERR_HIP.
+ */
+mtp_status mtp_refresh_weights(mtp_handle* h, void* stream);
 
 /*
  * K recursive draft steps for B sequences (speculators page, Architecture;

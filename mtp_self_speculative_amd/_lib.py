@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "mtp.h")
 MTP_OK = 0
 MTP_F32, MTP_BF16 = 0, 1
 DEVERR_TOKEN, DEVERR_CAPACITY, DEVERR_ACCEPT, DEVERR_COUNT = 1, 2, 4, 8
+CREATE_NO_PACKED_COPY = 1  # MTP_CREATE_NO_PACKED_COPY
 
 STATUS_NAMES = {0: "MTP_OK", 1: "MTP_ERR_INVALID_ARG", 2: "MTP_ERR_SHAPE", 3: "MTP_ERR_DTYPE",
                 4: "MTP_ERR_CAPACITY", 5: "MTP_ERR_UNSUPPORTED", 6: "MTP_ERR_HIP",
@@ -69,6 +70,11 @@ _SIGS = {
                                 ctypes.POINTER(ctypes.c_size_t)]),
     "mtp_create": (_I, [ctypes.POINTER(mtp_config), ctypes.POINTER(mtp_weights), _I, _I, _I, _P,
                         ctypes.c_size_t, ctypes.POINTER(_P)]),
+    "mtp_workspace_size_ex": (_I, [ctypes.POINTER(mtp_config), _I, _I, _I, ctypes.c_uint32,
+                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "mtp_create_ex": (_I, [ctypes.POINTER(mtp_config), ctypes.POINTER(mtp_weights), _I, _I, _I,
+                           ctypes.c_uint32, _P, ctypes.c_size_t, ctypes.POINTER(_P)]),
+    "mtp_refresh_weights": (_I, [_P, _P]),
     "mtp_draft": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, _P, _P]),
     "mtp_draft_debug": (_I, [_P, _P, _P, ctypes.POINTER(mtp_kv), _I, _I, _P, _P, _P, _P, _P]),
     "mtp_verify": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
@@ -163,6 +169,27 @@ def mtp_create(cfg: mtp_config, weights: mtp_weights, max_batch: int, max_k: int
                           max_capacity, workspace, workspace_bytes, ctypes.byref(h)),
            "mtp_create")
     return h.value
+
+
+def mtp_workspace_size_ex(cfg: mtp_config, max_batch: int, max_k: int, max_capacity: int,
+                          flags: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(LIB.mtp_workspace_size_ex(ctypes.byref(cfg), max_batch, max_k, max_capacity, flags,
+                                     ctypes.byref(n)), "mtp_workspace_size_ex")
+    return int(n.value)
+
+
+def mtp_create_ex(cfg: mtp_config, weights: mtp_weights, max_batch: int, max_k: int,
+                  max_capacity: int, flags: int, workspace: int, workspace_bytes: int) -> int:
+    h = ctypes.c_void_p(0)
+    _check(LIB.mtp_create_ex(ctypes.byref(cfg), ctypes.byref(weights), max_batch, max_k,
+                             max_capacity, flags, workspace, workspace_bytes, ctypes.byref(h)),
+           "mtp_create_ex")
+    return h.value
+
+
+def mtp_refresh_weights(handle: int, stream: int | None) -> None:
+    _check(LIB.mtp_refresh_weights(handle, stream), "mtp_refresh_weights")
 
 
 def mtp_draft(handle: int, hidden: int, last_tokens: int, kv: mtp_kv, B: int, K: int,

@@ -342,6 +342,17 @@ __device__ __forceinline__ unsigned long long take_key(unsigned long long* p) {
   return __hip_atomic_exchange(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The only two ways a workgroup publishes a value that the winner of last_to_arrive reads
+// back: a returning device-scope atomic whose result is kept live, so that the wait at the
+// top of last_to_arrive covers it. A plain or non-returning store in their place would
+// not be covered by that wait, and the winner could read a stale value.
+__device__ __forceinline__ void publish_max_key(unsigned long long* p, unsigned long long k) {
+  keep_alive(atomic_max_key(p, k));
+}
+__device__ __forceinline__ void publish_exchange(unsigned long long* p, unsigned long long v) {
+  keep_alive(__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Steps of sequence b in a call of K steps: its own length kseq[b] clamped to [0, K], or K
 // when the call has no per-sequence lengths.
 __device__ __forceinline__ int seq_steps(const int* kseq, int b, int K) {

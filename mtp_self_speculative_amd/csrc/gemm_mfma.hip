@@ -374,8 +374,9 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
       unsigned long long k = 0ull;
 #pragma unroll
       for (int w = 0; w < WV; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
-      if (k) keep_alive(atomic_max_key(p.keys + tid, k));
+      if (k) publish_max_key(p.keys + tid, k);
     }
+    // the winner reads back only keys published by publish_max_key
     if (last_to_arrive(p.counter, gridDim.x, &flag)) {
       for (int b = tid; b < p.B; b += NT) {
         const unsigned long long k = take_key(p.keys + b);

@@ -266,8 +266,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
       const int b = b0 + threadIdx.x;
       unsigned long long k = 0ull;
       for (int w = 0; w < kWavesPerBlock; ++w) k = kred[w][threadIdx.x] > k ? kred[w][threadIdx.x] : k;
-      if (b < p.B && k) keep_alive(atomic_max_key(p.keys + b, k));
+      if (b < p.B && k) publish_max_key(p.keys + b, k);
     }
+    // the winner reads back only keys published by publish_max_key
     if (last_to_arrive(p.counter, gridDim.x * gridDim.y, &flag)) {
       for (int b = threadIdx.x; b < p.B; b += kThreads) {
         const unsigned long long k = take_key(p.keys + b);

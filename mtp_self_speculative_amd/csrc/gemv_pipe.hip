@@ -317,8 +317,9 @@ __global__ __launch_bounds__(WPB * 64) void gemv_pipe_kernel(GemvParams p) {
     if (tid < NB && tid < B) {
       unsigned long long k = 0ull;
       for (int w = 0; w < WPB; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
-      if (k) keep_alive(atomic_max_key(p.keys + tid, k));
+      if (k) publish_max_key(p.keys + tid, k);
     }
+    // the winner reads back only keys published by publish_max_key
     if (last_to_arrive(p.counter, gridDim.x, &flag)) {
       for (int b = tid; b < B; b += NT) {
         const unsigned long long k = take_key(p.keys + b);

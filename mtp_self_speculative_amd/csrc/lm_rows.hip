@@ -221,9 +221,9 @@ __global__ __launch_bounds__(kLrThreads, 1) void lm_rows_kernel(LmRowsParams p) 
   if (tid < R) {
     unsigned long long k = 0ull;
     for (int w = 0; w < kLrWaves; ++w) k = kred[w][tid] > k ? kred[w][tid] : k;
-    // returning form, so that the completion counter's wait covers it
-    if (k) keep_alive(atomic_max_key(p.keys + tid, k));
+    if (k) publish_max_key(p.keys + tid, k);
   }
+  // the winner reads back only keys published by publish_max_key
   if (last_to_arrive(p.counter, gridDim.x, &flag)) {
     if (tid < R) p.tok_out[tid] = (int)key_index(take_key(p.keys + tid));
     __syncthreads();

@@ -22,6 +22,7 @@ constexpr int kMaxK = 100;
 static_assert(kMaxK <= kVsMaxK, "sampling verification holds 2K+1 log-sum-exps in LDS");
 constexpr int kMaxGroupHeads = 8;
 constexpr size_t kGemvLdsBudget = 32 * 1024;
+constexpr uint32_t kCreateFlags = MTP_CREATE_NO_PACKED_COPY;  // flags mtp_create_ex knows
 constexpr int kGemvMaxGrid = 2048;
 
 struct Layout {
@@ -80,8 +81,15 @@ int mm_split_max(int nrows, int ncols, int B) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
+// The re-laid-out weight copy exists for bf16 handles that can take the matrix-core path,
+// unless the caller asked for none.
+bool wants_packed(const mtp_config& c, int max_batch, uint32_t flags) {
+  return mm_eligible(c) && max_batch >= kMmMinBatch && !(flags & MTP_CREATE_NO_PACKED_COPY);
+}
+
+Layout make_layout(const mtp_config& c, int max_batch, int max_k, uint32_t flags) {
   Layout L{};
+  const bool packed = wants_packed(c, max_batch, flags);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -132,8 +140,8 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   // verification from the target's hidden states
   {
     const long rows_all = (long)max_batch * (max_k + 1);
-    // the packed lm_head copy exists under the same condition as below
-    const int grp = mm_eligible(c) && max_batch >= kMmMinBatch ? kVhGroupPk : kVhGroup;
+    // 128 rows per pass only on the packed lm_head copy
+    const int grp = packed ? kVhGroupPk : kVhGroup;
     L.vh_rows = (int)(rows_all < grp ? rows_all : grp);
     L.vh_ld = (c.hidden + 7) / 8 * 8;
     L.vh_x = take((size_t)L.vh_rows * c.hidden * 4);
@@ -174,7 +182,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k) {
   }
   // packed weights for the matrix-core draft path (made once by mtp_create)
   L.pk_eh = L.pk_qkv = L.pk_o = L.pk_gu = L.pk_down = L.pk_lm = 0;
-  if (mm_eligible(c) && max_batch >= kMmMinBatch) {
+  if (packed) {
     const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
     L.pk_eh = take(mm_packed_elems(H, 2 * H) * 2);
     L.pk_qkv = take(mm_packed_elems(qd + 2 * kvd, H) * 2);
@@ -214,6 +222,25 @@ mtp_status check_limits(int max_batch, int max_k, int max_capacity) {
 
 int nb_for(int B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8; }
 
+// Writes the packed copies of the batched path's matrices (contiguous matrix-core loads)
+// from the weights into the workspace, on stream s.
+hipError_t pack_weights(const Layout& L, const mtp_config& c, const mtp_weights& w, char* ws,
+                        hipStream_t s) {
+  if (!L.pk_lm) return hipSuccess;
+  auto pk = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  const int F = c.ffn;
+  hipError_t e = launch_pack(w.w_eh, w.w_eh, w.w_eh, H, H, H, 2 * H, pk(L.pk_eh), s);
+  if (e == hipSuccess)
+    e = launch_pack(w.w_q, w.w_k, w.w_v, qd, qd + kvd, qd + 2 * kvd, H, pk(L.pk_qkv), s);
+  if (e == hipSuccess) e = launch_pack(w.w_o, w.w_o, w.w_o, H, H, H, qd, pk(L.pk_o), s);
+  if (e == hipSuccess) e = launch_pack(w.w_gate, w.w_up, w.w_up, F, 2 * F, 2 * F, H, pk(L.pk_gu), s);
+  if (e == hipSuccess) e = launch_pack(w.w_down, w.w_down, w.w_down, H, H, H, F, pk(L.pk_down), s);
+  if (e == hipSuccess)
+    e = launch_pack(w.lm_head, w.lm_head, w.lm_head, c.vocab, c.vocab, c.vocab, H, pk(L.pk_lm), s);
+  return e;
+}
+
 int col_block_for(int ncols, int B, int dtype) {
   const int step = 64 * (dtype == MTP_F32 ? 4 : 8);
   const int nb = nb_for(B);
@@ -234,6 +261,7 @@ struct mtp_handle {
   mtp_config cfg;
   mtp_weights w;
   int max_batch, max_k, max_cap;
+  uint32_t flags;  // mtp_create_ex flags
   char* ws;
   size_t ws_bytes;
   Layout L;
@@ -330,22 +358,35 @@ mtp_status mtp_adapt_k(const int32_t* accepted_len, int32_t B, int32_t K, int32_
   return MTP_OK;
 }
 
-mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
-                              int32_t max_capacity, size_t* bytes) {
-  if (!bytes) return MTP_ERR_INVALID_ARG;
+mtp_status mtp_workspace_size_ex(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
+                                 int32_t max_capacity, uint32_t flags, size_t* bytes) {
+  if (!bytes || (flags & ~kCreateFlags)) return MTP_ERR_INVALID_ARG;
   mtp_status st = check_config(cfg);
   if (st != MTP_OK) return st;
   st = check_limits(max_batch, max_k, max_capacity);
   if (st != MTP_OK) return st;
-  *bytes = make_layout(*cfg, max_batch, max_k).total;
+  *bytes = make_layout(*cfg, max_batch, max_k, flags).total;
   return MTP_OK;
+}
+
+mtp_status mtp_workspace_size(const mtp_config* cfg, int32_t max_batch, int32_t max_k,
+                              int32_t max_capacity, size_t* bytes) {
+  return mtp_workspace_size_ex(cfg, max_batch, max_k, max_capacity, 0u, bytes);
 }
 
 mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
                       int32_t max_k, int32_t max_capacity, void* workspace, size_t workspace_bytes,
                       mtp_handle** out) {
+  return mtp_create_ex(cfg, w, max_batch, max_k, max_capacity, 0u, workspace, workspace_bytes,
+                       out);
+}
+
+mtp_status mtp_create_ex(const mtp_config* cfg, const mtp_weights* w, int32_t max_batch,
+                         int32_t max_k, int32_t max_capacity, uint32_t flags, void* workspace,
+                         size_t workspace_bytes, mtp_handle** out) {
   if (!out) return MTP_ERR_INVALID_ARG;
   *out = nullptr;
+  if (flags & ~kCreateFlags) return MTP_ERR_INVALID_ARG;
   mtp_status st = check_config(cfg);
   if (st != MTP_OK) return st;
   st = check_limits(max_batch, max_k, max_capacity);
@@ -356,27 +397,11 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
   for (const void* p : ptrs)
     if (!p || !aligned(p, 16)) return MTP_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MTP_ERR_INVALID_ARG;
-  const Layout L = make_layout(*cfg, max_batch, max_k);
+  const Layout L = make_layout(*cfg, max_batch, max_k, flags);
   if (workspace_bytes < L.total) return MTP_ERR_CAPACITY;
   if (hipMemset(workspace, 0, L.total) != hipSuccess) return MTP_ERR_HIP;
-  if (L.pk_lm) {
-    // Packed copies of the batched path's matrices (contiguous matrix-core loads).
-    char* ws = static_cast<char*>(workspace);
-    auto pk = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
-    const mtp_config& c = *cfg;
-    const int H = c.hidden, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
-    const int F = c.ffn;
-    hipError_t e = launch_pack(w->w_eh, w->w_eh, w->w_eh, H, H, H, 2 * H, pk(L.pk_eh), 0);
-    if (e == hipSuccess)
-      e = launch_pack(w->w_q, w->w_k, w->w_v, qd, qd + kvd, qd + 2 * kvd, H, pk(L.pk_qkv), 0);
-    if (e == hipSuccess) e = launch_pack(w->w_o, w->w_o, w->w_o, H, H, H, qd, pk(L.pk_o), 0);
-    if (e == hipSuccess)
-      e = launch_pack(w->w_gate, w->w_up, w->w_up, F, 2 * F, 2 * F, H, pk(L.pk_gu), 0);
-    if (e == hipSuccess) e = launch_pack(w->w_down, w->w_down, w->w_down, H, H, H, F, pk(L.pk_down), 0);
-    if (e == hipSuccess)
-      e = launch_pack(w->lm_head, w->lm_head, w->lm_head, c.vocab, c.vocab, c.vocab, H, pk(L.pk_lm), 0);
-    if (e != hipSuccess) return MTP_ERR_HIP;
-  }
+  if (pack_weights(L, *cfg, *w, static_cast<char*>(workspace), 0) != hipSuccess)
+    return MTP_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return MTP_ERR_HIP;
   mtp_handle* h = new (std::nothrow) mtp_handle();
   if (!h) return MTP_ERR_CAPACITY;
@@ -385,6 +410,7 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
   h->max_batch = max_batch;
   h->max_k = max_k;
   h->max_cap = max_capacity;
+  h->flags = flags;
   h->ws = static_cast<char*>(workspace);
   h->ws_bytes = workspace_bytes;
   h->L = L;
@@ -396,6 +422,13 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
   h->lm_rows_ok = cfg->dtype == MTP_BF16 && lm_rows_prepare() == hipSuccess;
   *out = h;
   return MTP_OK;
+}
+
+mtp_status mtp_refresh_weights(mtp_handle* h, void* stream) {
+  if (!h) return MTP_ERR_INVALID_ARG;
+  return pack_weights(h->L, h->cfg, h->w, h->ws, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MTP_OK
+             : MTP_ERR_HIP;
 }
 
 void mtp_destroy(mtp_handle* h) {

@@ -103,8 +103,9 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyParams p) {
   unsigned long long* kb = p.keys + (long)b * p.kstride;
   if (threadIdx.x == 0) {
     for (int w = 1; w < kVThreads / kWave; ++w) best = kred[w] > best ? kred[w] : best;
-    if (best) keep_alive(atomic_max_key(kb + j, best));
+    if (best) publish_max_key(kb + j, best);
   }
+  // the winner reads back only keys published by publish_max_key
   if (last_to_arrive(p.counters + (long)b * kSeqLineU32, gridDim.x * gridDim.y, &flag)) {
     // Take (and reset) the K+1 row keys and scan for the first mismatch.
     if (threadIdx.x == 0) {
@@ -216,8 +217,8 @@ __global__ __launch_bounds__(kVThreads) void vs_stats_kernel(VSampleParams p) {
   const float M = block_max(m, red);  // finite: every segment holds at least one entry
   const float S = block_sum(m > -INFINITY ? sum * hw_exp2(m - M) : 0.f, red);
   if (threadIdx.x == 0)
-    keep_alive(__hip_atomic_exchange(p.part + ((long)b * R + r) * p.nchunk + c, pack_pair(M, S),
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    publish_exchange(p.part + ((long)b * R + r) * p.nchunk + c, pack_pair(M, S));
+  // the winner reads back only pairs published by publish_exchange
   if (!last_to_arrive(p.counters + (long)b * kSeqLineU32, gridDim.x * gridDim.y, &flag)) return;
   // Merge each row's pairs: lane-local running (max, rescaled sum), then the wave.
   const int nseg = gridDim.x;
@@ -335,8 +336,9 @@ __global__ __launch_bounds__(kVThreads) void vs_resample_kernel(VSampleParams p)
   if (threadIdx.x < 2) {
     unsigned long long k = 0ull;
     for (int w = 0; w < kVThreads / kWave; ++w) k = kred[threadIdx.x][w] > k ? kred[threadIdx.x][w] : k;
-    if (k) keep_alive(atomic_max_key(kb + threadIdx.x, k));
+    if (k) publish_max_key(kb + threadIdx.x, k);
   }
+  // the winner reads back only keys published by publish_max_key
   if (last_to_arrive(p.counters + (long)b * kSeqLineU32, gridDim.x, &flag)) {
     if (threadIdx.x == 0) {
       const unsigned long long rk = take_key(kb);

@@ -70,7 +70,9 @@ class MtpHead:
     def __init__(self, *, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn: int,
                  vocab: int, weights: dict, max_batch: int, max_k: int, max_capacity: int,
                  rope_theta: float = 1.0e6, rms_eps: float = 1.0e-6,
-                 dtype: torch.dtype = torch.bfloat16):
+                 dtype: torch.dtype = torch.bfloat16, packed_copy: bool = True):
+        """packed_copy=False: keep no re-laid-out copy of the weights in the workspace
+        (MTP_CREATE_NO_PACKED_COPY); batches of 3+ sequences then read the weights in place."""
         self.dtype = dtype
         self.cfg = L.make_config(hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, rope_theta,
                                  rms_eps, _DT[dtype])
@@ -88,13 +90,14 @@ class MtpHead:
             self.weights[name] = weights[name]
         self.w = L.mtp_weights(*[self.weights[n].data_ptr() for n in L.WEIGHT_FIELDS])
         self.max_batch, self.max_k, self.max_capacity = max_batch, max_k, max_capacity
-        nbytes = L.mtp_workspace_size(self.cfg, max_batch, max_k, max_capacity)
+        self.flags = 0 if packed_copy else L.CREATE_NO_PACKED_COPY
+        nbytes = L.mtp_workspace_size_ex(self.cfg, max_batch, max_k, max_capacity, self.flags)
         self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8,
                                      device=self.weights["lm_head"].device)
         base = self.workspace.data_ptr()
         off = (-base) % 256
-        self.handle = L.mtp_create(self.cfg, self.w, max_batch, max_k, max_capacity, base + off,
-                                   nbytes)
+        self.handle = L.mtp_create_ex(self.cfg, self.w, max_batch, max_k, max_capacity,
+                                      self.flags, base + off, nbytes)
 
     def close(self) -> None:
         if getattr(self, "handle", None):
@@ -371,6 +374,11 @@ class MtpHead:
 
     def get_error(self, stream=None) -> int:
         return L.mtp_get_error(self.handle, _stream(stream))
+
+    def refresh_weights(self, stream=None) -> None:
+        """Rebuild the re-laid-out weight copy after the weight tensors changed in place
+        (nothing to do for a handle created with packed_copy=False)."""
+        L.mtp_refresh_weights(self.handle, _stream(stream))
 
     def info(self) -> dict:
         """Workspace and packed-copy bytes and the row grouping of this handle."""

@@ -288,3 +288,41 @@ def test_seqk_entry_points_reject_null_arguments():
     assert L.LIB.mtp_draft_seqk(None, p, p, ctypes.byref(kv), p, 1, 1, p, None) == 1
     assert L.LIB.mtp_verify_seqk(None, p, p, p, 1, 1, p, p, None) == 1
     assert L.LIB.mtp_kv_rollback_seqk(None, ctypes.byref(kv), p, p, 1, 1, None) == 1
+
+
+def _packed_bytes(c):
+    """Size of the re-laid-out copy: 128 x 256 blocks of every matrix of the batched path."""
+    def blocks(rows, cols):
+        return -(-rows // 128) * -(-cols // 256) * 128 * 256 * 2
+    H, qd, kvd = c.hidden, c.n_q_heads * c.head_dim, c.n_kv_heads * c.head_dim
+    return (blocks(H, 2 * H) + blocks(qd + 2 * kvd, H) + blocks(H, qd) + blocks(2 * c.ffn, H)
+            + blocks(H, c.ffn) + blocks(c.vocab, H))
+
+
+def test_workspace_without_packed_copy():
+    c = cfg()
+    assert L.mtp_workspace_size_ex(c, 8, 5, 4416, 0) == L.mtp_workspace_size(c, 8, 5, 4416)
+    full = L.mtp_workspace_size(c, 8, 5, 4416)
+    lean = L.mtp_workspace_size_ex(c, 8, 5, 4416, L.CREATE_NO_PACKED_COPY)
+    assert lean % 256 == 0
+    # the copy (1.7 GB here) goes; the 128-row verification group shrinks to 64 rows
+    assert full - lean >= _packed_bytes(c)
+    assert full - lean < _packed_bytes(c) + (64 << 20)
+    # handles that never hold the copy are unchanged by the flag
+    for c2, mb in ((cfg(), 2), (cfg(dtype=L.MTP_F32), 8)):
+        assert (L.mtp_workspace_size_ex(c2, mb, 5, 4416, L.CREATE_NO_PACKED_COPY)
+                == L.mtp_workspace_size(c2, mb, 5, 4416))
+
+
+def test_unknown_create_flags_rejected_before_any_device_call():
+    c = cfg()
+    n = ctypes.c_size_t(0)
+    assert L.LIB.mtp_workspace_size_ex(ctypes.byref(c), 8, 5, 4416, 2, ctypes.byref(n)) == 1
+    h = ctypes.c_void_p(0)
+    w = L.mtp_weights()
+    assert L.LIB.mtp_create_ex(ctypes.byref(c), ctypes.byref(w), 8, 5, 4416, 0x80000000, None, 0,
+                               ctypes.byref(h)) == 1
+    assert h.value is None
+    assert L.LIB.mtp_create_ex(ctypes.byref(c), ctypes.byref(w), 8, 5, 4416,
+                               L.CREATE_NO_PACKED_COPY, None, 0, ctypes.byref(h)) == 1
+    assert L.LIB.mtp_refresh_weights(None, None) == 1
