@@ -14,7 +14,8 @@ library's stream), and the oracle timed on the host's cores. The headline worklo
 is the Qwen3-8B-shaped head at batch 1; the same run also times the other workloads
 (B=32 ragged, the Qwen3-32B shape at 32K context, the wide B=64 head and the tiny
 fp32 head) under "workloads", each with its own throughput, HBM fraction, lm_head
-fraction and device memory.
+fraction and device memory; the batched ones also replay the same iterations on a
+handle without the re-laid-out weight copy ("without_packed_copy").
 """
 from __future__ import annotations
 
@@ -424,6 +425,39 @@ def run_workload(name: str, args, full: bool) -> dict:
                        "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                        "algorithmic_bytes_per_launch": int(ab["lm_head"])},
            "device_memory": memory}
+
+    if not full and info["packed_weight_bytes"]:
+        # The same recorded iterations on a handle without the re-laid-out weight copy
+        # (MTP_CREATE_NO_PACKED_COPY): the trade of workspace for speed, and a check that
+        # the row-major path reproduces the recorded tokens bit for bit.
+        lean = MtpHead(hidden=cfg.hidden, n_q_heads=cfg.n_q, n_kv_heads=cfg.n_kv,
+                       head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, weights=w,
+                       max_batch=B, max_k=K, max_capacity=cap, rope_theta=cfg.rope_theta,
+                       rms_eps=cfg.rms_eps, dtype=tdt, packed_copy=False)
+        cache.len.copy_(len0)
+        cache.pos.copy_(pos0)
+        last = last0
+        for it in range(iters):
+            if it == args.warmup:
+                torch.cuda.synchronize()
+                t0l = time.perf_counter()
+            lean.draft(hidden[it], last, cache, K, out=drafts[it])
+            lean.verify(logits[it], drafts[it], acc[it], nxt[it])
+            lean.rollback(cache, acc[it], K)
+            last = nxt[it]
+        torch.cuda.synchronize()
+        el_lean = time.perf_counter() - t0l
+        if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
+            raise RuntimeError("the handle without the packed copy diverged from the recording")
+        assert lean.get_error() == 0
+        res["without_packed_copy"] = {
+            "draft_steps_per_s": round(K * args.steps / el_lean, 3),
+            "hbm_roofline_frac": round(ab["iteration"] / (el_lean / args.steps) / 1e9
+                                       / HBM_PEAK_GBS, 4),
+            "workspace_bytes": lean.info()["workspace_bytes"],
+            "tokens_identical": True}
+        log(f"{name}: without the packed copy: {res['without_packed_copy']}")
+        lean.close()
 
     if full:
         # Per-call latency: HIP events (torch's current stream, which the library runs on)
