@@ -125,3 +125,38 @@ def test_refresh_weights_after_in_place_change():
     for h in (full, lean, fresh):
         assert h.get_error() == 0
         h.close()
+
+
+def test_full_size_batched_draft_identical_without_packed_copy():
+    """q8b-b32 shapes (H=4096, V=151936, 32 ragged sequences, K=3): the row-major
+    contractions give the default handle's tokens, hidden states and top-2 logits bit for
+    bit, and verification from hidden states (64-row passes instead of one 128-row pass)
+    gives the same accepted lengths and next tokens wherever the oracle's margin clears the
+    near-tie bar."""
+    cfg = S.get_config("q8b-b32")
+    inp = make_inputs(cfg)
+    w = {k: to_dev(v, cfg.dtype) for k, v in inp.weights.items()}
+    full, lean = head_for(cfg, inp, w), head_for(cfg, inp, w, packed_copy=False)
+    t1, h1, s1, c1 = draft(full, cfg, inp)
+    t2, h2, s2, c2 = draft(lean, cfg, inp)
+    assert np.array_equal(t1, t2)
+    assert np.array_equal(h1, h2) and np.array_equal(s1, s2)
+    assert torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v)
+    del c1, c2
+    K = cfg.K
+    th, gn = S.target_hidden(cfg, K), S.target_norm(cfg)
+    thd, gnd = to_dev(th, cfg.dtype), to_dev(gn, cfg.dtype)
+    dd = torch.from_numpy(t1).cuda()
+    af, nf = full.verify_hidden(thd, gnd, dd)
+    al, nl = lean.verify_hidden(thd, gnd, dd)
+    assert full.get_error() == 0 and lean.get_error() == 0
+    af, nf, al, nl = (x.cpu().numpy() for x in (af, nf, al, nl))
+    a_o, n_o, margin = O.verify_from_hidden(cfg, th, gn, inp.weights["lm_head"], t1)
+    checked = 0
+    for b in range(cfg.batch):
+        if np.all(margin[b, :a_o[b] + 1] > MARGIN):
+            assert (af[b], nf[b]) == (a_o[b], n_o[b]) == (al[b], nl[b]), b
+            checked += 1
+    assert checked >= cfg.batch // 2
+    full.close()
+    lean.close()
