@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "lm_head_argmax_q8b_counters.md")
 LMHEAD_SOURCES = ("mtp_self_speculative_amd/csrc/gemv_pipe.hip",
                   "mtp_self_speculative_amd/csrc/common.h",
@@ -561,9 +562,16 @@ def run_workload(name: str, args, full: bool) -> dict:
         pf_us = float(np.median(pf_ms)) * 1e3
         H, kvd = cfg.hidden, cfg.n_kv * cfg.head_dim
         pf_bytes = (2 * H * H + 2 * kvd * H) * esz + B * n * (H * esz + 4 + H * esz + 2 * kvd * esz)
+        # every prompt row goes through eh_proj (2H -> H) and the K / V projections (H -> 2 kvd):
+        # with thousands of rows the call is bound by these multiply-adds, not by HBM
+        pf_flops = 2.0 * B * n * (2 * H * H + 2 * kvd * H)
+        pf_tflops = pf_flops / (pf_us * 1e-6) / 1e12
         res["prefill"] = {"prompt_tokens": n, "sequences": B, "us_per_call": round(pf_us, 1),
                           "prompt_tok_per_s": round(B * n / (pf_us * 1e-6), 1),
                           "rows_per_pass": info["catchup_group_rows"],
+                          "algorithmic_flops": int(pf_flops),
+                          "tflop_per_s": round(pf_tflops, 2),
+                          "mfma_frac": round(pf_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                           "algorithmic_bytes": int(pf_bytes),
                           "hbm_frac": round(pf_bytes / (pf_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"{name}: prefill of {n} prompt tokens: {pf_us:.1f} us")
