@@ -256,10 +256,10 @@ mtp_status mtp_kv_rollback_seqk(mtp_handle* h, mtp_kv* kv, const int32_t* accept
  *                 outputs before its final norm at inputs [last_token, d_1 .. d_K]
  *   target_norm   [hidden] config dtype, 16-byte aligned: the target's final-norm gain
  *   draft_tokens, accepted_len, next_token: as mtp_verify.
- * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192) created for 3 or
- * more sequences, else of up to 64 (each group streams the lm_head once); a bf16 head created
- * for 1-2 sequences (no re-laid-out weight copy) with hidden <= 4096 and B (K+1) <= 16 does
- * the whole call in one launch.
+ * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192) that hold the
+ * re-laid-out weight copy (created for 3 or more sequences without MTP_CREATE_NO_PACKED_COPY),
+ * else of up to 64 (each group streams the lm_head once); a bf16 head without the copy, with
+ * hidden <= 4096 and B (K+1) <= 16, does the whole call in one launch.
  * Errors: as mtp_verify.
  */
 mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,
@@ -306,7 +306,9 @@ mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
  *   tokens        [B, n] device int32: the token after each of those positions
  *   n_valid       [B] device int32 rows to take per sequence (0..n), or NULL for n
  * 0 <= n <= kv->capacity (n = 0 enqueues nothing), 1 <= B <= min(max_batch, kv->batch).
- * Rows run in groups of up to 64 (each group streams eh_proj and the K/V projections once).
+ * Rows run in groups, each streaming eh_proj and the K/V projections once: on bf16 heads (hidden
+ * <= 8192) up to 1024 rows (at most max_batch x max_capacity), groups of more than 64 rows
+ * on a tiled matrix-core contraction; else up to 64.
  * Device conditions: a slot outside the capacity sets MTP_DEVERR_CAPACITY (the row is
  * skipped); a token outside [0, vocab) sets MTP_DEVERR_TOKEN (row 0 of the embedding is
  * used); an n_valid entry outside [0, n] sets MTP_DEVERR_COUNT and is clamped.
@@ -389,7 +391,7 @@ typedef struct {
   size_t workspace_bytes;       /* device workspace the handle uses (mtp_workspace_size)      */
   size_t packed_weight_bytes;   /* of which: the re-laid-out weight copy (0 when none)        */
   int32_t verify_hidden_group_rows; /* rows per lm_head pass of mtp_verify_hidden             */
-  int32_t catchup_group_rows;   /* candidate rows per pass of mtp_kv_catchup                  */
+  int32_t catchup_group_rows;   /* rows per pass of mtp_kv_catchup and mtp_kv_prefill          */
   int32_t matrix_core_min_batch; /* draft batches in [min, max] run the matrix-core path;     */
   int32_t matrix_core_max_batch; /* both 0 when the configuration has no such path (fp32)    */
 } mtp_info;

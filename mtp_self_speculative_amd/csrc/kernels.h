@@ -178,6 +178,31 @@ bool lm_rows_fits(int H, int R);
 hipError_t lm_rows_prepare();
 hipError_t launch_lm_rows(const LmRowsParams& p, int grid, hipStream_t s);
 
+// ---- many input rows (prompt prefill): tiled MFMA contraction (gemm_rows.hip)
+
+// part[s][b][r] = sum over the columns of K split s of W[r, c] * (x[b, c] + x_lo[b, c]), for
+// W rows r < nrows (bf16, row-major, leading dimension ncols; rows [0, seg1) from w0, the
+// rest from w1) and input rows b < B (bf16 hi / lo planes, leading dimension ldx). Same
+// splits, layout and bits as the weight-streaming contraction's EPI_STORE.
+struct GmParams {
+  const void* w0;
+  const void* w1;
+  int seg1;
+  int nrows, ncols;
+  const uint16_t* x;
+  const uint16_t* x_lo;
+  int ldx, B;
+  int nsplit;
+  float* part;  // [nsplit][bp][nrows]
+  int bp;       // >= B
+};
+// Splits that give at least one workgroup per CU (a divisor of the 256-column chunk count),
+// with split x B <= max_part_rows (the room of the partial sums) unless that leaves 1.
+int gm_split(int nrows, int ncols, int B, int num_cu, int max_part_rows);
+// Once per process and device before the first launch (raises the kernel's LDS limit).
+hipError_t gm_prepare();
+hipError_t launch_gm(const GmParams& p, hipStream_t s);
+
 // ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions
 
 // y[b, r] = sum_c W[r, c] * x[b, c] for r < nrows, with W bf16 rows (segments as in

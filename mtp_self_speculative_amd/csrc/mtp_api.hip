@@ -54,6 +54,11 @@ constexpr int kMmMinBatch = 3;
 constexpr int kVhGroup = 64;      // rows per pass of the general lm_head / contraction
 constexpr int kVhGroupPk = 128;   // rows per greedy lm_head pass on the packed copy
 constexpr int kMmMaxBatch = 64;
+// Input-side row groups (catch-up, prompt prefill) of more than kMmMaxBatch rows go to the
+// tiled contraction, up to kGmGroup rows per group; its K splits keep split x rows within
+// kGmPartRows, which sizes the partial sums.
+constexpr int kGmGroup = 1024;
+constexpr int kGmPartRows = 2048;
 bool mm_eligible(const mtp_config& c) {
   return c.dtype == MTP_BF16 && c.hidden <= red_max_cols();
 }
@@ -87,7 +92,7 @@ bool wants_packed(const mtp_config& c, int max_batch, uint32_t flags) {
   return mm_eligible(c) && max_batch >= kMmMinBatch && !(flags & MTP_CREATE_NO_PACKED_COPY);
 }
 
-Layout make_layout(const mtp_config& c, int max_batch, int max_k, uint32_t flags) {
+Layout make_layout(const mtp_config& c, int max_batch, int max_k, int max_cap, uint32_t flags) {
   Layout L{};
   const bool packed = wants_packed(c, max_batch, flags);
   size_t off = 0;
@@ -156,9 +161,14 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k, uint32_t flags
   }
   // exact cache catch-up
   {
-    // up to kVhGroup rows per pass: catch-up has max_batch * max_k candidate rows, prefill
-    // up to max_batch * capacity
+    // Catch-up has max_batch * max_k candidate rows, prefill up to max_batch * capacity.
+    // Rows per pass: kVhGroup, or on matrix-core handles up to kGmGroup (the tiled
+    // contraction above 64 rows), never more than a call can bring.
     L.cu_rows = kVhGroup;
+    if (mm_eligible(c)) {
+      const long most = (long)max_batch * (max_cap > max_k ? max_cap : max_k);
+      L.cu_rows = most < kVhGroup ? kVhGroup : most > kGmGroup ? kGmGroup : (int)most;
+    }
     L.cu_ld = (2 * c.hidden + 7) / 8 * 8;
     const int kvd2 = 2 * c.n_kv_heads * c.head_dim;
     const int rr = L.cu_rows > 0 ? L.cu_rows : 1;
@@ -170,12 +180,17 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k, uint32_t flags
       L.cu_q = take((size_t)mm_batch_pad(L.cu_rows) * L.cu_ld * 2);
       L.cu_q_lo = take((size_t)mm_batch_pad(L.cu_rows) * L.cu_ld * 2);
       size_t part = 0;
-      for (int b = kMmMinBatch; b <= L.cu_rows; ++b) {
+      for (int b = kMmMinBatch; b <= L.cu_rows && b <= kMmMaxBatch; ++b) {
         const size_t e1 =
             (size_t)mm_split_max(c.hidden, 2 * c.hidden, b) * mm_batch_pad(b) * c.hidden;
         const size_t e2 = (size_t)mm_split_max(kvd2, c.hidden, b) * mm_batch_pad(b) * kvd2;
         part = e1 > part ? e1 : part;
         part = e2 > part ? e2 : part;
+      }
+      if (L.cu_rows > kMmMaxBatch) {  // tiled groups: splits x rows <= kGmPartRows
+        const size_t wide = (size_t)(c.hidden > kvd2 ? c.hidden : kvd2);
+        const size_t pr = (size_t)(L.cu_rows > kGmPartRows ? L.cu_rows : kGmPartRows);
+        part = pr * wide > part ? pr * wide : part;
       }
       L.cu_part = take(part * 4);
     }
@@ -267,6 +282,7 @@ struct mtp_handle {
   Layout L;
   int num_cu = 256;
   bool lm_rows_ok = false;  // the single-launch small-row verification kernel is usable
+  bool gm_ok = false;       // the tiled contraction is usable (its LDS limit was raised)
   uint32_t prof_mask = 0;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
@@ -365,7 +381,7 @@ mtp_status mtp_workspace_size_ex(const mtp_config* cfg, int32_t max_batch, int32
   if (st != MTP_OK) return st;
   st = check_limits(max_batch, max_k, max_capacity);
   if (st != MTP_OK) return st;
-  *bytes = make_layout(*cfg, max_batch, max_k, flags).total;
+  *bytes = make_layout(*cfg, max_batch, max_k, max_capacity, flags).total;
   return MTP_OK;
 }
 
@@ -397,7 +413,7 @@ mtp_status mtp_create_ex(const mtp_config* cfg, const mtp_weights* w, int32_t ma
   for (const void* p : ptrs)
     if (!p || !aligned(p, 16)) return MTP_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MTP_ERR_INVALID_ARG;
-  const Layout L = make_layout(*cfg, max_batch, max_k, flags);
+  const Layout L = make_layout(*cfg, max_batch, max_k, max_capacity, flags);
   if (workspace_bytes < L.total) return MTP_ERR_CAPACITY;
   if (hipMemset(workspace, 0, L.total) != hipSuccess) return MTP_ERR_HIP;
   if (pack_weights(L, *cfg, *w, static_cast<char*>(workspace), 0) != hipSuccess)
@@ -420,6 +436,7 @@ mtp_status mtp_create_ex(const mtp_config* cfg, const mtp_weights* w, int32_t ma
       ncu > 0)
     h->num_cu = ncu;
   h->lm_rows_ok = cfg->dtype == MTP_BF16 && lm_rows_prepare() == hipSuccess;
+  h->gm_ok = mm_eligible(*cfg) && gm_prepare() == hipSuccess;
   *out = h;
   return MTP_OK;
 }
@@ -1003,7 +1020,8 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
 // The layer's input side over R candidate rows (exact catch-up and prompt prefill): row r
 // of sequence b = r / per, index j = r % per, reads hidden row (b * src_per + j) of `src`
 // and token tokens[r]; eh_proj, attention norm and K/V projections run in groups of
-// L.cu_rows rows (matrix cores from 3 rows on for bf16, else the GEMV); rows with
+// L.cu_rows rows (matrix cores from 3 rows on for bf16: the weight-streaming contraction up
+// to 64 rows, the tiled one above; else the GEMV); rows with
 // j < limit[b] are rotated and written (catchup_write_kernel), then len / pos advance by
 // limit[b] + add.
 static hipError_t input_side_pass(mtp_handle* h, mtp_kv* kv, const void* src, int per,
@@ -1019,15 +1037,18 @@ static hipError_t input_side_pass(mtp_handle* h, mtp_kv* kv, const void* src, in
   float* xrows = h->at<float>(L.cu_x);
   float* kvrows = h->at<float>(L.cu_kv);
   hipError_t e = hipSuccess;
-  for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.cu_rows) {
-    const int rows = R - r0 < L.cu_rows ? R - r0 : L.cu_rows;
+  // without the tiled contraction, groups stay within the weight-streaming one's 64 rows
+  const int group = h->gm_ok || L.cu_rows <= kMmMaxBatch ? L.cu_rows : kMmMaxBatch;
+  for (int r0 = 0; r0 < R && e == hipSuccess; r0 += group) {
+    const int rows = R - r0 < group ? R - r0 : group;
     e = launch_gather_rows(c.dtype, src, hrows, r0, rows, per, src_per, H, s);
     if (e != hipSuccess) break;
     if (mm_eligible(c) && rows >= kMmMinBatch) {
       uint16_t* q = h->at<uint16_t>(L.cu_q);
       uint16_t* qlo = h->at<uint16_t>(L.cu_q_lo);
       float* part = h->at<float>(L.cu_part);
-      const int bp = mm_batch_pad(rows);
+      const bool tiled = rows > kMmMaxBatch;  // (group > 64 implies gm_ok)
+      const int bp = tiled ? rows : mm_batch_pad(rows);
       RedParams r{};
       r.n = H; r.gain = static_cast<const uint16_t*>(w.g_h);
       r.gain2 = static_cast<const uint16_t*>(w.g_e); r.eps = c.rms_eps;
@@ -1038,6 +1059,15 @@ static hipError_t input_side_pass(mtp_handle* h, mtp_kv* kv, const void* src, in
       // packed: the matrix's rows in the handle's packed copy (or null: read w0/w1)
       auto mm = [&](const void* w0, const void* w1, int seg1, int N, int Kd,
                     const uint16_t* packed, int* ns) {
+        if (tiled) {
+          GmParams g{};
+          g.w0 = w0; g.w1 = w1; g.seg1 = seg1; g.nrows = N; g.ncols = Kd;
+          g.x = q; g.x_lo = qlo; g.ldx = L.cu_ld; g.B = rows;
+          g.nsplit = gm_split(N, Kd, rows, h->num_cu, kGmPartRows);
+          g.part = part; g.bp = rows;
+          *ns = g.nsplit;
+          return launch_gm(g, s);
+        }
         MmParams m{};
         m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
         m.nrows = N; m.ncols = Kd; m.x = q; m.x_lo = qlo; m.ldx = L.cu_ld; m.B = rows;

@@ -20,8 +20,8 @@ CASES = {
                  ctx_lo=1, ctx_hi=100),
     # bf16, 1 x 2 rows: pipelined GEMV route
     "bf16-pipe": small(name="cu3", cid=162, batch=1, K=2, ctx_lo=30, ctx_hi=None),
-    # bf16, 20 x 4 = 80 rows: two groups
-    "bf16-groups": small(name="cu4", cid=163, batch=20, K=4, hidden=512, n_q=8, n_kv=2,
+    # bf16, 20 x 4 = 80 rows: one group on the tiled contraction (more than 64 rows)
+    "bf16-tiled-80": small(name="cu4", cid=163, batch=20, K=4, hidden=512, n_q=8, n_kv=2,
                          ctx_lo=0, ctx_hi=120),
     # bf16, 4 x 3 rows on the matrix cores with n_q * d = 320, not a whole 128-row tile:
     # eh_proj from the packed copy, the K/V rows from the row-major weights
@@ -31,9 +31,15 @@ CASES = {
     # blocks, and the K/V rows start at the packed copy's third (odd) 128-row block
     "bf16-mm-odd-kv-block": small(name="cu6", cid=165, batch=12, K=4, hidden=384, n_q=3, n_kv=1,
                                 head_dim=128, ffn=768, vocab=3001, ctx_lo=2, ctx_hi=150),
-    # bf16, 33 x 4 = 132 rows: three groups (64, 64, then 4), all on the matrix cores
-    "bf16-three-groups": small(name="cu7", cid=166, batch=33, K=4, hidden=256, n_q=4, n_kv=2,
-                             head_dim=64, ffn=512, vocab=3001, ctx_lo=2, ctx_hi=100),
+    # bf16, 33 x 4 = 132 rows: one group on the tiled contraction, two 128-row input tiles
+    # (the second ragged)
+    "bf16-tiled-132": small(name="cu7", cid=166, batch=33, K=4, hidden=256, n_q=4, n_kv=2,
+                            head_dim=64, ffn=512, vocab=3001, ctx_lo=2, ctx_hi=100),
+    # bf16, 260 x 4 = 1040 rows: a 1024-row group on the tiled contraction, then 16 rows on
+    # the weight-streaming one (the draft before it, 260 sequences, takes the GEMV)
+    "bf16-tiled-then-streaming": small(name="cu8", cid=167, batch=260, K=4, hidden=256, n_q=4,
+                                       n_kv=2, head_dim=64, ffn=512, vocab=3001, ctx_lo=2,
+                                       ctx_hi=40),
     # the Qwen3-8B-shaped head at full size, B=1 K=5 and B=32 K=3
     "q8b": S.get_config("q8b"),
     "q8b-b32": S.get_config("q8b-b32"),

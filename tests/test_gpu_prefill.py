@@ -19,15 +19,22 @@ CASES = {
                   ctx_lo=1, ctx_hi=40), 9, [9, 4, 0]),
     # bf16, 1 x 2 rows: pipelined GEMV route
     "bf16-pipe": (small(name="pf2", cid=201, batch=1, K=1, ctx_lo=30, ctx_hi=None), 2, None),
-    # bf16, 3 x 30 = 90 rows on the matrix cores in two groups (64 + 26), ragged counts
+    # bf16, 3 x 30 = 90 rows in one group on the tiled contraction (more than 64 rows),
+    # ragged counts
     "bf16-mm": (small(name="pf3", cid=202, batch=3, K=2, ctx_lo=0, ctx_hi=60), 30, [30, 17, 0]),
-    # bf16, 5 x 13 = 65 rows: a 64-row group, then one row on the GEMV
+    # bf16, 5 x 13 = 65 rows: one group on the tiled contraction, its 128-row input tile
+    # ragged
     "bf16-mm-tail": (small(name="pf4", cid=203, batch=5, K=2, hidden=256, n_q=4, n_kv=2,
                            head_dim=64, ffn=512, vocab=2053, ctx_lo=3, ctx_hi=90), 13, None),
     # bf16, n_q * d = 320 (the K/V rows are not a whole 128-row block of the packed copy)
     "bf16-mm-kv-rowmajor": (small(name="pf5", cid=204, batch=4, K=3, hidden=320, n_q=5, n_kv=1,
                                   head_dim=64, ffn=640, vocab=2053, ctx_lo=0, ctx_hi=50), 11,
                             None),
+    # bf16, 2 x 530 = 1060 rows: a 1024-row group on the tiled contraction, then 36 rows on
+    # the weight-streaming one
+    "bf16-tiled-then-streaming": (small(name="pf6", cid=206, batch=2, K=1, hidden=256, n_q=4,
+                                        n_kv=2, head_dim=64, ffn=512, vocab=2053, ctx_lo=0,
+                                        ctx_hi=20), 530, [530, 530]),
 }
 
 
@@ -77,14 +84,15 @@ def test_prefill_parity(case):
 
 def test_prefill_q8b_4096_token_prompt():
     """The Qwen3-8B-shaped head at full size: a 4096-token prompt into an empty cache
-    (64 groups of 64 rows on the matrix cores), every slot against the oracle."""
+    (four groups of 1024 rows on the tiled contraction), every slot against the oracle."""
     cfg = S.get_config("q8b").with_(ctx_lo=0, ctx_hi=None)
     n = 4096
     _check(cfg, *_run(cfg, n, None, n + 64))
 
 
 def test_prefill_q8b_b32_ragged_prompts():
-    """The batched workload's shape: 32 prompts of ragged lengths (1..300 rows) in one call."""
+    """The batched workload's shape: 32 prompts of ragged lengths (1..300 rows) in one call
+    (9600 candidate rows: nine 1024-row groups and one of 384 on the tiled contraction)."""
     cfg = S.get_config("q8b-b32").with_(ctx_lo=0, ctx_hi=None)
     n = 300
     nv = [int(x) for x in np.random.default_rng(5).integers(1, n + 1, size=cfg.batch)]
