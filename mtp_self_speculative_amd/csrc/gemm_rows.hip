@@ -5,11 +5,13 @@
 // once per group of up to 64 input rows, which suits decode; with thousands of rows that
 // re-reads W dozens of times and pays its launches per group. Here a workgroup computes a
 // 256 (W rows) x 128 (input rows) tile: each 64-column stage of W and of both input planes
-// (hi, lo) goes from HBM through registers into LDS once, and the four waves (2 x 2) each
-// take 128 x 64 of the tile from LDS as 8 x 4 v_mfma_f32_16x16x32_bf16 blocks, the A
-// operand (16 W rows x 32 columns) shared by four input tiles and the B operands (16 input
-// rows x 32 columns, hi and lo) by eight W slices. Stages are double-buffered in LDS: the
-// next stage's global loads are in flight while the current one is multiplied.
+// (hi, lo) goes from HBM through registers into LDS once, and the eight waves (4 x 2, two per
+// SIMD, so that one wave's products overlap the other's LDS reads) each take 64 x 64 of the
+// tile from LDS as 4 x 4 v_mfma_f32_16x16x32_bf16 blocks, the A operand (16 W rows x 32
+// columns) shared by four input tiles and the B operands (16 input rows x 32 columns, hi and
+// lo) by four W slices. Stages are double-buffered in LDS: the next stage's global loads are
+// in flight while the current one is multiplied. (Four waves of 128 x 64, one per SIMD, were
+// 26-35% slower on the same shapes.)
 //
 // Results are the same K-split partial sums, in the same layout, as the weight-streaming
 // contraction's EPI_STORE (part[split][bp][N]; a row kernel adds the splits): split s covers
@@ -28,7 +30,7 @@ constexpr int kGmTM = 256;            // W rows per tile
 constexpr int kGmTN = 128;            // input rows per tile
 constexpr int kGmBK = 64;             // columns per stage
 constexpr int kGmLd = kGmBK + 8;      // LDS row stride (bf16): 144 B, conflict-free reads
-constexpr int kGmThreads = 256;       // four waves
+constexpr int kGmThreads = 512;       // eight waves
 constexpr int kGmChunk = 256;         // columns per K-split unit (as the streaming kernel)
 constexpr int kGmMaxSplit = 16;
 
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
   uint16_t* As = smem;             // [2][kGmTM][kGmLd]
   uint16_t* Bs = smem + kGmLdsA;   // [2][2 planes][kGmTN][kGmLd]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int N = p.nrows, Kd = p.ncols;
   const int tiles_m = (N + kGmTM - 1) / kGmTM;
   const int tiles_n = (p.B + kGmTN - 1) / kGmTN;
@@ -56,27 +58,27 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
   const int S = (k1 - k0) / kGmBK;                       // stages (kGmChunk % kGmBK == 0)
   const int m0 = tm * kGmTM, n0 = tn * kGmTN;
 
-  // Global -> register staging: 8 16-byte chunks of W and 8 of the input per thread and
-  // stage. Thread t takes column chunk t % 8 of rows t / 8 + 32 i. Rows past the end read
+  // Global -> register staging: 4 16-byte chunks of W and 4 of the input per thread and
+  // stage. Thread t takes column chunk t % 8 of rows t / 8 + 64 i. Rows past the end read
   // the last row (never stored); columns past Kd read the row's last 8 values, and the
   // input chunk is zeroed in LDS there, so they add nothing.
   const int cc = (tid & 7) * 8;
-  u32x4 ra[8], rb[8];
-  const uint16_t* arow[8];
-  const uint16_t* brow[8];
+  u32x4 ra[4], rb[4];
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = min(m0 + (tid >> 3) + 32 * i, N - 1);
+  for (int i = 0; i < 4; ++i) {
+    const int r = min(m0 + (tid >> 3) + 64 * i, N - 1);
     arow[i] = r < p.seg1 ? static_cast<const uint16_t*>(p.w0) + (long)r * Kd
                          : static_cast<const uint16_t*>(p.w1) + (long)(r - p.seg1) * Kd;
-    const int b = min(n0 + (tid >> 3) + 32 * (i & 3), p.B - 1);
-    brow[i] = (i < 4 ? p.x : p.x_lo) + (long)b * p.ldx;
+    const int b = min(n0 + (tid >> 3) + 64 * (i & 1), p.B - 1);
+    brow[i] = (i < 2 ? p.x : p.x_lo) + (long)b * p.ldx;
   }
   auto gload = [&](int st) {
     const int c = k0 + st * kGmBK + cc;
     const int cl = c < Kd ? c : Kd - 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + cl);
       rb[i] = *reinterpret_cast<const u32x4*>(brow[i] + cl);
     }
@@ -85,31 +87,31 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
     const bool live = k0 + st * kGmBK + cc < Kd;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(As + ((size_t)buf * kGmTM + (tid >> 3) + 32 * i) * kGmLd + cc) = ra[i];
-      const int pl = i >> 2;
-      *reinterpret_cast<u32x4*>(Bs + (((size_t)buf * 2 + pl) * kGmTN + (tid >> 3) + 32 * (i & 3)) * kGmLd + cc) =
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(As + ((size_t)buf * kGmTM + (tid >> 3) + 64 * i) * kGmLd + cc) = ra[i];
+      const int pl = i >> 1;
+      *reinterpret_cast<u32x4*>(Bs + (((size_t)buf * 2 + pl) * kGmTN + (tid >> 3) + 64 * (i & 1)) * kGmLd + cc) =
           live ? rb[i] : z;
     }
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Lane l reads row l % 16 of a 16-row slice, columns 8 (l / 16) .. + 7 of a 32-column step.
   const int fr = lane & 15, fc = (lane >> 4) * 8;
   auto compute = [&](int buf) {
-    const uint16_t* a = As + ((size_t)buf * kGmTM + wm * 128 + fr) * kGmLd + fc;
+    const uint16_t* a = As + ((size_t)buf * kGmTM + wm * 64 + fr) * kGmLd + fc;
     const uint16_t* bh = Bs + (((size_t)buf * 2 + 0) * kGmTN + wn * 64 + fr) * kGmLd + fc;
     const uint16_t* bl = Bs + (((size_t)buf * 2 + 1) * kGmTN + wn * 64 + fr) * kGmLd + fc;
 #pragma unroll
     for (int kk = 0; kk < kGmBK / 32; ++kk) {
-      bf16x8 fa[8], fh[4], fl[4];
+      bf16x8 fa[4], fh[4], fl[4];
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 4; ++m)
         fa[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a + m * 16 * kGmLd + kk * 32));
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
         fl[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bl + n * 16 * kGmLd + kk * 32));
       }
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fh[n], acc[m][n], 0, 0, 0);
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
 
   // Lane l holds W rows 4 (l / 16) + i (i < 4) of each slice for input row l % 16 of each tile.
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int r0 = m0 + wm * 128 + m * 16 + (lane >> 4) * 4;
+  for (int m = 0; m < 4; ++m) {
+    const int r0 = m0 + wm * 64 + m * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int b = n0 + wn * 64 + n * 16 + (lane & 15);
@@ -160,12 +162,12 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
 
 // K splits for a grid of at least one workgroup per CU: the smallest divisor s of the
 // chunk count with tiles * s >= num_cu, else the largest allowed; allowed are s <=
-// kGmMaxSplit with s * B <= max_part_rows (the partial sums' room), and always s = 1.
-int gm_split(int nrows, int ncols, int B, int num_cu, int max_part_rows) {
+// kGmMaxSplit with s * B * nrows <= max_part (the partial sums' room), and always s = 1.
+int gm_split(int nrows, int ncols, int B, int num_cu, long max_part) {
   const long tiles = (long)((nrows + kGmTM - 1) / kGmTM) * ((B + kGmTN - 1) / kGmTN);
   const int nch = (ncols + kGmChunk - 1) / kGmChunk;
   int best = 1;
-  for (int s = 2; s <= kGmMaxSplit && s <= nch && (long)s * B <= max_part_rows; ++s) {
+  for (int s = 2; s <= kGmMaxSplit && s <= nch && (long)s * B * nrows <= max_part; ++s) {
     if (tiles * best >= num_cu) break;
     if (nch % s == 0) best = s;
   }

@@ -197,8 +197,9 @@ struct GmParams {
   int bp;       // >= B
 };
 // Splits that give at least one workgroup per CU (a divisor of the 256-column chunk count),
-// with split x B <= max_part_rows (the room of the partial sums) unless that leaves 1.
-int gm_split(int nrows, int ncols, int B, int num_cu, int max_part_rows);
+// with split x B x nrows <= max_part (the room of the partial sums, in floats) unless that
+// leaves 1.
+int gm_split(int nrows, int ncols, int B, int num_cu, long max_part);
 // Once per process and device before the first launch (raises the kernel's LDS limit).
 hipError_t gm_prepare();
 hipError_t launch_gm(const GmParams& p, hipStream_t s);

@@ -39,6 +39,7 @@ struct Layout {
   int vh_rows, vh_ld;
   // exact cache catch-up: one group of up to kVhGroup candidate rows at a time
   size_t cu_h, cu_x, cu_kv, cu_q, cu_q_lo, cu_part;
+  size_t cu_part_elems;  // floats of room at cu_part
   int cu_rows, cu_ld;
   // sampling verification: (max, sum) pairs per (sequence, row, chunk), row a's lse, keys
   size_t vs_part, vs_lse, vs_keys;
@@ -55,8 +56,8 @@ constexpr int kVhGroup = 64;      // rows per pass of the general lm_head / cont
 constexpr int kVhGroupPk = 128;   // rows per greedy lm_head pass on the packed copy
 constexpr int kMmMaxBatch = 64;
 // Input-side row groups (catch-up, prompt prefill) of more than kMmMaxBatch rows go to the
-// tiled contraction, up to kGmGroup rows per group; its K splits keep split x rows within
-// kGmPartRows, which sizes the partial sums.
+// tiled contraction, up to kGmGroup rows per group; the partial sums get room for
+// kGmPartRows rows of the wider contraction, which bounds the tiled one's K splits.
 constexpr int kGmGroup = 1024;
 constexpr int kGmPartRows = 2048;
 bool mm_eligible(const mtp_config& c) {
@@ -193,6 +194,7 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k, int max_cap, u
         part = pr * wide > part ? pr * wide : part;
       }
       L.cu_part = take(part * 4);
+      L.cu_part_elems = part;
     }
   }
   // packed weights for the matrix-core draft path (made once by mtp_create)
@@ -1063,7 +1065,7 @@ static hipError_t input_side_pass(mtp_handle* h, mtp_kv* kv, const void* src, in
           GmParams g{};
           g.w0 = w0; g.w1 = w1; g.seg1 = seg1; g.nrows = N; g.ncols = Kd;
           g.x = q; g.x_lo = qlo; g.ldx = L.cu_ld; g.B = rows;
-          g.nsplit = gm_split(N, Kd, rows, h->num_cu, kGmPartRows);
+          g.nsplit = gm_split(N, Kd, rows, h->num_cu, (long)L.cu_part_elems);
           g.part = part; g.bp = rows;
           *ns = g.nsplit;
           return launch_gm(g, s);
