@@ -451,12 +451,28 @@ def run_workload(name: str, args, full: bool) -> dict:
         if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
             raise RuntimeError("the handle without the packed copy diverged from the recording")
         assert lean.get_error() == 0
+        # its verification from hidden states (row-major lm_head) on the same drafts
+        th_l, tn_l = up(S.target_hidden(cfg, K)), up(S.target_norm(cfg))
+        va = torch.empty(B, dtype=torch.int32, device=dev)
+        vn = torch.empty(B, dtype=torch.int32, device=dev)
+        for it in range(3):
+            lean.verify_hidden(th_l, tn_l, drafts[it], va, vn)
+        torch.cuda.synchronize()
+        t0l = time.perf_counter()
+        for it in range(args.steps):
+            lean.verify_hidden(th_l, tn_l, drafts[args.warmup + it], va, vn)
+        torch.cuda.synchronize()
+        vh_lean_us = (time.perf_counter() - t0l) / args.steps * 1e6
+        assert lean.get_error() == 0
         res["without_packed_copy"] = {
             "draft_steps_per_s": round(K * args.steps / el_lean, 3),
             "hbm_roofline_frac": round(ab["iteration"] / (el_lean / args.steps) / 1e9
                                        / HBM_PEAK_GBS, 4),
             "workspace_bytes": lean.info()["workspace_bytes"],
+            "verify_from_hidden_us_per_call": round(vh_lean_us, 2),
+            "verify_hidden_group_rows": lean.info()["verify_hidden_group_rows"],
             "tokens_identical": True}
+        del th_l, tn_l
         log(f"{name}: without the packed copy: {res['without_packed_copy']}")
         lean.close()
 

@@ -134,9 +134,8 @@ mtp_status mtp_create(const mtp_config* cfg, const mtp_weights* w, int32_t max_b
  * Training Process: embed_tokens and lm_head are shared with the verifier). The workspace
  * shrinks by mtp_info.packed_weight_bytes of the default handle (1.7 GB for a
  * Qwen3-8B-shaped head); batches of 3 or more sequences take the matrix-core kernels on the
- * row-major weights instead, which are slower (the lm_head at 32 sequences by about 15%),
- * and verification from hidden states runs 64 rows per lm_head pass instead of 128. Later
- * changes to the weights are then seen by every call without mtp_refresh_weights.
+ * row-major weights instead, which are slower (the lm_head at 32 sequences by about 15%).
+ * Later changes to the weights are then seen by every call without mtp_refresh_weights.
  * Unknown flag bits give MTP_ERR_INVALID_ARG.
  */
 #define MTP_CREATE_NO_PACKED_COPY 1u
@@ -256,10 +255,10 @@ mtp_status mtp_kv_rollback_seqk(mtp_handle* h, mtp_kv* kv, const int32_t* accept
  *                 outputs before its final norm at inputs [last_token, d_1 .. d_K]
  *   target_norm   [hidden] config dtype, 16-byte aligned: the target's final-norm gain
  *   draft_tokens, accepted_len, next_token: as mtp_verify.
- * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192) that hold the
- * re-laid-out weight copy (created for 3 or more sequences without MTP_CREATE_NO_PACKED_COPY),
- * else of up to 64 (each group streams the lm_head once); a bf16 head without the copy, with
- * hidden <= 4096 and B (K+1) <= 16, does the whole call in one launch.
+ * Rows are processed in groups of up to 128 for bf16 heads (hidden <= 8192), else of up to 64
+ * (each group streams the lm_head once; groups of more than 64 rows on a tiled matrix-core
+ * contraction of the row-major lm_head); a bf16 head without the re-laid-out weight copy,
+ * with hidden <= 4096 and B (K+1) <= 16, does the whole call in one launch.
  * Errors: as mtp_verify.
  */
 mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const void* target_norm,

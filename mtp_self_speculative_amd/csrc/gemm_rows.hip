@@ -13,11 +13,14 @@
 // in flight while the current one is multiplied. (Four waves of 128 x 64, one per SIMD, were
 // 26-35% slower on the same shapes.)
 //
-// Results are the same K-split partial sums, in the same layout, as the weight-streaming
+// EPI_STORE gives the same K-split partial sums, in the same layout, as the weight-streaming
 // contraction's EPI_STORE (part[split][bp][N]; a row kernel adds the splits): split s covers
 // columns [s * Kd / nsplit, (s + 1) * Kd / nsplit) in 256-column chunks, and each output
 // accumulates its 32-column steps in column order, the hi product before the lo one, so the
-// two contractions give bit-identical partials for the same split.
+// two contractions give bit-identical partials for the same split. EPI_ARGMAX (one split;
+// the greedy lm_head of verification from hidden states) reduces each input row's values over
+// its W rows to a packed (value, index) key, publishes one key per input row and workgroup by
+// atomic max, and the last workgroup to arrive writes each input row's argmax.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,6 +41,7 @@ constexpr size_t kGmLdsA = (size_t)2 * kGmTM * kGmLd;       // bf16 elements, tw
 constexpr size_t kGmLdsB = (size_t)2 * 2 * kGmTN * kGmLd;   // two buffers x two planes
 size_t gm_lds_bytes() { return (kGmLdsA + kGmLdsB) * sizeof(uint16_t); }
 
+template <int EPI>
 __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* As = smem;             // [2][kGmTM][kGmLd]
@@ -141,6 +145,41 @@ __global__ __launch_bounds__(kGmThreads, 1) void gm_kernel(GmParams p) {
   }
 
   // Lane l holds W rows 4 (l / 16) + i (i < 4) of each slice for input row l % 16 of each tile.
+  if constexpr (EPI == EPI_ARGMAX) {
+    __shared__ unsigned long long kred[kGmThreads / kWave][64];  // [wave][its 64 input rows]
+    __shared__ int flag;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r0 = m0 + wm * 64 + m * 16 + (lane >> 4) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const unsigned long long ki = r0 + i < N ? pack_key(acc[m][n][i], (uint32_t)(r0 + i)) : 0ull;
+          k = ki > k ? ki : k;
+        }
+      }
+      unsigned long long o = __shfl_xor(k, 16, kWave);
+      k = o > k ? o : k;
+      o = __shfl_xor(k, 32, kWave);
+      k = o > k ? o : k;
+      if (lane < 16) kred[wave][n * 16 + lane] = k;
+    }
+    __syncthreads();
+    if (tid < kGmTN) {  // input row n0 + tid: the four waves that share its columns
+      const int g = tid >> 6, j = tid & 63;
+      unsigned long long k = 0ull;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) k = kred[q + 4 * g][j] > k ? kred[q + 4 * g][j] : k;
+      if (n0 + tid < p.B && k) publish_max_key(p.keys + n0 + tid, k);
+    }
+    // the winner reads back only keys published by publish_max_key
+    if (last_to_arrive(p.counter, gridDim.x, &flag)) {
+      for (int b = tid; b < p.B; b += kGmThreads) p.tok_out[b] = (int)key_index(take_key(p.keys + b));
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int r0 = m0 + wm * 64 + m * 16 + (lane >> 4) * 4;
@@ -175,19 +214,29 @@ int gm_split(int nrows, int ncols, int B, int num_cu, long max_part) {
 }
 
 hipError_t gm_prepare() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gm_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)gm_lds_bytes());
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gm_kernel<EPI_STORE>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)gm_lds_bytes());
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gm_kernel<EPI_ARGMAX>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)gm_lds_bytes());
+  return e;
 }
 
-hipError_t launch_gm(const GmParams& p, hipStream_t s) {
-  if (!p.w0 || !p.w1 || !p.x || !p.x_lo || !p.part || p.nrows < 1 || p.ncols < 8 ||
+hipError_t launch_gm(Epi epi, const GmParams& p, hipStream_t s) {
+  if (epi != EPI_STORE && epi != EPI_ARGMAX) return hipErrorInvalidValue;
+  if (epi == EPI_STORE ? !p.part : (p.nsplit != 1 || !p.keys || !p.counter || !p.tok_out))
+    return hipErrorInvalidValue;
+  if (!p.w0 || !p.w1 || !p.x || !p.x_lo || p.nrows < 1 || p.ncols < 8 ||
       p.ncols % 8 != 0 || p.ldx < p.ncols || p.ldx % 8 != 0 || p.B < 1 || p.bp < p.B ||
       p.seg1 < 0 || p.seg1 > p.nrows || p.nsplit < 1 || p.nsplit > kGmMaxSplit)
     return hipErrorInvalidValue;
   const int nch = (p.ncols + kGmChunk - 1) / kGmChunk;
   if (nch % p.nsplit != 0) return hipErrorInvalidValue;
   const long grid = (long)((p.nrows + kGmTM - 1) / kGmTM) * ((p.B + kGmTN - 1) / kGmTN) * p.nsplit;
-  hipLaunchKernelGGL(gm_kernel, dim3((unsigned)grid), dim3(kGmThreads), gm_lds_bytes(), s, p);
+  if (epi == EPI_ARGMAX)
+    hipLaunchKernelGGL(gm_kernel<EPI_ARGMAX>, dim3((unsigned)grid), dim3(kGmThreads), gm_lds_bytes(), s, p);
+  else
+    hipLaunchKernelGGL(gm_kernel<EPI_STORE>, dim3((unsigned)grid), dim3(kGmThreads), gm_lds_bytes(), s, p);
   return hipGetLastError();
 }
 

@@ -193,8 +193,13 @@ struct GmParams {
   const uint16_t* x_lo;
   int ldx, B;
   int nsplit;
-  float* part;  // [nsplit][bp][nrows]
+  float* part;  // [nsplit][bp][nrows] (EPI_STORE)
   int bp;       // >= B
+  // EPI_ARGMAX (nsplit == 1): argmax over the W rows of each input row, keys [B] and the
+  // counter zero on entry and left zero, tok_out [B]
+  unsigned long long* keys;
+  unsigned* counter;
+  int* tok_out;
 };
 // Splits that give at least one workgroup per CU (a divisor of the 256-column chunk count),
 // with split x B x nrows <= max_part (the room of the partial sums, in floats) unless that
@@ -202,7 +207,7 @@ struct GmParams {
 int gm_split(int nrows, int ncols, int B, int num_cu, long max_part);
 // Once per process and device before the first launch (raises the kernel's LDS limit).
 hipError_t gm_prepare();
-hipError_t launch_gm(const GmParams& p, hipStream_t s);
+hipError_t launch_gm(Epi epi, const GmParams& p, hipStream_t s);
 
 // ---- batched path (bf16 weights, 3..64 sequences): MFMA contraction + row reductions
 

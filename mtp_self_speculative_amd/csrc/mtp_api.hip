@@ -146,8 +146,9 @@ Layout make_layout(const mtp_config& c, int max_batch, int max_k, int max_cap, u
   // verification from the target's hidden states
   {
     const long rows_all = (long)max_batch * (max_k + 1);
-    // 128 rows per pass only on the packed lm_head copy
-    const int grp = packed ? kVhGroupPk : kVhGroup;
+    // 128 rows per pass on matrix-core handles (the eight-tile streaming kernel on the packed
+    // lm_head copy, else the tiled contraction on the row-major lm_head)
+    const int grp = mm_eligible(c) ? kVhGroupPk : kVhGroup;
     L.vh_rows = (int)(rows_all < grp ? rows_all : grp);
     L.vh_ld = (c.hidden + 7) / 8 * 8;
     L.vh_x = take((size_t)L.vh_rows * c.hidden * 4);
@@ -967,10 +968,12 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
                ? MTP_OK
                : MTP_ERR_HIP;
   }
+  // more than 64 rows per pass need the tiled contraction or the packed copy
+  const int group = h->gm_ok || L.pk_lm || L.vh_rows <= kMmMaxBatch ? L.vh_rows : kMmMaxBatch;
   auto run = [&]() -> hipError_t {
     hipError_t e = hipSuccess;
-    for (int r0 = 0; r0 < R && e == hipSuccess; r0 += L.vh_rows) {
-      const int rows = R - r0 < L.vh_rows ? R - r0 : L.vh_rows;
+    for (int r0 = 0; r0 < R && e == hipSuccess; r0 += group) {
+      const int rows = R - r0 < group ? R - r0 : group;
       const char* src = static_cast<const char*>(target_hidden) + (size_t)r0 * H * esz;
       if (mm_eligible(c) && rows >= kMmMinBatch) {
         RedParams r{};
@@ -979,6 +982,21 @@ mtp_status mtp_verify_hidden(mtp_handle* h, const void* target_hidden, const voi
         r.h16 = reinterpret_cast<const uint16_t*>(src);
         e = launch_red(PREP_NORM, r, rows, s);
         if (e != hipSuccess) break;
+        if (rows > kMmMaxBatch && !L.pk_lm && h->gm_ok) {
+          // Without the packed copy: the tiled contraction on the row-major lm_head, argmax
+          // epilogue. (With the copy, the eight-tile streaming kernel is faster: its
+          // persistent items balance over the CUs, while 151936 vocabulary rows make 594
+          // tiles, three rounds of 256 at 77% occupancy.)
+          GmParams g{};
+          g.w0 = g.w1 = h->w.lm_head; g.seg1 = V; g.nrows = V; g.ncols = H;
+          g.x = h->at<uint16_t>(L.vh_q); g.x_lo = h->at<uint16_t>(L.vh_q_lo); g.ldx = L.vh_ld;
+          g.B = rows; g.nsplit = 1; g.bp = rows;
+          g.keys = h->at<unsigned long long>(L.vh_keys);
+          g.counter = h->at<unsigned>(L.vh_cnt);
+          g.tok_out = tok + r0;
+          e = launch_gm(EPI_ARGMAX, g, s);
+          continue;
+        }
         MmParams m{};
         m.w0 = m.w1 = m.w2 = h->w.lm_head;
         m.packed = L.pk_lm ? reinterpret_cast<const uint16_t*>(h->ws + L.pk_lm) : nullptr;
@@ -1068,7 +1086,7 @@ static hipError_t input_side_pass(mtp_handle* h, mtp_kv* kv, const void* src, in
           g.nsplit = gm_split(N, Kd, rows, h->num_cu, (long)L.cu_part_elems);
           g.part = part; g.bp = rows;
           *ns = g.nsplit;
-          return launch_gm(g, s);
+          return launch_gm(EPI_STORE, g, s);
         }
         MmParams m{};
         m.w0 = w0; m.w1 = w1; m.w2 = w1; m.seg1 = seg1; m.seg2 = N;
@@ -1290,7 +1308,8 @@ mtp_status mtp_get_info(const mtp_handle* h, mtp_info* out) {
              mm_packed_elems(H, qd) + mm_packed_elems(2 * c.ffn, H) +
              mm_packed_elems(H, c.ffn) + mm_packed_elems(c.vocab, H));
   }
-  i.verify_hidden_group_rows = L.vh_rows;
+  i.verify_hidden_group_rows =
+      h->gm_ok || L.pk_lm || L.vh_rows <= kMmMaxBatch ? L.vh_rows : kMmMaxBatch;
   i.catchup_group_rows = L.cu_rows;
   i.matrix_core_min_batch = mm_eligible(h->cfg) ? kMmMinBatch : 0;
   i.matrix_core_max_batch = mm_eligible(h->cfg) ? kMmMaxBatch : 0;

@@ -70,8 +70,8 @@ def test_draft_without_packed_copy_matches_packed_and_oracle():
 
 
 def test_verify_hidden_without_packed_copy():
-    """5 x 4 = 20 rows: one 64-row pass on the row-major lm_head (the default handle takes
-    one 128-row pass on its copy); both agree, and agree with the oracle off near-ties."""
+    """5 x 4 = 20 rows: one pass on the row-major lm_head (the default handle reads its
+    copy); both agree, and agree with the oracle off near-ties."""
     cfg = CFG
     K = cfg.K
     inp = make_inputs(cfg)
@@ -130,9 +130,9 @@ def test_refresh_weights_after_in_place_change():
 def test_full_size_batched_draft_identical_without_packed_copy():
     """q8b-b32 shapes (H=4096, V=151936, 32 ragged sequences, K=3): the row-major
     contractions give the default handle's tokens, hidden states and top-2 logits bit for
-    bit, and verification from hidden states (64-row passes instead of one 128-row pass)
-    gives the same accepted lengths and next tokens wherever the oracle's margin clears the
-    near-tie bar."""
+    bit, and verification from hidden states (128 rows: the tiled contraction on the
+    row-major lm_head in both handles) gives the same accepted lengths and next tokens
+    wherever the oracle's margin clears the near-tie bar."""
     cfg = S.get_config("q8b-b32")
     inp = make_inputs(cfg)
     w = {k: to_dev(v, cfg.dtype) for k, v in inp.weights.items()}
