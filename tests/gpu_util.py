@@ -33,7 +33,7 @@ def cache_to_np(t, storage: str) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def make_head(cfg, inp, max_batch=None, max_k=None):
+def make_head(cfg, inp, max_batch=None, max_k=None, packed_copy=True):
     torch = torch_mod()
     from mtp_self_speculative_amd import MtpCache, MtpHead
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -42,7 +42,7 @@ def make_head(cfg, inp, max_batch=None, max_k=None):
                    head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, weights=w,
                    max_batch=max_batch or cfg.batch, max_k=max_k or max(cfg.K, 1),
                    max_capacity=inp.capacity, rope_theta=cfg.rope_theta, rms_eps=cfg.rms_eps,
-                   dtype=dt)
+                   dtype=dt, packed_copy=packed_copy)
     cache = MtpCache(to_dev(inp.k_cache, cfg.dtype), to_dev(inp.v_cache, cfg.dtype),
                      torch.from_numpy(inp.lens.astype(np.int32)).cuda(),
                      torch.from_numpy(inp.pos.astype(np.int32)).cuda())

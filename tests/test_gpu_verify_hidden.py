@@ -25,6 +25,12 @@ CASES = {
     "bf16-groups": small(name="vh4", cid=153, batch=20, K=3, hidden=512, vocab=4099),
     # bf16, 30 x 5 = 150 rows: two groups (128 + 22) of lm_head passes
     "bf16-two-groups": small(name="vh6", cid=155, batch=30, K=4, hidden=384, vocab=5003),
+    # the same two shapes on handles without the packed lm_head copy: 80 rows and the first
+    # 128 of 150 through the tiled contraction's argmax on the row-major lm_head (ragged
+    # vocabulary; 384 columns end inside a 256-column chunk), the last 22 through the
+    # weight-streaming kernel on the row-major lm_head
+    "bf16-groups-lean": small(name="vh4", cid=153, batch=20, K=3, hidden=512, vocab=4099),
+    "bf16-two-groups-lean": small(name="vh6", cid=155, batch=30, K=4, hidden=384, vocab=5003),
     # K = 0: the target's token of row 0 only
     "bf16-k0": small(name="vh5", cid=154, batch=5, K=0),
     # 3..8 rows of a handle without the packed lm_head (1-2 sequences): the pipelined GEMV
@@ -73,7 +79,11 @@ def test_verify_hidden_parity(case):
     a_o, n_o, margin = O.verify_from_hidden(cfg, th, gn, inp.weights["lm_head"], d)
     assert np.array_equal(a_o, stop)
 
-    head, _ = make_head(cfg, inp, max_batch=cfg.batch, max_k=max(K, 1))
+    lean = case.endswith("-lean")
+    head, _ = make_head(cfg, inp, max_batch=cfg.batch, max_k=max(K, 1), packed_copy=not lean)
+    if lean:
+        assert head.info()["packed_weight_bytes"] == 0
+        assert head.info()["verify_hidden_group_rows"] == min(cfg.batch * (K + 1), 128)
     thd, gnd = to_dev(th, st), to_dev(gn, st)
     dd = torch.from_numpy(d).cuda() if K else None
     for rep in range(2):  # the second call checks that keys / counters were reset
