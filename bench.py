@@ -15,7 +15,10 @@ is the Qwen3-8B-shaped head at batch 1; the same run also times the other worklo
 (B=32 ragged, the Qwen3-32B shape at 32K context, the wide B=64 head and the tiny
 fp32 head) under "workloads", each with its own throughput, HBM fraction, lm_head
 fraction and device memory; the batched ones also replay the same iterations on a
-handle without the re-laid-out weight copy ("without_packed_copy").
+handle without the re-laid-out weight copy ("without_packed_copy"). Every workload
+also replays its timed iterations from one captured HIP graph ("graph_replay": the same
+kernels without host-side launch work, checked against the recording); the headline
+value stays the eager replay.
 """
 from __future__ import annotations
 
@@ -426,6 +429,49 @@ def run_workload(name: str, args, full: bool) -> dict:
                        "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                        "algorithmic_bytes_per_launch": int(ab["lm_head"])},
            "device_memory": memory}
+
+    # The timed iterations captured once into a HIP graph (the entry points only launch
+    # kernels) and replayed: the same kernels with no host-side launch work between them.
+    # Capture runs nothing, so the state before each replay is the one after the eager
+    # warm-up; the first replay is untimed, the second is timed and checked against the
+    # recording.
+    def graph_state():
+        cache.len.copy_(len0)
+        cache.pos.copy_(pos0)
+        last = last0
+        for it in range(args.warmup):
+            last = run(it, last)
+        drafts[args.warmup:].fill_(-1)
+        acc[args.warmup:].fill_(-1)
+        torch.cuda.synchronize()
+        return last
+
+    head.set_profiling(0)
+    last_g = graph_state()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lg = last_g
+        for it in range(args.warmup, iters):
+            lg = run(it, lg)
+    torch.cuda.synchronize()
+    graph.replay()
+    graph_state()
+    t0g = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    el_graph = time.perf_counter() - t0g
+    if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
+        raise RuntimeError("the graph replay diverged from the recording pass")
+    assert head.get_error() == 0
+    del graph
+    res["graph_replay"] = {
+        "draft_steps_per_s": round(K * args.steps / el_graph, 3),
+        "ms_per_iteration": round(el_graph / args.steps * 1e3, 4),
+        "hbm_roofline_frac": round(ab["iteration"] / (el_graph / args.steps) / 1e9
+                                   / HBM_PEAK_GBS, 4),
+        "vs_eager": round(elapsed / el_graph, 4),
+        "tokens_identical": True}
+    log(f"{name}: graph replay: {res['graph_replay']}")
 
     if not full and info["packed_weight_bytes"]:
         # The same recorded iterations on a handle without the re-laid-out weight copy
