@@ -709,7 +709,8 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": lm_bytes},
     }
     for k in ("us_per_draft_step", "latency_us", "kernel_us_per_launch", "verify_from_hidden",
-              "kv_catchup", "prefill", "attention_large_cache", "sampling", "graph_replay", "device_memory"):
+              "kv_catchup", "prefill", "attention_large_cache", "sampling", "graph_replay",
+              "device_memory"):
         if k in head_res:
             out[k] = head_res[k]
     if not args.no_extra:
