@@ -432,14 +432,20 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
   return hipGetLastError();
 }
 
+// The greedy lm_head over four 16-sequence tiles in 256-row items streams half-chunk stages
+// (128 columns): the wave's two weight stages then take 64 registers instead of 128, which
+// leaves the compiler room to overlap the products with the input reads (timed against
+// full-chunk stages on the wide head's 129280 x 7168 lm_head at 64 sequences: 10% faster,
+// the same bits). The projections keep full chunks (within ±8% either way, no clear gain).
 template <int NB, bool PK, int WV, int MT>
 static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   constexpr int CK = kMmChunk;
+  constexpr int CKA = (PK && NB == 4 && WV == 2 * kMmWaves) ? kMmChunk / 2 : kMmChunk;
   const size_t lds = mm_lds_bytes(NB, CK);
   const dim3 block(WV * kWave);
   if (epi == EPI_ARGMAX)
-    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV, MT, CK>), dim3(grid), block, lds, s,
-                       p);
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_ARGMAX, 1, PK, WV, MT, CKA>), dim3(grid), block,
+                       mm_lds_bytes(NB, CKA), s, p);
   else if (epi == EPI_STORE)
     hipLaunchKernelGGL((mm_kernel<NB, EPI_STORE, 1, PK, WV, MT, CK>), dim3(grid), block, lds, s, p);
   else if constexpr (WV == kMmWaves && MT == kMmMT)
