@@ -88,12 +88,13 @@ int mm_split(int nrows, int ncols, int B, int tile_rows) {
 // B <= 32 they lose 1-30%, and with a quarter or an eighth of the grid in items (the
 // small catch-up contractions) twice the rows per workgroup cost about twice the time.
 // So: 256-row items for packed weights at 16NB >= 48 when their split gives at least
-// three quarters of num_cu items. The sampling epilogue keeps 128 rows (its random
-// blocks would spill at eight waves).
+// three quarters of num_cu items. The sampling epilogue keeps 128 rows below four tiles (its
+// random blocks would spill at eight waves); at four tiles it streams half-chunk stages,
+// which leave them room (wide head, 64 sequences: 461-487 -> 347-349 us, the same bits).
 MmPlan mm_plan(Epi epi, int nrows, int ncols, int B, bool packed, int num_cu) {
   const bool split = epi == EPI_STORE;
   MmPlan q{kMmTileRows, split ? mm_split(nrows, ncols, B, kMmTileRows) : 1, 0};
-  if (packed && epi != EPI_SAMPLE && mm_batch_pad(B) / 16 >= 3) {
+  if (packed && mm_batch_pad(B) / 16 >= (epi == EPI_SAMPLE ? 4 : 3)) {
     const int tr = 2 * kMmTileRows;
     const int s8 = split ? mm_split(nrows, ncols, B, tr) : 1;
     if (4L * ((nrows + tr - 1) / tr) * s8 >= 3L * num_cu) {
@@ -432,11 +433,12 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
   return hipGetLastError();
 }
 
-// The greedy lm_head over four 16-sequence tiles in 256-row items streams half-chunk stages
-// (128 columns): the wave's two weight stages then take 64 registers instead of 128, which
-// leaves the compiler room to overlap the products with the input reads (timed against
-// full-chunk stages on the wide head's 129280 x 7168 lm_head at 64 sequences: 10% faster,
-// the same bits). The projections keep full chunks (within ±8% either way, no clear gain).
+// The lm_head over four 16-sequence tiles in 256-row items (greedy or sampling) streams
+// half-chunk stages (128 columns): the wave's two weight stages then take 64 registers
+// instead of 128, which leaves the compiler room to overlap the products with the input
+// reads (timed against full-chunk stages on the wide head's 129280 x 7168 lm_head at 64
+// sequences: 10% faster, the same bits) and the sampling epilogue room for its random
+// blocks. The projections keep full chunks (within ±8% either way, no clear gain).
 template <int NB, bool PK, int WV, int MT>
 static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   constexpr int CK = kMmChunk;
@@ -451,6 +453,9 @@ static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   else if constexpr (WV == kMmWaves && MT == kMmMT)
     hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, NB <= 2 ? 2 : 1, PK, WV, MT, CK>), dim3(grid),
                        block, lds, s, p);
+  else if constexpr (CKA != CK)
+    hipLaunchKernelGGL((mm_kernel<NB, EPI_SAMPLE, 1, PK, WV, MT, CKA>), dim3(grid), block,
+                       mm_lds_bytes(NB, CKA), s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -495,7 +500,7 @@ hipError_t launch_mm(Epi epi, const MmParams& p, int grid, hipStream_t s) {
     return hipErrorInvalidValue;
   if (epi == EPI_STORE && !p.part) return hipErrorInvalidValue;
   if (p.tile_rows != 0 && p.tile_rows != kMmTileRows &&
-      !(p.tile_rows == 2 * kMmTileRows && p.packed && epi != EPI_SAMPLE && p.B > 32 &&
+      !(p.tile_rows == 2 * kMmTileRows && p.packed && p.B > (epi == EPI_SAMPLE ? 48 : 32) &&
         (p.B <= 16 * kMmMaxNB || epi == EPI_ARGMAX)))
     return hipErrorInvalidValue;
   static_assert(16 * kMmChunk * 2 <= kDummyBytes && kMmPackBlock * 2 <= kDummyBytes,

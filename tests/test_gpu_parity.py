@@ -84,6 +84,10 @@ CASES = {
     # last one ending inside its first 128-row block, so its second block reads the dummy
     "mm-b40-wide-items": small(name="w8lm", cid=109, hidden=256, n_q=4, n_kv=2, head_dim=64,
                                ffn=512, vocab=50000, batch=40, K=2, ctx_lo=1, ctx_hi=200),
+    # the same vocabulary at B = 64: four 16-sequence tiles on 256-row items, whose greedy
+    # lm_head streams 128-column stages
+    "mm-b64-wide-items": small(name="w8lm64", cid=110, hidden=256, n_q=4, n_kv=2, head_dim=64,
+                               ffn=512, vocab=50000, batch=64, K=2, ctx_lo=1, ctx_hi=200),
     # bf16, B = 2, a cache long enough for several attention splits (len 3000..3100)
     "small-bf16-long": small(name="long", cid=103, hidden=256, n_q=4, n_kv=4, head_dim=128,
                              ffn=512, vocab=2048, batch=2, K=3, ctx_lo=3000, ctx_hi=3100),

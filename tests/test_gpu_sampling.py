@@ -128,6 +128,10 @@ DCASES = {
     "bf16-mm-b33": (small(name="ds4", cid=183, batch=33, K=2, hidden=256, n_q=4, n_kv=2,
                           head_dim=64, ffn=512, vocab=4099, ctx_hi=64), 1.0),
     "f32-b3": (small(name="ds5", cid=184, batch=3, K=3, hidden=256, vocab=3001, dtype="f32"), 0.7),
+    # 64 sequences over a 50021-row vocabulary: the sampling lm_head on 256-row items in
+    # 128-column stages (the last item ends inside its first 128-row block)
+    "bf16-mm-b64-wide-items": (small(name="ds6", cid=185, batch=64, K=2, hidden=256, n_q=4,
+                                     n_kv=2, head_dim=64, ffn=512, vocab=50021, ctx_hi=64), 1.0),
     # full q8b head: each wave of the lm_head kernel draws noise for 64 rows at a time and
     # owns more than 64 vocabulary rows here, so the refill is exercised
     "q8b": (S.get_config("q8b"), 1.0),
