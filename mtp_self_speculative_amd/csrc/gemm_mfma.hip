@@ -139,8 +139,8 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   constexpr int LROW = CK + 8;       // bf16 per LDS row: 16-byte pad against bank conflicts
   constexpr int CPR = CK / 8;        // 16-byte column groups per input row and stage
   constexpr int HALVES = kMmChunk / CK;
-  constexpr int XPASS = BP * CPR / NT;  // 16-byte input loads per thread, plane and stage
-  static_assert(XPASS * NT == BP * CPR, "input staging must divide over the threads");
+  constexpr int XQ = BP * CPR;           // 16-byte input groups per plane and stage
+  constexpr int XPASS = (XQ + NT - 1) / NT;  // per thread (the last pass may be partial)
   extern __shared__ __align__(16) uint16_t xl[];  // [2 buffers][2 planes][BP][LROW]
   __shared__ unsigned long long kred[WV][BP];
   __shared__ uint64_t seed_s[EPI == EPI_SAMPLE ? BP : 1];  // random-stream seeds, read once
@@ -230,6 +230,7 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
 #pragma unroll
     for (int j = 0; j < XPASS; ++j) {
       const int q = tid + j * NT;
+      if (XQ % NT != 0 && q >= XQ) continue;  // past the stage's groups (its load was clamped)
       const int row = q / CPR, cp = q % CPR;
       const bool live = row < p.B && c0 + cp * 8 < Kd;
       const u32x4 z = {0u, 0u, 0u, 0u};
@@ -433,16 +434,16 @@ hipError_t launch_pack(const void* w0, const void* w1, const void* w2, int seg1,
   return hipGetLastError();
 }
 
-// The lm_head over four 16-sequence tiles in 256-row items (greedy or sampling) streams
-// half-chunk stages (128 columns): the wave's two weight stages then take 64 registers
-// instead of 128, which leaves the compiler room to overlap the products with the input
-// reads (timed against full-chunk stages on the wide head's 129280 x 7168 lm_head at 64
-// sequences: 10% faster, the same bits) and the sampling epilogue room for its random
+// The lm_head over three or four 16-sequence tiles in 256-row items (greedy, or sampling at
+// four) streams half-chunk stages (128 columns): the wave's two weight stages then take 64
+// registers instead of 128, which leaves the compiler room to overlap the products with the
+// input reads (timed against full-chunk stages on the wide head's 129280 x 7168 lm_head at
+// 64 sequences: 10% faster, the same bits) and the sampling epilogue room for its random
 // blocks. The projections keep full chunks (within ±8% either way, no clear gain).
 template <int NB, bool PK, int WV, int MT>
 static hipError_t mm_nbp(Epi epi, const MmParams& p, int grid, hipStream_t s) {
   constexpr int CK = kMmChunk;
-  constexpr int CKA = (PK && NB == 4 && WV == 2 * kMmWaves) ? kMmChunk / 2 : kMmChunk;
+  constexpr int CKA = (PK && NB >= 3 && WV == 2 * kMmWaves) ? kMmChunk / 2 : kMmChunk;
   const size_t lds = mm_lds_bytes(NB, CK);
   const dim3 block(WV * kWave);
   if (epi == EPI_ARGMAX)
