@@ -171,20 +171,25 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
   // the K-split projections at B = 32..64 1-7% slower, so they load normally.
   constexpr bool kStream = EPI != EPI_STORE || NB == 1;
   u32x4 A[MT][KS], Bf[MT][KS];
+  // The packed path's weight pointer of stage it for this lane: contiguous 1 KB per wave
+  // instruction, one base per wave; the second block of a 256-row item past the last block
+  // row reads the dummy.
+  auto wbase = [&](int it) -> const uint16_t* {
+    const bool live = it < stages;
+    const int sl0 = wave * MT;  // the wave's first 16-row slice in the item (8 per block)
+    const int brow = (item_of(it) / p.nsplit) * (TR / kMmTileRows) + sl0 / 8;
+    const bool lw = live && brow < nblk_rows;
+    const long blk = (long)brow * mm_chunks(Kd) + chunk_of(it) / HALVES;
+    return (lw ? p.packed + blk * kMmPackBlock : static_cast<const uint16_t*>(p.dummy)) +
+           (long)(sl0 % 8) * (kMmKSteps * kWave * 8) + (chunk_of(it) % HALVES) * (KS * kWave * 8) +
+           lane * 8;
+  };
   // Stages past the workgroup's last one are prefetched from the dummy region and never
   // consumed (packed: the same offsets in a 64 KB dummy block; else 16 rows of 256 bf16).
   auto wload = [&](u32x4 (&buf)[MT][KS], int it) {
     const bool live = it < stages;
-    if constexpr (PK) {  // contiguous 1 KB per wave instruction, one base per wave
-      // the second block of a 256-row item past the last block row reads the dummy
-      const int sl0 = wave * MT;  // the wave's first 16-row slice in the item (8 per block)
-      const int brow = (item_of(it) / p.nsplit) * (TR / kMmTileRows) + sl0 / 8;
-      const bool lw = live && brow < nblk_rows;
-      const long blk = (long)brow * mm_chunks(Kd) + chunk_of(it) / HALVES;
-      const uint16_t* bp = (lw ? p.packed + blk * kMmPackBlock
-                               : static_cast<const uint16_t*>(p.dummy)) +
-                           (long)(sl0 % 8) * (kMmKSteps * kWave * 8) +
-                           (chunk_of(it) % HALVES) * (KS * kWave * 8) + lane * 8;
+    if constexpr (PK) {
+      const uint16_t* bp = wbase(it);
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -271,6 +276,36 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
       }
     }
   };
+  // The same products, each k-step's registers refilled with the stage two ahead as soon as
+  // its last product is issued: a steady stream of weight loads instead of one burst per
+  // stage. Timed against consume + wload (alternating runs, caches flushed): the greedy
+  // lm_head 3% faster at 32 sequences and 2% at 64, the same bits; no better for the
+  // projections, the sampling epilogue or eight tiles, which keep the burst.
+  auto consume_reload = [&](u32x4 (&buf)[MT][KS], int it, const uint16_t* nxt) {
+    const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * LROW + (lane & 15) * LROW +
+                         (lane >> 4) * 8;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 bh = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + nb * 16 * LROW + k * 32));
+        const bf16x8 bl = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * LROW + k * 32));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const bf16x8 w = __builtin_bit_cast(bf16x8, buf[m][k]);
+          acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bh, acc[m][nb], 0, 0, 0);
+          acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bl, acc[m][nb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4* a = reinterpret_cast<const u32x4*>(nxt + (m * kMmKSteps + k) * kWave * 8);
+        buf[m][k] = kStream ? __builtin_nontemporal_load(a) : *a;
+      }
+    }
+  };
 
   const bool vec_logits =
       p.logits && (p.logits_ld & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
@@ -340,10 +375,15 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     }
   };
 
+  constexpr bool kSteady = PK && EPI == EPI_ARGMAX && NB <= kMmMaxNB;
   auto stage = [&](u32x4 (&buf)[MT][KS], int it) {
     xload(it + 1);
-    consume(buf, it);
-    wload(buf, it + 2);
+    if constexpr (kSteady) {
+      consume_reload(buf, it, wbase(it + 2));
+    } else {
+      consume(buf, it);
+      wload(buf, it + 2);
+    }
     if (it % C == C - 1) finish_item(it);
     xstore(it + 1, (it + 1) & 1);
     __syncthreads();
