@@ -255,8 +255,15 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) best[nb] = 0ull;
 
-  // Each input fragment read from LDS serves both 16-row slices of the wave.
-  auto consume = [&](u32x4 (&buf)[MT][KS], int it) {
+  // Each input fragment read from LDS serves both 16-row slices of the wave. With kSteady
+  // (the greedy lm_head on packed weights, up to four tiles) each k-step's registers are
+  // refilled from nxt, the stage two ahead, as soon as the k-step's last product is issued:
+  // a steady stream of weight loads instead of one burst per stage. Timed against the burst
+  // (alternating runs, caches flushed): the greedy lm_head 3% faster at 32 sequences and 2%
+  // at 64, the same bits; no better for the projections, the sampling epilogue or eight
+  // tiles, which keep the burst.
+  constexpr bool kSteady = PK && EPI == EPI_ARGMAX && NB <= kMmMaxNB;
+  auto consume = [&](u32x4 (&buf)[MT][KS], int it, const uint16_t* nxt) {
     const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * LROW + (lane & 15) * LROW +
                          (lane >> 4) * 8;
 #pragma unroll
@@ -274,35 +281,12 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
           acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bl, acc[m][nb], 0, 0, 0);
         }
       }
-    }
-  };
-  // The same products, each k-step's registers refilled with the stage two ahead as soon as
-  // its last product is issued: a steady stream of weight loads instead of one burst per
-  // stage. Timed against consume + wload (alternating runs, caches flushed): the greedy
-  // lm_head 3% faster at 32 sequences and 2% at 64, the same bits; no better for the
-  // projections, the sampling epilogue or eight tiles, which keep the burst.
-  auto consume_reload = [&](u32x4 (&buf)[MT][KS], int it, const uint16_t* nxt) {
-    const uint16_t* xb = xl + (long)(it & 1) * 2 * BP * LROW + (lane & 15) * LROW +
-                         (lane >> 4) * 8;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 bh = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(xb + nb * 16 * LROW + k * 32));
-        const bf16x8 bl = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(xb + (BP + nb * 16) * LROW + k * 32));
+      if constexpr (kSteady) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const bf16x8 w = __builtin_bit_cast(bf16x8, buf[m][k]);
-          acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bh, acc[m][nb], 0, 0, 0);
-          acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, bl, acc[m][nb], 0, 0, 0);
+          const u32x4* a = reinterpret_cast<const u32x4*>(nxt + (m * kMmKSteps + k) * kWave * 8);
+          buf[m][k] = kStream ? __builtin_nontemporal_load(a) : *a;
         }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const u32x4* a = reinterpret_cast<const u32x4*>(nxt + (m * kMmKSteps + k) * kWave * 8);
-        buf[m][k] = kStream ? __builtin_nontemporal_load(a) : *a;
       }
     }
   };
@@ -375,13 +359,12 @@ __global__ __launch_bounds__(WV * kWave, OCC) void mm_kernel(MmParams p) {
     }
   };
 
-  constexpr bool kSteady = PK && EPI == EPI_ARGMAX && NB <= kMmMaxNB;
   auto stage = [&](u32x4 (&buf)[MT][KS], int it) {
     xload(it + 1);
     if constexpr (kSteady) {
-      consume_reload(buf, it, wbase(it + 2));
+      consume(buf, it, wbase(it + 2));
     } else {
-      consume(buf, it);
+      consume(buf, it, nullptr);
       wload(buf, it + 2);
     }
     if (it % C == C - 1) finish_item(it);
