@@ -306,7 +306,7 @@ mtp_status mtp_kv_catchup(mtp_handle* h, mtp_kv* kv, const void* target_hidden,
  *   n_valid       [B] device int32 rows to take per sequence (0..n), or NULL for n
  * 0 <= n <= kv->capacity (n = 0 enqueues nothing), 1 <= B <= min(max_batch, kv->batch).
  * Rows run in groups, each streaming eh_proj and the K/V projections once: on bf16 heads (hidden
- * <= 8192) up to 1024 rows (at most max_batch x max_capacity), groups of more than 64 rows
+ * <= 8192) up to 2048 rows (at most max_batch x max_capacity), groups of more than 64 rows
  * on a tiled matrix-core contraction; else up to 64.
  * Device conditions: a slot outside the capacity sets MTP_DEVERR_CAPACITY (the row is
  * skipped); a token outside [0, vocab) sets MTP_DEVERR_TOKEN (row 0 of the embedding is

@@ -35,9 +35,9 @@ CASES = {
     # (the second ragged)
     "bf16-tiled-132": small(name="cu7", cid=166, batch=33, K=4, hidden=256, n_q=4, n_kv=2,
                             head_dim=64, ffn=512, vocab=3001, ctx_lo=2, ctx_hi=100),
-    # bf16, 260 x 4 = 1040 rows: a 1024-row group on the tiled contraction, then 16 rows on
+    # bf16, 260 x 8 = 2080 rows: a 2048-row group on the tiled contraction, then 32 rows on
     # the weight-streaming one (the draft before it, 260 sequences, takes the GEMV)
-    "bf16-tiled-then-streaming": small(name="cu8", cid=167, batch=260, K=4, hidden=256, n_q=4,
+    "bf16-tiled-then-streaming": small(name="cu8", cid=167, batch=260, K=8, hidden=256, n_q=4,
                                        n_kv=2, head_dim=64, ffn=512, vocab=3001, ctx_lo=2,
                                        ctx_hi=40),
     # the Qwen3-8B-shaped head at full size, B=1 K=5 and B=32 K=3

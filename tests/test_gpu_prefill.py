@@ -30,11 +30,11 @@ CASES = {
     "bf16-mm-kv-rowmajor": (small(name="pf5", cid=204, batch=4, K=3, hidden=320, n_q=5, n_kv=1,
                                   head_dim=64, ffn=640, vocab=2053, ctx_lo=0, ctx_hi=50), 11,
                             None),
-    # bf16, 2 x 530 = 1060 rows: a 1024-row group on the tiled contraction, then 36 rows on
+    # bf16, 2 x 1050 = 2100 rows: a 2048-row group on the tiled contraction, then 52 rows on
     # the weight-streaming one
     "bf16-tiled-then-streaming": (small(name="pf6", cid=206, batch=2, K=1, hidden=256, n_q=4,
                                         n_kv=2, head_dim=64, ffn=512, vocab=2053, ctx_lo=0,
-                                        ctx_hi=20), 530, [530, 530]),
+                                        ctx_hi=20), 1050, [1050, 1050]),
 }
 
 
@@ -84,7 +84,7 @@ def test_prefill_parity(case):
 
 def test_prefill_q8b_4096_token_prompt():
     """The Qwen3-8B-shaped head at full size: a 4096-token prompt into an empty cache
-    (four groups of 1024 rows on the tiled contraction), every slot against the oracle."""
+    (two groups of 2048 rows on the tiled contraction), every slot against the oracle."""
     cfg = S.get_config("q8b").with_(ctx_lo=0, ctx_hi=None)
     n = 4096
     _check(cfg, *_run(cfg, n, None, n + 64))
@@ -92,7 +92,7 @@ def test_prefill_q8b_4096_token_prompt():
 
 def test_prefill_q8b_b32_ragged_prompts():
     """The batched workload's shape: 32 prompts of ragged lengths (1..300 rows) in one call
-    (9600 candidate rows: nine 1024-row groups and one of 384 on the tiled contraction)."""
+    (9600 candidate rows: four 2048-row groups and one of 1408 on the tiled contraction)."""
     cfg = S.get_config("q8b-b32").with_(ctx_lo=0, ctx_hi=None)
     n = 300
     nv = [int(x) for x in np.random.default_rng(5).integers(1, n + 1, size=cfg.batch)]
