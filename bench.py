@@ -672,7 +672,7 @@ def main() -> int:
         copy_calibration()
         return 0
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark measures one GPU; --gpus must be 1 "
                                    "(the path shards by sequence with no exchange step)"}))
         return 2
 
