@@ -144,3 +144,55 @@ def test_sampling_iterations_replay_from_a_graph():
         assert head.get_error() == 0
         assert _same(_state(cache, drafts, acc, nxt, dlog), eager), rep
     head.close()
+
+
+@pytest.mark.parametrize("case", ["bf16-b1", "bf16-b5"])
+def test_prefill_hidden_verification_and_catchup_replay_from_a_graph(case):
+    """Prompt prefill, then iterations of draft, verification from the target's hidden
+    states and exact cache catch-up, all captured: every replay matches the eager run."""
+    cfg = CASES[case]
+    K, B, n = cfg.K, cfg.batch, 70
+    cap = int(S.cache_lengths(cfg).max()) + n + (ITERS + 2) * K + 8
+    inp = S.make_inputs(cfg, capacity=cap)
+    head, cache = make_head(cfg, inp)
+    dev = torch.device("cuda:0")
+    hidden = torch.stack([to_dev(S.hidden_states(cfg, it), cfg.dtype) for it in range(ITERS)])
+    th = torch.stack([to_dev(S.target_hidden(cfg, K, it), cfg.dtype) for it in range(ITERS)])
+    gn = to_dev(S.target_norm(cfg), cfg.dtype)
+    ph = to_dev(S.prefill_hidden(cfg, n), cfg.dtype)
+    pt = torch.from_numpy(S.prefill_tokens(cfg, n)).to(dev)
+    last0 = torch.from_numpy(inp.last_tokens.astype(np.int32)).to(dev)
+    drafts = torch.zeros((ITERS, B, K), dtype=torch.int32, device=dev)
+    acc = torch.zeros((ITERS, B), dtype=torch.int32, device=dev)
+    nxt = torch.zeros((ITERS, B), dtype=torch.int32, device=dev)
+    saved = (cache.k.clone(), cache.v.clone(), cache.len.clone(), cache.pos.clone())
+
+    def chain():
+        head.prefill(cache, ph, pt)
+        last = last0
+        for it in range(ITERS):
+            head.draft(hidden[it], last, cache, K, out=drafts[it])
+            head.verify_hidden(th[it], gn, drafts[it], acc[it], nxt[it])
+            head.catchup(cache, th[it], drafts[it], acc[it])
+            last = nxt[it]
+
+    chain()
+    torch.cuda.synchronize()
+    assert head.get_error() == 0
+    eager = _state(cache, drafts, acc, nxt)
+    _restore(cache, saved)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _restore(cache, saved)
+        for t in (drafts, acc, nxt):
+            t.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert head.get_error() == 0
+        assert _same(_state(cache, drafts, acc, nxt), eager), (case, rep)
+    head.close()
