@@ -446,31 +446,37 @@ def run_workload(name: str, args, full: bool) -> dict:
         torch.cuda.synchronize()
         return last
 
-    head.set_profiling(0)
-    last_g = graph_state()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        lg = last_g
-        for it in range(args.warmup, iters):
-            lg = run(it, lg)
-    torch.cuda.synchronize()
-    graph.replay()
-    graph_state()
-    t0g = time.perf_counter()
-    graph.replay()
-    torch.cuda.synchronize()
-    el_graph = time.perf_counter() - t0g
-    if not (torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)):
-        raise RuntimeError("the graph replay diverged from the recording pass")
-    assert head.get_error() == 0
-    del graph
-    res["graph_replay"] = {
-        "draft_steps_per_s": round(K * args.steps / el_graph, 3),
-        "ms_per_iteration": round(el_graph / args.steps * 1e3, 4),
-        "hbm_roofline_frac": round(ab["iteration"] / (el_graph / args.steps) / 1e9
-                                   / HBM_PEAK_GBS, 4),
-        "vs_eager": round(elapsed / el_graph, 4),
-        "tokens_identical": True}
+    def graph_pass() -> dict:
+        head.set_profiling(0)
+        last_g = graph_state()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            lg = last_g
+            for it in range(args.warmup, iters):
+                lg = run(it, lg)
+        torch.cuda.synchronize()
+        graph.replay()
+        graph_state()
+        t0g = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        el_graph = time.perf_counter() - t0g
+        same = torch.equal(drafts, rec_drafts) and torch.equal(acc, rec_acc)
+        assert head.get_error() == 0
+        del graph
+        if not same:
+            return {"error": "the graph replay diverged from the recording pass"}
+        return {"draft_steps_per_s": round(K * args.steps / el_graph, 3),
+                "ms_per_iteration": round(el_graph / args.steps * 1e3, 4),
+                "hbm_roofline_frac": round(ab["iteration"] / (el_graph / args.steps) / 1e9
+                                           / HBM_PEAK_GBS, 4),
+                "vs_eager": round(elapsed / el_graph, 4),
+                "tokens_identical": True}
+
+    try:
+        res["graph_replay"] = graph_pass()
+    except RuntimeError as e:  # a capture the runtime refuses: reported, the eager line stands
+        res["graph_replay"] = {"error": str(e)[:200]}
     log(f"{name}: graph replay: {res['graph_replay']}")
 
     if not full and info["packed_weight_bytes"]:
