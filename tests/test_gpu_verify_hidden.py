@@ -43,6 +43,13 @@ CASES = {
     # 2 x 4 rows too wide for the LDS of that GEMV (8 x 8192 floats): the matrix-core route
     "bf16-rows8-wide": small(name="vr9", cid=171, batch=2, K=3, hidden=8192, n_q=8, n_kv=2,
                              ffn=512, vocab=2053),
+    # 16 x 4 = 64 and 12 x 4 = 48 rows over a 50021-row vocabulary: the lm_head pass on
+    # 256-row items in 128-column stages (four and three 16-sequence tiles; the input
+    # staging of three tiles ends in a partial pass)
+    "bf16-rows64-wide-items": small(name="vw64", cid=186, batch=16, K=3, hidden=256, n_q=4,
+                                    n_kv=2, head_dim=64, ffn=512, vocab=50021, ctx_hi=64),
+    "bf16-rows48-wide-items": small(name="vw48", cid=187, batch=12, K=3, hidden=256, n_q=4,
+                                    n_kv=2, head_dim=64, ffn=512, vocab=50021, ctx_hi=64),
     # full Qwen3-8B-shaped head (H=4096, V=151936), one sequence, K=5
     "q8b": S.get_config("q8b"),
     # same head, 32 sequences, K=3: 128 rows
