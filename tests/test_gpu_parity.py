@@ -88,6 +88,11 @@ CASES = {
     # lm_head streams 128-column stages
     "mm-b64-wide-items": small(name="w8lm64", cid=110, hidden=256, n_q=4, n_kv=2, head_dim=64,
                                ffn=512, vocab=50000, batch=64, K=2, ctx_lo=1, ctx_hi=200),
+    # the same with H = 320: the second 256-column chunk ends inside its first half, so one
+    # 128-column stage of every item lies wholly past the row end
+    "mm-b64-wide-items-ragged-h": small(name="w8lm64r", cid=111, hidden=320, n_q=5, n_kv=1,
+                                        head_dim=64, ffn=640, vocab=50000, batch=64, K=2,
+                                        ctx_lo=1, ctx_hi=150),
     # bf16, B = 2, a cache long enough for several attention splits (len 3000..3100)
     "small-bf16-long": small(name="long", cid=103, hidden=256, n_q=4, n_kv=4, head_dim=128,
                              ffn=512, vocab=2048, batch=2, K=3, ctx_lo=3000, ctx_hi=3100),
