@@ -754,20 +754,44 @@ __global__ void draft_setup_kernel(float* tab, const int* pos, int B, int K, int
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (cp.chunk_out && blockIdx.x == 0) {  // the call's attention chunk, from the lengths
     __shared__ int wmax[256 / kWave];
+    __shared__ long wsum[256 / kWave];
     int m = 0;
-    for (int b = threadIdx.x; b < B; b += blockDim.x) m = max(m, cp.len[b]);
+    long sum = 0;  // sum of T_b (balance rule only)
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+      m = max(m, cp.len[b]);
+      sum += min((long)cp.len[b] + K, (long)cp.capacity);
+    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    for (int o = 32; o >= 1; o >>= 1) {
+      m = max(m, __shfl_xor(m, o, kWave));
+      sum += __shfl_xor(sum, o, kWave);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      wmax[threadIdx.x >> 6] = m;
+      wsum[threadIdx.x >> 6] = sum;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-      for (int w = 1; w < (int)blockDim.x / kWave; ++w) m = max(m, wmax[w]);
+      for (int w = 1; w < (int)blockDim.x / kWave; ++w) {
+        m = max(m, wmax[w]);
+        sum += wsum[w];
+      }
       long T = (long)m + K;
       if (T > cp.capacity) T = cp.capacity;
-      const long per = (T + cp.nsplit - 1) / cp.nsplit;
-      long ch = (per + cp.q - 1) / cp.q * cp.q;
+      long ch;
+      if (cp.balance && T > 0 && sum > 0) {
+        const double r = (double)sum / ((double)B * (double)T);  // mean T / max T
+        const double S = (double)sum * cp.n_kv / cp.num_cu * r * r;
+        long n = (long)((double)T / S + 0.5);
+        if (n < 1) n = 1;
+        if (n > cp.nsplit) n = cp.nsplit;
+        ch = ((T + n - 1) / n + cp.q - 1) / cp.q * cp.q;
+      } else {
+        const long per = (T + cp.nsplit - 1) / cp.nsplit;
+        ch = (per + cp.q - 1) / cp.q * cp.q;
+        if (ch > cp.max_chunk) ch = cp.max_chunk;
+      }
       if (ch < cp.q) ch = cp.q;
-      if (ch > cp.max_chunk) ch = cp.max_chunk;
       cp.chunk_out[0] = (int)ch;
     }
   }

@@ -99,13 +99,20 @@ hipError_t launch_gemv_pipe(int wdtype, Pro pro, Epi epi, const GemvParams& p, i
 // tab[k][b][d/2..d) = sin of (pos[b] + k) * theta^(-2i/d), evaluated in fp64 and rounded
 // to fp32) and hidden [B, H] (weight dtype) widened to fp32 into hf.
 // With kseq (per-sequence step counts) it also sets `err_bit` for a count outside [0, K].
-// With chunk_out it writes the call's attention chunk: the positions the longest sequence
-// attends at the call's last step, min(max_b len[b] + K, capacity), spread over nsplit
-// splits and rounded up to a multiple of q, at most max_chunk.
+// With chunk_out it writes the call's attention chunk. T_b = min(len[b] + K, capacity) is
+// what sequence b attends at the call's last step. Without `balance` the longest T_b is
+// spread over nsplit splits, rounded up to a multiple of q, at most max_chunk. With
+// `balance` (bf16 cache, many items) the longest T_b is cut into n equal splits,
+// 1 <= n <= nsplit, with n = round(max T / S) and S = (sum_b T_b * n_kv / num_cu) *
+// (mean T / max T)^2, rounded up to a multiple of q (max_chunk does not apply): one item
+// per CU when the lengths are equal, smaller items for the longest-first order to balance
+// when they are not.
 struct ChunkPlan {
   const int* len;
   int capacity, nsplit, q, max_chunk;
   int* chunk_out;
+  int balance = 0;  // the rule for many items (bf16 cache only)
+  int n_kv = 0, num_cu = 0;
 };
 hipError_t launch_draft_setup(int dtype, float* tab, const int* pos, int B, int K, int d,
                               float theta, const void* hidden, float* hf, int H, const int* kseq,
@@ -126,7 +133,8 @@ struct AttnParams {
   int chunk;  // positions per workgroup (multiple of attn_chunk_quantum())
   int nsplit;
   // When set, the call's chunk as the set-up kernel computed it from the lengths on the
-  // device (used instead of `chunk`; never larger).
+  // device (used instead of `chunk`; never larger for the fp32 cache, whose kernel sizes
+  // its LDS from `chunk`; at most chunk * nsplit covers what a sequence attends either way).
   const int* chunk_dev;
   const float* rope;  // [B, d]: cos then sin of the step's position
   float scale;

@@ -722,12 +722,33 @@ static mtp_status draft_impl(mtp_handle* h, const void* hidden, const int32_t* l
   if (chunk > attn_max_chunk(c.dtype)) chunk = attn_max_chunk(c.dtype);
   const int min_chunk = (kv->capacity + kMaxSplits - 1) / kMaxSplits;
   if (chunk < min_chunk) chunk = (min_chunk + q - 1) / q * q;
-  const int nsplit = (kv->capacity + chunk - 1) / chunk;
+  int nsplit = (kv->capacity + chunk - 1) / chunk;
+  // With more items than the chip runs at once (bf16 cache), the grid gets eight times as
+  // many splits as one item per CU would need, and the set-up kernel picks how many of
+  // them each sequence uses from the lengths (the balance rule of ChunkPlan). Measured on
+  // MI355X (attention + merge): 64 sequences of 4096 slots 182 -> 173 us (512 items of
+  // 4097 positions instead of 1536 of 1408), 32 ragged sequences of 1109-7733 slots
+  // 101 -> 95-97 us (splits of 1152-1536 instead of 2048); 8 sequences of 32768 slots
+  // 173 -> 168 us (4 splits of 8320). Item counts between one and two per CU are avoided:
+  // 320 items took 227 us there, the CUs holding two being the bottleneck.
+  const bool balance = c.dtype != 0 && (long)nsplit * nkv * B > 2L * h->num_cu;
+  if (balance) {
+    const long want8 = ((long)kv->capacity * B * nkv + 8L * h->num_cu - 1) / (8L * h->num_cu);
+    int ch = (int)((want8 + q - 1) / q * q);
+    if (ch < q) ch = q;
+    if (ch > attn_max_chunk(c.dtype)) ch = attn_max_chunk(c.dtype);
+    if (ch < min_chunk) ch = (min_chunk + q - 1) / q * q;
+    chunk = ch;
+    nsplit = (kv->capacity + chunk - 1) / chunk;
+  }
 
   // The grid has nsplit splits per (kv head, sequence), sized for the capacity; the chunk
   // itself is chosen on the device from the lengths, so a cache much larger than its
   // contents still spreads the attended positions over every split.
-  const ChunkPlan cp{kv->len, kv->capacity, nsplit, q, chunk, h->at<int>(L.attn_chunk)};
+  ChunkPlan cp{kv->len, kv->capacity, nsplit, q, chunk, h->at<int>(L.attn_chunk)};
+  cp.balance = balance ? 1 : 0;
+  cp.n_kv = nkv;
+  cp.num_cu = h->num_cu;
   if (launch_draft_setup(c.dtype, h->at<float>(L.rope), kv->pos, B, K, d, c.rope_theta, hidden,
                          hb, H, kseq, MTP_DEVERR_COUNT, err, cp, s) != hipSuccess)
     return MTP_ERR_HIP;
