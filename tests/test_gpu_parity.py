@@ -326,6 +326,30 @@ def test_q8b_cache_much_larger_than_its_contents():
     check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
 
 
+@pytest.mark.parametrize("kind", ["one-long", "equal"])
+def test_attention_chunks_from_the_length_spread(kind):
+    """Many attention items on a bf16 cache, where each call's chunk comes from the sum and
+    the spread of the lengths: one sequence of 3000 positions among 47 of 1-20 (its split
+    count capped by the grid's five splits), and 80 equal lengths of 1000 (one item per kv
+    head and sequence, a chunk longer than the grid was sized with). Both match the oracle."""
+    B, L = (48, 3000) if kind == "one-long" else (80, 1000)
+    cfg = small(name="spread-" + kind, cid=230 if kind == "one-long" else 231, hidden=256,
+                n_q=16, n_kv=8, head_dim=64, ffn=512, vocab=2048, batch=B, K=2, ctx_lo=1,
+                ctx_hi=20)
+    inp = S.make_inputs(cfg, capacity=L + cfg.K + 7)
+    if kind == "one-long":
+        inp.lens[:] = 1 + (np.arange(B) * 7) % 20
+        inp.lens[0] = L
+    else:
+        inp.lens[:] = L
+    inp.pos[:] = inp.lens
+    g = run_draft(cfg, inp, cfg.K)
+    r = oracle_forced(cfg, inp, cfg.K, g["tokens"])
+    n = compare_draft(cfg, r, g["tokens"], g["hidden"], g["top2"], g["logits"])
+    assert n >= 0.5 * cfg.K * cfg.batch, f"only {n} tokens above the near-tie margin"
+    check_cache(cfg, inp, g, r, cfg.K, cfg.batch)
+
+
 @pytest.mark.parametrize("name", ["q8b-b32", "q32b", "wide"])
 def test_batched_full_size_parity(name):
     """The batched workloads at their real sizes, in the launch configuration the
