@@ -327,6 +327,7 @@ def run_workload(name: str, args, full: bool) -> dict:
     cfg = S.get_config(name)
     B, K = cfg.batch, cfg.K
     iters = args.warmup + args.steps
+    hot = args.hot_only
     lens0 = S.cache_lengths(cfg)
     cap = int(lens0.max()) + (iters + 2) * K + 8
     t0 = time.time()
@@ -474,12 +475,13 @@ def run_workload(name: str, args, full: bool) -> dict:
                 "tokens_identical": True}
 
     try:
-        res["graph_replay"] = graph_pass()
+        if not hot:
+            res["graph_replay"] = graph_pass()
     except RuntimeError as e:  # a capture the runtime refuses: reported, the eager line stands
         res["graph_replay"] = {"error": str(e)[:200]}
-    log(f"{name}: graph replay: {res['graph_replay']}")
+    log(f"{name}: graph replay: {res.get('graph_replay', 'not run')}")
 
-    if not full and info["packed_weight_bytes"]:
+    if not full and info["packed_weight_bytes"] and not hot:
         # The same recorded iterations on a handle without the re-laid-out weight copy
         # (MTP_CREATE_NO_PACKED_COPY): the trade of workspace for speed, and a check that
         # the row-major path reproduces the recorded tokens bit for bit.
@@ -528,7 +530,7 @@ def run_workload(name: str, args, full: bool) -> dict:
         log(f"{name}: without the packed copy: {res['without_packed_copy']}")
         lean.close()
 
-    if full:
+    if full and not hot:
         # Per-call latency: HIP events (torch's current stream, which the library runs on)
         # bracket each ABI call of the same replay; median and 10th / 90th percentiles.
         cache.len.copy_(len0)
@@ -567,7 +569,10 @@ def run_workload(name: str, args, full: bool) -> dict:
             log(f"{name}: per-kernel us/launch: {res['kernel_us_per_launch']}")
         res["_lm_head_prof"] = (lm_avg_s, lm_n, int(ab["lm_head"]), lm_gbs)
 
-    if cfg.dtype == "bf16":
+    if full:
+        res.setdefault("_lm_head_prof", (lm_avg_s, lm_n, int(ab["lm_head"]), lm_gbs))
+
+    if cfg.dtype == "bf16" and not hot:
         # Verification from the target's hidden states (the alternative to mtp_verify that
         # never materialises target logits): one call per recorded iteration's drafts.
         th = up(S.target_hidden(cfg, K))
@@ -610,7 +615,7 @@ def run_workload(name: str, args, full: bool) -> dict:
         assert head.get_error() == 0
         log(f"{name}: exact cache catch-up: {res['kv_catchup']['us_per_call']} us per call")
 
-    if full and cfg.dtype == "bf16":
+    if full and cfg.dtype == "bf16" and not hot:
         # Prompt prefill: a 4096-token prompt per sequence into an emptied cache.
         n = min(4096, cap)
         ph = up(S.prefill_hidden(cfg.with_(batch=1), n)).expand(B, n, cfg.hidden).contiguous()
@@ -645,11 +650,12 @@ def run_workload(name: str, args, full: bool) -> dict:
         log(f"{name}: prefill of {n} prompt tokens: {pf_us:.1f} us")
         del ph, pt
 
-    if full and name == "q8b":
+    if full and name == "q8b" and not hot:
         res["attention_large_cache"] = large_cache_probe(args, cfg, w, head, cache, hidden,
                                                          last0, len0, pos0)
-    if full:
+    if full and not hot:
         res["sampling"] = sampling_pass(args, cfg, head, cache, hidden, last0, len0, pos0, up)
+    if full:
         res["_inp"] = inp
     head.close()
     del w, cache, hidden, logits
@@ -671,6 +677,10 @@ def main() -> int:
                     help="time only the headline workload (not the other workloads)")
     ap.add_argument("--breakdown", action="store_true",
                     help="extra untimed pass with HIP events around every kernel class")
+    ap.add_argument("--hot-only", action="store_true",
+                    help="only the timed draft / verify / rollback iterations and the lm_head "
+                         "events (no graph, lean-handle, verification-from-hidden, catch-up, "
+                         "prefill, large-cache or sampling passes), for clean kernel traces")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (counter calibration)")
     args = ap.parse_args()
